@@ -1,0 +1,160 @@
+"""CPU oracle: the gated residual add and the weightless-RMSNorm modulation,
+written as plain binary32 loops with one final bf16 round-to-nearest-even.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` import this package. The product path
+never does, and this package never imports the product.
+
+Arrays are numpy ``uint16`` holding bf16 bit patterns, row-major contiguous.
+The arithmetic and its sources are documented in ``oracle.c``; this module
+only marshals arguments through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIBRARY, build_oracle
+
+GATE_FULL = 0
+GATE_BCAST = 1
+
+RMS_PINNED = 0
+RMS_SEQUENTIAL = 1
+RMS_F64 = 2
+
+_LIB = None
+
+
+def _load():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIBRARY):
+        build_oracle()
+    lib = ctypes.CDLL(LIBRARY)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_gate_add.argtypes = [p, p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gate_add.restype = None
+    lib.oracle_rms_modulate.argtypes = [
+        p, p, p, ctypes.c_float, p, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_rms_modulate.restype = ctypes.c_int
+    lib.oracle_rms_norm.argtypes = [
+        p, ctypes.c_float, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_rms_norm.restype = ctypes.c_int
+    lib.oracle_rms_factors.argtypes = [
+        p, p, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int]
+    lib.oracle_rms_factors.restype = ctypes.c_int
+    lib.oracle_bf16_from_f32.argtypes = [p, p, i64]
+    lib.oracle_bf16_from_f32.restype = None
+    lib.oracle_f32_from_bf16.argtypes = [p, p, i64]
+    lib.oracle_f32_from_bf16.restype = None
+    lib.oracle_contraction_probe.argtypes = []
+    lib.oracle_contraction_probe.restype = ctypes.c_float
+    _LIB = lib
+    return lib
+
+
+def _bits(a, name):
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name}: expected uint16 bf16 bit patterns, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError(f"{name}: must be C-contiguous")
+    return a
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def gate_add(x, u, g, gate_mode, out=None):
+    """out = bf16_rne(x + u*g) (binary32 mul, then add). x, u: [B, L, D];
+    g: [B, L, D] (GATE_FULL) or [B, 1, D] (GATE_BCAST). ``out`` may be ``x``."""
+    x, u, g = _bits(x, "x"), _bits(u, "u"), _bits(g, "g")
+    if x.ndim != 3 or u.shape != x.shape:
+        raise ValueError("x and u must share one [B, L, D] shape")
+    B, L, D = x.shape
+    want = x.shape if gate_mode == GATE_FULL else (B, 1, D)
+    if gate_mode not in (GATE_FULL, GATE_BCAST) or g.shape != want:
+        raise ValueError(f"gate shape {g.shape} does not fit mode {gate_mode}")
+    if out is None:
+        out = np.empty_like(x)
+    out = _bits(out, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must be [B, L, D]")
+    _load().oracle_gate_add(_ptr(x), _ptr(u), _ptr(g), _ptr(out), B, L, D,
+                            gate_mode)
+    return out
+
+
+def rms_modulate(x, scale, shift, eps, out=None, variant=RMS_PINNED,
+                 partials=64):
+    """out = bf16_rne(rms_norm(x, eps) * (1 + scale) + shift), scale and shift
+    [B, 1, D]. ``variant`` selects the sum of squares: the pinned P-partial
+    order (default, P = ``partials``), a sequential binary32 sum, or binary64."""
+    x = _bits(x, "x")
+    scale, shift = _bits(scale, "scale"), _bits(shift, "shift")
+    if x.ndim != 3:
+        raise ValueError("x must be [B, L, D]")
+    B, L, D = x.shape
+    if scale.shape != (B, 1, D) or shift.shape != (B, 1, D):
+        raise ValueError("scale and shift must be [B, 1, D]")
+    if out is None:
+        out = np.empty_like(x)
+    out = _bits(out, "out")
+    rc = _load().oracle_rms_modulate(_ptr(x), _ptr(scale), _ptr(shift),
+                                     float(eps), _ptr(out), B, L, D, variant,
+                                     partials)
+    if rc:
+        raise ValueError("oracle_rms_modulate: D must be a multiple of 8 and "
+                         "partials a power of two <= 256")
+    return out
+
+
+def rms_norm(x, eps, partials=64):
+    """Weightless RMSNorm: bf16_rne(x * r) with the pinned factor r."""
+    x = _bits(x, "x")
+    B, L, D = x.shape
+    out = np.empty_like(x)
+    rc = _load().oracle_rms_norm(_ptr(x), float(eps), _ptr(out), B, L, D,
+                                 partials)
+    if rc:
+        raise ValueError("oracle_rms_norm: bad D or partials")
+    return out
+
+
+def rms_factors(x, eps, variant=RMS_PINNED, partials=64):
+    """Per-row binary32 factor r = 1/sqrt(mean(x^2) + eps), shape [B, L]."""
+    x = _bits(x, "x")
+    B, L, D = x.shape
+    f = np.empty((B, L), dtype=np.float32)
+    rc = _load().oracle_rms_factors(_ptr(x), _ptr(f), B, L, D, float(eps),
+                                    variant, partials)
+    if rc:
+        raise ValueError("oracle_rms_factors: bad D or partials")
+    return f
+
+
+def bf16_from_f32(a):
+    """The oracle's own binary32 -> bf16 round-to-nearest-even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_bf16_from_f32(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def f32_from_bf16(a):
+    """The oracle's own bf16 -> binary32 widening."""
+    a = _bits(np.ascontiguousarray(a), "a")
+    out = np.empty(a.shape, dtype=np.float32)
+    _load().oracle_f32_from_bf16(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def contraction_probe():
+    """0.0 when the oracle build does not fuse multiply-add, 2**-24 if it does."""
+    return float(_load().oracle_contraction_probe())

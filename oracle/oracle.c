@@ -1,0 +1,286 @@
+/*
+ * CPU oracle for the gated residual add and the weightless-RMSNorm adaLN
+ * modulation of LTX-2-style video diffusion transformer blocks.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the bench's CPU
+ * baseline leg may load this library. The product path (the HIP library and
+ * its Python binding) never links, loads or calls it, and this file shares no
+ * code, header or constant with that path; even the bf16 helpers are written
+ * here a second time.
+ *
+ * Sources:
+ *   - "[KDA-Pilot] Add diffusion residual-gate CUDA fast path for LTX2"
+ *     (sglang PR #29361), section "Motivation": the residual-gate update adds
+ *     update * gate to hidden_states over contiguous [B, L, D] tensors, the
+ *     gate being either a full [B, L, D] tensor or a [B, 1, D] row broadcast
+ *     over L.
+ *   - prhub summary of sglang PR #34172 ("LTX-2 quality=high fused
+ *     RMSNorm+modulate"), sections "功能与动机" and "关键源码片段": the adaLN
+ *     modulation is rms_norm(x, eps) * (1 + scale) + shift with a weightless
+ *     RMSNorm (RMSNormNoWeight), eps = 1e-6 in the unit test, and the fused
+ *     kernel is allowed to differ from eager by at most one bf16 ULP
+ *     ("风险与影响", item 1).
+ *
+ * Arithmetic (the reading this oracle fixes, since the pages give only the
+ * torch expression): every step is IEEE binary32 with round-to-nearest-even,
+ * no fused multiply-add, no flush of subnormals, and exactly one rounding to
+ * bf16 (round-to-nearest-even) at the end. The multi-step order is spelled
+ * out at each function. Build with -ffp-contract=off and without
+ * -ffast-math / -march=native (see build.py).
+ *
+ * Data: bf16 values travel as their 16-bit patterns (uint16_t), row-major
+ * contiguous [B, L, D]; row (b, l) starts at element (b*L + l)*D and a
+ * broadcast row of batch b starts at b*D.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_GATE_FULL 0
+#define ORACLE_GATE_BCAST 1
+
+/* ---- bf16 <-> binary32, from the formats' definitions ------------------ */
+
+/* bf16 is the upper half of a binary32 pattern, so widening is exact. */
+static float widen(uint16_t h)
+{
+    uint32_t w = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+/*
+ * binary32 -> bf16, round to nearest, ties to even. Dropping the low 16 bits
+ * after adding 0x7FFF plus the lowest kept bit rounds up exactly when the
+ * dropped part is above half, or equal to half with an odd kept part; a carry
+ * out of the significand correctly bumps the exponent (up to infinity).
+ * NaN must not take that route (0x7F800001 would become infinity): a NaN
+ * keeps its sign and upper payload and is forced quiet.
+ */
+static uint16_t narrow_rne(float f)
+{
+    uint32_t w;
+    memcpy(&w, &f, sizeof w);
+    if ((w & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((w >> 16) | 0x0040u);
+    w += 0x7FFFu + ((w >> 16) & 1u);
+    return (uint16_t)(w >> 16);
+}
+
+/* Exported so tests can pin the rounding routine on its own. */
+void oracle_bf16_from_f32(const float* src, uint16_t* dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = narrow_rne(src[i]);
+}
+
+void oracle_f32_from_bf16(const uint16_t* src, float* dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = widen(src[i]);
+}
+
+/* ---- gated residual add -------------------------------------------------
+ *
+ * out = x + u * g over [B, L, D] (residual-gate page, "Motivation"); with
+ * gate_mode == ORACLE_GATE_BCAST the gate is [B, 1, D] and batch b uses gate
+ * row b for every l. Per element:
+ *     p = u * g        (binary32; exact for two bf16 operands unless the
+ *                       product is subnormal or overflows)
+ *     s = x + p        (binary32, one rounding)
+ *     out = bf16_rne(s)
+ * out may be x, u or (full mode) g: each element is read before it is
+ * written and no element depends on another.
+ */
+void oracle_gate_add(const uint16_t* x, const uint16_t* u, const uint16_t* g,
+                     uint16_t* out, int64_t B, int64_t L, int64_t D,
+                     int gate_mode)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t l = 0; l < L; ++l) {
+            const int64_t row = (b * L + l) * D;
+            for (int64_t d = 0; d < D; ++d) {
+                const int64_t i = row + d;
+                const uint16_t gi =
+                    (gate_mode == ORACLE_GATE_FULL) ? g[i] : g[b * D + d];
+                const float p = widen(u[i]) * widen(gi);
+                const float s = widen(x[i]) + p;
+                out[i] = narrow_rne(s);
+            }
+        }
+    }
+}
+
+/* ---- RMS factor ----------------------------------------------------------
+ *
+ * r = 1 / sqrt(mean(x^2) + eps) for one row of D elements (weightless
+ * RMSNorm; eps inside the square root as torch's rms_norm places it).
+ *
+ * The pages fix the sum only up to "at most one bf16 ULP" of eager, and a
+ * plain sequential sum cannot meet that bound against any other order at
+ * cancellation points of the modulation. The oracle therefore fixes one
+ * order, with P partial sums (P a power of two, 64 by default, at most 256):
+ *   - the row is cut into groups of 8 consecutive elements, group k holding
+ *     elements 8k .. 8k+7;
+ *   - group k goes to partial k mod P; partials start at +0 and take their
+ *     groups in increasing k, and inside a group the 8 squares in increasing
+ *     element order, each as part = part + (x*x) with two roundings;
+ *   - the P partials are then combined pairwise by index distance
+ *     m = 1, 2, 4, ..., P/2: every partial j becomes part[j] + part[j^m]
+ *     (all from the previous level), so after the last level every slot
+ *     holds the same sum ss;
+ *   - ms = ss / D, t = ms + eps, q = sqrt(t), r = 1 / q, each one IEEE
+ *     binary32 operation.
+ * D must be a multiple of 8.
+ */
+static float rms_factor_pinned(const uint16_t* row, int64_t D, float eps,
+                               int P)
+{
+    float part[256];
+    float next[256];
+    for (int j = 0; j < P; ++j)
+        part[j] = 0.0f;
+    const int64_t groups = D / 8;
+    for (int64_t k = 0; k < groups; ++k) {
+        const int j = (int)(k % P);
+        for (int e = 0; e < 8; ++e) {
+            const float v = widen(row[8 * k + e]);
+            const float sq = v * v;
+            part[j] = part[j] + sq;
+        }
+    }
+    for (int m = 1; m < P; m <<= 1) {
+        for (int j = 0; j < P; ++j)
+            next[j] = part[j] + part[j ^ m];
+        for (int j = 0; j < P; ++j)
+            part[j] = next[j];
+    }
+    const float ss = part[0];
+    const float ms = ss / (float)D;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    return 1.0f / q;
+}
+
+/* Diagnostic: the same factor with a plain left-to-right binary32 sum. */
+static float rms_factor_sequential(const uint16_t* row, int64_t D, float eps)
+{
+    float ss = 0.0f;
+    for (int64_t d = 0; d < D; ++d) {
+        const float v = widen(row[d]);
+        const float sq = v * v;
+        ss = ss + sq;
+    }
+    const float ms = ss / (float)D;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    return 1.0f / q;
+}
+
+/* Diagnostic: the factor computed in binary64 and rounded once to binary32. */
+static float rms_factor_f64(const uint16_t* row, int64_t D, float eps)
+{
+    double ss = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+        const double v = (double)widen(row[d]);
+        ss += v * v;
+    }
+    const double r = 1.0 / sqrt(ss / (double)D + (double)eps);
+    return (float)r;
+}
+
+#define ORACLE_RMS_PINNED 0
+#define ORACLE_RMS_SEQUENTIAL 1
+#define ORACLE_RMS_F64 2
+
+static float rms_factor(const uint16_t* row, int64_t D, float eps,
+                        int variant, int P)
+{
+    if (variant == ORACLE_RMS_SEQUENTIAL)
+        return rms_factor_sequential(row, D, eps);
+    if (variant == ORACLE_RMS_F64)
+        return rms_factor_f64(row, D, eps);
+    return rms_factor_pinned(row, D, eps, P);
+}
+
+/* Valid P: a power of two in [1, 256]. Returns 0 when valid. */
+static int bad_partials(int P)
+{
+    return P < 1 || P > 256 || (P & (P - 1)) != 0;
+}
+
+/* r for every row of x [B, L, D] into factors[B*L] (binary32). */
+int oracle_rms_factors(const uint16_t* x, float* factors, int64_t B,
+                       int64_t L, int64_t D, float eps, int variant, int P)
+{
+    if (bad_partials(P) || D % 8 != 0)
+        return 1;
+    for (int64_t r = 0; r < B * L; ++r)
+        factors[r] = rms_factor(x + r * D, D, eps, variant, P);
+    return 0;
+}
+
+/* ---- adaLN modulation ----------------------------------------------------
+ *
+ * out = rms_norm(x, eps) * (1 + scale) + shift, scale and shift [B, 1, D]
+ * (batch b uses row b for every l). Per element, with r the row's factor:
+ *     n = x * r;  a = 1 + scale;  m = n * a;  y = m + shift;
+ *     out = bf16_rne(y)
+ * each a binary32 operation, left to right as the expression is written.
+ * out may be x (the whole row is reduced before any element is written).
+ * Returns nonzero (and writes nothing) for an invalid P or D % 8 != 0.
+ */
+int oracle_rms_modulate(const uint16_t* x, const uint16_t* scale,
+                        const uint16_t* shift, float eps, uint16_t* out,
+                        int64_t B, int64_t L, int64_t D, int variant, int P)
+{
+    if (bad_partials(P) || D % 8 != 0)
+        return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint16_t* sc = scale + b * D;
+        const uint16_t* sh = shift + b * D;
+        for (int64_t l = 0; l < L; ++l) {
+            const int64_t row = (b * L + l) * D;
+            const float r = rms_factor(x + row, D, eps, variant, P);
+            for (int64_t d = 0; d < D; ++d) {
+                const float n = widen(x[row + d]) * r;
+                const float a = 1.0f + widen(sc[d]);
+                const float m = n * a;
+                const float y = m + widen(sh[d]);
+                out[row + d] = narrow_rne(y);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Weightless RMSNorm alone: out = bf16_rne(x * r), the pinned factor. */
+int oracle_rms_norm(const uint16_t* x, float eps, uint16_t* out, int64_t B,
+                    int64_t L, int64_t D, int P)
+{
+    if (bad_partials(P) || D % 8 != 0)
+        return 1;
+    for (int64_t r = 0; r < B * L; ++r) {
+        const float f = rms_factor_pinned(x + r * D, D, eps, P);
+        for (int64_t d = 0; d < D; ++d)
+            out[r * D + d] = narrow_rne(widen(x[r * D + d]) * f);
+    }
+    return 0;
+}
+
+/* ---- build self-check ------------------------------------------------------
+ *
+ * With a = b = 1 + 2^-12 and c = -(1 + 2^-11): a*b = 1 + 2^-11 + 2^-24
+ * rounds to 1 + 2^-11 in binary32, so a*b + c is exactly 0 with two
+ * roundings, while a fused multiply-add would return 2^-24. Returns the
+ * computed value; a build that contracts returns 2^-24.
+ */
+float oracle_contraction_probe(void)
+{
+    volatile float a = 1.0f + 0x1p-12f;
+    volatile float b = 1.0f + 0x1p-12f;
+    volatile float c = -(1.0f + 0x1p-11f);
+    const float p = a * b;
+    return p + c;
+}
