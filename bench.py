@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Bench of the gated residual add and the RMSNorm modulation on one MI355X.
+
+One step is one pass of the whole path over the workload resident in HBM:
+  1. gated residual add, full gate,  [1, 8160, 4096]           (out-of-place)
+  2. gated residual add, bcast gate, [1, 32640, 4096]          (in place on x)
+  3. rms_modulate,                   [2, 32640, 4096] -> y
+  4. gated residual add, bcast gate, [2, 32640, 4096]          (in place on x)
+Steps 1 and 2 are the two shapes the headline metric names (the
+ltx2_full_s8160_c4096 and ltx2_bcast_s32640_c4096 workloads of the
+residual-gate page's kernel benchmark); steps 3-4 are the modulation then the
+gated residual of one DiT block at B = 2 (video hidden 4096).
+
+Reported (one JSON line on stdout):
+  value        algorithmic bytes of one step / measured time of one step, GB/s
+  per_launch   per-call microseconds and GB/s from HIP events recorded on the
+               launch stream around every call of the timed steps
+  cold         per-call microseconds with the caches flushed before each call
+               (a 1 GiB read with cache-allocating loads pushes earlier data
+               out of the L2s and the 256 MB memory-side cache and leaves
+               only clean lines), median of repetitions
+  roofline     the kernel with the largest share of the step's time, against
+               the 8 TB/s HBM peak
+  cpu_baseline the CPU oracle on the same workload on this host's cores
+Algorithmic bytes: each input element read once and each output element
+written once, 2 bytes per element; a broadcast row counts once per call.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("achieved HBM GB/s and µs/call at [1,32640,4096] bcast and "
+          "[1,8160,4096] full")
+HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 1 << 30
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cold-reps", type=int, default=30,
+                   help="repetitions per launch of the cache-flushed timing (0: skip)")
+    p.add_argument("--cpu-fraction", type=float, default=1.0,
+                   help="fraction of each launch's rows the CPU oracle runs on (0: skip)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="repeat the CPU oracle sample until this much time has passed")
+    return p.parse_args()
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU only (asked for {max(args.gpus, world)}); "
+              "the workload is row-local and would shard over tokens with no exchange, "
+              "but multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import diffusion_transformer_elementwise_amd as dte
+    from synth_inputs import CASES, GATE_BCAST, GATE_FULL, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+
+    c3, c4, c5 = CASES["c3"], CASES["c4"], CASES["c5"]
+    log("generating seeded inputs (c3, c4, c5)")
+    host = {k: make_inputs(CASES[k]) for k in ("c3", "c4", "c5")}
+    d3 = {k: to_dev(v) for k, v in host["c3"].items()}
+    d4 = {k: to_dev(v) for k, v in host["c4"].items()}
+    d5 = {k: to_dev(v) for k, v in host["c5"].items()}
+    out3 = torch.empty_like(d3["x"])
+    y5 = torch.empty_like(d5["x"])
+    if args.cpu_fraction <= 0:
+        host = None
+
+    def gate_bytes(c):
+        return (4 * c.elems if c.gate == GATE_FULL else 3 * c.elems + c.B * c.D) * 2
+
+    launches = [
+        ("c3_full_gate_add", "gate_add_full_kernel", gate_bytes(c3),
+         lambda: dte.rga_residual_gate_add(d3["x"], d3["u"], d3["g"], out=out3, gate_mode=GATE_FULL)),
+        ("c4_bcast_gate_add_inplace", "gate_add_bcast_kernel", gate_bytes(c4),
+         lambda: dte.rga_residual_gate_add(d4["x"], d4["u"], d4["g"], out=d4["x"], gate_mode=GATE_BCAST)),
+        ("c5_rms_modulate", "rms_modulate_kernel", (2 * c5.elems + 2 * c5.B * c5.D) * 2,
+         lambda: dte.rms_modulate(d5["x"], d5["scale"], d5["shift"], c5.eps, out=y5)),
+        ("c5_bcast_gate_add_inplace", "gate_add_bcast_kernel", gate_bytes(c5),
+         lambda: dte.rga_residual_gate_add(d5["x"], d5["u"], d5["g"], out=d5["x"], gate_mode=GATE_BCAST)),
+    ]
+    step_bytes = sum(l[2] for l in launches)
+
+    # copy ceiling on 1 GiB (also the known-size kernel for counter scaling)
+    src = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    dte.fill_(src, 0x3F803F80)
+    dte.copy_(dst, src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(10):
+        dte.copy_(dst, src)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * FLUSH_BYTES / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    log(f"copy ceiling {copy_gbps:.0f} GB/s")
+
+    def run_step(events=None):
+        for i, l in enumerate(launches):
+            if events is not None:
+                events[i].record(stream)
+            l[3]()
+        if events is not None:
+            events[len(launches)].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    durations = {l[0]: [] for l in launches}
+    for k in range(args.steps):
+        for i, l in enumerate(launches):
+            durations[l[0]].append(evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3)  # us
+    gpu_step_ms = statistics.mean(
+        evs[k][0].elapsed_time(evs[k][-1]) for k in range(args.steps))
+
+    per_launch = {}
+    for name, kernel, nbytes, _ in launches:
+        us = statistics.mean(durations[name])
+        per_launch[name] = {
+            "kernel": kernel, "bytes": nbytes, "us": round(us, 2),
+            "us_median": round(statistics.median(durations[name]), 2),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    # cold protocol: flush, then time one call, per launch
+    cold = {}
+    if args.cold_reps > 0:
+        log(f"cold timing, {args.cold_reps} reps per launch")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for name, kernel, nbytes, fn in launches:
+            ts = []
+            for _ in range(args.cold_reps):
+                dte.read_(src, sink)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            med = statistics.median(ts)
+            cold[name] = {"us_median": round(med, 2),
+                          "us_p10": round(float(np.percentile(ts, 10)), 2),
+                          "us_p90": round(float(np.percentile(ts, 90)), 2),
+                          "GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
+
+    # roofline of the kernel with the largest share of the step
+    by_kernel = {}
+    for name, kernel, nbytes, _ in launches:
+        agg = by_kernel.setdefault(kernel, {"bytes": 0, "us": 0.0, "launches": 0})
+        agg["bytes"] += nbytes
+        agg["us"] += statistics.mean(durations[name])
+        agg["launches"] += 1
+    dom = max(by_kernel, key=lambda k: by_kernel[k]["us"])
+    agg = by_kernel[dom]
+    bytes_per_launch = agg["bytes"] / agg["launches"]
+    avg_us = agg["us"] / agg["launches"]
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic(dom),
+                "bytes_per_launch": bytes_per_launch,
+                "avg_launch_us": round(avg_us, 2),
+                "launches_per_step": agg["launches"]}
+
+    cpu = None
+    if host is not None:
+        del d3, d4, d5, out3, y5, src, dst
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(host, args.cpu_fraction, args.cpu_seconds, log)
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ltx2 DiT elementwise step: full gate-add [1,8160,4096]; "
+                        "bcast gate-add in place [1,32640,4096]; rms_modulate + "
+                        "bcast gate-add in place [2,32640,4096]",
+            "step_bytes": step_bytes,
+            "gpu_time_per_step_ms": round(gpu_step_ms, 4),
+            "headline": {
+                "bcast_[1,32640,4096]": {k: per_launch["c4_bcast_gate_add_inplace"][k] for k in ("us", "GBps")},
+                "full_[1,8160,4096]": {k: per_launch["c3_full_gate_add"][k] for k in ("us", "GBps")},
+            },
+        },
+        "per_launch": per_launch,
+        "cold": cold,
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def kernel_source_digest() -> str:
+    csrc = os.path.join(ROOT, "diffusion_transformer_elementwise_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".hpp", ".cpp", ".py")):
+            continue
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed counter summaries, only while the
+    kernel sources are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != kernel_source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(host, fraction, min_seconds, log):
+    """The oracle (single-threaded C, as it stands) on the first `fraction` of
+    each launch's rows, same launch mix as one step, repeated until at least
+    `min_seconds` have passed."""
+    import numpy as np
+
+    import oracle
+    from synth_inputs import CASES, GATE_BCAST, GATE_FULL
+
+    def rows(a, c):
+        n = max(1, int(round(c.L * fraction)))
+        return np.ascontiguousarray(a[:, :n]), n
+
+    c3, c4, c5 = CASES["c3"], CASES["c4"], CASES["c5"]
+    h3, h4, h5 = host["c3"], host["c4"], host["c5"]
+    x3, n3 = rows(h3["x"], c3); u3, _ = rows(h3["u"], c3); g3, _ = rows(h3["g"], c3)
+    x4, n4 = rows(h4["x"], c4); u4, _ = rows(h4["u"], c4)
+    x5, n5 = rows(h5["x"], c5); u5, _ = rows(h5["u"], c5)
+    out3 = np.empty_like(x3)
+    y5 = np.empty_like(x5)
+    sample = (8 * c3.B * n3 * c3.D
+              + 6 * c4.B * n4 * c4.D + 2 * c4.B * c4.D
+              + 4 * c5.B * n5 * c5.D + 4 * c5.B * c5.D
+              + 6 * c5.B * n5 * c5.D + 2 * c5.B * c5.D)
+    log(f"cpu baseline: oracle on {fraction:.2f} of every launch's rows, "
+        f"repeated for at least {min_seconds:.0f} s")
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gate_add(x3, u3, g3, GATE_FULL, out=out3)
+        oracle.gate_add(x4, u4, h4["g"], GATE_BCAST, out=x4)
+        oracle.rms_modulate(x5, h5["scale"], h5["shift"], c5.eps, out=y5)
+        oracle.gate_add(x5, u5, h5["g"], GATE_BCAST, out=x5)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    total = sample * reps
+    log(f"cpu baseline: {total / 1e9:.2f} GB in {dt:.1f} s ({reps} passes)")
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} passes over the first {fraction:.2f} of the rows of each of "
+                      f"the step's 4 launches ({total} algorithmic bytes in {dt:.1f} s, "
+                      "single-threaded C oracle)",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,42 @@
+"""MI355X (gfx950) elementwise kernels for video diffusion transformer blocks.
+
+Thin Python binding over the C ABI in ``include/rga.h`` (``librga.so``):
+argument marshalling only. Every element of every result is computed by the
+library's HIP kernels; torch supplies device memory and the current stream.
+There is no CPU path: importing fails loudly when the library is not built.
+
+    rga_residual_gate_add(x, u, g, out=None, gate_mode=None)   out = x + u*g
+    rms_modulate(x, scale, shift, eps=1e-6, out=None)
+        out = rms_norm(x, eps) * (1 + scale) + shift
+
+Tensors are contiguous bf16 on one HIP device; x, u, out are [B, L, D]; g is
+[B, L, D] (full) or [B, 1, D] (broadcast); scale and shift are [B, 1, D].
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    GATE_BCAST,
+    GATE_FULL,
+    RGA_ERR_ALIAS,
+    RGA_ERR_HIP,
+    RGA_ERR_INVALID_ARG,
+    RGA_ERR_UNSUPPORTED,
+    RGA_OK,
+    RGA_RMS_MAX_D,
+    RGAError,
+    check_residual_gate_add,
+    check_rms_modulate,
+    library,
+    library_path,
+    status_string,
+)
+from .ops import copy_, fill_, read_, rga_residual_gate_add, rms_modulate  # noqa: F401
+
+__all__ = [
+    "rga_residual_gate_add",
+    "rms_modulate",
+    "GATE_FULL",
+    "GATE_BCAST",
+    "RGAError",
+    "library_path",
+]

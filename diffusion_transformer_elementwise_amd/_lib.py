@@ -1,0 +1,92 @@
+"""ctypes declarations of the C ABI (include/rga.h, include/rga_measure.h).
+
+Loading happens at import: a missing or unloadable ``librga.so`` raises
+ImportError, so nothing can run without the HIP library.
+
+torch is imported first on purpose. The ROCm build of torch ships its own
+HIP runtime (SONAME libamdhip64.so.7); once it is loaded, the dynamic linker
+resolves librga.so's dependency on that SONAME to the same copy, so the
+library launches on torch's streams and sees torch's allocations. Loaded the
+other way round, the process would hold two HIP runtimes and torch's stream
+handles would be foreign to the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must precede the CDLL below)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_PATH = os.path.join(_HERE, "librga.so")
+
+GATE_FULL = 0
+GATE_BCAST = 1
+
+RGA_OK = 0
+RGA_ERR_INVALID_ARG = 1
+RGA_ERR_UNSUPPORTED = 2
+RGA_ERR_ALIAS = 3
+RGA_ERR_HIP = 4
+
+RGA_RMS_MAX_D = 8192
+
+
+class RGAError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: status {status}: {status_string(status)}")
+
+
+def library_path() -> str:
+    return _PATH
+
+
+def _load():
+    if not os.path.exists(_PATH):
+        raise ImportError(
+            f"{_PATH} is not built; run __graft_entry__.build() "
+            "(hipcc for gfx950). There is no CPU fallback.")
+    try:
+        lib = ctypes.CDLL(_PATH)
+    except OSError as e:
+        raise ImportError(f"cannot load {_PATH}: {e}") from e
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    f32, u32 = ctypes.c_float, ctypes.c_uint32
+    lib.rga_residual_gate_add.argtypes = [p, p, p, p, i64, i64, i64, i32, p]
+    lib.rga_residual_gate_add.restype = i32
+    lib.rms_modulate.argtypes = [p, p, p, f32, p, i64, i64, i64, p]
+    lib.rms_modulate.restype = i32
+    lib.rga_check_residual_gate_add.argtypes = [p, p, p, p, i64, i64, i64, i32]
+    lib.rga_check_residual_gate_add.restype = i32
+    lib.rga_check_rms_modulate.argtypes = [p, p, p, f32, p, i64, i64, i64]
+    lib.rga_check_rms_modulate.restype = i32
+    lib.rga_status_string.argtypes = [i32]
+    lib.rga_status_string.restype = ctypes.c_char_p
+    lib.rga_copy.argtypes = [p, p, i64, p]
+    lib.rga_copy.restype = i32
+    lib.rga_fill.argtypes = [p, i64, u32, p]
+    lib.rga_fill.restype = i32
+    lib.rga_read.argtypes = [p, i64, p, p]
+    lib.rga_read.restype = i32
+    return lib
+
+
+_LIB = _load()
+
+
+def library():
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return _LIB.rga_status_string(int(status)).decode()
+
+
+def check_residual_gate_add(x, u, g, out, B, L, D, gate_mode) -> int:
+    """Host-only validation through the C ABI (addresses as integers)."""
+    return _LIB.rga_check_residual_gate_add(x, u, g, out, B, L, D, gate_mode)
+
+
+def check_rms_modulate(x, scale, shift, eps, out, B, L, D) -> int:
+    return _LIB.rga_check_rms_modulate(x, scale, shift, eps, out, B, L, D)

@@ -1,0 +1,33 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel files.
+// Every launcher expects arguments already validated by api.cpp and returns
+// the HIP status of its launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace rga {
+
+// gated residual add (gate_add.hip)
+bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode);
+hipError_t launch_gate_add(const void* x, const void* u, const void* g,
+                           void* out, int64_t B, int64_t L, int64_t D,
+                           int gate_mode, hipStream_t stream);
+
+// modulation (rms_modulate.hip)
+bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D);
+hipError_t launch_rms_modulate(const void* x, const void* scale,
+                               const void* shift, float eps, void* out,
+                               int64_t B, int64_t L, int64_t D,
+                               hipStream_t stream);
+
+// measurement helpers (measure.hip); n16 = number of 16-byte vectors
+bool stream_grid_fits(int64_t n16);
+hipError_t launch_copy(const void* src, void* dst, int64_t n16,
+                       hipStream_t stream);
+hipError_t launch_fill(void* dst, int64_t n16, uint32_t value,
+                       hipStream_t stream);
+hipError_t launch_read(const void* src, int64_t n16, void* sink,
+                       hipStream_t stream);
+
+}  // namespace rga

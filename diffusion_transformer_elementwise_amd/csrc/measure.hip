@@ -1,0 +1,110 @@
+// Measurement helpers.
+//   copy: the attainable streaming copy rate, with the launch shape and
+//         cache hints of the gate-add kernels (one wave per workgroup, one
+//         16-byte vector per lane, nontemporal loads and stores); also the
+//         known-traffic kernel that calibrates HBM byte counters.
+//   fill: writes a constant with plain stores.
+//   read: reads a buffer with plain (cache-allocating) loads, which evicts
+//         earlier data from the L2s and the memory-side cache while leaving
+//         only clean lines, i.e. a cache flush that bills no write-back to
+//         the next kernel; the words are XOR-folded into a 16-byte sink so
+//         the loads cannot be dropped.
+#include "bf16x8.hpp"
+#include "launch.hpp"
+
+namespace rga {
+namespace {
+
+constexpr int kCopyBlock = 64;
+constexpr int kBlock = 256;
+constexpr int kFillUnroll = 4;
+constexpr int kReadGrid = 256 * 16;  // workgroups of the grid-stride read
+
+__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const u32x4* src,
+                                                          u32x4* dst,
+                                                          int64_t n16)
+{
+    const int64_t i = (int64_t)blockIdx.x * kCopyBlock + threadIdx.x;
+    if (i < n16)
+        store16_stream(dst + i, load16_stream(src + i));
+}
+
+__global__ __launch_bounds__(kBlock) void fill_kernel(u32x4* dst, int64_t n16,
+                                                      uint32_t value)
+{
+    const int64_t base =
+        (int64_t)blockIdx.x * (kBlock * kFillUnroll) + threadIdx.x;
+    const u32x4 v = {value, value, value, value};
+#pragma unroll
+    for (int k = 0; k < kFillUnroll; ++k) {
+        const int64_t i = base + k * kBlock;
+        if (i < n16)
+            store16(dst + i, v);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void read_kernel(const u32x4* src,
+                                                      int64_t n16,
+                                                      uint32_t* sink)
+{
+    u32x4 acc = {0, 0, 0, 0};
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16;
+         i += stride)
+        acc ^= load16(src + i);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            acc[w] ^= (uint32_t)__shfl_xor((int)acc[w], m);
+    }
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            atomicXor(sink + w, acc[w]);
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+bool stream_grid_fits(int64_t n16)
+{
+    return ceil_div(n16, kCopyBlock) <= (((int64_t)1 << 32) - 1) / kCopyBlock;
+}
+
+hipError_t launch_copy(const void* src, void* dst, int64_t n16,
+                       hipStream_t stream)
+{
+    const u32x4* s = static_cast<const u32x4*>(src);
+    u32x4* d = static_cast<u32x4*>(dst);
+    void* args[] = {&s, &d, &n16};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&copy_kernel),
+                           dim3((uint32_t)ceil_div(n16, kCopyBlock)),
+                           dim3(kCopyBlock), args, 0, stream);
+}
+
+hipError_t launch_fill(void* dst, int64_t n16, uint32_t value,
+                       hipStream_t stream)
+{
+    u32x4* d = static_cast<u32x4*>(dst);
+    void* args[] = {&d, &n16, &value};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fill_kernel),
+                           dim3((uint32_t)ceil_div(n16, (int64_t)kBlock * kFillUnroll)),
+                           dim3(kBlock), args, 0, stream);
+}
+
+hipError_t launch_read(const void* src, int64_t n16, void* sink,
+                       hipStream_t stream)
+{
+    const u32x4* s = static_cast<const u32x4*>(src);
+    uint32_t* k = static_cast<uint32_t*>(sink);
+    void* args[] = {&s, &n16, &k};
+    const int64_t blocks = ceil_div(n16, kBlock) < kReadGrid ? ceil_div(n16, kBlock) : kReadGrid;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&read_kernel),
+                           dim3((uint32_t)blocks), dim3(kBlock), args, 0,
+                           stream);
+}
+
+}  // namespace rga

@@ -1,0 +1,127 @@
+/*
+ * rga.h — C ABI of the MI355X (gfx950) elementwise library for video
+ * diffusion transformer blocks: the gated residual add and the
+ * weightless-RMSNorm adaLN modulation over contiguous bf16 [B, L, D].
+ *
+ * Conventions shared by every call below:
+ *   - Tensor pointers are DEVICE pointers (HIP device memory of the current
+ *     device) to row-major contiguous bf16 values (bfloat16: sign, 8 exponent bits,
+ *     7 fraction bits, the upper half of a binary32), passed as void*.
+ *     Row (b, l) of a [B, L, D] tensor starts at element (b*L + l)*D; the
+ *     broadcast row of batch b of a [B, 1, D] tensor starts at b*D.
+ *   - Ownership: the caller allocates and owns every buffer. The library
+ *     allocates nothing, keeps no pointer after a call returns and holds no
+ *     state between calls. Calls are asynchronous: they validate on the host,
+ *     enqueue one kernel on `stream` (0 is the null stream) and return without
+ *     synchronising; buffers must stay alive until that work completes.
+ *     Calls may be made from several host threads at once.
+ *   - Arithmetic: IEEE binary32 with round-to-nearest-even, no fused
+ *     multiply-add, subnormals kept, then one rounding to bf16
+ *     (round-to-nearest-even; a NaN stays a NaN, its payload unspecified).
+ *   - Errors: every call returns an RGA_* status and never throws or aborts.
+ *     Validation runs before anything is enqueued; on any non-zero status
+ *     nothing was enqueued except for RGA_ERR_HIP, which reports the HIP
+ *     error of the launch itself. There is no fallback path inside the
+ *     library: a caller that wants one decides on a non-zero status.
+ *   - Sizes: B, L, D >= 0; B*L*D == 0 is a valid no-op (RGA_OK, nothing
+ *     enqueued, pointers may then be NULL). D must be a multiple of 8 and
+ *     every pointer 16-byte aligned (one 128-bit access moves 8 elements),
+ *     else RGA_ERR_UNSUPPORTED.
+ */
+#ifndef RGA_H
+#define RGA_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Gate layouts of rga_residual_gate_add. */
+enum {
+    RGA_GATE_FULL = 0,  /* g is [B, L, D] */
+    RGA_GATE_BCAST = 1, /* g is [B, 1, D]: row b is used for every l */
+};
+
+/* Status codes. */
+enum {
+    RGA_OK = 0,
+    RGA_ERR_INVALID_ARG = 1, /* negative dim, size overflow, bad gate_mode,
+                                bad eps, NULL pointer with B*L*D > 0 */
+    RGA_ERR_UNSUPPORTED = 2, /* D % 8 != 0, misaligned pointer, D above the
+                                modulation's limit, grid too large */
+    RGA_ERR_ALIAS = 3,       /* out overlaps an input other than as allowed */
+    RGA_ERR_HIP = 4,         /* the HIP runtime rejected the launch */
+};
+
+/* Largest D that rms_modulate accepts (one row is held in registers). */
+#define RGA_RMS_MAX_D 8192
+
+/*
+ * Gated residual add: out = x + u * g.
+ *
+ * Source: "[KDA-Pilot] Add diffusion residual-gate CUDA fast path for LTX2"
+ * (sglang PR #29361), section "Motivation": hidden_states plus update times
+ * gate over contiguous [B, L, D] tensors, with a full gate or a gate
+ * broadcast over L as [B, 1, D].
+ *
+ * Per element: p = u * g (binary32), s = x + p (binary32), out = bf16(s).
+ *   x, u, out : [B, L, D]
+ *   g         : [B, L, D] if gate_mode == RGA_GATE_FULL,
+ *               [B, 1, D] if gate_mode == RGA_GATE_BCAST
+ * Aliasing: out == x and out == u are allowed (in place), and out == g in
+ * full mode; any other overlap of out with an input is RGA_ERR_ALIAS.
+ * Inputs may overlap one another freely.
+ */
+int rga_residual_gate_add(const void* x, const void* u, const void* g,
+                          void* out, int64_t B, int64_t L, int64_t D,
+                          int gate_mode, hipStream_t stream);
+
+/*
+ * adaLN modulation with a weightless RMSNorm:
+ *   out = rms_norm(x, eps) * (1 + scale) + shift.
+ *
+ * Source: prhub summary of sglang PR #34172 ("LTX-2 quality=high fused
+ * RMSNorm+modulate"), sections "功能与动机" and "关键源码片段": the
+ * per-block adaLN expression with RMSNormNoWeight, eps 1e-6 in its test.
+ *
+ *   x, out        : [B, L, D]
+ *   scale, shift  : [B, 1, D]; row b is used for every l
+ *   eps           : finite, >= 0 (else RGA_ERR_INVALID_ARG)
+ *   D             : multiple of 8, at most RGA_RMS_MAX_D
+ * Per row (b, l): ss = sum of x_d^2, r = 1 / sqrt(ss / D + eps); per element
+ * y = ((x_d * r) * (1 + scale_d)) + shift_d, each step binary32, then bf16.
+ * The sum of squares has one fixed order: the row is cut into groups of 8
+ * consecutive elements, group k is accumulated (in element order, square
+ * then add) into partial k mod 64 in increasing k, and the 64 partials are
+ * combined pairwise by index distance 1, 2, 4, ..., 32 (partial j takes
+ * partial j xor m). Results are therefore reproducible bit for bit.
+ * Aliasing: out == x is allowed (in place); any other overlap of out with
+ * an input is RGA_ERR_ALIAS.
+ */
+int rms_modulate(const void* x, const void* scale, const void* shift,
+                 float eps, void* out, int64_t B, int64_t L, int64_t D,
+                 hipStream_t stream);
+
+/*
+ * Host-only validation of the arguments of the two calls above, with the
+ * same rules and the same status the call would return before launching.
+ * Touches neither the device nor the pointed-to memory.
+ */
+int rga_check_residual_gate_add(const void* x, const void* u, const void* g,
+                                const void* out, int64_t B, int64_t L,
+                                int64_t D, int gate_mode);
+int rga_check_rms_modulate(const void* x, const void* scale,
+                           const void* shift, float eps, const void* out,
+                           int64_t B, int64_t L, int64_t D);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* rga_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGA_H */
