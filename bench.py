@@ -14,11 +14,17 @@ gated residual of one DiT block at B = 2 (video hidden 4096).
 Reported (one JSON line on stdout):
   value        algorithmic bytes of one step / measured time of one step, GB/s
   per_launch   per-call microseconds and GB/s from HIP events recorded on the
-               launch stream around every call of the timed steps
+               launch stream around every call of the timed steps (timing-only
+               events without the system-scope cache fence)
   cold         per-call microseconds with the caches flushed before each call
                (a 1 GiB read with cache-allocating loads pushes earlier data
                out of the L2s and the 256 MB memory-side cache and leaves
                only clean lines), median of repetitions
+  small_configs with --small-configs 1: the other workload configurations
+               (c1 full [1,126,2048] + rms_modulate, c2 bcast [1,L,3072] for
+               L = 512, 4096, 4608): cold per-call time, and back-to-back
+               per-call time (launch overhead and cache-resident inputs
+               dominate at these sizes)
   roofline     the kernel with the largest share of the step's time, against
                the 8 TB/s HBM peak
   cpu_baseline the CPU oracle on the same workload on this host's cores
@@ -41,6 +47,53 @@ if ROOT not in sys.path:
 
 METRIC = ("achieved HBM GB/s and µs/call at [1,32640,4096] bcast and "
           "[1,8160,4096] full")
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvents:
+    """Timing events straight from the HIP runtime that torch loaded (same
+    SONAME, so dlopen returns torch's copy), created with
+    hipEventDisableSystemFence: recording them does not write back and
+    invalidate the caches the way default timing events do, which otherwise
+    adds microseconds to every bracketed launch and cools the next one."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def new(self):
+        ev = self.ct.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(self.ct.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        self._check(self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def sync(self, ev):
+        self._check(self.hip.hipEventSynchronize(ev), "hipEventSynchronize")
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.ct.byref(out), a, b), "hipEventElapsedTime")
+        return out.value
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30
 
@@ -54,6 +107,9 @@ def parse_args():
                    help="repetitions per launch of the cache-flushed timing (0: skip)")
     p.add_argument("--cpu-fraction", type=float, default=1.0,
                    help="fraction of each launch's rows the CPU oracle runs on (0: skip)")
+    p.add_argument("--small-configs", type=int, default=0,
+                   help="1: also time the c1/c2 configurations (kept out of the default "
+                        "run so a profile of it averages the step's launches only)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="repeat the CPU oracle sample until this much time has passed")
     return p.parse_args()
@@ -118,22 +174,23 @@ def main():
     dte.fill_(src, 0x3F803F80)
     dte.copy_(dst, src)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
+    hev = HipEvents()
+    ev = [hev.new() for _ in range(2)]
+    hev.record(ev[0], stream)
     for _ in range(10):
         dte.copy_(dst, src)
-    ev[1].record(stream)
+    hev.record(ev[1], stream)
     torch.cuda.synchronize()
-    copy_gbps = 10 * 2 * FLUSH_BYTES / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    copy_gbps = 10 * 2 * FLUSH_BYTES / (hev.ms(ev[0], ev[1]) * 1e-3) / 1e9
     log(f"copy ceiling {copy_gbps:.0f} GB/s")
 
     def run_step(events=None):
         for i, l in enumerate(launches):
             if events is not None:
-                events[i].record(stream)
+                hev.record(events[i], stream)
             l[3]()
         if events is not None:
-            events[len(launches)].record(stream)
+            hev.record(events[len(launches)], stream)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -141,8 +198,7 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
-           for _ in range(args.steps)]
+    evs = [[hev.new() for _ in range(len(launches) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -153,9 +209,9 @@ def main():
     durations = {l[0]: [] for l in launches}
     for k in range(args.steps):
         for i, l in enumerate(launches):
-            durations[l[0]].append(evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3)  # us
+            durations[l[0]].append(hev.ms(evs[k][i], evs[k][i + 1]) * 1e3)  # us
     gpu_step_ms = statistics.mean(
-        evs[k][0].elapsed_time(evs[k][-1]) for k in range(args.steps))
+        hev.ms(evs[k][0], evs[k][-1]) for k in range(args.steps))
 
     per_launch = {}
     for name, kernel, nbytes, _ in launches:
@@ -170,21 +226,61 @@ def main():
     cold = {}
     if args.cold_reps > 0:
         log(f"cold timing, {args.cold_reps} reps per launch")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = hev.new(), hev.new()
         for name, kernel, nbytes, fn in launches:
             ts = []
             for _ in range(args.cold_reps):
                 dte.read_(src, sink)
-                e0.record(stream)
+                hev.record(e0, stream)
                 fn()
-                e1.record(stream)
-                e1.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
+                hev.record(e1, stream)
+                hev.sync(e1)
+                ts.append(hev.ms(e0, e1) * 1e3)
             med = statistics.median(ts)
             cold[name] = {"us_median": round(med, 2),
                           "us_p10": round(float(np.percentile(ts, 10)), 2),
                           "us_p90": round(float(np.percentile(ts, 90)), 2),
                           "GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
+
+    small = {}
+    if args.small_configs and args.cold_reps > 0:
+        log("small configs c1, c2")
+        e0, e1 = hev.new(), hev.new()
+
+        def cold_and_warm(fn, nbytes):
+            ts = []
+            for _ in range(args.cold_reps):
+                dte.read_(src, sink)
+                hev.record(e0, stream)
+                fn()
+                hev.record(e1, stream)
+                hev.sync(e1)
+                ts.append(hev.ms(e0, e1) * 1e3)
+            hev.record(e0, stream)
+            for _ in range(100):
+                fn()
+            hev.record(e1, stream)
+            hev.sync(e1)
+            warm = hev.ms(e0, e1) * 1e3 / 100
+            med = statistics.median(ts)
+            return {"bytes": nbytes, "cold_us_median": round(med, 2),
+                    "cold_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                    "back_to_back_us": round(warm, 2),
+                    "back_to_back_GBps": round(nbytes / (warm * 1e-6) / 1e9, 1)}
+
+        for key in ("c1", "c2a", "c2b", "c2c"):
+            c = CASES[key]
+            h = make_inputs(c)
+            d = {k: to_dev(v) for k, v in h.items()}
+            o = torch.empty_like(d["x"])
+            small[c.name + "_gate_add"] = cold_and_warm(
+                lambda: dte.rga_residual_gate_add(d["x"], d["u"], d["g"], out=o, gate_mode=c.gate),
+                gate_bytes(c))
+            if c.rms:
+                small[c.name + "_rms_modulate"] = cold_and_warm(
+                    lambda: dte.rms_modulate(d["x"], d["scale"], d["shift"], c.eps, out=o),
+                    (2 * c.elems + 2 * c.B * c.D) * 2)
+            del d, o
 
     # roofline of the kernel with the largest share of the step
     by_kernel = {}
@@ -206,6 +302,7 @@ def main():
                 "avg_launch_us": round(avg_us, 2),
                 "launches_per_step": agg["launches"]}
 
+    hev.close()
     cpu = None
     if host is not None:
         del d3, d4, d5, out3, y5, src, dst
@@ -239,6 +336,7 @@ def main():
         },
         "per_launch": per_launch,
         "cold": cold,
+        "small_configs": small,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
