@@ -25,6 +25,9 @@ Reported (one JSON line on stdout):
                L = 512, 4096, 4608): cold per-call time, and back-to-back
                per-call time (launch overhead and cache-resident inputs
                dominate at these sizes)
+  fused        the residual update + next modulation fused into one pass
+               (rga_gate_add_rms_modulate) at the [2,32640,4096] shapes,
+               against the step's own separate launches of the two kernels
   roofline     the kernel with the largest share of the step's time, against
                the 8 TB/s HBM peak
   cpu_baseline the CPU oracle on the same workload on this host's cores
@@ -110,6 +113,8 @@ def parse_args():
     p.add_argument("--small-configs", type=int, default=0,
                    help="1: also time the c1/c2 configurations (kept out of the default "
                         "run so a profile of it averages the step's launches only)")
+    p.add_argument("--fused-reps", type=int, default=30,
+                   help="repetitions of the fused-vs-separate comparison (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="repeat the CPU oracle sample until this much time has passed")
     return p.parse_args()
@@ -282,6 +287,43 @@ def main():
                     (2 * c.elems + 2 * c.B * c.D) * 2)
             del d, o
 
+    fused = {}
+    if args.fused_reps > 0:
+        log(f"fused residual + modulation, {args.fused_reps} reps")
+        n5 = c5.elems
+        fused_bytes = (4 * n5 + c5.B * c5.D + 2 * c5.B * c5.D) * 2
+        pair_bytes = gate_bytes(c5) + (2 * n5 + 2 * c5.B * c5.D) * 2
+        # warm-up launches first (the first launch of a kernel also loads its
+        # code object); then all reps enqueued back to back (a host sync per
+        # rep would leave the stream idle and bill the host's submission
+        # latency to the launch after it), read after one sync
+        fn = lambda: dte.rga_gate_add_rms_modulate(
+            d5["x"], d5["u"], d5["g"], d5["scale"], d5["shift"], c5.eps,
+            x_out=d5["x"], y=y5, gate_mode=GATE_BCAST)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        efs = [hev.new() for _ in range(args.fused_reps + 1)]
+        for k in range(args.fused_reps):
+            hev.record(efs[k], stream)
+            fn()
+        hev.record(efs[-1], stream)
+        torch.cuda.synchronize()
+        tf = [hev.ms(efs[k], efs[k + 1]) * 1e3 for k in range(args.fused_reps)]
+        fus = statistics.mean(tf)
+        # the same two steps as separate launches: the step's own c5 gate-add
+        # and rms_modulate launches (same kernels, shapes and bytes)
+        pair = per_launch["c5_bcast_gate_add_inplace"]["us"] + per_launch["c5_rms_modulate"]["us"]
+        fused = {"shape": "[2,32640,4096] bcast gate, x_out in place",
+                 "kernel": "gate_add_rms_modulate_kernel",
+                 "bytes": fused_bytes, "us": round(fus, 2),
+                 "GBps": round(fused_bytes / (fus * 1e-6) / 1e9, 1),
+                 "frac_of_hbm_peak": round(fused_bytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "separate_pair_bytes": pair_bytes,
+                 "separate_pair_us": round(pair, 2),
+                 "separate_pair_from": "per_launch c5_bcast_gate_add_inplace + c5_rms_modulate",
+                 "speedup_vs_separate": round(pair / fus, 3)}
+
     # roofline of the kernel with the largest share of the step
     by_kernel = {}
     for name, kernel, nbytes, _ in launches:
@@ -337,6 +379,7 @@ def main():
         "per_launch": per_launch,
         "cold": cold,
         "small_configs": small,
+        "fused": fused,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

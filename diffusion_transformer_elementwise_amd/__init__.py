@@ -8,6 +8,8 @@ There is no CPU path: importing fails loudly when the library is not built.
     rga_residual_gate_add(x, u, g, out=None, gate_mode=None)   out = x + u*g
     rms_modulate(x, scale, shift, eps=1e-6, out=None)
         out = rms_norm(x, eps) * (1 + scale) + shift
+    rga_gate_add_rms_modulate(x, u, g, scale, shift, eps=1e-6)
+        x_out = x + u*g, then y = rms_norm(x_out, eps) * (1 + scale) + shift
 
 Tensors are contiguous bf16 on one HIP device; x, u, out are [B, L, D]; g is
 [B, L, D] (full) or [B, 1, D] (broadcast); scale and shift are [B, 1, D].
@@ -24,17 +26,26 @@ from ._lib import (  # noqa: F401
     RGA_OK,
     RGA_RMS_MAX_D,
     RGAError,
+    check_gate_add_rms_modulate,
     check_residual_gate_add,
     check_rms_modulate,
     library,
     library_path,
     status_string,
 )
-from .ops import copy_, fill_, read_, rga_residual_gate_add, rms_modulate  # noqa: F401
+from .ops import (  # noqa: F401
+    copy_,
+    fill_,
+    read_,
+    rga_gate_add_rms_modulate,
+    rga_residual_gate_add,
+    rms_modulate,
+)
 
 __all__ = [
     "rga_residual_gate_add",
     "rms_modulate",
+    "rga_gate_add_rms_modulate",
     "GATE_FULL",
     "GATE_BCAST",
     "RGAError",

@@ -61,6 +61,10 @@ def _load():
     lib.rga_check_residual_gate_add.restype = i32
     lib.rga_check_rms_modulate.argtypes = [p, p, p, f32, p, i64, i64, i64]
     lib.rga_check_rms_modulate.restype = i32
+    lib.rga_gate_add_rms_modulate.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32, p]
+    lib.rga_gate_add_rms_modulate.restype = i32
+    lib.rga_check_gate_add_rms_modulate.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32]
+    lib.rga_check_gate_add_rms_modulate.restype = i32
     lib.rga_status_string.argtypes = [i32]
     lib.rga_status_string.restype = ctypes.c_char_p
     lib.rga_copy.argtypes = [p, p, i64, p]
@@ -90,3 +94,9 @@ def check_residual_gate_add(x, u, g, out, B, L, D, gate_mode) -> int:
 
 def check_rms_modulate(x, scale, shift, eps, out, B, L, D) -> int:
     return _LIB.rga_check_rms_modulate(x, scale, shift, eps, out, B, L, D)
+
+
+def check_gate_add_rms_modulate(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                                gate_mode) -> int:
+    return _LIB.rga_check_gate_add_rms_modulate(x, u, g, scale, shift, eps,
+                                                x_out, y, B, L, D, gate_mode)

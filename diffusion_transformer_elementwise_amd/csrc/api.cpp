@@ -124,6 +124,72 @@ int rga_check_rms_modulate(const void* x, const void* scale,
     return RGA_OK;
 }
 
+int rga_check_gate_add_rms_modulate(const void* x, const void* u,
+                                    const void* g, const void* scale,
+                                    const void* shift, float eps,
+                                    const void* x_out, const void* y,
+                                    int64_t B, int64_t L, int64_t D,
+                                    int gate_mode)
+{
+    if (B < 0 || L < 0 || D < 0)
+        return RGA_ERR_INVALID_ARG;
+    if (gate_mode != RGA_GATE_FULL && gate_mode != RGA_GATE_BCAST)
+        return RGA_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.0f)
+        return RGA_ERR_INVALID_ARG;
+    int64_t n = 0, bytes = 0;
+    if (!sizes(B, L, D, &n, &bytes))
+        return RGA_ERR_INVALID_ARG;
+    if (n == 0)
+        return RGA_OK;
+    if (!x || !u || !g || !scale || !shift || !x_out || !y)
+        return RGA_ERR_INVALID_ARG;
+    if (D % 8 != 0 || D > RGA_RMS_MAX_D)
+        return RGA_ERR_UNSUPPORTED;
+    const void* all[] = {x, u, g, scale, shift, x_out, y};
+    for (const void* p : all)
+        if (!aligned16(p))
+            return RGA_ERR_UNSUPPORTED;
+    if (!rga::gate_add_rms_modulate_grid_fits(B, L, D))
+        return RGA_ERR_UNSUPPORTED;
+
+    const bool full = gate_mode == RGA_GATE_FULL;
+    const int64_t row_bytes = B * D * 2;
+    const Range rows[] = {range_of(scale, row_bytes), range_of(shift, row_bytes)};
+    const void* outs[] = {x_out, y};
+    for (const void* o : outs) {
+        const Range r = range_of(o, bytes);
+        if (overlaps(r, range_of(x, bytes)) && o != x)
+            return RGA_ERR_ALIAS;
+        if (overlaps(r, range_of(u, bytes)) && o != u)
+            return RGA_ERR_ALIAS;
+        if (overlaps(r, range_of(g, full ? bytes : row_bytes)) && !(full && o == g))
+            return RGA_ERR_ALIAS;
+        for (const Range& q : rows)
+            if (overlaps(r, q))
+                return RGA_ERR_ALIAS;
+    }
+    if (overlaps(range_of(x_out, bytes), range_of(y, bytes)))
+        return RGA_ERR_ALIAS;
+    return RGA_OK;
+}
+
+int rga_gate_add_rms_modulate(const void* x, const void* u, const void* g,
+                              const void* scale, const void* shift, float eps,
+                              void* x_out, void* y, int64_t B, int64_t L,
+                              int64_t D, int gate_mode, hipStream_t stream)
+{
+    const int st = rga_check_gate_add_rms_modulate(
+        x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return rga::launch_gate_add_rms_modulate(x, u, g, scale, shift, eps,
+                                             x_out, y, B, L, D, gate_mode,
+                                             stream) == hipSuccess
+               ? RGA_OK
+               : RGA_ERR_HIP;
+}
+
 int rga_residual_gate_add(const void* x, const void* u, const void* g,
                           void* out, int64_t B, int64_t L, int64_t D,
                           int gate_mode, hipStream_t stream)

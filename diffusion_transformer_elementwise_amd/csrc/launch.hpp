@@ -21,6 +21,15 @@ hipError_t launch_rms_modulate(const void* x, const void* scale,
                                int64_t B, int64_t L, int64_t D,
                                hipStream_t stream);
 
+// residual update then modulation, one pass (gate_add_rms_modulate.hip)
+bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D);
+hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
+                                        const void* g, const void* scale,
+                                        const void* shift, float eps,
+                                        void* x_out, void* y, int64_t B,
+                                        int64_t L, int64_t D, int gate_mode,
+                                        hipStream_t stream);
+
 // measurement helpers (measure.hip); n16 = number of 16-byte vectors
 bool stream_grid_fits(int64_t n16);
 hipError_t launch_copy(const void* src, void* dst, int64_t n16,

@@ -88,6 +88,48 @@ def rms_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     return out
 
 
+def rga_gate_add_rms_modulate(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
+                              scale: torch.Tensor, shift: torch.Tensor,
+                              eps: float = 1e-6,
+                              x_out: torch.Tensor | None = None,
+                              y: torch.Tensor | None = None,
+                              gate_mode: int | None = None):
+    """x_out = x + u * g, then y = rms_norm(x_out, eps) * (1 + scale) + shift,
+    in one pass. Returns (x_out, y). x_out and y may each be x or u."""
+    _require(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [B, L, D]")
+    B, L, D = x.shape
+    _require(u, "u", x.device)
+    _require(g, "g", x.device)
+    if u.shape != x.shape:
+        raise ValueError(f"u has shape {tuple(u.shape)}, expected {tuple(x.shape)}")
+    if gate_mode is None:
+        gate_mode = GATE_FULL if g.shape == x.shape else GATE_BCAST
+    want = (B, L, D) if gate_mode == GATE_FULL else (B, 1, D)
+    if gate_mode in (GATE_FULL, GATE_BCAST) and tuple(g.shape) != want:
+        raise ValueError(f"g has shape {tuple(g.shape)}, expected {want}")
+    for name, t in (("scale", scale), ("shift", shift)):
+        _require(t, name, x.device)
+        if tuple(t.shape) != (B, 1, D):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, 1, D)}")
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if y is None:
+        y = torch.empty_like(x)
+    for name, t in (("x_out", x_out), ("y", y)):
+        _require(t, name, x.device)
+        if t.shape != x.shape:
+            raise ValueError(f"{name} must have x's shape")
+    st = library().rga_gate_add_rms_modulate(
+        x.data_ptr(), u.data_ptr(), g.data_ptr(), scale.data_ptr(),
+        shift.data_ptr(), float(eps), x_out.data_ptr(), y.data_ptr(), B, L, D,
+        int(gate_mode), _stream_handle(x.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_gate_add_rms_modulate")
+    return x_out, y
+
+
 def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
     """Measurement helper: 128-bit device copy of src's bytes into dst."""
     if src.device.type != "cuda" or dst.device != src.device:

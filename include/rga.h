@@ -56,7 +56,8 @@ enum {
     RGA_ERR_HIP = 4,         /* the HIP runtime rejected the launch */
 };
 
-/* Largest D that rms_modulate accepts (one row is held in registers). */
+/* Largest D that rms_modulate and rga_gate_add_rms_modulate accept (one
+ * row is held in registers). */
 #define RGA_RMS_MAX_D 8192
 
 /*
@@ -106,8 +107,35 @@ int rms_modulate(const void* x, const void* scale, const void* shift,
                  hipStream_t stream);
 
 /*
- * Host-only validation of the arguments of the two calls above, with the
- * same rules and the same status the call would return before launching.
+ * Residual update followed by the next modulation, in one pass:
+ *   x_out = x + u * g                                 (as rga_residual_gate_add)
+ *   y     = rms_norm(x_out, eps) * (1 + scale) + shift (as rms_modulate)
+ *
+ * Source: the two steps are adjacent in a DiT block — the residual-gate update
+ * of hidden_states ("[KDA-Pilot] Add diffusion residual-gate CUDA fast path
+ * for LTX2", "Motivation") and the adaLN modulation of the updated
+ * hidden_states before the next sub-layer (prhub summary of sglang PR #34172,
+ * "关键源码片段", LTX2TransformerBlock.forward). Fused, x_out is never read
+ * back: 8 bytes per element instead of 10.
+ *
+ *   x, u, x_out, y : [B, L, D]
+ *   g              : [B, L, D] (RGA_GATE_FULL) or [B, 1, D] (RGA_GATE_BCAST)
+ *   scale, shift   : [B, 1, D]
+ *   eps            : finite, >= 0;  D: multiple of 8, at most RGA_RMS_MAX_D
+ * Results are bit-identical to rga_residual_gate_add(x, u, g, x_out) followed
+ * by rms_modulate(x_out, scale, shift, eps, y): the modulation reads the
+ * bf16-rounded x_out, with the same fixed reduction order.
+ * Aliasing: x_out and y may each be exactly x or u (or g in full mode); they
+ * must not overlap each other, scale, shift or a broadcast g (RGA_ERR_ALIAS).
+ */
+int rga_gate_add_rms_modulate(const void* x, const void* u, const void* g,
+                              const void* scale, const void* shift, float eps,
+                              void* x_out, void* y, int64_t B, int64_t L,
+                              int64_t D, int gate_mode, hipStream_t stream);
+
+/*
+ * Host-only validation of the arguments of the calls above, with the same
+ * rules and the same status the call would return before launching.
  * Touches neither the device nor the pointed-to memory.
  */
 int rga_check_residual_gate_add(const void* x, const void* u, const void* g,
@@ -116,6 +144,12 @@ int rga_check_residual_gate_add(const void* x, const void* u, const void* g,
 int rga_check_rms_modulate(const void* x, const void* scale,
                            const void* shift, float eps, const void* out,
                            int64_t B, int64_t L, int64_t D);
+int rga_check_gate_add_rms_modulate(const void* x, const void* u,
+                                    const void* g, const void* scale,
+                                    const void* shift, float eps,
+                                    const void* x_out, const void* y,
+                                    int64_t B, int64_t L, int64_t D,
+                                    int gate_mode);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rga_status_string(int status);

@@ -52,6 +52,10 @@ def _load():
     lib.oracle_bf16_from_f32.restype = None
     lib.oracle_f32_from_bf16.argtypes = [p, p, i64]
     lib.oracle_f32_from_bf16.restype = None
+    lib.oracle_gate_add_rms_modulate.argtypes = [
+        p, p, p, p, p, ctypes.c_float, p, p, i64, i64, i64, ctypes.c_int,
+        ctypes.c_int]
+    lib.oracle_gate_add_rms_modulate.restype = ctypes.c_int
     lib.oracle_contraction_probe.argtypes = []
     lib.oracle_contraction_probe.restype = ctypes.c_float
     _LIB = lib
@@ -113,6 +117,32 @@ def rms_modulate(x, scale, shift, eps, out=None, variant=RMS_PINNED,
         raise ValueError("oracle_rms_modulate: D must be a multiple of 8 and "
                          "partials a power of two <= 256")
     return out
+
+
+def gate_add_rms_modulate(x, u, g, scale, shift, eps, gate_mode, x_out=None,
+                          partials=64):
+    """x_out = bf16(x + u*g) (as gate_add), then y = rms_modulate(x_out,
+    scale, shift, eps). Returns (x_out, y). ``x_out`` may be ``x``."""
+    x, u, g = _bits(x, "x"), _bits(u, "u"), _bits(g, "g")
+    scale, shift = _bits(scale, "scale"), _bits(shift, "shift")
+    B, L, D = x.shape
+    if u.shape != x.shape:
+        raise ValueError("x and u must share one [B, L, D] shape")
+    want = x.shape if gate_mode == GATE_FULL else (B, 1, D)
+    if gate_mode not in (GATE_FULL, GATE_BCAST) or g.shape != want:
+        raise ValueError(f"gate shape {g.shape} does not fit mode {gate_mode}")
+    if scale.shape != (B, 1, D) or shift.shape != (B, 1, D):
+        raise ValueError("scale and shift must be [B, 1, D]")
+    if x_out is None:
+        x_out = np.empty_like(x)
+    x_out = _bits(x_out, "x_out")
+    y = np.empty_like(x)
+    rc = _load().oracle_gate_add_rms_modulate(
+        _ptr(x), _ptr(u), _ptr(g), _ptr(scale), _ptr(shift), float(eps),
+        _ptr(x_out), _ptr(y), B, L, D, gate_mode, partials)
+    if rc:
+        raise ValueError("oracle_gate_add_rms_modulate: bad D or partials")
+    return x_out, y
 
 
 def rms_norm(x, eps, partials=64):

@@ -269,6 +269,29 @@ int oracle_rms_norm(const uint16_t* x, float eps, uint16_t* out, int64_t B,
     return 0;
 }
 
+/* ---- residual update followed by the next modulation --------------------
+ *
+ * The two steps that follow each other in a DiT block (the residual-gate
+ * update of hidden_states, then the adaLN modulation of the updated
+ * hidden_states before the next sub-layer): x_out = bf16(x + u * g) exactly
+ * as oracle_gate_add, then y = oracle_rms_modulate(x_out, scale, shift, eps)
+ * on the rounded bf16 x_out. Written as the composition of the two
+ * functions, so it is their definition by construction. x_out may be x or u.
+ * Returns nonzero for an invalid P or D % 8 != 0.
+ */
+int oracle_gate_add_rms_modulate(const uint16_t* x, const uint16_t* u,
+                                 const uint16_t* g, const uint16_t* scale,
+                                 const uint16_t* shift, float eps,
+                                 uint16_t* x_out, uint16_t* y, int64_t B,
+                                 int64_t L, int64_t D, int gate_mode, int P)
+{
+    if (bad_partials(P) || D % 8 != 0)
+        return 1;
+    oracle_gate_add(x, u, g, x_out, B, L, D, gate_mode);
+    return oracle_rms_modulate(x_out, scale, shift, eps, y, B, L, D,
+                               ORACLE_RMS_PINNED, P);
+}
+
 /* ---- build self-check ------------------------------------------------------
  *
  * With a = b = 1 + 2^-12 and c = -(1 + 2^-11): a*b = 1 + 2^-11 + 2^-24

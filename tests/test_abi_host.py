@@ -199,3 +199,34 @@ def test_one_hip_runtime_per_process():
     assert lines[0] == "1", lines
     import torch
     assert os.path.dirname(torch.__file__) in lines[1], lines
+
+
+def test_fused_validation_rules(dte):
+    ck = dte.check_gate_add_rms_modulate
+    FULL, BCAST = dte.GATE_FULL, dte.GATE_BCAST
+    ok, bad, uns, ali = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED, dte.RGA_ERR_ALIAS
+    x, u, g, s, t, xo, y = (A + k * 64 * MB for k in range(7))
+    args = lambda **kw: {**dict(x=x, u=u, g=g, scale=s, shift=t, eps=1e-6, x_out=xo, y=y,
+                                B=2, L=5, D=4096, gate_mode=BCAST), **kw}
+    call = lambda **kw: ck(*args(**kw).values())
+    assert call() == ok
+    assert call(gate_mode=FULL) == ok
+    assert call(gate_mode=3) == bad
+    assert call(eps=-1.0) == bad
+    assert call(eps=float("nan")) == bad
+    assert call(B=-1) == bad
+    assert call(y=0) == bad
+    assert call(x=0, u=0, g=0, scale=0, shift=0, x_out=0, y=0, L=0) == ok
+    assert call(D=4100) == uns
+    assert call(D=8200) == uns
+    assert call(shift=t + 8) == uns
+    # in place: each output may be x or u (or g in full mode)
+    assert call(x_out=x) == ok
+    assert call(x_out=u, y=x) == ok
+    assert call(y=u) == ok
+    assert call(x_out=g, gate_mode=FULL) == ok
+    assert call(x_out=g, gate_mode=BCAST) == ali
+    assert call(x_out=x, y=x) == ali           # both outputs on one buffer
+    assert call(y=xo + 16) == ali              # outputs overlap
+    assert call(y=s) == ali                    # output over scale row
+    assert call(x_out=x + 32) == ali           # partial overlap with x

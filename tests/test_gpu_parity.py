@@ -273,3 +273,40 @@ def test_read_helper_folds_every_word(dte):
     dte.read_(src, sink)
     want = np.bitwise_xor.reduce(src.cpu().numpy().reshape(-1, 4), axis=0)
     assert np.array_equal(sink.cpu().numpy(), want)
+
+
+def _fused_case(dte, B, L, D, mode, seed, inplace=None):
+    x = random_bits(seed, (B, L, D), N02)
+    u = random_bits(seed + 1, (B, L, D), N01)
+    g = random_bits(seed + 2, (B, L, D) if mode == GATE_FULL else (B, 1, D), N001)
+    s = random_bits(seed + 3, (B, 1, D), N001)
+    t = random_bits(seed + 4, (B, 1, D), N001)
+    want_x, want_y = oracle.gate_add_rms_modulate(x, u, g, s, t, 1e-6, mode)
+    xd, ud, gd = to_dev(x), to_dev(u), to_dev(g)
+    xo = {"x": xd, "u": ud}.get(inplace[0]) if inplace else None
+    yo = {"x": xd, "u": ud}.get(inplace[1]) if inplace else None
+    got_x, got_y = dte.rga_gate_add_rms_modulate(xd, ud, gd, to_dev(s), to_dev(t), 1e-6,
+                                                 x_out=xo, y=yo, gate_mode=mode)
+    hx, hy = to_host(got_x), to_host(got_y)
+    assert same_bits(hx, want_x), first_mismatch(hx, want_x)
+    d = _rms_check(hy, want_y, f"fused {B}x{L}x{D} mode {mode}")
+    assert d.max() == 0
+
+
+@pytest.mark.parametrize("mode", [GATE_FULL, GATE_BCAST])
+def test_fused_residual_then_modulation_at_video_scale(dte, mode):
+    say(f"[fused] [2,32640,4096] mode={mode}")
+    _fused_case(dte, 2, 32640, 4096, mode, 1200 + mode)
+
+
+@pytest.mark.parametrize("B,L,D", RAGGED + [(1, 17, 6144)])
+@pytest.mark.parametrize("mode", [GATE_FULL, GATE_BCAST])
+def test_fused_ragged_shapes(dte, B, L, D, mode):
+    say(f"[fused ragged] B={B} L={L} D={D} mode={mode}")
+    _fused_case(dte, B, L, D, mode, 1300 + 3 * B + L + D + mode)
+
+
+@pytest.mark.parametrize("inplace", [("x", None), ("u", "x"), (None, "u"), ("x", "u")])
+def test_fused_in_place(dte, inplace):
+    say(f"[fused in place] x_out={inplace[0]} y={inplace[1]}")
+    _fused_case(dte, 2, 301, 2048, GATE_BCAST, 1400, inplace=inplace)

@@ -210,3 +210,25 @@ def test_rejects_d_not_multiple_of_8():
     s = np.zeros((1, 1, 12), dtype=np.uint16)
     with pytest.raises(ValueError):
         oracle.rms_modulate(x, s, s, EPS)
+
+
+@pytest.mark.parametrize("mode", [oracle.GATE_FULL, oracle.GATE_BCAST])
+def test_fused_residual_then_modulation_is_the_composition(mode):
+    # the fused step is defined as the two operations in sequence, the
+    # modulation reading the bf16-rounded updated residual
+    B, L, D = 2, 17, 1032
+    x = random_bits(1100, (B, L, D), N02)
+    u = random_bits(1101, (B, L, D), N01)
+    g = random_bits(1102, (B, L, D) if mode == oracle.GATE_FULL else (B, 1, D), N001)
+    s = random_bits(1103, (B, 1, D), N001)
+    t = random_bits(1104, (B, 1, D), N001)
+    xo, y = oracle.gate_add_rms_modulate(x, u, g, s, t, EPS, mode)
+    want_x = oracle.gate_add(x, u, g, mode)
+    assert np.array_equal(xo, want_x)
+    assert np.array_equal(y, oracle.rms_modulate(want_x, s, t, EPS))
+    # in place on x gives the same two outputs
+    xx = x.copy()
+    xo2, y2 = oracle.gate_add_rms_modulate(xx, u, g, s, t, EPS, mode, x_out=xx)
+    assert np.array_equal(xx, want_x) and np.array_equal(y2, y)
+    # and the modulation is within the binary64 bound of the updated residual
+    _check_against_f64(y, want_x, s, t, EPS)
