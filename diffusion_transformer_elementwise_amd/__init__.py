@@ -13,12 +13,25 @@ There is no CPU path: importing fails loudly when the library is not built.
 
 Tensors are contiguous bf16 on one HIP device; x, u, out are [B, L, D]; g is
 [B, L, D] (full) or [B, 1, D] (broadcast); scale and shift are [B, 1, D].
+
+The ``_ex`` forms take bf16, float16 or float32 (one type per call), any D,
+tensors starting at any element offset, and per-token scale/shift [B, L, D]:
+
+    rga_residual_gate_add_ex(x, u, g, out=None, gate_mode=None)
+    rga_rms_modulate_ex(x, scale, shift, eps=1e-6, out=None, mod_mode=None)
+    rga_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps=1e-6, x_out=None,
+                                 y=None, gate_mode=None, mod_mode=None)
 """
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F16,
+    DTYPE_F32,
     GATE_BCAST,
     GATE_FULL,
+    MOD_ROW,
+    MOD_TOKEN,
     RGA_ERR_ALIAS,
     RGA_ERR_HIP,
     RGA_ERR_INVALID_ARG,
@@ -27,8 +40,11 @@ from ._lib import (  # noqa: F401
     RGA_RMS_MAX_D,
     RGAError,
     check_gate_add_rms_modulate,
+    check_gate_add_rms_modulate_ex,
     check_residual_gate_add,
+    check_residual_gate_add_ex,
     check_rms_modulate,
+    check_rms_modulate_ex,
     library,
     library_path,
     status_string,
@@ -38,7 +54,10 @@ from .ops import (  # noqa: F401
     fill_,
     read_,
     rga_gate_add_rms_modulate,
+    rga_gate_add_rms_modulate_ex,
     rga_residual_gate_add,
+    rga_residual_gate_add_ex,
+    rga_rms_modulate_ex,
     rms_modulate,
 )
 
@@ -46,6 +65,9 @@ __all__ = [
     "rga_residual_gate_add",
     "rms_modulate",
     "rga_gate_add_rms_modulate",
+    "rga_residual_gate_add_ex",
+    "rga_rms_modulate_ex",
+    "rga_gate_add_rms_modulate_ex",
     "GATE_FULL",
     "GATE_BCAST",
     "RGAError",

@@ -23,6 +23,13 @@ _PATH = os.path.join(_HERE, "librga.so")
 GATE_FULL = 0
 GATE_BCAST = 1
 
+DTYPE_BF16 = 0
+DTYPE_F16 = 1
+DTYPE_F32 = 2
+
+MOD_ROW = 0
+MOD_TOKEN = 1
+
 RGA_OK = 0
 RGA_ERR_INVALID_ARG = 1
 RGA_ERR_UNSUPPORTED = 2
@@ -65,6 +72,20 @@ def _load():
     lib.rga_gate_add_rms_modulate.restype = i32
     lib.rga_check_gate_add_rms_modulate.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32]
     lib.rga_check_gate_add_rms_modulate.restype = i32
+    lib.rga_residual_gate_add_ex.argtypes = [p, p, p, p, i64, i64, i64, i32, i32, p]
+    lib.rga_residual_gate_add_ex.restype = i32
+    lib.rga_rms_modulate_ex.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, i32, p]
+    lib.rga_rms_modulate_ex.restype = i32
+    lib.rga_gate_add_rms_modulate_ex.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64,
+                                                 i32, i32, i32, p]
+    lib.rga_gate_add_rms_modulate_ex.restype = i32
+    lib.rga_check_residual_gate_add_ex.argtypes = [p, p, p, p, i64, i64, i64, i32, i32]
+    lib.rga_check_residual_gate_add_ex.restype = i32
+    lib.rga_check_rms_modulate_ex.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, i32]
+    lib.rga_check_rms_modulate_ex.restype = i32
+    lib.rga_check_gate_add_rms_modulate_ex.argtypes = [p, p, p, p, p, f32, p, p, i64, i64,
+                                                       i64, i32, i32, i32]
+    lib.rga_check_gate_add_rms_modulate_ex.restype = i32
     lib.rga_status_string.argtypes = [i32]
     lib.rga_status_string.restype = ctypes.c_char_p
     lib.rga_copy.argtypes = [p, p, i64, p]
@@ -100,3 +121,19 @@ def check_gate_add_rms_modulate(x, u, g, scale, shift, eps, x_out, y, B, L, D,
                                 gate_mode) -> int:
     return _LIB.rga_check_gate_add_rms_modulate(x, u, g, scale, shift, eps,
                                                 x_out, y, B, L, D, gate_mode)
+
+
+def check_residual_gate_add_ex(x, u, g, out, B, L, D, gate_mode, dtype) -> int:
+    return _LIB.rga_check_residual_gate_add_ex(x, u, g, out, B, L, D, gate_mode, dtype)
+
+
+def check_rms_modulate_ex(x, scale, shift, eps, out, B, L, D, mod_mode, dtype) -> int:
+    return _LIB.rga_check_rms_modulate_ex(x, scale, shift, eps, out, B, L, D,
+                                          mod_mode, dtype)
+
+
+def check_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                                   gate_mode, mod_mode, dtype) -> int:
+    return _LIB.rga_check_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps, x_out,
+                                                   y, B, L, D, gate_mode, mod_mode,
+                                                   dtype)

@@ -2,14 +2,20 @@
 // validation, then one kernel launch on the caller's stream.
 //
 // Validation order (the first failing rule decides the status):
-//   1. RGA_ERR_INVALID_ARG: a negative dimension, a bad gate_mode, a
-//      non-finite or negative eps, B*L*D*2 bytes overflowing int64;
+//   1. RGA_ERR_INVALID_ARG: a negative dimension, a bad gate_mode, mod_mode
+//      or dtype, a non-finite or negative eps, the byte size overflowing
+//      int64;
 //   2. RGA_OK without a launch when B*L*D == 0 (pointers may be NULL);
 //   3. RGA_ERR_INVALID_ARG: a NULL pointer;
-//   4. RGA_ERR_UNSUPPORTED: D % 8 != 0, a pointer not 16-byte aligned, D
-//      above RGA_RMS_MAX_D (modulation), a grid beyond the dispatch limit;
-//   5. RGA_ERR_ALIAS: out overlapping an input other than the exact in-place
-//      aliases each call allows.
+//   4. RGA_ERR_UNSUPPORTED: for the original calls D % 8 != 0, a pointer not
+//      16-byte aligned or D above RGA_RMS_MAX_D (modulation); for the _ex
+//      calls a pointer not aligned to the element size; a grid beyond the
+//      dispatch limit;
+//   5. RGA_ERR_ALIAS: an output overlapping an input other than the exact
+//      in-place aliases each call allows.
+// The _ex calls take the 16-byte-pack kernels when D % 8 == 0, every pointer
+// is 16-byte aligned and (modulation) D <= RGA_RMS_MAX_D, and the
+// element-wise kernels otherwise.
 // The gate-add rejection of unsupported inputs mirrors the residual-gate
 // page's test list ("unsupported input rejection"); the bf16-only contract
 // mirrors the modulation page's guard that admits only bf16 tensors.
@@ -52,34 +58,67 @@ bool sizes(int64_t B, int64_t L, int64_t D, int64_t* elems, int64_t* bytes)
     return !__builtin_mul_overflow(*elems, (int64_t)2, bytes);
 }
 
-}  // namespace
+int elem_size(int dtype) { return dtype == RGA_DTYPE_F32 ? 4 : 2; }
 
-extern "C" {
+bool valid_dtype(int dtype)
+{
+    return dtype == RGA_DTYPE_BF16 || dtype == RGA_DTYPE_F16 ||
+           dtype == RGA_DTYPE_F32;
+}
 
-int rga_check_residual_gate_add(const void* x, const void* u, const void* g,
-                                const void* out, int64_t B, int64_t L,
-                                int64_t D, int gate_mode)
+bool aligned_to(const void* p, int n)
+{
+    return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(n - 1)) == 0;
+}
+
+// Layout rule shared by the three operations. strict: the original calls
+// (bf16 only, D % 8 == 0 and 16-byte alignment or RGA_ERR_UNSUPPORTED);
+// otherwise pointers need only element alignment and *fast tells whether the
+// 16-byte-pack kernels can run. max_d > 0 caps the fast path's D (the
+// modulation holds a row in registers); in strict mode a larger D is
+// unsupported.
+int layout(const void* const* ptrs, int nptr, int64_t D, int es, bool strict,
+           int64_t max_d, bool* fast)
+{
+    bool all16 = true;
+    for (int i = 0; i < nptr; ++i) {
+        if (!aligned_to(ptrs[i], es))
+            return RGA_ERR_UNSUPPORTED;
+        all16 = all16 && aligned16(ptrs[i]);
+    }
+    *fast = all16 && D % 8 == 0 && (max_d <= 0 || D <= max_d);
+    if (strict && !*fast)
+        return RGA_ERR_UNSUPPORTED;
+    return RGA_OK;
+}
+
+int check_gate_add(const void* x, const void* u, const void* g,
+                   const void* out, int64_t B, int64_t L, int64_t D,
+                   int gate_mode, int dtype, bool strict, bool* fast)
 {
     if (B < 0 || L < 0 || D < 0)
         return RGA_ERR_INVALID_ARG;
     if (gate_mode != RGA_GATE_FULL && gate_mode != RGA_GATE_BCAST)
         return RGA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype))
+        return RGA_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
     int64_t n = 0, bytes = 0;
-    if (!sizes(B, L, D, &n, &bytes))
+    if (!sizes(B, L, D, &n, &bytes) || __builtin_mul_overflow(n, (int64_t)es, &bytes))
         return RGA_ERR_INVALID_ARG;
     if (n == 0)
         return RGA_OK;
     if (!x || !u || !g || !out)
         return RGA_ERR_INVALID_ARG;
-    if (D % 8 != 0)
-        return RGA_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(u) || !aligned16(g) || !aligned16(out))
-        return RGA_ERR_UNSUPPORTED;
-    if (!rga::gate_add_grid_fits(B, L, D, gate_mode))
+    const void* ptrs[] = {x, u, g, out};
+    int st = layout(ptrs, 4, D, es, strict, 0, fast);
+    if (st != RGA_OK)
+        return st;
+    if (!rga::gate_add_grid_fits(B, L, D, gate_mode, *fast))
         return RGA_ERR_UNSUPPORTED;
 
     const bool full = gate_mode == RGA_GATE_FULL;
-    const int64_t gate_bytes = full ? bytes : B * D * 2;  // <= bytes
+    const int64_t gate_bytes = full ? bytes : B * D * es;  // <= bytes
     const Range o = range_of(out, bytes);
     if (overlaps(o, range_of(x, bytes)) && out != x)
         return RGA_ERR_ALIAS;
@@ -90,72 +129,79 @@ int rga_check_residual_gate_add(const void* x, const void* u, const void* g,
     return RGA_OK;
 }
 
-int rga_check_rms_modulate(const void* x, const void* scale,
-                           const void* shift, float eps, const void* out,
-                           int64_t B, int64_t L, int64_t D)
+int check_rms(const void* x, const void* scale, const void* shift, float eps,
+              const void* out, int64_t B, int64_t L, int64_t D, int mod_mode,
+              int dtype, bool strict, bool* fast)
 {
     if (B < 0 || L < 0 || D < 0)
         return RGA_ERR_INVALID_ARG;
     if (!std::isfinite(eps) || eps < 0.0f)
         return RGA_ERR_INVALID_ARG;
+    if (mod_mode != RGA_MOD_ROW && mod_mode != RGA_MOD_TOKEN)
+        return RGA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype))
+        return RGA_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
     int64_t n = 0, bytes = 0;
-    if (!sizes(B, L, D, &n, &bytes))
+    if (!sizes(B, L, D, &n, &bytes) || __builtin_mul_overflow(n, (int64_t)es, &bytes))
         return RGA_ERR_INVALID_ARG;
     if (n == 0)
         return RGA_OK;
     if (!x || !scale || !shift || !out)
         return RGA_ERR_INVALID_ARG;
-    if (D % 8 != 0 || D > RGA_RMS_MAX_D)
-        return RGA_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(scale) || !aligned16(shift) ||
-        !aligned16(out))
-        return RGA_ERR_UNSUPPORTED;
-    if (!rga::rms_modulate_grid_fits(B, L, D))
+    const void* ptrs[] = {x, scale, shift, out};
+    int st = layout(ptrs, 4, D, es, strict, RGA_RMS_MAX_D, fast);
+    if (st != RGA_OK)
+        return st;
+    if (!rga::rms_modulate_grid_fits(B, L, D, *fast))
         return RGA_ERR_UNSUPPORTED;
 
-    const int64_t row_bytes = B * D * 2;
+    const int64_t mod_bytes = mod_mode == RGA_MOD_TOKEN ? bytes : B * D * es;
     const Range o = range_of(out, bytes);
     if (overlaps(o, range_of(x, bytes)) && out != x)
         return RGA_ERR_ALIAS;
-    if (overlaps(o, range_of(scale, row_bytes)))
+    if (overlaps(o, range_of(scale, mod_bytes)))
         return RGA_ERR_ALIAS;
-    if (overlaps(o, range_of(shift, row_bytes)))
+    if (overlaps(o, range_of(shift, mod_bytes)))
         return RGA_ERR_ALIAS;
     return RGA_OK;
 }
 
-int rga_check_gate_add_rms_modulate(const void* x, const void* u,
-                                    const void* g, const void* scale,
-                                    const void* shift, float eps,
-                                    const void* x_out, const void* y,
-                                    int64_t B, int64_t L, int64_t D,
-                                    int gate_mode)
+int check_fused(const void* x, const void* u, const void* g,
+                const void* scale, const void* shift, float eps,
+                const void* x_out, const void* y, int64_t B, int64_t L,
+                int64_t D, int gate_mode, int mod_mode, int dtype,
+                bool strict, bool* fast)
 {
     if (B < 0 || L < 0 || D < 0)
         return RGA_ERR_INVALID_ARG;
     if (gate_mode != RGA_GATE_FULL && gate_mode != RGA_GATE_BCAST)
         return RGA_ERR_INVALID_ARG;
+    if (mod_mode != RGA_MOD_ROW && mod_mode != RGA_MOD_TOKEN)
+        return RGA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype))
+        return RGA_ERR_INVALID_ARG;
     if (!std::isfinite(eps) || eps < 0.0f)
         return RGA_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
     int64_t n = 0, bytes = 0;
-    if (!sizes(B, L, D, &n, &bytes))
+    if (!sizes(B, L, D, &n, &bytes) || __builtin_mul_overflow(n, (int64_t)es, &bytes))
         return RGA_ERR_INVALID_ARG;
     if (n == 0)
         return RGA_OK;
     if (!x || !u || !g || !scale || !shift || !x_out || !y)
         return RGA_ERR_INVALID_ARG;
-    if (D % 8 != 0 || D > RGA_RMS_MAX_D)
-        return RGA_ERR_UNSUPPORTED;
-    const void* all[] = {x, u, g, scale, shift, x_out, y};
-    for (const void* p : all)
-        if (!aligned16(p))
-            return RGA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {x, u, g, scale, shift, x_out, y};
+    int st = layout(ptrs, 7, D, es, strict, RGA_RMS_MAX_D, fast);
+    if (st != RGA_OK)
+        return st;
     if (!rga::gate_add_rms_modulate_grid_fits(B, L, D))
         return RGA_ERR_UNSUPPORTED;
 
     const bool full = gate_mode == RGA_GATE_FULL;
-    const int64_t row_bytes = B * D * 2;
-    const Range rows[] = {range_of(scale, row_bytes), range_of(shift, row_bytes)};
+    const int64_t row_bytes = B * D * es;
+    const int64_t mod_bytes = mod_mode == RGA_MOD_TOKEN ? bytes : row_bytes;
+    const Range mods[] = {range_of(scale, mod_bytes), range_of(shift, mod_bytes)};
     const void* outs[] = {x_out, y};
     for (const void* o : outs) {
         const Range r = range_of(o, bytes);
@@ -165,7 +211,7 @@ int rga_check_gate_add_rms_modulate(const void* x, const void* u,
             return RGA_ERR_ALIAS;
         if (overlaps(r, range_of(g, full ? bytes : row_bytes)) && !(full && o == g))
             return RGA_ERR_ALIAS;
-        for (const Range& q : rows)
+        for (const Range& q : mods)
             if (overlaps(r, q))
                 return RGA_ERR_ALIAS;
     }
@@ -174,47 +220,164 @@ int rga_check_gate_add_rms_modulate(const void* x, const void* u,
     return RGA_OK;
 }
 
-int rga_gate_add_rms_modulate(const void* x, const void* u, const void* g,
-                              const void* scale, const void* shift, float eps,
-                              void* x_out, void* y, int64_t B, int64_t L,
-                              int64_t D, int gate_mode, hipStream_t stream)
+int launched(hipError_t e) { return e == hipSuccess ? RGA_OK : RGA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int rga_check_residual_gate_add(const void* x, const void* u, const void* g,
+                                const void* out, int64_t B, int64_t L,
+                                int64_t D, int gate_mode)
 {
-    const int st = rga_check_gate_add_rms_modulate(
-        x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode);
+    bool fast = false;
+    return check_gate_add(x, u, g, out, B, L, D, gate_mode, RGA_DTYPE_BF16,
+                          true, &fast);
+}
+
+int rga_check_residual_gate_add_ex(const void* x, const void* u,
+                                   const void* g, const void* out, int64_t B,
+                                   int64_t L, int64_t D, int gate_mode,
+                                   int dtype)
+{
+    bool fast = false;
+    return check_gate_add(x, u, g, out, B, L, D, gate_mode, dtype, false,
+                          &fast);
+}
+
+int rga_check_rms_modulate(const void* x, const void* scale,
+                           const void* shift, float eps, const void* out,
+                           int64_t B, int64_t L, int64_t D)
+{
+    bool fast = false;
+    return check_rms(x, scale, shift, eps, out, B, L, D, RGA_MOD_ROW,
+                     RGA_DTYPE_BF16, true, &fast);
+}
+
+int rga_check_rms_modulate_ex(const void* x, const void* scale,
+                              const void* shift, float eps, const void* out,
+                              int64_t B, int64_t L, int64_t D, int mod_mode,
+                              int dtype)
+{
+    bool fast = false;
+    return check_rms(x, scale, shift, eps, out, B, L, D, mod_mode, dtype,
+                     false, &fast);
+}
+
+int rga_check_gate_add_rms_modulate(const void* x, const void* u,
+                                    const void* g, const void* scale,
+                                    const void* shift, float eps,
+                                    const void* x_out, const void* y,
+                                    int64_t B, int64_t L, int64_t D,
+                                    int gate_mode)
+{
+    bool fast = false;
+    return check_fused(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                       gate_mode, RGA_MOD_ROW, RGA_DTYPE_BF16, true, &fast);
+}
+
+int rga_check_gate_add_rms_modulate_ex(const void* x, const void* u,
+                                       const void* g, const void* scale,
+                                       const void* shift, float eps,
+                                       const void* x_out, const void* y,
+                                       int64_t B, int64_t L, int64_t D,
+                                       int gate_mode, int mod_mode, int dtype)
+{
+    bool fast = false;
+    return check_fused(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                       gate_mode, mod_mode, dtype, false, &fast);
+}
+
+static int gate_add(const void* x, const void* u, const void* g, void* out,
+                    int64_t B, int64_t L, int64_t D, int gate_mode, int dtype,
+                    bool strict, hipStream_t stream)
+{
+    bool fast = false;
+    const int st = check_gate_add(x, u, g, out, B, L, D, gate_mode, dtype,
+                                  strict, &fast);
     if (st != RGA_OK || B == 0 || L == 0 || D == 0)
         return st;
-    return rga::launch_gate_add_rms_modulate(x, u, g, scale, shift, eps,
-                                             x_out, y, B, L, D, gate_mode,
-                                             stream) == hipSuccess
-               ? RGA_OK
-               : RGA_ERR_HIP;
+    return launched(rga::launch_gate_add(x, u, g, out, B, L, D, gate_mode,
+                                         dtype, fast, stream));
 }
 
 int rga_residual_gate_add(const void* x, const void* u, const void* g,
                           void* out, int64_t B, int64_t L, int64_t D,
                           int gate_mode, hipStream_t stream)
 {
-    const int st =
-        rga_check_residual_gate_add(x, u, g, out, B, L, D, gate_mode);
+    return gate_add(x, u, g, out, B, L, D, gate_mode, RGA_DTYPE_BF16, true,
+                    stream);
+}
+
+int rga_residual_gate_add_ex(const void* x, const void* u, const void* g,
+                             void* out, int64_t B, int64_t L, int64_t D,
+                             int gate_mode, int dtype, hipStream_t stream)
+{
+    return gate_add(x, u, g, out, B, L, D, gate_mode, dtype, false, stream);
+}
+
+static int rms(const void* x, const void* scale, const void* shift, float eps,
+               void* out, int64_t B, int64_t L, int64_t D, int mod_mode,
+               int dtype, bool strict, hipStream_t stream)
+{
+    bool fast = false;
+    const int st = check_rms(x, scale, shift, eps, out, B, L, D, mod_mode,
+                             dtype, strict, &fast);
     if (st != RGA_OK || B == 0 || L == 0 || D == 0)
         return st;
-    return rga::launch_gate_add(x, u, g, out, B, L, D, gate_mode, stream) ==
-                   hipSuccess
-               ? RGA_OK
-               : RGA_ERR_HIP;
+    return launched(rga::launch_rms_modulate(x, scale, shift, eps, out, B, L,
+                                             D, mod_mode, dtype, fast,
+                                             stream));
 }
 
 int rms_modulate(const void* x, const void* scale, const void* shift,
                  float eps, void* out, int64_t B, int64_t L, int64_t D,
                  hipStream_t stream)
 {
-    const int st = rga_check_rms_modulate(x, scale, shift, eps, out, B, L, D);
+    return rms(x, scale, shift, eps, out, B, L, D, RGA_MOD_ROW,
+               RGA_DTYPE_BF16, true, stream);
+}
+
+int rga_rms_modulate_ex(const void* x, const void* scale, const void* shift,
+                        float eps, void* out, int64_t B, int64_t L, int64_t D,
+                        int mod_mode, int dtype, hipStream_t stream)
+{
+    return rms(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, false,
+               stream);
+}
+
+static int fused(const void* x, const void* u, const void* g,
+                 const void* scale, const void* shift, float eps, void* x_out,
+                 void* y, int64_t B, int64_t L, int64_t D, int gate_mode,
+                 int mod_mode, int dtype, bool strict, hipStream_t stream)
+{
+    bool fast = false;
+    const int st = check_fused(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                               gate_mode, mod_mode, dtype, strict, &fast);
     if (st != RGA_OK || B == 0 || L == 0 || D == 0)
         return st;
-    return rga::launch_rms_modulate(x, scale, shift, eps, out, B, L, D,
-                                    stream) == hipSuccess
-               ? RGA_OK
-               : RGA_ERR_HIP;
+    return launched(rga::launch_gate_add_rms_modulate(
+        x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode,
+        dtype, fast, stream));
+}
+
+int rga_gate_add_rms_modulate(const void* x, const void* u, const void* g,
+                              const void* scale, const void* shift, float eps,
+                              void* x_out, void* y, int64_t B, int64_t L,
+                              int64_t D, int gate_mode, hipStream_t stream)
+{
+    return fused(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode,
+                 RGA_MOD_ROW, RGA_DTYPE_BF16, true, stream);
+}
+
+int rga_gate_add_rms_modulate_ex(const void* x, const void* u, const void* g,
+                                 const void* scale, const void* shift,
+                                 float eps, void* x_out, void* y, int64_t B,
+                                 int64_t L, int64_t D, int gate_mode,
+                                 int mod_mode, int dtype, hipStream_t stream)
+{
+    return fused(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode,
+                 mod_mode, dtype, false, stream);
 }
 
 // Shared rules of the measurement helpers for one destination range and an

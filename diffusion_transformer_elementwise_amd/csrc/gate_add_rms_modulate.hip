@@ -6,22 +6,29 @@
 // LTX2", "Motivation") and the modulation of the updated hidden_states before
 // the next sub-layer (prhub summary of sglang PR #34172, "关键源码片段", the
 // adaLN sites of LTX2TransformerBlock.forward). Run separately they move
-// 10 bytes per element (x, u in, x_out out; x_out in, y out); fused, x_out is
-// never read back: 8 bytes per element.
+// 10 bytes per element (x, u in, x_out out; x_out in, y out) for bf16; fused,
+// x_out is never read back: 8 bytes per element.
 //
 // Arithmetic is exactly that of the two separate operations: x_out is
-// rounded to bf16 first, and the modulation works on the rounded values with
-// the library's fixed reduction order (lane j accumulates groups j, j+64, ...
-// of the row, then xor-distance lane exchanges 1..32), so the outputs are
-// bit-identical to rga_residual_gate_add followed by rms_modulate.
+// rounded to the storage type first, and the modulation works on the rounded
+// values with the library's fixed reduction order (lane j accumulates groups
+// j, j+64, ... of the row, then xor-distance lane exchanges 1..32), so the
+// outputs are bit-identical to rga_residual_gate_add followed by
+// rms_modulate.
 //
-// Launch shape (measured on MI355X): one wave per workgroup and one row per
-// wave, nontemporal loads and stores; each x_out vector is stored as soon as
-// it is formed, and scale and shift are read through the caches only in the
-// apply phase, which keeps the wave at 79 registers for D = 4096. A
-// broadcast gate row is read through the caches (it stays in L2), a full gate
-// streams from HBM like x and u.
-#include "bf16x8.hpp"
+// Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers),
+// launch shape measured on MI355X: one wave per workgroup and one row per
+// wave, nontemporal loads and stores; each x_out pack is stored as soon as it
+// is formed, and scale and shift are read only in the apply phase (through
+// the caches for row modulation, streamed for per-token modulation), which
+// keeps the wave at 79 registers for bf16 and D = 4096. A broadcast gate row
+// is read through the caches (it stays in L2), a full gate streams from HBM
+// like x and u.
+//
+// Generic path (any D, element-aligned pointers): the same operations in two
+// passes over the row, element by element; the second pass re-reads x_out,
+// which the same lane wrote in the first.
+#include "dtype.hpp"
 #include "launch.hpp"
 
 #include <rga.h>
@@ -31,47 +38,59 @@ namespace {
 
 constexpr int kBlock = 64;
 
-__device__ __forceinline__ u32x4 gate_add8(u32x4 x, u32x4 u, u32x4 g)
+template <int DT>
+__device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
+                                              const Pack<DT>& u,
+                                              const Pack<DT>& g)
 {
-    u32x4 o;
+    float o[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float p0 = bf16_lo(u[i]) * bf16_lo(g[i]);
-        const float p1 = bf16_hi(u[i]) * bf16_hi(g[i]);
-        const float s0 = bf16_lo(x[i]) + p0;
-        const float s1 = bf16_hi(x[i]) + p1;
-        o[i] = pack_bf16(s0, s1);
+    for (int e = 0; e < 8; ++e) {
+        const float p = u.get(e) * g.get(e);
+        o[e] = x.get(e) + p;
     }
-    return o;
+    return Pack<DT>::make(o);
 }
 
-// Grid: x = row l, y = batch b. G = ceil(D / 512) groups per lane; lanes
-// past the row end hold zeros (they add +0 to a partial that is never -0
-// and store nothing).
-template <int G, bool FULL>
+// binary32 value of s after one rounding to the storage type
+template <int DT>
+__device__ __forceinline__ float rounded(float s)
+{
+    if constexpr (DT == kF32) {
+        return s;
+    } else if constexpr (DT == kF16) {
+        return (float)(_Float16)s;
+    } else {
+        return __uint_as_float(pack_bf16(s, 0.0f) << 16);
+    }
+}
+
+// Grid: x = row l, y = batch b. G = packs per lane (at least ceil(D / 512));
+// lanes past the row end hold zeros (they add +0 to a partial that is never
+// -0 and store nothing).
+template <int G, bool FULL, int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
-    const u32x4* x, const u32x4* u, const u32x4* g, const u32x4* scale,
-    const u32x4* shift, float eps, float d_float, u32x4* x_out, u32x4* y,
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
     int64_t L, int vpr)
 {
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * vpr;
-    const u32x4 zero = {0, 0, 0, 0};
 
-    u32x4 xn[G];
+    Pack<DT> xn[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int col = lane + 64 * i;
         if (col < vpr) {
-            const u32x4 xv = load16_stream(x + row + col);
-            const u32x4 uv = load16_stream(u + row + col);
-            const u32x4 gv = FULL ? load16_stream(g + row + col)
-                                  : load16(g + b * vpr + col);
-            xn[i] = gate_add8(xv, uv, gv);
-            store16_stream(x_out + row + col, xn[i]);
+            const Pack<DT> xv = Pack<DT>::load_stream(x, row + col);
+            const Pack<DT> uv = Pack<DT>::load_stream(u, row + col);
+            const Pack<DT> gv = FULL ? Pack<DT>::load_stream(g, row + col)
+                                     : Pack<DT>::load(g, b * vpr + col);
+            xn[i] = gate_add8<DT>(xv, uv, gv);
+            xn[i].store_stream(x_out, row + col);
         } else {
-            xn[i] = zero;
+            xn[i] = Pack<DT>::zero();
         }
     }
 
@@ -79,13 +98,10 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
 #pragma unroll
     for (int i = 0; i < G; ++i) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float a = bf16_lo(xn[i][w]);
+        for (int e = 0; e < 8; ++e) {
+            const float a = xn[i].get(e);
             const float sa = a * a;
             acc = acc + sa;
-            const float c = bf16_hi(xn[i][w]);
-            const float sc2 = c * c;
-            acc = acc + sc2;
         }
     }
 #pragma unroll
@@ -101,44 +117,135 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
         const int col = lane + 64 * i;
         if (col >= vpr)
             continue;
-        const u32x4 sc = load16(scale + b * vpr + col);
-        const u32x4 sh = load16(shift + b * vpr + col);
-        u32x4 o;
+        const Pack<DT> sc = MOD == kModToken ? Pack<DT>::load_stream(scale, row + col)
+                                             : Pack<DT>::load(scale, b * vpr + col);
+        const Pack<DT> sh = MOD == kModToken ? Pack<DT>::load_stream(shift, row + col)
+                                             : Pack<DT>::load(shift, b * vpr + col);
+        float o[8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float n0 = bf16_lo(xn[i][w]) * rr;
-            const float n1 = bf16_hi(xn[i][w]) * rr;
-            const float a0 = 1.0f + bf16_lo(sc[w]);
-            const float a1 = 1.0f + bf16_hi(sc[w]);
-            const float m0 = n0 * a0;
-            const float m1 = n1 * a1;
-            const float y0 = m0 + bf16_lo(sh[w]);
-            const float y1 = m1 + bf16_hi(sh[w]);
-            o[w] = pack_bf16(y0, y1);
+        for (int e = 0; e < 8; ++e) {
+            const float n = xn[i].get(e) * rr;
+            const float a = 1.0f + sc.get(e);
+            const float m = n * a;
+            o[e] = m + sh.get(e);
         }
-        store16_stream(y + row + col, o);
+        Pack<DT>::make(o).store_stream(y, row + col);
     }
 }
 
-typedef void (*fused_kernel_t)(const u32x4*, const u32x4*, const u32x4*,
-                               const u32x4*, const u32x4*, float, float,
-                               u32x4*, u32x4*, int64_t, int);
+// Generic: one wave per row; grid x = row l, y = batch b.
+template <bool FULL, int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int64_t D)
+{
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t mrow = (MOD == kModToken) ? row : b * D;
+    const int64_t groups = (D + 7) / 8;
 
-template <bool FULL, int... Gs>
-struct FusedTable {
-    static fused_kernel_t get(int g)
-    {
-        fused_kernel_t table[] = {&gate_add_rms_modulate_kernel<Gs, FULL>...};
-        return (g >= 1 && g <= (int)sizeof...(Gs)) ? table[g - 1] : nullptr;
+    float acc = 0.0f;
+    for (int64_t k = lane; k < groups; k += 64) {
+        for (int e = 0; e < 8; ++e) {
+            const int64_t d = 8 * k + e;
+            if (d < D) {
+                const float p = load_elem<DT>(u, row + d) *
+                                load_elem<DT>(g, FULL ? row + d : b * D + d);
+                const float s = load_elem<DT>(x, row + d) + p;
+                store_elem<DT>(x_out, row + d, s);
+                const float v = rounded<DT>(s);
+                const float sv = v * v;
+                acc = acc + sv;
+            }
+        }
     }
-};
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        acc = acc + __shfl_xor(acc, m);
+    const float ms = acc / d_float;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    const float rr = 1.0f / q;
 
-template <bool FULL>
-using Table = FusedTable<FULL, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14,
-                         15, 16>;
-static_assert(RGA_RMS_MAX_D / 512 == 16, "table covers groups 1..16");
+    for (int64_t k = lane; k < groups; k += 64) {
+        for (int e = 0; e < 8; ++e) {
+            const int64_t d = 8 * k + e;
+            if (d < D) {
+                const float n = load_elem<DT>(x_out, row + d) * rr;
+                const float a = 1.0f + load_elem<DT>(scale, mrow + d);
+                const float m = n * a;
+                store_elem<DT>(y, row + d, m + load_elem<DT>(shift, mrow + d));
+            }
+        }
+    }
+}
+
+typedef void (*fused_kernel_t)(const void*, const void*, const void*,
+                               const void*, const void*, float, float, void*,
+                               void*, int64_t, int);
+
+constexpr int kLadder[] = {1, 2, 4, 6, 8, 12, 16};
+static_assert(RGA_RMS_MAX_D / 512 == 16, "ladder tops out at RGA_RMS_MAX_D");
+
+template <bool FULL, int DT, int MOD>
+fused_kernel_t pick(int groups)
+{
+    fused_kernel_t t[] = {&gate_add_rms_modulate_kernel<1, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<2, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<4, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<6, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<8, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<12, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<16, FULL, DT, MOD>};
+    for (int i = 0; i < 7; ++i)
+        if (groups <= kLadder[i])
+            return t[i];
+    return nullptr;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <bool FULL, int DT, int MOD>
+hipError_t launch_typed(const void* x, const void* u, const void* g,
+                        const void* scale, const void* shift, float eps,
+                        void* x_out, void* y, int64_t B, int64_t L, int64_t D,
+                        bool fast, hipStream_t stream)
+{
+    float d_float = (float)D;
+    if (!fast) {
+        void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &D};
+        return hipLaunchKernel(
+            reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
+            dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
+    }
+    int vpr = (int)(D / 8);
+    fused_kernel_t k = pick<FULL, DT, MOD>((int)ceil_div(vpr, 64));
+    if (k == nullptr)
+        return hipErrorInvalidValue;
+    void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k),
+                           dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
+                           stream);
+}
+
+template <int DT>
+hipError_t launch_dt(const void* x, const void* u, const void* g,
+                     const void* scale, const void* shift, float eps,
+                     void* x_out, void* y, int64_t B, int64_t L, int64_t D,
+                     int gate_mode, int mod_mode, bool fast, hipStream_t stream)
+{
+    const bool full = gate_mode == RGA_GATE_FULL;
+    const bool token = mod_mode == RGA_MOD_TOKEN;
+    if (full && token)
+        return launch_typed<true, DT, kModToken>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+    if (full)
+        return launch_typed<true, DT, kModRow>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+    if (token)
+        return launch_typed<false, DT, kModToken>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+    return launch_typed<false, DT, kModRow>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+}
 
 }  // namespace
 
@@ -153,26 +260,17 @@ hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
                                         const void* shift, float eps,
                                         void* x_out, void* y, int64_t B,
                                         int64_t L, int64_t D, int gate_mode,
+                                        int mod_mode, int dtype, bool fast,
                                         hipStream_t stream)
 {
-    int vpr = (int)(D / 8);
-    const int groups = (int)ceil_div(vpr, 64);
-    fused_kernel_t k = gate_mode == RGA_GATE_FULL ? Table<true>::get(groups)
-                                                  : Table<false>::get(groups);
-    if (k == nullptr)
-        return hipErrorInvalidValue;
-    const u32x4* xv = static_cast<const u32x4*>(x);
-    const u32x4* uv = static_cast<const u32x4*>(u);
-    const u32x4* gv = static_cast<const u32x4*>(g);
-    const u32x4* sv = static_cast<const u32x4*>(scale);
-    const u32x4* hv = static_cast<const u32x4*>(shift);
-    u32x4* xo = static_cast<u32x4*>(x_out);
-    u32x4* yo = static_cast<u32x4*>(y);
-    float d_float = (float)D;
-    void* args[] = {&xv, &uv, &gv, &sv, &hv, &eps, &d_float, &xo, &yo, &L, &vpr};
-    return hipLaunchKernel(reinterpret_cast<const void*>(k),
-                           dim3((uint32_t)L, (uint32_t)B),
-                           dim3(kBlock), args, 0, stream);
+    switch (dtype) {
+    case RGA_DTYPE_F16:
+        return launch_dt<kF16>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream);
+    case RGA_DTYPE_F32:
+        return launch_dt<kF32>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream);
+    default:
+        return launch_dt<kBF16>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream);
+    }
 }
 
 }  // namespace rga

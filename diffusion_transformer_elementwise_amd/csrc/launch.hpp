@@ -1,6 +1,9 @@
 // Internal interface between the C-ABI layer (api.cpp) and the kernel files.
 // Every launcher expects arguments already validated by api.cpp and returns
-// the HIP status of its launch.
+// the HIP status of its launch. `fast` selects the 16-byte-pack kernels (D a
+// multiple of 8, every pointer 16-byte aligned, and for the modulation
+// D <= RGA_RMS_MAX_D); otherwise the element-wise kernels run. dtype and
+// mod_mode take the RGA_DTYPE_* and RGA_MOD_* values of rga.h.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -9,17 +12,19 @@
 namespace rga {
 
 // gated residual add (gate_add.hip)
-bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode);
+bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode,
+                        bool fast);
 hipError_t launch_gate_add(const void* x, const void* u, const void* g,
                            void* out, int64_t B, int64_t L, int64_t D,
-                           int gate_mode, hipStream_t stream);
+                           int gate_mode, int dtype, bool fast,
+                           hipStream_t stream);
 
 // modulation (rms_modulate.hip)
-bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D);
+bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, bool fast);
 hipError_t launch_rms_modulate(const void* x, const void* scale,
                                const void* shift, float eps, void* out,
-                               int64_t B, int64_t L, int64_t D,
-                               hipStream_t stream);
+                               int64_t B, int64_t L, int64_t D, int mod_mode,
+                               int dtype, bool fast, hipStream_t stream);
 
 // residual update then modulation, one pass (gate_add_rms_modulate.hip)
 bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D);
@@ -28,6 +33,7 @@ hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
                                         const void* shift, float eps,
                                         void* x_out, void* y, int64_t B,
                                         int64_t L, int64_t D, int gate_mode,
+                                        int mod_mode, int dtype, bool fast,
                                         hipStream_t stream);
 
 // measurement helpers (measure.hip); n16 = number of 16-byte vectors

@@ -1,25 +1,32 @@
 // adaLN modulation with a weightless RMSNorm,
 //   out = rms_norm(x, eps) * (1 + scale) + shift,
-// over contiguous bf16 x [B, L, D] with scale and shift rows [B, 1, D]
-// (prhub summary of sglang PR #34172, "关键源码片段": the expression and
-// RMSNormNoWeight; "风险与影响": the fused kernel's one-ULP allowance).
+// over contiguous x [B, L, D] with scale and shift rows [B, 1, D] or per
+// token [B, L, D] (prhub summary of sglang PR #34172, "关键源码片段": the
+// expression and RMSNormNoWeight; "风险与影响": the fused kernel's one-ULP
+// allowance).
 //
-// One wave64 owns one row at a time. Lane j loads the 16-byte groups
-// k = j, j + 64, ..., (group k = elements 8k .. 8k+7), keeps them in
-// registers, and accumulates their squares in increasing k and element
-// order into one binary32 partial; the 64 partials are then combined with
+// The fixed summation order: the row is cut into groups of 8 consecutive
+// elements (the last group may be shorter); one wave64 owns the row; lane j
+// accumulates the squares of groups j, j+64, ... in increasing group and
+// element order into one binary32 partial; the 64 partials are combined with
 // xor-distance lane exchanges 1, 2, ..., 32 (every lane ends with the same
-// sum, because a + b == b + a bit for bit). That is the fixed order the
-// library documents, so the result does not depend on the launch shape.
-// Then r = 1 / sqrt(ss / D + eps) with IEEE division and square root, and
-// each element becomes ((x * r) * (1 + scale)) + shift, rounded once to bf16.
+// sum, because a + b == b + a bit for bit). Then r = 1 / sqrt(ss / D + eps)
+// with IEEE division and square root, and each element becomes
+// ((x * r) * (1 + scale)) + shift, rounded once to the storage type.
 //
-// The row is read once from HBM and written once, with nontemporal loads
-// and stores; scale and shift rows are loaded once per wave (two rows of one
-// batch, one wave per workgroup: the shape that measured fastest on MI355X
-// inside a chain of streaming kernels) and kept in registers. No LDS and no
-// barrier: nothing crosses a wave.
-#include "bf16x8.hpp"
+// Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers): the
+// row stays in registers (G packs per lane), read once from HBM and written
+// once, with nontemporal loads and stores; one wave per workgroup, two rows
+// per wave. With row modulation the packed 2-byte scale and shift rows stay
+// in registers across the wave's rows (the shape that measured fastest on
+// MI355X inside a chain of streaming kernels); per-token rows, and binary32
+// rows, are read in the apply phase instead.
+//
+// Generic path (any D, element-aligned pointers): the same order in two
+// passes over the row, element by element (the second pass re-reads x).
+//
+// No LDS and no barrier: nothing crosses a wave.
+#include "dtype.hpp"
 #include "launch.hpp"
 
 #include <rga.h>
@@ -27,58 +34,50 @@
 namespace rga {
 namespace {
 
-constexpr int kBlock = 64;      // one wave per workgroup
+constexpr int kBlock = 64;  // one wave per workgroup
 constexpr int kRowsPerWave = 2;
-constexpr int kMaxGroups = RGA_RMS_MAX_D / 512;  // groups per lane
 
-// G = groups per lane = ceil(D / 512). Lanes whose group index is past the
-// row end load zeros, which add +0 to a partial that is never -0, so they
-// change nothing.
-// Grid: x = tile of kRowsPerWave rows, y = batch.
-template <int G>
+// G = packs per lane (at least ceil(D / 512)); lanes whose pack index is
+// past the row end hold zeros, which add +0 to a partial that is never -0,
+// so they change nothing. Grid: x = tile of kRowsPerWave rows, y = batch.
+template <int G, int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
-    const u32x4* x, const u32x4* scale, const u32x4* shift, float eps,
-    float d_float, u32x4* out, int64_t L, int vpr)
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
 {
+    constexpr bool kHold = (MOD == kModRow) && (DT != kF32);
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t r0 = (int64_t)blockIdx.x * kRowsPerWave;
     const int64_t r1 = (r0 + kRowsPerWave < L) ? r0 + kRowsPerWave : L;
 
-    u32x4 sc[G], sh[G];
+    Pack<DT> sc[kHold ? G : 1], sh[kHold ? G : 1];
+    if constexpr (kHold) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const int col = lane + 64 * i;
-        if (col < vpr) {
-            sc[i] = load16(scale + b * vpr + col);
-            sh[i] = load16(shift + b * vpr + col);
-        } else {
-            sc[i] = u32x4{0, 0, 0, 0};
-            sh[i] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < G; ++i) {
+            const int col = lane + 64 * i;
+            sc[i] = (col < vpr) ? Pack<DT>::load(scale, b * vpr + col) : Pack<DT>::zero();
+            sh[i] = (col < vpr) ? Pack<DT>::load(shift, b * vpr + col) : Pack<DT>::zero();
         }
     }
 
     for (int64_t r = r0; r < r1; ++r) {
         const int64_t row = (b * L + r) * vpr;
-        u32x4 xv[G];
+        Pack<DT> xv[G];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int col = lane + 64 * i;
-            xv[i] = (col < vpr) ? load16_stream(x + row + col)
-                                : u32x4{0, 0, 0, 0};
+            xv[i] = (col < vpr) ? Pack<DT>::load_stream(x, row + col) : Pack<DT>::zero();
         }
 
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float a = bf16_lo(xv[i][w]);
+            for (int e = 0; e < 8; ++e) {
+                const float a = xv[i].get(e);
                 const float sa = a * a;
                 acc = acc + sa;
-                const float c = bf16_hi(xv[i][w]);
-                const float sc2 = c * c;
-                acc = acc + sc2;
             }
         }
 #pragma unroll
@@ -95,69 +94,150 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
             const int col = lane + 64 * i;
             if (col >= vpr)
                 continue;
-            u32x4 o;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float n0 = bf16_lo(xv[i][w]) * rr;
-                const float n1 = bf16_hi(xv[i][w]) * rr;
-                const float a0 = 1.0f + bf16_lo(sc[i][w]);
-                const float a1 = 1.0f + bf16_hi(sc[i][w]);
-                const float m0 = n0 * a0;
-                const float m1 = n1 * a1;
-                const float y0 = m0 + bf16_lo(sh[i][w]);
-                const float y1 = m1 + bf16_hi(sh[i][w]);
-                o[w] = pack_bf16(y0, y1);
+            Pack<DT> s_, h_;
+            if constexpr (kHold) {
+                s_ = sc[i];
+                h_ = sh[i];
+            } else if constexpr (MOD == kModToken) {
+                s_ = Pack<DT>::load_stream(scale, row + col);
+                h_ = Pack<DT>::load_stream(shift, row + col);
+            } else {
+                s_ = Pack<DT>::load(scale, b * vpr + col);
+                h_ = Pack<DT>::load(shift, b * vpr + col);
             }
-            store16_stream(out + row + col, o);
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float n = xv[i].get(e) * rr;
+                const float a = 1.0f + s_.get(e);
+                const float m = n * a;
+                o[e] = m + h_.get(e);
+            }
+            Pack<DT>::make(o).store_stream(out, row + col);
         }
     }
 }
 
-typedef void (*rms_kernel_t)(const u32x4*, const u32x4*, const u32x4*, float,
-                             float, u32x4*, int64_t, int);
+// Generic: one wave per row; grid x = row l, y = batch b.
+template <int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int64_t D)
+{
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t mrow = (MOD == kModToken) ? row : b * D;
+    const int64_t groups = (D + 7) / 8;
 
-template <int... Gs>
-struct KernelTable {
-    static rms_kernel_t get(int g)
-    {
-        rms_kernel_t table[] = {&rms_modulate_kernel<Gs>...};
-        return (g >= 1 && g <= (int)sizeof...(Gs)) ? table[g - 1] : nullptr;
+    float acc = 0.0f;
+    for (int64_t k = lane; k < groups; k += 64) {
+        for (int e = 0; e < 8; ++e) {
+            const int64_t d = 8 * k + e;
+            if (d < D) {
+                const float v = load_elem<DT>(x, row + d);
+                const float sv = v * v;
+                acc = acc + sv;
+            }
+        }
     }
-};
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        acc = acc + __shfl_xor(acc, m);
+    const float ms = acc / d_float;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    const float rr = 1.0f / q;
 
-using Table = KernelTable<1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15,
-                          16>;
-static_assert(kMaxGroups == 16, "table covers groups 1..16");
+    for (int64_t k = lane; k < groups; k += 64) {
+        for (int e = 0; e < 8; ++e) {
+            const int64_t d = 8 * k + e;
+            if (d < D) {
+                const float n = load_elem<DT>(x, row + d) * rr;
+                const float a = 1.0f + load_elem<DT>(scale, mrow + d);
+                const float m = n * a;
+                store_elem<DT>(out, row + d, m + load_elem<DT>(shift, mrow + d));
+            }
+        }
+    }
+}
+
+typedef void (*rms_kernel_t)(const void*, const void*, const void*, float,
+                             float, void*, int64_t, int);
+
+// Packs per lane are taken from a ladder (the smallest entry >= ceil(D/512)).
+constexpr int kLadder[] = {1, 2, 4, 6, 8, 12, 16};
+static_assert(RGA_RMS_MAX_D / 512 == 16, "ladder tops out at RGA_RMS_MAX_D");
+
+template <int DT, int MOD>
+rms_kernel_t pick(int groups)
+{
+    rms_kernel_t t[] = {&rms_modulate_kernel<1, DT, MOD>, &rms_modulate_kernel<2, DT, MOD>,
+                        &rms_modulate_kernel<4, DT, MOD>, &rms_modulate_kernel<6, DT, MOD>,
+                        &rms_modulate_kernel<8, DT, MOD>, &rms_modulate_kernel<12, DT, MOD>,
+                        &rms_modulate_kernel<16, DT, MOD>};
+    for (int i = 0; i < 7; ++i)
+        if (groups <= kLadder[i])
+            return t[i];
+    return nullptr;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+template <int DT, int MOD>
+hipError_t launch_typed(const void* x, const void* scale, const void* shift,
+                        float eps, void* out, int64_t B, int64_t L, int64_t D,
+                        bool fast, hipStream_t stream)
+{
+    float d_float = (float)D;
+    if (!fast) {
+        void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &D};
+        return hipLaunchKernel(
+            reinterpret_cast<const void*>(&rms_modulate_generic_kernel<DT, MOD>),
+            dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
+    }
+    int vpr = (int)(D / 8);
+    rms_kernel_t k = pick<DT, MOD>((int)ceil_div(vpr, 64));
+    if (k == nullptr)
+        return hipErrorInvalidValue;
+    void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &vpr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k),
+                           dim3((uint32_t)ceil_div(L, kRowsPerWave), (uint32_t)B),
+                           dim3(kBlock), args, 0, stream);
+}
+
+template <int DT>
+hipError_t launch_mod(const void* x, const void* scale, const void* shift,
+                      float eps, void* out, int64_t B, int64_t L, int64_t D,
+                      int mod_mode, bool fast, hipStream_t stream)
+{
+    return mod_mode == RGA_MOD_TOKEN
+               ? launch_typed<DT, kModToken>(x, scale, shift, eps, out, B, L, D, fast, stream)
+               : launch_typed<DT, kModRow>(x, scale, shift, eps, out, B, L, D, fast, stream);
+}
+
 }  // namespace
 
-bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D)
+bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, bool fast)
 {
     (void)D;
-    return ceil_div(L, kRowsPerWave) <= (((int64_t)1 << 32) - 1) / kBlock &&
-           B <= 65535;
+    const int64_t rows = fast ? ceil_div(L, kRowsPerWave) : L;
+    return rows <= (((int64_t)1 << 32) - 1) / kBlock && B <= 65535;
 }
 
 hipError_t launch_rms_modulate(const void* x, const void* scale,
                                const void* shift, float eps, void* out,
-                               int64_t B, int64_t L, int64_t D,
-                               hipStream_t stream)
+                               int64_t B, int64_t L, int64_t D, int mod_mode,
+                               int dtype, bool fast, hipStream_t stream)
 {
-    int vpr = (int)(D / 8);
-    rms_kernel_t k = Table::get((int)ceil_div(vpr, 64));
-    if (k == nullptr)
-        return hipErrorInvalidValue;
-    const u32x4* xv = static_cast<const u32x4*>(x);
-    const u32x4* sv = static_cast<const u32x4*>(scale);
-    const u32x4* hv = static_cast<const u32x4*>(shift);
-    u32x4* ov = static_cast<u32x4*>(out);
-    float d_float = (float)D;
-    void* args[] = {&xv, &sv, &hv, &eps, &d_float, &ov, &L, &vpr};
-    return hipLaunchKernel(reinterpret_cast<const void*>(k),
-                           dim3((uint32_t)ceil_div(L, kRowsPerWave), (uint32_t)B),
-                           dim3(kBlock), args, 0, stream);
+    switch (dtype) {
+    case RGA_DTYPE_F16:
+        return launch_mod<kF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+    case RGA_DTYPE_F32:
+        return launch_mod<kF32>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+    default:
+        return launch_mod<kBF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+    }
 }
 
 }  // namespace rga

@@ -4,24 +4,79 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import GATE_BCAST, GATE_FULL, RGA_OK, RGAError, library
+from ._lib import (DTYPE_BF16, DTYPE_F16, DTYPE_F32, GATE_BCAST, GATE_FULL, MOD_ROW,
+                   MOD_TOKEN, RGA_OK, RGAError, library)
 
 
 def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require(t: torch.Tensor, name: str, device=None) -> None:
+# storage types of the _ex calls
+_DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}
+
+
+def _require(t: torch.Tensor, name: str, device=None, dtype=torch.bfloat16) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a HIP device, got {t.device}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _x_shape(x: torch.Tensor, dtype) -> tuple:
+    _require(x, "x", dtype=dtype)
+    if x.dim() != 3:
+        raise ValueError("x must be [B, L, D]")
+    return tuple(x.shape)
+
+
+def _storage(x) -> torch.dtype:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16, float16 or float32, got {x.dtype}")
+    return x.dtype
+
+
+def _gate(x, u, g, gate_mode, dtype) -> int:
+    B, L, D = x.shape
+    _require(u, "u", x.device, dtype)
+    _require(g, "g", x.device, dtype)
+    if u.shape != x.shape:
+        raise ValueError(f"u has shape {tuple(u.shape)}, expected {tuple(x.shape)}")
+    if gate_mode is None:
+        gate_mode = GATE_FULL if g.shape == x.shape else GATE_BCAST
+    want = (B, L, D) if gate_mode == GATE_FULL else (B, 1, D)
+    if gate_mode in (GATE_FULL, GATE_BCAST) and tuple(g.shape) != want:
+        raise ValueError(f"g has shape {tuple(g.shape)}, expected {want}")
+    return int(gate_mode)
+
+
+def _modulation(x, scale, shift, mod_mode, dtype) -> int:
+    B, L, D = x.shape
+    if mod_mode is None:
+        mod_mode = MOD_TOKEN if (L != 1 and tuple(scale.shape) == (B, L, D)) else MOD_ROW
+    want = (B, L, D) if mod_mode == MOD_TOKEN else (B, 1, D)
+    for name, t in (("scale", scale), ("shift", shift)):
+        _require(t, name, x.device, dtype)
+        if mod_mode in (MOD_ROW, MOD_TOKEN) and tuple(t.shape) != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+    return int(mod_mode)
+
+
+def _output(t, name, x):
+    if t is None:
+        return torch.empty_like(x)
+    _require(t, name, x.device, x.dtype)
+    if t.shape != x.shape:
+        raise ValueError(f"{name} must have x's shape")
+    return t
 
 
 def rga_residual_gate_add(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
@@ -32,30 +87,31 @@ def rga_residual_gate_add(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
     x, u: [B, L, D]; g: [B, L, D] (GATE_FULL) or [B, 1, D] (GATE_BCAST);
     gate_mode is inferred from g's shape when None. ``out`` may be x or u
     (in place), or g in full mode. Enqueued on the current stream."""
-    _require(x, "x")
-    if x.dim() != 3:
-        raise ValueError("x must be [B, L, D]")
-    B, L, D = x.shape
-    _require(u, "u", x.device)
-    _require(g, "g", x.device)
-    if u.shape != x.shape:
-        raise ValueError(f"u has shape {tuple(u.shape)}, expected {tuple(x.shape)}")
-    if gate_mode is None:
-        gate_mode = GATE_FULL if g.shape == x.shape else GATE_BCAST
-    want = (B, L, D) if gate_mode == GATE_FULL else (B, 1, D)
-    if gate_mode in (GATE_FULL, GATE_BCAST) and tuple(g.shape) != want:
-        raise ValueError(f"g has shape {tuple(g.shape)}, expected {want}")
-    if out is None:
-        out = torch.empty_like(x)
-    else:
-        _require(out, "out", x.device)
-        if out.shape != x.shape:
-            raise ValueError("out must have x's shape")
+    B, L, D = _x_shape(x, torch.bfloat16)
+    gate_mode = _gate(x, u, g, gate_mode, torch.bfloat16)
+    out = _output(out, "out", x)
     st = library().rga_residual_gate_add(
         x.data_ptr(), u.data_ptr(), g.data_ptr(), out.data_ptr(), B, L, D,
-        int(gate_mode), _stream_handle(x.device))
+        gate_mode, _stream_handle(x.device))
     if st != RGA_OK:
         raise RGAError(st, "rga_residual_gate_add")
+    return out
+
+
+def rga_residual_gate_add_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
+                             out: torch.Tensor | None = None,
+                             gate_mode: int | None = None) -> torch.Tensor:
+    """rga_residual_gate_add for bf16, float16 or float32 tensors (all of one
+    type), any D, and tensors that start at any element offset."""
+    dt = _storage(x)
+    B, L, D = _x_shape(x, dt)
+    gate_mode = _gate(x, u, g, gate_mode, dt)
+    out = _output(out, "out", x)
+    st = library().rga_residual_gate_add_ex(
+        x.data_ptr(), u.data_ptr(), g.data_ptr(), out.data_ptr(), B, L, D,
+        gate_mode, _DTYPES[dt], _stream_handle(x.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_residual_gate_add_ex")
     return out
 
 
@@ -66,25 +122,32 @@ def rms_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
 
     x: [B, L, D]; scale, shift: [B, 1, D]; ``out`` may be x (in place).
     eps is passed as binary32. Enqueued on the current stream."""
-    _require(x, "x")
-    if x.dim() != 3:
-        raise ValueError("x must be [B, L, D]")
-    B, L, D = x.shape
-    for name, t in (("scale", scale), ("shift", shift)):
-        _require(t, name, x.device)
-        if tuple(t.shape) != (B, 1, D):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, 1, D)}")
-    if out is None:
-        out = torch.empty_like(x)
-    else:
-        _require(out, "out", x.device)
-        if out.shape != x.shape:
-            raise ValueError("out must have x's shape")
+    B, L, D = _x_shape(x, torch.bfloat16)
+    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16)
+    out = _output(out, "out", x)
     st = library().rms_modulate(
         x.data_ptr(), scale.data_ptr(), shift.data_ptr(), float(eps),
         out.data_ptr(), B, L, D, _stream_handle(x.device))
     if st != RGA_OK:
         raise RGAError(st, "rms_modulate")
+    return out
+
+
+def rga_rms_modulate_ex(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                        eps: float = 1e-6, out: torch.Tensor | None = None,
+                        mod_mode: int | None = None) -> torch.Tensor:
+    """rms_modulate for bf16, float16 or float32, any D, any element offset,
+    and scale/shift per token ([B, L, D], MOD_TOKEN) or per batch row
+    ([B, 1, D], MOD_ROW); mod_mode is inferred from scale's shape when None."""
+    dt = _storage(x)
+    B, L, D = _x_shape(x, dt)
+    mod_mode = _modulation(x, scale, shift, mod_mode, dt)
+    out = _output(out, "out", x)
+    st = library().rga_rms_modulate_ex(
+        x.data_ptr(), scale.data_ptr(), shift.data_ptr(), float(eps),
+        out.data_ptr(), B, L, D, mod_mode, _DTYPES[dt], _stream_handle(x.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_rms_modulate_ex")
     return out
 
 
@@ -96,37 +159,41 @@ def rga_gate_add_rms_modulate(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
                               gate_mode: int | None = None):
     """x_out = x + u * g, then y = rms_norm(x_out, eps) * (1 + scale) + shift,
     in one pass. Returns (x_out, y). x_out and y may each be x or u."""
-    _require(x, "x")
-    if x.dim() != 3:
-        raise ValueError("x must be [B, L, D]")
-    B, L, D = x.shape
-    _require(u, "u", x.device)
-    _require(g, "g", x.device)
-    if u.shape != x.shape:
-        raise ValueError(f"u has shape {tuple(u.shape)}, expected {tuple(x.shape)}")
-    if gate_mode is None:
-        gate_mode = GATE_FULL if g.shape == x.shape else GATE_BCAST
-    want = (B, L, D) if gate_mode == GATE_FULL else (B, 1, D)
-    if gate_mode in (GATE_FULL, GATE_BCAST) and tuple(g.shape) != want:
-        raise ValueError(f"g has shape {tuple(g.shape)}, expected {want}")
-    for name, t in (("scale", scale), ("shift", shift)):
-        _require(t, name, x.device)
-        if tuple(t.shape) != (B, 1, D):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, 1, D)}")
-    if x_out is None:
-        x_out = torch.empty_like(x)
-    if y is None:
-        y = torch.empty_like(x)
-    for name, t in (("x_out", x_out), ("y", y)):
-        _require(t, name, x.device)
-        if t.shape != x.shape:
-            raise ValueError(f"{name} must have x's shape")
+    B, L, D = _x_shape(x, torch.bfloat16)
+    gate_mode = _gate(x, u, g, gate_mode, torch.bfloat16)
+    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16)
+    x_out = _output(x_out, "x_out", x)
+    y = _output(y, "y", x)
     st = library().rga_gate_add_rms_modulate(
         x.data_ptr(), u.data_ptr(), g.data_ptr(), scale.data_ptr(),
         shift.data_ptr(), float(eps), x_out.data_ptr(), y.data_ptr(), B, L, D,
-        int(gate_mode), _stream_handle(x.device))
+        gate_mode, _stream_handle(x.device))
     if st != RGA_OK:
         raise RGAError(st, "rga_gate_add_rms_modulate")
+    return x_out, y
+
+
+def rga_gate_add_rms_modulate_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
+                                 scale: torch.Tensor, shift: torch.Tensor,
+                                 eps: float = 1e-6,
+                                 x_out: torch.Tensor | None = None,
+                                 y: torch.Tensor | None = None,
+                                 gate_mode: int | None = None,
+                                 mod_mode: int | None = None):
+    """rga_gate_add_rms_modulate for bf16, float16 or float32, any D, any
+    element offset, and per-token or per-batch-row scale/shift."""
+    dt = _storage(x)
+    B, L, D = _x_shape(x, dt)
+    gate_mode = _gate(x, u, g, gate_mode, dt)
+    mod_mode = _modulation(x, scale, shift, mod_mode, dt)
+    x_out = _output(x_out, "x_out", x)
+    y = _output(y, "y", x)
+    st = library().rga_gate_add_rms_modulate_ex(
+        x.data_ptr(), u.data_ptr(), g.data_ptr(), scale.data_ptr(),
+        shift.data_ptr(), float(eps), x_out.data_ptr(), y.data_ptr(), B, L, D,
+        gate_mode, mod_mode, _DTYPES[dt], _stream_handle(x.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_gate_add_rms_modulate_ex")
     return x_out, y
 
 

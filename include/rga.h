@@ -57,8 +57,24 @@ enum {
 };
 
 /* Largest D that rms_modulate and rga_gate_add_rms_modulate accept (one
- * row is held in registers). */
+ * row is held in registers). The _ex calls accept any D (larger rows, and
+ * D % 8 != 0, run the element-wise kernels). */
 #define RGA_RMS_MAX_D 8192
+
+/* Storage types of the _ex calls (all tensors of a call share one type).
+ * Arithmetic is binary32 for every type; one round-to-nearest-even to the
+ * storage type at the end (none for binary32). */
+enum {
+    RGA_DTYPE_BF16 = 0,
+    RGA_DTYPE_F16 = 1, /* IEEE binary16 */
+    RGA_DTYPE_F32 = 2, /* IEEE binary32 */
+};
+
+/* Layouts of scale and shift in the _ex modulation calls. */
+enum {
+    RGA_MOD_ROW = 0,   /* [B, 1, D]: row b used for every l */
+    RGA_MOD_TOKEN = 1, /* [B, L, D]: one row per token */
+};
 
 /*
  * Gated residual add: out = x + u * g.
@@ -134,6 +150,32 @@ int rga_gate_add_rms_modulate(const void* x, const void* u, const void* g,
                               int64_t D, int gate_mode, hipStream_t stream);
 
 /*
+ * Extended forms: any storage type (RGA_DTYPE_*), any D >= 0, pointers aligned
+ * to the element size (2 or 4 bytes; else RGA_ERR_UNSUPPORTED), per-token
+ * modulation (RGA_MOD_TOKEN). Source: the residual-gate page
+ * ("[KDA-Pilot] Add diffusion residual-gate CUDA fast path for LTX2",
+ * "Modifications") lists a correctness test over several storage types and
+ * ragged tail shapes.
+ * Same operations, aliasing rules and status codes as the calls above; with
+ * RGA_DTYPE_BF16, RGA_MOD_ROW, D % 8 == 0, D <= RGA_RMS_MAX_D and 16-byte
+ * aligned pointers they run the same kernels and give the same results.
+ * Otherwise element-wise kernels with the same arithmetic and the same
+ * summation order run (the last group of 8 may be shorter). For per-token
+ * modulation scale and shift are [B, L, D] and must not overlap the outputs.
+ */
+int rga_residual_gate_add_ex(const void* x, const void* u, const void* g,
+                             void* out, int64_t B, int64_t L, int64_t D,
+                             int gate_mode, int dtype, hipStream_t stream);
+int rga_rms_modulate_ex(const void* x, const void* scale, const void* shift,
+                        float eps, void* out, int64_t B, int64_t L, int64_t D,
+                        int mod_mode, int dtype, hipStream_t stream);
+int rga_gate_add_rms_modulate_ex(const void* x, const void* u, const void* g,
+                                 const void* scale, const void* shift,
+                                 float eps, void* x_out, void* y, int64_t B,
+                                 int64_t L, int64_t D, int gate_mode,
+                                 int mod_mode, int dtype, hipStream_t stream);
+
+/*
  * Host-only validation of the arguments of the calls above, with the same
  * rules and the same status the call would return before launching.
  * Touches neither the device nor the pointed-to memory.
@@ -150,6 +192,21 @@ int rga_check_gate_add_rms_modulate(const void* x, const void* u,
                                     const void* x_out, const void* y,
                                     int64_t B, int64_t L, int64_t D,
                                     int gate_mode);
+int rga_check_residual_gate_add_ex(const void* x, const void* u,
+                                   const void* g, const void* out, int64_t B,
+                                   int64_t L, int64_t D, int gate_mode,
+                                   int dtype);
+int rga_check_rms_modulate_ex(const void* x, const void* scale,
+                              const void* shift, float eps, const void* out,
+                              int64_t B, int64_t L, int64_t D, int mod_mode,
+                              int dtype);
+int rga_check_gate_add_rms_modulate_ex(const void* x, const void* u,
+                                       const void* g, const void* scale,
+                                       const void* shift, float eps,
+                                       const void* x_out, const void* y,
+                                       int64_t B, int64_t L, int64_t D,
+                                       int gate_mode, int mod_mode,
+                                       int dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rga_status_string(int status);

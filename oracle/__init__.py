@@ -21,6 +21,13 @@ from .build import LIBRARY, build_oracle
 GATE_FULL = 0
 GATE_BCAST = 1
 
+BF16 = 0
+F16 = 1
+F32 = 2
+MOD_ROW = 0
+MOD_TOKEN = 1
+_NP = {BF16: np.uint16, F16: np.uint16, F32: np.float32}
+
 RMS_PINNED = 0
 RMS_SEQUENTIAL = 1
 RMS_F64 = 2
@@ -56,6 +63,19 @@ def _load():
         p, p, p, p, p, ctypes.c_float, p, p, i64, i64, i64, ctypes.c_int,
         ctypes.c_int]
     lib.oracle_gate_add_rms_modulate.restype = ctypes.c_int
+    lib.oracle_gate_add_ex.argtypes = [p, p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_gate_add_ex.restype = ctypes.c_int
+    lib.oracle_rms_modulate_ex.argtypes = [
+        p, p, p, ctypes.c_float, p, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_rms_modulate_ex.restype = ctypes.c_int
+    lib.oracle_gate_add_rms_modulate_ex.argtypes = [
+        p, p, p, p, p, ctypes.c_float, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int]
+    lib.oracle_gate_add_rms_modulate_ex.restype = ctypes.c_int
+    lib.oracle_f16_from_f32.argtypes = [p, p, i64]
+    lib.oracle_f16_from_f32.restype = None
+    lib.oracle_f32_from_f16.argtypes = [p, p, i64]
+    lib.oracle_f32_from_f16.restype = None
     lib.oracle_contraction_probe.argtypes = []
     lib.oracle_contraction_probe.restype = ctypes.c_float
     _LIB = lib
@@ -182,6 +202,83 @@ def f32_from_bf16(a):
     a = _bits(np.ascontiguousarray(a), "a")
     out = np.empty(a.shape, dtype=np.float32)
     _load().oracle_f32_from_bf16(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def _typed(a, name, dtype):
+    a = np.asarray(a)
+    if a.dtype != _NP[dtype]:
+        raise TypeError(f"{name}: expected {np.dtype(_NP[dtype])} storage for dtype {dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError(f"{name}: must be C-contiguous")
+    return a
+
+
+def gate_add_ex(x, u, g, gate_mode, dtype, out=None):
+    """out = x + u*g for storage dtype BF16/F16 (uint16 patterns) or F32
+    (float32 arrays); binary32 arithmetic, one round-to-nearest-even."""
+    x, u, g = _typed(x, "x", dtype), _typed(u, "u", dtype), _typed(g, "g", dtype)
+    B, L, D = x.shape
+    want = x.shape if gate_mode == GATE_FULL else (B, 1, D)
+    if u.shape != x.shape or g.shape != want:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = np.empty_like(x)
+    rc = _load().oracle_gate_add_ex(_ptr(x), _ptr(u), _ptr(g), _ptr(out), B, L, D,
+                                    gate_mode, dtype)
+    if rc:
+        raise ValueError("oracle_gate_add_ex: bad dtype")
+    return out
+
+
+def rms_modulate_ex(x, scale, shift, eps, mod_mode, dtype, out=None, partials=64):
+    """rms_norm(x, eps) * (1 + scale) + shift for any D, storage dtype and
+    modulation layout (MOD_ROW: [B,1,D], MOD_TOKEN: [B,L,D])."""
+    x = _typed(x, "x", dtype)
+    scale, shift = _typed(scale, "scale", dtype), _typed(shift, "shift", dtype)
+    B, L, D = x.shape
+    want = (B, 1, D) if mod_mode == MOD_ROW else (B, L, D)
+    if scale.shape != want or shift.shape != want:
+        raise ValueError("scale/shift shape does not fit the modulation layout")
+    if out is None:
+        out = np.empty_like(x)
+    rc = _load().oracle_rms_modulate_ex(_ptr(x), _ptr(scale), _ptr(shift), float(eps),
+                                        _ptr(out), B, L, D, mod_mode, dtype, partials)
+    if rc:
+        raise ValueError("oracle_rms_modulate_ex: bad dtype or partials")
+    return out
+
+
+def gate_add_rms_modulate_ex(x, u, g, scale, shift, eps, gate_mode, mod_mode, dtype,
+                             x_out=None, partials=64):
+    """(x + u*g, rms_modulate_ex(x + u*g, ...)) for any storage dtype."""
+    x, u, g = _typed(x, "x", dtype), _typed(u, "u", dtype), _typed(g, "g", dtype)
+    scale, shift = _typed(scale, "scale", dtype), _typed(shift, "shift", dtype)
+    B, L, D = x.shape
+    if x_out is None:
+        x_out = np.empty_like(x)
+    y = np.empty_like(x)
+    rc = _load().oracle_gate_add_rms_modulate_ex(
+        _ptr(x), _ptr(u), _ptr(g), _ptr(scale), _ptr(shift), float(eps), _ptr(x_out),
+        _ptr(y), B, L, D, gate_mode, mod_mode, dtype, partials)
+    if rc:
+        raise ValueError("oracle_gate_add_rms_modulate_ex: bad dtype or partials")
+    return x_out, y
+
+
+def f16_from_f32(a):
+    """The oracle's own binary32 -> binary16 round-to-nearest-even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_f16_from_f32(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def f32_from_f16(a):
+    """The oracle's own binary16 -> binary32 widening."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    out = np.empty(a.shape, dtype=np.float32)
+    _load().oracle_f32_from_f16(_ptr(a), _ptr(out), a.size)
     return out
 
 

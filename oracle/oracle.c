@@ -292,6 +292,205 @@ int oracle_gate_add_rms_modulate(const uint16_t* x, const uint16_t* u,
                                ORACLE_RMS_PINNED, P);
 }
 
+/* ---- storage types other than bf16, per-token modulation, any D ---------
+ *
+ * The residual-gate page's test covers "dtype coverage" and "tail shapes"
+ * ("[KDA-Pilot] ...", "Modifications"), and the RMSNorm+modulate page's
+ * fused path is bf16-only while its sibling fusions take per-token inputs.
+ * Reading taken for these variants: the arithmetic stays binary32 exactly as
+ * above; only the storage type of every tensor changes (bf16, IEEE binary16,
+ * or binary32), with one round-to-nearest-even narrowing at the end (none for
+ * binary32); scale/shift may be per token ([B, L, D]); and D may be any
+ * size, the last group of the fixed summation order holding D mod 8
+ * elements. For bf16 storage, row modulation and D % 8 == 0 these functions
+ * compute exactly what the functions above compute.
+ */
+#define ORACLE_BF16 0
+#define ORACLE_F16 1
+#define ORACLE_F32 2
+#define ORACLE_MOD_ROW 0
+#define ORACLE_MOD_TOKEN 1
+
+/* binary16 -> binary32, exact (every binary16 value is a binary32 value). */
+static float widen_f16(uint16_t h)
+{
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1Fu;
+    const uint32_t m = h & 0x3FFu;
+    uint32_t w;
+    if (e == 0) {
+        /* zero or subnormal: m * 2^-24, exact in binary32 */
+        float f = (float)m * 0x1p-24f;
+        memcpy(&w, &f, sizeof w);
+        w |= sign;
+    } else if (e == 31) {
+        w = sign | 0x7F800000u | (m << 13); /* inf, NaN keeps its payload */
+    } else {
+        w = sign | ((e + 112u) << 23) | (m << 13); /* rebias 15 -> 127 */
+    }
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+/*
+ * binary32 -> binary16, round to nearest, ties to even.
+ *   NaN stays NaN (quiet, sign kept); |f| >= 65520 (half-way above the
+ *   largest finite 65504, whose significand is odd) becomes infinity;
+ *   normal results: drop 13 significand bits after rebiasing the exponent,
+ *   rounding by adding 0xFFF plus the lowest kept bit (a carry moves to the
+ *   next binade correctly); subnormal results (|f| < 2^-14): |f| * 2^24 is
+ *   exact in binary32 and rintf (round-half-even in the default mode) gives
+ *   the integer significand, 1024 landing on the smallest normal.
+ */
+static uint16_t narrow_f16(float f)
+{
+    uint32_t w;
+    memcpy(&w, &f, sizeof w);
+    const uint16_t sign = (uint16_t)((w >> 16) & 0x8000u);
+    const uint32_t a = w & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return (uint16_t)(sign | 0x7E00u | ((a >> 13) & 0x3FFu));
+    if (a >= 0x477FF000u)
+        return (uint16_t)(sign | 0x7C00u);
+    if (a >= 0x38800000u) {
+        const uint32_t m = a - 0x38000000u;
+        return (uint16_t)(sign | ((m + 0xFFFu + ((m >> 13) & 1u)) >> 13));
+    }
+    float mag;
+    memcpy(&mag, &a, sizeof mag);
+    return (uint16_t)(sign | (uint16_t)rintf(mag * 0x1p24f));
+}
+
+void oracle_f16_from_f32(const float* src, uint16_t* dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = narrow_f16(src[i]);
+}
+
+void oracle_f32_from_f16(const uint16_t* src, float* dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = widen_f16(src[i]);
+}
+
+static float load_elem(const void* p, int64_t i, int dtype)
+{
+    if (dtype == ORACLE_F32)
+        return ((const float*)p)[i];
+    const uint16_t h = ((const uint16_t*)p)[i];
+    return dtype == ORACLE_F16 ? widen_f16(h) : widen(h);
+}
+
+static void store_elem(void* p, int64_t i, float v, int dtype)
+{
+    if (dtype == ORACLE_F32)
+        ((float*)p)[i] = v;
+    else if (dtype == ORACLE_F16)
+        ((uint16_t*)p)[i] = narrow_f16(v);
+    else
+        ((uint16_t*)p)[i] = narrow_rne(v);
+}
+
+static int bad_dtype(int dtype)
+{
+    return dtype != ORACLE_BF16 && dtype != ORACLE_F16 && dtype != ORACLE_F32;
+}
+
+/* out = x + u * g for any storage type (binary32 multiply and add). */
+int oracle_gate_add_ex(const void* x, const void* u, const void* g, void* out,
+                       int64_t B, int64_t L, int64_t D, int gate_mode,
+                       int dtype)
+{
+    if (bad_dtype(dtype))
+        return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t l = 0; l < L; ++l) {
+            const int64_t row = (b * L + l) * D;
+            for (int64_t d = 0; d < D; ++d) {
+                const int64_t i = row + d;
+                const int64_t gi = (gate_mode == ORACLE_GATE_FULL) ? i : b * D + d;
+                const float p = load_elem(u, i, dtype) * load_elem(g, gi, dtype);
+                const float s = load_elem(x, i, dtype) + p;
+                store_elem(out, i, s, dtype);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The fixed-order factor of one row for any storage type and any D: group k
+ * holds elements 8k .. min(8k + 8, D) - 1; otherwise as rms_factor_pinned. */
+static float rms_factor_ex(const void* x, int64_t row, int64_t D, float eps,
+                           int dtype, int P)
+{
+    float part[256];
+    float next[256];
+    for (int j = 0; j < P; ++j)
+        part[j] = 0.0f;
+    const int64_t groups = (D + 7) / 8;
+    for (int64_t k = 0; k < groups; ++k) {
+        const int j = (int)(k % P);
+        for (int64_t d = 8 * k; d < 8 * k + 8 && d < D; ++d) {
+            const float v = load_elem(x, row + d, dtype);
+            const float sq = v * v;
+            part[j] = part[j] + sq;
+        }
+    }
+    for (int m = 1; m < P; m <<= 1) {
+        for (int j = 0; j < P; ++j)
+            next[j] = part[j] + part[j ^ m];
+        for (int j = 0; j < P; ++j)
+            part[j] = next[j];
+    }
+    const float ss = part[0];
+    const float ms = ss / (float)D;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    return 1.0f / q;
+}
+
+/* out = rms_norm(x, eps) * (1 + scale) + shift for any storage type;
+ * scale/shift [B, 1, D] (ORACLE_MOD_ROW) or [B, L, D] (ORACLE_MOD_TOKEN). */
+int oracle_rms_modulate_ex(const void* x, const void* scale,
+                           const void* shift, float eps, void* out,
+                           int64_t B, int64_t L, int64_t D, int mod_mode,
+                           int dtype, int P)
+{
+    if (bad_partials(P) || bad_dtype(dtype))
+        return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t l = 0; l < L; ++l) {
+            const int64_t row = (b * L + l) * D;
+            const int64_t mrow = (mod_mode == ORACLE_MOD_TOKEN) ? row : b * D;
+            const float r = rms_factor_ex(x, row, D, eps, dtype, P);
+            for (int64_t d = 0; d < D; ++d) {
+                const float n = load_elem(x, row + d, dtype) * r;
+                const float a = 1.0f + load_elem(scale, mrow + d, dtype);
+                const float m = n * a;
+                const float y = m + load_elem(shift, mrow + d, dtype);
+                store_elem(out, row + d, y, dtype);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The composition for any storage type and modulation layout. */
+int oracle_gate_add_rms_modulate_ex(const void* x, const void* u,
+                                    const void* g, const void* scale,
+                                    const void* shift, float eps, void* x_out,
+                                    void* y, int64_t B, int64_t L, int64_t D,
+                                    int gate_mode, int mod_mode, int dtype,
+                                    int P)
+{
+    if (bad_partials(P) || bad_dtype(dtype))
+        return 1;
+    oracle_gate_add_ex(x, u, g, x_out, B, L, D, gate_mode, dtype);
+    return oracle_rms_modulate_ex(x_out, scale, shift, eps, y, B, L, D,
+                                  mod_mode, dtype, P);
+}
+
 /* ---- build self-check ------------------------------------------------------
  *
  * With a = b = 1 + 2^-12 and c = -(1 + 2^-11): a*b = 1 + 2^-11 + 2^-24

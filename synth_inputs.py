@@ -25,6 +25,11 @@ import torch
 GATE_FULL = 0
 GATE_BCAST = 1
 
+# storage types (the library's and the oracle's numbering)
+BF16 = 0
+F16 = 1
+F32 = 2
+
 
 @dataclass(frozen=True)
 class Dist:
@@ -95,6 +100,12 @@ CASES = {
                GATE_BCAST, x=N02, u=N01, g=N001, rms=True, inplace=True),
 }
 
+# Other shapes from the residual-gate page's benchmark table, outside the
+# five configurations: parity cases and extra bench lines.
+EXTRA_CASES = {
+    "ideogram4": Case("ideogram4_bcast_s4096_c4608", 1, 4096, 4608, 108, GATE_BCAST),
+}
+
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """binary32 -> bf16 bit patterns via torch's CPU conversion."""
@@ -137,3 +148,18 @@ def random_bits(seed: int, shape, dist: Dist = N01) -> np.ndarray:
     """Small ad-hoc tensors for edge-case tests."""
     rng = np.random.default_rng(seed)
     return to_bf16_bits(dist.draw(rng, shape)).reshape(shape)
+
+
+def random_typed(seed: int, shape, dist: Dist = N01, dtype: int = BF16) -> np.ndarray:
+    """random_bits for any storage type: uint16 bf16 or binary16 patterns,
+    or a float32 array. The binary32 draw is the same for every type; the
+    2-byte types round it to nearest even (torch for bf16, numpy for f16)."""
+    rng = np.random.default_rng(seed)
+    a = dist.draw(rng, shape).reshape(shape)
+    if dtype == BF16:
+        return to_bf16_bits(a).reshape(shape)
+    if dtype == F16:
+        return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+    if dtype == F32:
+        return np.ascontiguousarray(a, dtype=np.float32)
+    raise ValueError(f"unknown storage type {dtype}")

@@ -49,6 +49,39 @@ def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.where(na ^ nb, 1 << 20, d)
 
 
+# Storage-type aware forms: uint16 patterns for bf16 (0) and binary16 (1),
+# float32 arrays (compared through their uint32 patterns) for binary32 (2).
+_LAYOUT = {0: (0x8000, 0x7F80, 0x007F), 1: (0x8000, 0x7C00, 0x03FF),
+           2: (0x80000000, 0x7F800000, 0x007FFFFF)}
+
+
+def _as_bits(a: np.ndarray, dtype: int) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if dtype == 2:
+        return a.astype(np.float32, copy=False).view(np.uint32).astype(np.int64)
+    return a.astype(np.uint16, copy=False).astype(np.int64)
+
+
+def is_nan_typed(a: np.ndarray, dtype: int) -> np.ndarray:
+    sign, exp, frac = _LAYOUT[dtype]
+    b = _as_bits(a, dtype)
+    return ((b & exp) == exp) & ((b & frac) != 0)
+
+
+def ulp_diff_typed(a: np.ndarray, b: np.ndarray, dtype: int) -> np.ndarray:
+    """ulp_diff for any storage type: the count of representable values
+    between a and b (+0 and -0 both 0; NaN vs NaN 0; NaN vs other huge)."""
+    sign = _LAYOUT[dtype][0]
+    def order(v):
+        bits = _as_bits(v, dtype)
+        mag = bits & (sign - 1)
+        return np.where(bits & sign, -mag, mag)
+    d = np.abs(order(a) - order(b))
+    na, nb = is_nan_typed(a, dtype), is_nan_typed(b, dtype)
+    d = np.where(na & nb, 0, d)
+    return np.where(na ^ nb, 1 << 40, d)
+
+
 def _floor_log2(a: Fraction) -> int:
     e = a.numerator.bit_length() - a.denominator.bit_length()
     if a < Fraction(2) ** e:

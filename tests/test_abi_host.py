@@ -163,27 +163,43 @@ def _kernel_bodies(asm):
 
 
 def test_gate_add_isa_has_no_fused_multiply_add():
-    # The product of two bf16 values is exact in binary32, so a fused
-    # multiply-add would change results only for subnormal products; the
-    # build must still not contract. Also check 128-bit accesses.
+    # The product of two 2-byte values is exact in binary32, so a fused
+    # multiply-add would change results only for subnormal products (and for
+    # binary32 storage it would change many); the build must never contract.
     bodies = _kernel_bodies(_device_asm("gate_add.hip"))
-    assert len(bodies) == 2
+    # {full, bcast, generic full, generic bcast} x {bf16, f16, f32}
+    assert len(bodies) == 12, sorted(bodies)
+    fast = {n: b for n, b in bodies.items() if "generic" not in n}
+    assert len(fast) == 6
     for name, body in bodies.items():
         # float multiply-adds of any form (integer v_mad_u64_u32 address
         # arithmetic is fine)
         assert not re.search(r"\bv_(pk_)?(fma|fmac|fmamk|fmaak|mad|mac)(_mix\w*)?_f(16|32|64)", body), name
-        assert "global_load_dwordx4" in body and "global_store_dwordx4" in body, name
-        assert "v_cvt_pk_bf16_f32" in body, name
         assert not re.search(r"\bv_pk_(add|mul|fma)_f32", body), name
+    for name, body in fast.items():
+        # 128-bit accesses on the pack path: every word of every pack is
+        # loaded and stored (an f16 build once read only the first word of
+        # each pack, through a bit_cast of a vector element)
+        words = 2 if "ILi2E" in name else 1
+        nload = len(re.findall(r"global_load_dwordx4", body))
+        nstore = len(re.findall(r"global_store_dwordx4", body))
+        assert nstore == words, name
+        assert nload == 3 * words, name  # x, u and g
+    # bf16 storage narrows with the hardware round-to-nearest-even convert
+    bf16 = [b for n, b in bodies.items() if re.search(r"kernelILi0E", n)]
+    assert len(bf16) == 4 and all("v_cvt_pk_bf16_f32" in b for b in bf16)
 
 
 def test_device_code_keeps_subnormals_and_ieee_sqrt_div():
-    asm = _device_asm("rms_modulate.hip")
-    assert ".amdhsa_float_denorm_mode_32 3" in asm
-    body = next(iter(_kernel_bodies(asm).values()))
-    assert "v_div_fixup_f32" in body          # IEEE division sequence
-    assert "v_rsq_f32" not in body            # no approximate reciprocal sqrt
-    assert not re.search(r"\bv_pk_(add|mul|fma)_f32", body)
+    for src in ("rms_modulate.hip", "gate_add_rms_modulate.hip"):
+        asm = _device_asm(src)
+        assert ".amdhsa_float_denorm_mode_32 0" not in asm, src
+        bodies = _kernel_bodies(asm)
+        assert asm.count(".amdhsa_float_denorm_mode_32 3") == len(bodies), src
+        for name, body in bodies.items():
+            assert "v_div_fixup_f32" in body, name      # IEEE division sequence
+            assert "v_rsq_f32" not in body, name        # no approximate rsqrt
+            assert not re.search(r"\bv_pk_(add|mul|fma)_f32", body), name
 
 
 def test_one_hip_runtime_per_process():
@@ -230,3 +246,69 @@ def test_fused_validation_rules(dte):
     assert call(y=xo + 16) == ali              # outputs overlap
     assert call(y=s) == ali                    # output over scale row
     assert call(x_out=x + 32) == ali           # partial overlap with x
+
+
+def test_ex_validation_rules(dte):
+    ok, bad, uns, ali = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED, dte.RGA_ERR_ALIAS
+    BF, F16, F32 = dte.DTYPE_BF16, dte.DTYPE_F16, dte.DTYPE_F32
+    ROW, TOK = dte.MOD_ROW, dte.MOD_TOKEN
+    FULL, BCAST = dte.GATE_FULL, dte.GATE_BCAST
+    x, u, g, o = A, A + 64 * MB, A + 128 * MB, A + 192 * MB
+    ga = dte.check_residual_gate_add_ex
+    # any D, element alignment only; the strict call still rejects them
+    for D in (1, 7, 12, 4100):
+        assert ga(x, u, g, o, 2, 3, D, FULL, BF) == ok
+        assert dte.check_residual_gate_add(x, u, g, o, 2, 3, D, FULL) == (ok if D % 8 == 0 else uns)
+    assert ga(x + 2, u, g, o, 1, 1, 8, FULL, BF) == ok
+    assert ga(x + 2, u, g, o, 1, 1, 8, FULL, F16) == ok
+    assert ga(x + 2, u, g, o, 1, 1, 8, FULL, F32) == uns
+    assert ga(x + 4, u, g + 12, o, 1, 1, 8, BCAST, F32) == ok
+    assert ga(x + 1, u, g, o, 1, 1, 8, FULL, BF) == uns
+    assert ga(x, u, g, o, 1, 1, 8, FULL, 3) == bad
+    assert ga(x, u, g, o, 1, 1, 8, FULL, -1) == bad
+    assert ga(0, 0, 0, 0, 0, 1, 8, FULL, 7) == bad      # dtype checked before the no-op
+    assert ga(0, 0, 0, 0, 0, 1, 8, FULL, F32) == ok
+    # byte ranges scale with the element size
+    n = 1 * 4 * 8
+    assert ga(x, u, g, x + 2 * n, 1, 4, 8, FULL, BF) == ok
+    assert ga(x, u, g, x + 2 * n, 1, 4, 8, FULL, F32) == ali
+    assert ga(x, u, g, x + 4 * n, 1, 4, 8, FULL, F32) == ok
+    assert ga(x, u, g, u, 1, 4, 8, FULL, F16) == ok
+    assert ga(x, u, g, g, 1, 4, 8, BCAST, F32) == ali
+    assert ga(1 << 20, 0, 0, 0, 1 << 30, 1 << 30, 1 << 2, FULL, F32) == bad  # overflow
+
+    rm = dte.check_rms_modulate_ex
+    s, t = A + 64 * MB, A + 96 * MB
+    assert rm(x, s, t, 1e-6, o, 1, 3, dte.RGA_RMS_MAX_D + 8, ROW, BF) == ok
+    assert dte.check_rms_modulate(x, s, t, 1e-6, o, 1, 3, dte.RGA_RMS_MAX_D + 8) == uns
+    assert rm(x, s, t, 1e-6, o, 1, 3, 4097, TOK, F16) == ok
+    assert rm(x, s, t, 1e-6, o, 1, 3, 8, 2, BF) == bad
+    assert rm(x, s, t, -1.0, o, 1, 3, 8, ROW, BF) == bad
+    assert rm(x, s + 2, t, 1e-6, o, 1, 3, 8, ROW, F32) == uns
+    assert rm(x, s, t, 1e-6, x, 1, 3, 8, TOK, F32) == ok   # in place
+    # per-token scale covers [B, L, D]; a row covers [B, 1, D]
+    rowb, tokb = 1 * 8 * 2, 1 * 3 * 8 * 2
+    assert rm(x, o - rowb, t, 1e-6, o, 1, 3, 8, ROW, BF) == ok
+    assert rm(x, o - rowb + 2, t, 1e-6, o, 1, 3, 8, ROW, BF) == ali
+    assert rm(x, o - rowb, t, 1e-6, o, 1, 3, 8, TOK, BF) == ali
+    assert rm(x, o - tokb, t, 1e-6, o, 1, 3, 8, TOK, BF) == ok
+
+    fu = dte.check_gate_add_rms_modulate_ex
+    xo, y, s, t = A + 224 * MB, A + 256 * MB, A + 288 * MB, A + 320 * MB
+    call = lambda **kw: fu(*{**dict(x=x, u=u, g=g, scale=s, shift=t, eps=1e-6, x_out=xo, y=y,
+                                   B=2, L=5, D=4100, gate_mode=BCAST, mod_mode=ROW,
+                                   dtype=BF), **kw}.values())
+    assert call() == ok
+    assert call(dtype=F32, mod_mode=TOK, gate_mode=FULL) == ok
+    assert call(D=dte.RGA_RMS_MAX_D + 8) == ok
+    assert call(mod_mode=5) == bad
+    assert call(dtype=3) == bad
+    assert call(y=y + 2, dtype=F32) == uns
+    assert call(x_out=x, y=u) == ok
+    assert call(x_out=x, y=x) == ali
+    assert call(y=xo + 2 * 2 * 5 * 4100 - 2) == ali                 # tail overlap
+    assert call(y=xo + 2 * 2 * 5 * 4100) == ok
+    assert call(y=xo + 2 * 2 * 5 * 4100, dtype=F32) == ali
+    assert call(scale=y + 2 * 5 * 4100 * 2 - 2 * 4100 * 2, mod_mode=ROW) == ali
+    assert call(scale=y - 2 * 5 * 4100 * 2, mod_mode=TOK) == ok
+    assert call(scale=y - 2 * 5 * 4100 * 2 + 2, mod_mode=TOK) == ali

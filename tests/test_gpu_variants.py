@@ -1,0 +1,242 @@
+"""Parity of the extended entry points (the _ex calls) with the oracle's
+extended functions: every storage type (bf16, binary16, binary32), D of any
+size (ragged last group, rows beyond the register-resident limit), tensors
+that start at any element offset, per-token modulation, and the ideogram4
+shape from the residual-gate page's benchmark table.
+
+Bars, as for the bf16 calls: the gated residual add is bit-exact for every
+storage type; the modulation is within one ULP of its storage type and, since
+the library and the oracle fix the same binary32 order, in fact identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth_inputs import (BF16, EXTRA_CASES, F16, F32, GATE_BCAST, GATE_FULL, N001, N01, N02,
+                          U11, make_inputs, random_typed)
+from tests.gpu_util import (first_mismatch_typed, same_bits_typed, say, to_dev, to_dev_typed,
+                            to_host, to_host_typed, ulp_diff_typed)
+
+pytestmark = pytest.mark.gpu
+
+MOD_ROW, MOD_TOKEN = oracle.MOD_ROW, oracle.MOD_TOKEN
+DTYPES = [BF16, F16, F32]
+NAMES = {BF16: "bf16", F16: "f16", F32: "f32"}
+
+
+@pytest.fixture(scope="module")
+def dte():
+    import diffusion_transformer_elementwise_amd as m
+    return m
+
+
+def _bit_exact(got, want, dtype, label):
+    assert same_bits_typed(got, want, dtype), f"{label}: " + first_mismatch_typed(got, want, dtype)
+
+
+def _zero_ulp(got, want, dtype, label):
+    d = ulp_diff_typed(got, want, dtype)
+    hist = np.bincount(np.minimum(d.ravel(), 3), minlength=4)
+    say(f"[{label}] ULP histogram 0:{hist[0]} 1:{hist[1]} 2:{hist[2]} >2:{hist[3]}")
+    assert d.max() <= 1, f"{label}: max {d.max()} ULP"
+    assert d.max() == 0, f"{label}: pinned order, expected identical results"
+
+
+# (B, L, D): multiples of 8 (pack path), ragged D (element path), one-element
+# rows, rows longer than the register-resident limit
+SHAPES = [
+    (1, 1, 8), (2, 5, 24), (3, 7, 520), (2, 33, 1032), (1, 333, 3072),
+    (1, 3, 1), (2, 5, 7), (3, 7, 13), (2, 9, 1001), (1, 17, 4100), (2, 3, 8200),
+]
+
+
+def _gate_inputs(seed, B, L, D, mode, dtype):
+    x = random_typed(seed, (B, L, D), N02, dtype)
+    u = random_typed(seed + 1, (B, L, D), N01, dtype)
+    g = random_typed(seed + 2, (B, L, D) if mode == GATE_FULL else (B, 1, D), U11, dtype)
+    return x, u, g
+
+
+def _mod_inputs(seed, B, L, D, mod, dtype):
+    shape = (B, L, D) if mod == MOD_TOKEN else (B, 1, D)
+    return random_typed(seed, shape, N001, dtype), random_typed(seed + 1, shape, N001, dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=NAMES.get)
+@pytest.mark.parametrize("mode", [GATE_FULL, GATE_BCAST])
+@pytest.mark.parametrize("B,L,D", SHAPES)
+def test_gate_add_ex(dte, B, L, D, mode, dtype):
+    say(f"[gate-add ex] {NAMES[dtype]} B={B} L={L} D={D} mode={mode}")
+    x, u, g = _gate_inputs(1000 + 7 * B + L + D, B, L, D, mode, dtype)
+    want = oracle.gate_add_ex(x, u, g, mode, dtype)
+    out = dte.rga_residual_gate_add_ex(to_dev_typed(x, dtype), to_dev_typed(u, dtype),
+                                       to_dev_typed(g, dtype), gate_mode=mode)
+    _bit_exact(to_host_typed(out), want, dtype, "gate-add ex")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=NAMES.get)
+@pytest.mark.parametrize("mod", [MOD_ROW, MOD_TOKEN])
+@pytest.mark.parametrize("B,L,D", SHAPES)
+def test_rms_modulate_ex(dte, B, L, D, mod, dtype):
+    say(f"[rms ex] {NAMES[dtype]} B={B} L={L} D={D} mod={mod}")
+    seed = 2000 + 5 * B + L + D
+    x = random_typed(seed, (B, L, D), N02, dtype)
+    s, t = _mod_inputs(seed + 1, B, L, D, mod, dtype)
+    want = oracle.rms_modulate_ex(x, s, t, 1e-6, mod, dtype)
+    out = dte.rga_rms_modulate_ex(to_dev_typed(x, dtype), to_dev_typed(s, dtype),
+                                  to_dev_typed(t, dtype), 1e-6, mod_mode=mod)
+    _zero_ulp(to_host_typed(out), want, dtype, f"rms ex {NAMES[dtype]} {B}x{L}x{D} mod={mod}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=NAMES.get)
+@pytest.mark.parametrize("mode,mod", [(GATE_FULL, MOD_ROW), (GATE_BCAST, MOD_ROW),
+                                      (GATE_BCAST, MOD_TOKEN), (GATE_FULL, MOD_TOKEN)])
+@pytest.mark.parametrize("B,L,D", SHAPES)
+def test_fused_ex(dte, B, L, D, mode, mod, dtype):
+    say(f"[fused ex] {NAMES[dtype]} B={B} L={L} D={D} mode={mode} mod={mod}")
+    seed = 3000 + 3 * B + L + D
+    x, u, g = _gate_inputs(seed, B, L, D, mode, dtype)
+    s, t = _mod_inputs(seed + 3, B, L, D, mod, dtype)
+    want_x, want_y = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, mode, mod, dtype)
+    xo, y = dte.rga_gate_add_rms_modulate_ex(
+        to_dev_typed(x, dtype), to_dev_typed(u, dtype), to_dev_typed(g, dtype),
+        to_dev_typed(s, dtype), to_dev_typed(t, dtype), 1e-6, gate_mode=mode, mod_mode=mod)
+    _bit_exact(to_host_typed(xo), want_x, dtype, "fused ex x_out")
+    _zero_ulp(to_host_typed(y), want_y, dtype, f"fused ex y {NAMES[dtype]} {B}x{L}x{D}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=NAMES.get)
+@pytest.mark.parametrize("D", [64, 4096, 13])
+def test_element_offsets(dte, D, dtype):
+    # every tensor one element into its allocation: 2- or 4-byte aligned
+    # addresses take the element-wise kernels, with the same results
+    B, L = 2, 37
+    say(f"[offsets] {NAMES[dtype]} B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(4000 + D, B, L, D, GATE_BCAST, dtype)
+    s, t = _mod_inputs(4100 + D, B, L, D, MOD_ROW, dtype)
+    dx, du, dg = (to_dev_typed(a, dtype, offset=1) for a in (x, u, g))
+    ds, dt = (to_dev_typed(a, dtype, offset=1) for a in (s, t))
+    assert dx.data_ptr() % 16 != 0
+    want = oracle.gate_add_ex(x, u, g, GATE_BCAST, dtype)
+    _bit_exact(to_host_typed(dte.rga_residual_gate_add_ex(dx, du, dg)), want, dtype, "gate")
+    want_y = oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_ROW, dtype)
+    _zero_ulp(to_host_typed(dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6)), want_y, dtype, "rms")
+    wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_BCAST, MOD_ROW, dtype)
+    xo = torch.empty(B * L * D + 1, dtype=dx.dtype, device=dx.device)[1:].view(B, L, D)
+    yo = torch.empty(B * L * D + 1, dtype=dx.dtype, device=dx.device)[1:].view(B, L, D)
+    dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6, x_out=xo, y=yo)
+    _bit_exact(to_host_typed(xo), wx, dtype, "fused x_out")
+    _zero_ulp(to_host_typed(yo), wy, dtype, "fused y")
+
+
+def test_bf16_ex_runs_the_same_kernels_as_the_bf16_calls(dte):
+    # with bf16, row modulation, D % 8 == 0 and aligned tensors the _ex calls
+    # take the pack path: identical results to the original calls
+    B, L, D = 2, 129, 4096
+    say(f"[ex == original] B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(5000, B, L, D, GATE_BCAST, BF16)
+    s, t = _mod_inputs(5003, B, L, D, MOD_ROW, BF16)
+    dx, du, dg, ds, dt = (to_dev(a) for a in (x, u, g, s, t))
+    a = to_host(dte.rga_residual_gate_add_ex(dx, du, dg))
+    b = to_host(dte.rga_residual_gate_add(dx, du, dg))
+    assert np.array_equal(a, b)
+    a = to_host(dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6))
+    b = to_host(dte.rms_modulate(dx, ds, dt, 1e-6))
+    assert np.array_equal(a, b)
+    a = [to_host(v) for v in dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6)]
+    b = [to_host(v) for v in dte.rga_gate_add_rms_modulate(dx, du, dg, ds, dt, 1e-6)]
+    assert all(np.array_equal(p, q) for p, q in zip(a, b))
+
+
+@pytest.mark.parametrize("dtype", [F16, F32], ids=NAMES.get)
+def test_gate_add_every_pattern(dtype, dte):
+    # x over bit patterns (every binary16 pattern; 2**16 spread binary32
+    # patterns incl. NaN, inf, subnormals), u and g random patterns: special
+    # values, overflow to inf and subnormal results go through both sides
+    say(f"[patterns] {NAMES[dtype]}")
+    rng = np.random.default_rng(6000 + dtype)
+    n = 1 << 16
+    if dtype == F16:
+        x = np.arange(n, dtype=np.uint16).reshape(1, 64, 1024)
+        u = rng.integers(0, 1 << 16, size=n, dtype=np.uint16).reshape(x.shape)
+        g = rng.integers(0, 1 << 16, size=n, dtype=np.uint16).reshape(x.shape)
+    else:
+        w = lambda: rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+        x = w().view(np.float32).reshape(1, 64, 1024)
+        u = w().view(np.float32).reshape(x.shape)
+        g = w().view(np.float32).reshape(x.shape)
+        # exponents near the bottom and the top of the range
+        u[0, :8] = (np.arange(8 * 1024, dtype=np.uint32) | 0x00700000).view(np.float32).reshape(8, 1024)
+        g[0, 8:16] = np.float32(2.0 ** 100)
+    want = oracle.gate_add_ex(x, u, g, GATE_FULL, dtype)
+    got = to_host_typed(dte.rga_residual_gate_add_ex(
+        to_dev_typed(x, dtype), to_dev_typed(u, dtype), to_dev_typed(g, dtype)))
+    _bit_exact(got, want, dtype, f"patterns {NAMES[dtype]}")
+
+
+def test_ideogram4_bcast_full_size(dte):
+    case = EXTRA_CASES["ideogram4"]
+    say(f"[gate-add] {case.name} B={case.B} L={case.L} D={case.D}")
+    inp = make_inputs(case)
+    want = oracle.gate_add(inp["x"], inp["u"], inp["g"], case.gate)
+    out = dte.rga_residual_gate_add(to_dev(inp["x"]), to_dev(inp["u"]), to_dev(inp["g"]),
+                                    gate_mode=case.gate)
+    _bit_exact(to_host(out), want, BF16, case.name)
+
+
+@pytest.mark.parametrize("dtype", [F16, F32], ids=NAMES.get)
+def test_token_modulation_at_video_scale(dte, dtype):
+    # per-token scale/shift at a DiT shape, through the pack path
+    B, L, D = 1, 4096, 3072
+    say(f"[token mod] {NAMES[dtype]} B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(7000 + dtype, B, L, D, GATE_BCAST, dtype)
+    s, t = _mod_inputs(7003 + dtype, B, L, D, MOD_TOKEN, dtype)
+    want_y = oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_TOKEN, dtype)
+    dx, ds, dt = (to_dev_typed(a, dtype) for a in (x, s, t))
+    _zero_ulp(to_host_typed(dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6)), want_y, dtype, "token rms")
+    wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_BCAST, MOD_TOKEN, dtype)
+    xo, y = dte.rga_gate_add_rms_modulate_ex(dx, to_dev_typed(u, dtype), to_dev_typed(g, dtype),
+                                             ds, dt, 1e-6)
+    _bit_exact(to_host_typed(xo), wx, dtype, "token fused x_out")
+    _zero_ulp(to_host_typed(y), wy, dtype, "token fused y")
+
+
+def test_in_place_ex(dte):
+    # element path in place: out == x for the gate-add and the modulation,
+    # x_out == x and y == u for the fused call (D % 8 != 0)
+    B, L, D, dtype = 2, 11, 1003, F16
+    say(f"[in place ex] B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(8000, B, L, D, GATE_FULL, dtype)
+    s, t = _mod_inputs(8003, B, L, D, MOD_TOKEN, dtype)
+    dx = to_dev_typed(x, dtype)
+    dte.rga_residual_gate_add_ex(dx, to_dev_typed(u, dtype), to_dev_typed(g, dtype), out=dx)
+    _bit_exact(to_host_typed(dx), oracle.gate_add_ex(x, u, g, GATE_FULL, dtype), dtype, "gate")
+    dx = to_dev_typed(x, dtype)
+    dte.rga_rms_modulate_ex(dx, to_dev_typed(s, dtype), to_dev_typed(t, dtype), 1e-6, out=dx)
+    _zero_ulp(to_host_typed(dx), oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_TOKEN, dtype),
+              dtype, "rms in place")
+    dx, du = to_dev_typed(x, dtype), to_dev_typed(u, dtype)
+    dte.rga_gate_add_rms_modulate_ex(dx, du, to_dev_typed(g, dtype), to_dev_typed(s, dtype),
+                                     to_dev_typed(t, dtype), 1e-6, x_out=dx, y=du)
+    wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_FULL, MOD_TOKEN, dtype)
+    _bit_exact(to_host_typed(dx), wx, dtype, "fused x_out in place")
+    _zero_ulp(to_host_typed(du), wy, dtype, "fused y over u")
+
+
+def test_ex_rejections(dte):
+    x = torch.zeros(1, 2, 8, dtype=torch.float64, device="cuda")
+    with pytest.raises(TypeError):
+        dte.rga_residual_gate_add_ex(x, x, x)
+    a = torch.zeros(1, 2, 8, dtype=torch.float16, device="cuda")
+    b = torch.zeros(1, 2, 8, dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        dte.rga_residual_gate_add_ex(a, b, a)        # mixed storage types
+    with pytest.raises(TypeError):
+        dte.rga_residual_gate_add(a, a, a)           # original call is bf16 only
+    odd = torch.zeros(1, 2, 9, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dte.RGAError) as e:
+        dte.rga_residual_gate_add(odd, odd, odd)
+    assert e.value.status == dte.RGA_ERR_UNSUPPORTED
+    dte.rga_residual_gate_add_ex(odd, odd, odd)      # the _ex call takes it
+    torch.cuda.synchronize()

@@ -92,3 +92,29 @@ def test_distributions_have_the_stated_moments():
     c3 = make_inputs(Case("m", 1, 512, 1024, 8, GATE_FULL))
     gu = bf16_bits_to_f32(c3["g"])
     assert gu.min() >= -1 and gu.max() <= 1 and abs(gu.std() - 1 / np.sqrt(3)) < 0.01
+
+
+def test_typed_ulp_metric():
+    # neighbours, signed zeros, NaN classes and infinities for each layout
+    from tests.exact_round import is_nan_typed, ulp_diff_typed
+    h = lambda *v: np.array(v, dtype=np.uint16)
+    assert list(ulp_diff_typed(h(0x3C00, 0x8000, 0x7E00, 0x7C00),
+                               h(0x3C01, 0x0000, 0x7C01, 0x7BFF), 1)) == [1, 0, 0, 1]
+    assert list(is_nan_typed(h(0x7C00, 0x7C01, 0xFE00, 0x7F80), 1)) == [False, True, True, True]
+    f = np.array([1.0, -0.0, np.inf, np.nan], dtype=np.float32)
+    g = np.array([np.nextafter(np.float32(1), np.float32(2)), 0.0,
+                  np.finfo(np.float32).max, np.nan], dtype=np.float32)
+    assert list(ulp_diff_typed(f, g, 2)) == [1, 0, 1, 0]
+    assert ulp_diff_typed(np.float32([np.nan]), np.float32([1.0]), 2)[0] > 1 << 30
+    # one step across zero: the smallest subnormals of either sign are 2 apart
+    assert ulp_diff_typed(h(0x0001), h(0x8001), 1)[0] == 2
+    assert ulp_diff_typed(h(0x0001), h(0x8001), 0)[0] == 2
+
+
+def test_typed_generator_matches_library_conversions():
+    from synth_inputs import BF16, F16, F32, N01, random_bits, random_typed
+    a32 = random_typed(9, (2, 3, 40), N01, F32)
+    assert a32.dtype == np.float32 and a32.shape == (2, 3, 40)
+    a16 = random_typed(9, (2, 3, 40), N01, F16)
+    assert np.array_equal(a16.view(np.float16), a32.astype(np.float16))
+    assert np.array_equal(random_typed(9, (2, 3, 40), N01, BF16), random_bits(9, (2, 3, 40), N01))
