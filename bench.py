@@ -20,6 +20,11 @@ Reported (one JSON line on stdout):
                (a 1 GiB read with cache-allocating loads pushes earlier data
                out of the L2s and the 256 MB memory-side cache and leaves
                only clean lines), median of repetitions
+  variants     with --variants 1: the _ex calls at DiT shapes (binary16 and
+               binary32 storage, per-token modulation, the element-wise paths
+               for ragged D, element offsets and rows past the register
+               limit) and the ideogram4 [1,4096,4608] bcast shape; cold and
+               back-to-back per-call time
   small_configs with --small-configs 1: the other workload configurations
                (c1 full [1,126,2048] + rms_modulate, c2 bcast [1,L,3072] for
                L = 512, 4096, 4608): cold per-call time, and back-to-back
@@ -113,6 +118,9 @@ def parse_args():
     p.add_argument("--small-configs", type=int, default=0,
                    help="1: also time the c1/c2 configurations (kept out of the default "
                         "run so a profile of it averages the step's launches only)")
+    p.add_argument("--variants", type=int, default=0,
+                   help="1: also time the _ex variants (storage types, per-token "
+                        "modulation, element-wise paths) and the ideogram4 shape")
     p.add_argument("--fused-reps", type=int, default=30,
                    help="repetitions of the fused-vs-separate comparison (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -247,32 +255,34 @@ def main():
                           "us_p90": round(float(np.percentile(ts, 90)), 2),
                           "GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
 
+    e0, e1 = hev.new(), hev.new()
+
+    def cold_and_warm(fn, nbytes, kernel):
+        ts = []
+        for _ in range(args.cold_reps):
+            dte.read_(src, sink)
+            hev.record(e0, stream)
+            fn()
+            hev.record(e1, stream)
+            hev.sync(e1)
+            ts.append(hev.ms(e0, e1) * 1e3)
+        hev.record(e0, stream)
+        for _ in range(100):
+            fn()
+        hev.record(e1, stream)
+        hev.sync(e1)
+        warm = hev.ms(e0, e1) * 1e3 / 100
+        med = statistics.median(ts)
+        return {"kernel": kernel, "bytes": nbytes, "cold_us_median": round(med, 2),
+                "cold_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                "back_to_back_us": round(warm, 2),
+                "back_to_back_GBps": round(nbytes / (warm * 1e-6) / 1e9, 1),
+                "frac_of_hbm_peak": round(max(nbytes / (med * 1e-6), nbytes / (warm * 1e-6))
+                                          / 1e9 / HBM_PEAK_GBPS, 4)}
+
     small = {}
     if args.small_configs and args.cold_reps > 0:
         log("small configs c1, c2")
-        e0, e1 = hev.new(), hev.new()
-
-        def cold_and_warm(fn, nbytes):
-            ts = []
-            for _ in range(args.cold_reps):
-                dte.read_(src, sink)
-                hev.record(e0, stream)
-                fn()
-                hev.record(e1, stream)
-                hev.sync(e1)
-                ts.append(hev.ms(e0, e1) * 1e3)
-            hev.record(e0, stream)
-            for _ in range(100):
-                fn()
-            hev.record(e1, stream)
-            hev.sync(e1)
-            warm = hev.ms(e0, e1) * 1e3 / 100
-            med = statistics.median(ts)
-            return {"bytes": nbytes, "cold_us_median": round(med, 2),
-                    "cold_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                    "back_to_back_us": round(warm, 2),
-                    "back_to_back_GBps": round(nbytes / (warm * 1e-6) / 1e9, 1)}
-
         for key in ("c1", "c2a", "c2b", "c2c"):
             c = CASES[key]
             h = make_inputs(c)
@@ -280,12 +290,18 @@ def main():
             o = torch.empty_like(d["x"])
             small[c.name + "_gate_add"] = cold_and_warm(
                 lambda: dte.rga_residual_gate_add(d["x"], d["u"], d["g"], out=o, gate_mode=c.gate),
-                gate_bytes(c))
+                gate_bytes(c), "gate_add_full_kernel" if c.gate == GATE_FULL else "gate_add_bcast_kernel")
             if c.rms:
                 small[c.name + "_rms_modulate"] = cold_and_warm(
                     lambda: dte.rms_modulate(d["x"], d["scale"], d["shift"], c.eps, out=o),
-                    (2 * c.elems + 2 * c.B * c.D) * 2)
+                    (2 * c.elems + 2 * c.B * c.D) * 2, "rms_modulate_kernel")
             del d, o
+
+    variants = {}
+    if args.variants and args.cold_reps > 0:
+        log("variants: storage types, per-token modulation, element-wise paths, ideogram4")
+        variants = run_variants(dte, torch, dev, cold_and_warm, log)
+        torch.cuda.empty_cache()
 
     fused = {}
     if args.fused_reps > 0:
@@ -379,12 +395,113 @@ def main():
         "per_launch": per_launch,
         "cold": cold,
         "small_configs": small,
+        "variants": variants,
         "fused": fused,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def run_variants(dte, torch, dev, cold_and_warm, log):
+    """The _ex variants at DiT shapes, each timed cold (caches flushed) and
+    back to back. Inputs: seeded normal draws on the device (x N(0,2), u
+    N(0,1), gate uniform(-1,1), scale/shift N(0,0.1)), out of place.
+    Algorithmic bytes: every input element read once (a broadcast row once
+    per call), every output element written once, at the storage size."""
+    from synth_inputs import EXTRA_CASES, make_inputs
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240)
+    T = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+    def draw(shape, dt, std=1.0, uniform=False, offset=0):
+        n = 1
+        for v in shape:
+            n *= v
+        flat = torch.empty(n + offset, dtype=T[dt], device=dev)
+        if uniform:
+            a = torch.rand(n, generator=gen, device=dev) * 2 - 1
+        else:
+            a = torch.randn(n, generator=gen, device=dev) * std
+        flat[offset:].copy_(a)
+        return flat[offset:].view(shape)
+
+    out = {}
+
+    def gate(name, B, L, D, dt, mode, offset=0):
+        x = draw((B, L, D), dt, 2.0, offset=offset)
+        u = draw((B, L, D), dt, offset=offset)
+        g = draw((B, L, D) if mode == dte.GATE_FULL else (B, 1, D), dt, uniform=True, offset=offset)
+        o = draw((B, L, D), dt, offset=offset)
+        es = x.element_size()
+        n = B * L * D
+        nbytes = (4 * n if mode == dte.GATE_FULL else 3 * n + B * D) * es
+        fast = D % 8 == 0 and offset == 0
+        kern = ("gate_add_full_kernel" if mode == dte.GATE_FULL else "gate_add_bcast_kernel") \
+            if fast else "gate_add_generic_kernel"
+        log(f"variant {name}")
+        out[name] = cold_and_warm(lambda: dte.rga_residual_gate_add_ex(x, u, g, out=o),
+                                  nbytes, kern)
+
+    def rms(name, B, L, D, dt, mod, offset=0):
+        mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
+        x = draw((B, L, D), dt, 2.0, offset=offset)
+        sc, sh = draw(mshape, dt, 0.1, offset=offset), draw(mshape, dt, 0.1, offset=offset)
+        o = draw((B, L, D), dt, offset=offset)
+        es = x.element_size()
+        n = B * L * D
+        nbytes = (2 * n + 2 * (n if mod == dte.MOD_TOKEN else B * D)) * es
+        fast = D % 8 == 0 and offset == 0 and D <= dte.RGA_RMS_MAX_D
+        log(f"variant {name}")
+        out[name] = cold_and_warm(
+            lambda: dte.rga_rms_modulate_ex(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
+            "rms_modulate_kernel" if fast else "rms_modulate_generic_kernel")
+
+    def fused(name, B, L, D, dt, mode, mod):
+        mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
+        x, u = draw((B, L, D), dt, 2.0), draw((B, L, D), dt)
+        g = draw((B, L, D) if mode == dte.GATE_FULL else (B, 1, D), dt, uniform=True)
+        sc, sh = draw(mshape, dt, 0.1), draw(mshape, dt, 0.1)
+        xo, y = torch.empty_like(x), torch.empty_like(x)
+        es = x.element_size()
+        n = B * L * D
+        nbytes = (4 * n + (n if mode == dte.GATE_FULL else B * D)
+                  + 2 * (n if mod == dte.MOD_TOKEN else B * D)) * es
+        log(f"variant {name}")
+        out[name] = cold_and_warm(
+            lambda: dte.rga_gate_add_rms_modulate_ex(x, u, g, sc, sh, 1e-6, x_out=xo, y=y,
+                                                     gate_mode=mode, mod_mode=mod),
+            nbytes, "gate_add_rms_modulate_kernel")
+
+    # the ideogram4 shape of the residual-gate page's table, bf16, its seeded case
+    c = EXTRA_CASES["ideogram4"]
+    h = make_inputs(c)
+    to = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+    dx, du, dg = to(h["x"]), to(h["u"]), to(h["g"])
+    do = torch.empty_like(dx)
+    log(f"variant {c.name}")
+    out[c.name + "_gate_add"] = cold_and_warm(
+        lambda: dte.rga_residual_gate_add(dx, du, dg, out=do, gate_mode=c.gate),
+        (3 * c.elems + c.B * c.D) * 2, "gate_add_bcast_kernel")
+    del dx, du, dg, do
+
+    for dt in ("f16", "f32"):
+        gate(f"{dt}_bcast_gate_add_[1,32640,4096]", 1, 32640, 4096, dt, dte.GATE_BCAST)
+        gate(f"{dt}_full_gate_add_[1,8160,4096]", 1, 8160, 4096, dt, dte.GATE_FULL)
+        rms(f"{dt}_rms_modulate_[2,32640,4096]", 2, 32640, 4096, dt, dte.MOD_ROW)
+    rms("bf16_rms_modulate_token_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_TOKEN)
+    fused("bf16_fused_token_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.GATE_BCAST, dte.MOD_TOKEN)
+    fused("f16_fused_[2,32640,4096]", 2, 32640, 4096, "f16", dte.GATE_BCAST, dte.MOD_ROW)
+    # element-wise paths: ragged D, an element offset, rows past the register limit
+    gate("bf16_bcast_gate_add_ragged_[1,32640,4100]", 1, 32640, 4100, "bf16", dte.GATE_BCAST)
+    gate("bf16_bcast_gate_add_offset1_[1,32640,4096]", 1, 32640, 4096, "bf16", dte.GATE_BCAST,
+         offset=1)
+    rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
+    rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
+    torch.cuda.synchronize()
+    return out
 
 
 def kernel_source_digest() -> str:
