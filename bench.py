@@ -23,7 +23,8 @@ Reported (one JSON line on stdout):
   variants     with --variants 1: the _ex calls at DiT shapes (binary16 and
                binary32 storage, per-token modulation, the element-wise paths
                for ragged D, element offsets and rows past the register
-               limit) and the ideogram4 [1,4096,4608] bcast shape; cold and
+               limit), the ideogram4 [1,4096,4608] bcast shape and the
+               tanh-GELU on the FFN intermediate [1,32640,16384]; cold and
                back-to-back per-call time
   small_configs with --small-configs 1: the other workload configurations
                (c1 full [1,126,2048] + rms_modulate, c2 bcast [1,L,3072] for
@@ -500,6 +501,22 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
          offset=1)
     rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
     rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
+    # tanh-GELU on the FFN intermediate (video tokens x 4 hidden)
+    def gelu(name, rows, F, dt, with_bias=False):
+        x = draw((1, rows, F), dt, 2.0)
+        b = draw((F,), dt) if with_bias else None
+        o = torch.empty_like(x)
+        nbytes = (2 * rows * F + (F if with_bias else 0)) * x.element_size()
+        fast = (F % 8 == 0) if with_bias else True
+        log(f"variant {name}")
+        out[name] = cold_and_warm(lambda: dte.gelu_tanh(x, b, out=o), nbytes,
+                                  ("gelu_tanh_bias_kernel" if with_bias else "gelu_tanh_flat_kernel")
+                                  if fast else "gelu_tanh_generic_kernel")
+
+    gelu("bf16_gelu_tanh_[1,32640,16384]", 32640, 16384, "bf16")
+    gelu("bf16_gelu_tanh_bias_[1,32640,16384]", 32640, 16384, "bf16", with_bias=True)
+    gelu("f16_gelu_tanh_[1,32640,16384]", 32640, 16384, "f16")
+    gelu("f32_gelu_tanh_[1,8160,16384]", 8160, 16384, "f32")
     torch.cuda.synchronize()
     return out
 

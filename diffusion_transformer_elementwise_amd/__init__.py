@@ -21,6 +21,10 @@ tensors starting at any element offset, and per-token scale/shift [B, L, D]:
     rga_rms_modulate_ex(x, scale, shift, eps=1e-6, out=None, mod_mode=None)
     rga_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps=1e-6, x_out=None,
                                  y=None, gate_mode=None, mod_mode=None)
+
+The FFN's tanh-GELU, any storage type, over the last dimension F:
+
+    gelu_tanh(x, bias=None, out=None)   out = gelu(x + bias)
 """
 from __future__ import annotations
 
@@ -44,6 +48,7 @@ from ._lib import (  # noqa: F401
     check_residual_gate_add,
     check_residual_gate_add_ex,
     check_rms_modulate,
+    check_gelu_tanh,
     check_rms_modulate_ex,
     library,
     library_path,
@@ -52,6 +57,7 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     copy_,
     fill_,
+    gelu_tanh,
     read_,
     rga_gate_add_rms_modulate,
     rga_gate_add_rms_modulate_ex,
@@ -68,6 +74,7 @@ __all__ = [
     "rga_residual_gate_add_ex",
     "rga_rms_modulate_ex",
     "rga_gate_add_rms_modulate_ex",
+    "gelu_tanh",
     "GATE_FULL",
     "GATE_BCAST",
     "RGAError",

@@ -86,6 +86,10 @@ def _load():
     lib.rga_check_gate_add_rms_modulate_ex.argtypes = [p, p, p, p, p, f32, p, p, i64, i64,
                                                        i64, i32, i32, i32]
     lib.rga_check_gate_add_rms_modulate_ex.restype = i32
+    lib.rga_gelu_tanh.argtypes = [p, p, p, i64, i64, i32, p]
+    lib.rga_gelu_tanh.restype = i32
+    lib.rga_check_gelu_tanh.argtypes = [p, p, p, i64, i64, i32]
+    lib.rga_check_gelu_tanh.restype = i32
     lib.rga_status_string.argtypes = [i32]
     lib.rga_status_string.restype = ctypes.c_char_p
     lib.rga_copy.argtypes = [p, p, i64, p]
@@ -137,3 +141,7 @@ def check_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps, x_out, y, B, L, D
     return _LIB.rga_check_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps, x_out,
                                                    y, B, L, D, gate_mode, mod_mode,
                                                    dtype)
+
+
+def check_gelu_tanh(x, bias, out, rows, F, dtype) -> int:
+    return _LIB.rga_check_gelu_tanh(x, bias, out, rows, F, dtype)

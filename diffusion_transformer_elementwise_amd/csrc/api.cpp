@@ -13,9 +13,10 @@
 //      dispatch limit;
 //   5. RGA_ERR_ALIAS: an output overlapping an input other than the exact
 //      in-place aliases each call allows.
-// The _ex calls take the 16-byte-pack kernels when D % 8 == 0, every pointer
-// is 16-byte aligned and (modulation) D <= RGA_RMS_MAX_D, and the
-// element-wise kernels otherwise.
+// The _ex calls take the 16-byte-pack kernels when every pointer is 16-byte
+// aligned and D % 8 == 0 (any D for a full-gate add, which is one flat
+// stream) and, for the modulation, D <= RGA_RMS_MAX_D; the element-wise
+// kernels otherwise.
 // The gate-add rejection of unsupported inputs mirrors the residual-gate
 // page's test list ("unsupported input rejection"); the bf16-only contract
 // mirrors the modulation page's guard that admits only bf16 tensors.
@@ -114,6 +115,10 @@ int check_gate_add(const void* x, const void* u, const void* g,
     int st = layout(ptrs, 4, D, es, strict, 0, fast);
     if (st != RGA_OK)
         return st;
+    // a full gate is one flat stream: the pack kernel takes any D (its last
+    // lane adds the trailing B*L*D % 8 elements)
+    if (!strict && gate_mode == RGA_GATE_FULL)
+        *fast = aligned16(x) && aligned16(u) && aligned16(g) && aligned16(out);
     if (!rga::gate_add_grid_fits(B, L, D, gate_mode, *fast))
         return RGA_ERR_UNSUPPORTED;
 
@@ -216,6 +221,34 @@ int check_fused(const void* x, const void* u, const void* g,
                 return RGA_ERR_ALIAS;
     }
     if (overlaps(range_of(x_out, bytes), range_of(y, bytes)))
+        return RGA_ERR_ALIAS;
+    return RGA_OK;
+}
+
+int check_gelu(const void* x, const void* bias, const void* out, int64_t rows,
+               int64_t F, int dtype, bool* fast)
+{
+    if (rows < 0 || F < 0)
+        return RGA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype))
+        return RGA_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    int64_t n = 0, bytes = 0;
+    if (__builtin_mul_overflow(rows, F, &n) || __builtin_mul_overflow(n, (int64_t)es, &bytes))
+        return RGA_ERR_INVALID_ARG;
+    if (n == 0)
+        return RGA_OK;
+    if (!x || !out)
+        return RGA_ERR_INVALID_ARG;
+    if (!aligned_to(x, es) || !aligned_to(out, es) || (bias && !aligned_to(bias, es)))
+        return RGA_ERR_UNSUPPORTED;
+    *fast = aligned16(x) && aligned16(out) && (!bias || (aligned16(bias) && F % 8 == 0));
+    if (!rga::gelu_tanh_grid_fits(rows, F, bias != nullptr, *fast))
+        return RGA_ERR_UNSUPPORTED;
+    const Range o = range_of(out, bytes);
+    if (overlaps(o, range_of(x, bytes)) && out != x)
+        return RGA_ERR_ALIAS;
+    if (bias && overlaps(o, range_of(bias, F * es)))
         return RGA_ERR_ALIAS;
     return RGA_OK;
 }
@@ -378,6 +411,23 @@ int rga_gate_add_rms_modulate_ex(const void* x, const void* u, const void* g,
 {
     return fused(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode,
                  mod_mode, dtype, false, stream);
+}
+
+int rga_check_gelu_tanh(const void* x, const void* bias, const void* out,
+                        int64_t rows, int64_t F, int dtype)
+{
+    bool fast = false;
+    return check_gelu(x, bias, out, rows, F, dtype, &fast);
+}
+
+int rga_gelu_tanh(const void* x, const void* bias, void* out, int64_t rows,
+                  int64_t F, int dtype, hipStream_t stream)
+{
+    bool fast = false;
+    const int st = check_gelu(x, bias, out, rows, F, dtype, &fast);
+    if (st != RGA_OK || rows == 0 || F == 0)
+        return st;
+    return launched(rga::launch_gelu_tanh(x, bias, out, rows, F, dtype, fast, stream));
 }
 
 // Shared rules of the measurement helpers for one destination range and an

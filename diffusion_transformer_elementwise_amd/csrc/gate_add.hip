@@ -11,10 +11,13 @@
 // measured on MI355X: one wave64 per workgroup, one 8-element pack per lane
 // and stream, nontemporal loads and stores. Many short waves spread over the
 // 256 CUs keep the HBM request stream even; more packs per lane, larger
-// workgroups and persistent grids all measured slower.
+// workgroups and persistent grids all measured slower. Which 8 elements a
+// lane holds does not matter here, so binary32 packs are lane-interleaved
+// (Interleaved in dtype.hpp) for contiguous wave-wide accesses.
 //
-// Generic path (any D, pointers aligned to the element size): one element per
-// thread, same arithmetic, for shapes the fast path cannot take.
+// Generic path (any D, pointers aligned to the element size): element
+// loads and stores with the same arithmetic, for shapes the fast path cannot
+// take.
 //
 // Every thread reads its own elements before writing them and no element
 // depends on another, so out may alias x or u (and g in full mode).
@@ -26,8 +29,8 @@
 namespace rga {
 namespace {
 
-constexpr int kBlock = 64;           // fast path: one wave per workgroup
-constexpr int kGenericBlock = 256;   // generic path: elements per workgroup
+constexpr int kBlock = 64;  // one wave per workgroup
+constexpr int kSpan = 8;    // generic path: elements per lane
 
 template <int DT>
 __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
@@ -43,25 +46,38 @@ __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
     return Pack<DT>::make(o);
 }
 
-// Full gate: a flat stream of n8 = B*L*D/8 packs; lane t of workgroup w
-// takes pack w*64 + t.
+// Full gate: a flat stream of n8 = floor(n / 8) packs plus n % 8 trailing
+// elements (n = B*L*D; rows play no part). Workgroup w takes the chunk of
+// packs 64w .. 64w + h - 1 (h = 64 but for the last chunk), lane t its share
+// of it (see Interleaved); lane h of the last chunk (in a workgroup of its
+// own when n8 is a multiple of 64) takes the trailing elements one by one.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_full_kernel(
-    const void* x, const void* u, const void* g, void* out, int64_t n8)
+    const void* x, const void* u, const void* g, void* out, int64_t n8, int tail)
 {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= n8)
-        return;
-    const Pack<DT> xv = Pack<DT>::load_stream(x, i);
-    const Pack<DT> uv = Pack<DT>::load_stream(u, i);
-    const Pack<DT> gv = Pack<DT>::load_stream(g, i);
-    gate_add8<DT>(xv, uv, gv).store_stream(out, i);
+    const int64_t c0 = (int64_t)blockIdx.x * kBlock;
+    const int t = threadIdx.x;
+    const int h = (n8 - c0 < kBlock) ? (int)(n8 - c0) : kBlock;
+    if (t < h) {
+        using I = Interleaved<DT>;
+        const Pack<DT> xv = I::load_stream(x, c0, t, h);
+        const Pack<DT> uv = I::load_stream(u, c0, t, h);
+        const Pack<DT> gv = I::load_stream(g, c0, t, h);
+        I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
+    } else if (t == h && c0 + h == n8) {
+        for (int e = 0; e < tail; ++e) {
+            const int64_t i = 8 * n8 + e;
+            const float p = load_elem<DT>(u, i) * load_elem<DT>(g, i);
+            store_elem<DT>(out, i, load_elem<DT>(x, i) + p);
+        }
+    }
 }
 
 // Broadcast gate [B, 1, D]. Grid: x = (row l of the batch) * chunks + chunk,
-// y = batch b, where a chunk is 64 packs of a row. Lane t handles pack
-// chunk*64 + t of row (b, l); its gate pack comes from row b of g, which
-// stays in the caches while the streams of x, u and out pass through.
+// y = batch b, where a chunk is up to 64 packs of a row. The lanes of a
+// chunk take its packs as in the full kernel; the matching gate packs come
+// from row b of g, which stays in the caches while the streams of x, u and
+// out pass through.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t L,
@@ -69,33 +85,78 @@ __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
 {
     const uint32_t l = blockIdx.x / chunks;
     const uint32_t chunk = blockIdx.x - l * chunks;
-    const uint32_t col = chunk * kBlock + threadIdx.x;
-    if (col >= vpr)
+    const uint32_t col0 = chunk * kBlock;
+    const int t = threadIdx.x;
+    const int h = (vpr - col0 < (uint32_t)kBlock) ? (int)(vpr - col0) : kBlock;
+    if (t >= h)
         return;
     const int64_t b = blockIdx.y;
-    const int64_t i = (b * L + l) * vpr + col;
-    const Pack<DT> xv = Pack<DT>::load_stream(x, i);
-    const Pack<DT> uv = Pack<DT>::load_stream(u, i);
-    const Pack<DT> gv = Pack<DT>::load(g, b * vpr + col);
-    gate_add8<DT>(xv, uv, gv).store_stream(out, i);
+    const int64_t c0 = (b * L + l) * vpr + col0;
+    using I = Interleaved<DT>;
+    const Pack<DT> xv = I::load_stream(x, c0, t, h);
+    const Pack<DT> uv = I::load_stream(u, c0, t, h);
+    const Pack<DT> gv = I::load(g, b * vpr + col0, t, h);
+    I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
 }
 
-// Generic: grid x = (row l) * cD + c, y = batch b; element d = c*256 + t.
-template <int DT, bool FULL>
-__global__ __launch_bounds__(kGenericBlock) void gate_add_generic_kernel(
-    const void* x, const void* u, const void* g, void* out, int64_t L,
-    int64_t D, uint32_t cD)
+// Generic path: each workgroup (one wave) takes a span of 64 * kSpan
+// elements, lane t the elements span_start + 64 e + t for e < kSpan, so that
+// every load and store instruction of the wave touches one contiguous run and
+// each lane keeps kSpan independent loads per stream in flight.
+// Full gate: spans tile the flat B*L*D elements; grid x = span.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gate_add_generic_full_kernel(
+    const void* x, const void* u, const void* g, void* out, int64_t n)
 {
-    const uint32_t l = blockIdx.x / cD;
-    const uint32_t c = blockIdx.x - l * cD;
-    const int64_t d = (int64_t)c * kGenericBlock + threadIdx.x;
-    if (d >= D)
-        return;
+    const int64_t s0 = (int64_t)blockIdx.x * (kBlock * kSpan) + threadIdx.x;
+    float xv[kSpan], uv[kSpan], gv[kSpan];
+#pragma unroll
+    for (int e = 0; e < kSpan; ++e) {
+        const int64_t i = s0 + (int64_t)e * kBlock;
+        const bool in = i < n;
+        xv[e] = in ? load_elem_stream<DT>(x, i) : 0.0f;
+        uv[e] = in ? load_elem_stream<DT>(u, i) : 0.0f;
+        gv[e] = in ? load_elem_stream<DT>(g, i) : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kSpan; ++e) {
+        const int64_t i = s0 + (int64_t)e * kBlock;
+        if (i < n) {
+            const float p = uv[e] * gv[e];
+            store_elem_stream<DT>(out, i, xv[e] + p);
+        }
+    }
+}
+
+// Broadcast gate: spans tile each row; grid x = (row l) * spans per row +
+// span, y = batch b; the gate element of column d is g[b*D + d].
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gate_add_generic_bcast_kernel(
+    const void* x, const void* u, const void* g, void* out, int64_t L,
+    int64_t D, uint32_t spans)
+{
+    const uint32_t l = blockIdx.x / spans;
+    const uint32_t sp = blockIdx.x - l * spans;
     const int64_t b = blockIdx.y;
-    const int64_t i = (b * L + l) * D + d;
-    const float p = load_elem<DT>(u, i) * load_elem<DT>(g, FULL ? i : b * D + d);
-    const float s = load_elem<DT>(x, i) + p;
-    store_elem<DT>(out, i, s);
+    const int64_t d0 = (int64_t)sp * (kBlock * kSpan) + threadIdx.x;
+    const int64_t row = (b * L + l) * D;
+    float xv[kSpan], uv[kSpan], gv[kSpan];
+#pragma unroll
+    for (int e = 0; e < kSpan; ++e) {
+        const int64_t d = d0 + (int64_t)e * kBlock;
+        const bool in = d < D;
+        xv[e] = in ? load_elem_stream<DT>(x, row + d) : 0.0f;
+        uv[e] = in ? load_elem_stream<DT>(u, row + d) : 0.0f;
+        gv[e] = in ? load_elem<DT>(g, b * D + d) : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kSpan; ++e) {
+        const int64_t d = d0 + (int64_t)e * kBlock;
+        if (d < D) {
+            const float p = uv[e] * gv[e];
+            store_elem_stream<DT>(out, row + d, xv[e] + p);
+        }
+    }
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -106,20 +167,27 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
                         int gate_mode, bool fast, hipStream_t stream)
 {
     if (!fast) {
-        uint32_t cD = (uint32_t)ceil_div(D, kGenericBlock);
-        void* args[] = {&x, &u, &g, &out, &L, &D, &cD};
-        const void* k = gate_mode == RGA_GATE_FULL
-                            ? reinterpret_cast<const void*>(&gate_add_generic_kernel<DT, true>)
-                            : reinterpret_cast<const void*>(&gate_add_generic_kernel<DT, false>);
-        return hipLaunchKernel(k, dim3((uint32_t)(L * cD), (uint32_t)B),
-                               dim3(kGenericBlock), args, 0, stream);
+        if (gate_mode == RGA_GATE_FULL) {
+            int64_t n = B * L * D;
+            void* args[] = {&x, &u, &g, &out, &n};
+            return hipLaunchKernel(
+                reinterpret_cast<const void*>(&gate_add_generic_full_kernel<DT>),
+                dim3((uint32_t)ceil_div(n, kBlock * kSpan)), dim3(kBlock), args, 0, stream);
+        }
+        uint32_t spans = (uint32_t)ceil_div(D, kBlock * kSpan);
+        void* args[] = {&x, &u, &g, &out, &L, &D, &spans};
+        return hipLaunchKernel(
+            reinterpret_cast<const void*>(&gate_add_generic_bcast_kernel<DT>),
+            dim3((uint32_t)(L * spans), (uint32_t)B), dim3(kBlock), args, 0, stream);
     }
     if (gate_mode == RGA_GATE_FULL) {
-        int64_t n8 = B * L * D / 8;
-        void* args[] = {&x, &u, &g, &out, &n8};
+        const int64_t n = B * L * D;
+        int64_t n8 = n / 8;
+        int tail = (int)(n % 8);
+        void* args[] = {&x, &u, &g, &out, &n8, &tail};
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_full_kernel<DT>),
-            dim3((uint32_t)ceil_div(n8, kBlock)), dim3(kBlock), args, 0,
+            dim3((uint32_t)ceil_div(n8 + (tail ? 1 : 0), kBlock)), dim3(kBlock), args, 0,
             stream);
     }
     uint32_t vpr = (uint32_t)(D / 8);
@@ -139,14 +207,17 @@ bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode,
                         bool fast)
 {
     const int64_t max_x = (((int64_t)1 << 32) - 1);
+    if (gate_mode == RGA_GATE_FULL && fast)  // one flat grid dimension
+        return ceil_div(B * L * D / 8 + 1, kBlock) <= max_x / kBlock;
     if (B > 65535)
         return false;
-    if (!fast)
-        return L * ceil_div(D, kGenericBlock) <= max_x / kGenericBlock;
-    const int64_t vpr = D / 8;
-    if (gate_mode == RGA_GATE_FULL)
-        return ceil_div(B * L * vpr, kBlock) <= max_x / kBlock;
-    return L * ceil_div(vpr, kBlock) <= max_x / kBlock;
+    if (!fast) {
+        const int64_t span = kBlock * kSpan;
+        if (gate_mode == RGA_GATE_FULL)
+            return ceil_div(B * L * D, span) <= max_x / kBlock;
+        return L * ceil_div(D, span) <= max_x / kBlock;
+    }
+    return L * ceil_div(D / 8, kBlock) <= max_x / kBlock;
 }
 
 hipError_t launch_gate_add(const void* x, const void* u, const void* g,

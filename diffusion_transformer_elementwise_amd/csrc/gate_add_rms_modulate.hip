@@ -26,7 +26,7 @@
 // like x and u.
 //
 // Generic path (any D, element-aligned pointers): the same operations in two
-// passes over the row, element by element; the second pass re-reads x_out,
+// passes over the row with element loads; the second pass re-reads x_out,
 // which the same lane wrote in the first.
 #include "dtype.hpp"
 #include "launch.hpp"
@@ -37,6 +37,8 @@ namespace rga {
 namespace {
 
 constexpr int kBlock = 64;
+constexpr int kStage = 2048;  // generic path: elements staged in LDS per step
+constexpr int kSpan = 8;      // generic path: elements per lane in pass 2
 
 template <int DT>
 __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
@@ -50,19 +52,6 @@ __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
         o[e] = x.get(e) + p;
     }
     return Pack<DT>::make(o);
-}
-
-// binary32 value of s after one rounding to the storage type
-template <int DT>
-__device__ __forceinline__ float rounded(float s)
-{
-    if constexpr (DT == kF32) {
-        return s;
-    } else if constexpr (DT == kF16) {
-        return (float)(_Float16)s;
-    } else {
-        return __uint_as_float(pack_bf16(s, 0.0f) << 16);
-    }
 }
 
 // Grid: x = row l, y = batch b. G = packs per lane (at least ceil(D / 512));
@@ -133,33 +122,60 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
     }
 }
 
-// Generic: one wave per row; grid x = row l, y = batch b.
+// Generic: one wave per row; grid x = row l, y = batch b. Pass 1 walks the
+// row in stages of kStage elements: wave-contiguous loads (lane t takes
+// elements 64e + t), x_out formed and stored, its rounded values staged in
+// LDS, from where lane j adds up groups j, j + 64, ... of the stage in the
+// fixed order. Pass 2 re-reads x_out (each lane the elements it wrote) and
+// writes y.
 template <bool FULL, int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     const void* x, const void* u, const void* g, const void* scale,
     const void* shift, float eps, float d_float, void* x_out, void* y,
     int64_t L, int64_t D)
 {
+    __shared__ float stage[kStage];
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t grow = FULL ? row : b * D;
     const int64_t mrow = (MOD == kModToken) ? row : b * D;
-    const int64_t groups = (D + 7) / 8;
 
     float acc = 0.0f;
-    for (int64_t k = lane; k < groups; k += 64) {
-        for (int e = 0; e < 8; ++e) {
-            const int64_t d = 8 * k + e;
-            if (d < D) {
-                const float p = load_elem<DT>(u, row + d) *
-                                load_elem<DT>(g, FULL ? row + d : b * D + d);
-                const float s = load_elem<DT>(x, row + d) + p;
-                store_elem<DT>(x_out, row + d, s);
-                const float v = rounded<DT>(s);
-                const float sv = v * v;
-                acc = acc + sv;
+    for (int64_t s0 = 0; s0 < D; s0 += kStage) {
+        float xv[kStage / kBlock], uv[kStage / kBlock], gv[kStage / kBlock];
+#pragma unroll
+        for (int e = 0; e < kStage / kBlock; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
+            const bool in = d < D;
+            xv[e] = in ? load_elem_stream<DT>(x, row + d) : 0.0f;
+            uv[e] = in ? load_elem_stream<DT>(u, row + d) : 0.0f;
+            gv[e] = in ? (FULL ? load_elem_stream<DT>(g, grow + d) : load_elem<DT>(g, grow + d))
+                       : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kStage / kBlock; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
+            const float p = uv[e] * gv[e];
+            const float sum = xv[e] + p;
+            if (d < D)
+                store_elem<DT>(x_out, row + d, sum);
+            stage[e * kBlock + lane] = rounded<DT>(sum);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kStage / 512; ++m) {
+            const int g0 = (lane + kBlock * m) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (s0 + g0 + e < D) {
+                    const float a = stage[g0 + e];
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
             }
         }
+        __syncthreads();
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1)
@@ -169,14 +185,26 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     const float q = sqrtf(t);
     const float rr = 1.0f / q;
 
-    for (int64_t k = lane; k < groups; k += 64) {
-        for (int e = 0; e < 8; ++e) {
-            const int64_t d = 8 * k + e;
+    for (int64_t s0 = 0; s0 < D; s0 += kBlock * kSpan) {
+        float xv[kSpan], sv[kSpan], hv[kSpan];
+#pragma unroll
+        for (int e = 0; e < kSpan; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
+            const bool in = d < D;
+            xv[e] = in ? load_elem<DT>(x_out, row + d) : 0.0f;
+            sv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(scale, mrow + d)
+                                           : load_elem<DT>(scale, mrow + d)) : 0.0f;
+            hv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(shift, mrow + d)
+                                           : load_elem<DT>(shift, mrow + d)) : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kSpan; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
             if (d < D) {
-                const float n = load_elem<DT>(x_out, row + d) * rr;
-                const float a = 1.0f + load_elem<DT>(scale, mrow + d);
+                const float n = xv[e] * rr;
+                const float a = 1.0f + sv[e];
                 const float m = n * a;
-                store_elem<DT>(y, row + d, m + load_elem<DT>(shift, mrow + d));
+                store_elem_stream<DT>(y, row + d, m + hv[e]);
             }
         }
     }

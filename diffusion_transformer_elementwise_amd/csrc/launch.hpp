@@ -36,6 +36,13 @@ hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
                                         int mod_mode, int dtype, bool fast,
                                         hipStream_t stream);
 
+// tanh-GELU over [rows, F] with an optional bias row (gelu_tanh.hip); fast:
+// every pointer 16-byte aligned and, with a bias, F % 8 == 0
+bool gelu_tanh_grid_fits(int64_t rows, int64_t F, bool has_bias, bool fast);
+hipError_t launch_gelu_tanh(const void* x, const void* bias, void* out,
+                            int64_t rows, int64_t F, int dtype, bool fast,
+                            hipStream_t stream);
+
 // measurement helpers (measure.hip); n16 = number of 16-byte vectors
 bool stream_grid_fits(int64_t n16);
 hipError_t launch_copy(const void* src, void* dst, int64_t n16,

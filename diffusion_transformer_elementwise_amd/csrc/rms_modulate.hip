@@ -23,9 +23,11 @@
 // rows, are read in the apply phase instead.
 //
 // Generic path (any D, element-aligned pointers): the same order in two
-// passes over the row, element by element (the second pass re-reads x).
+// passes over the row with element loads (the second pass re-reads x).
 //
-// No LDS and no barrier: nothing crosses a wave.
+// One wave per workgroup: nothing crosses a wave. The fast path uses no LDS;
+// the generic path stages the row through LDS to read it with contiguous
+// wave-wide loads and still add in the fixed order.
 #include "dtype.hpp"
 #include "launch.hpp"
 
@@ -36,6 +38,8 @@ namespace {
 
 constexpr int kBlock = 64;  // one wave per workgroup
 constexpr int kRowsPerWave = 2;
+constexpr int kStage = 2048;  // generic path: elements staged in LDS per step
+constexpr int kSpan = 8;      // generic path: elements per lane in the apply
 
 // G = packs per lane (at least ceil(D / 512)); lanes whose pack index is
 // past the row end hold zeros, which add +0 to a partial that is never -0,
@@ -118,28 +122,48 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
     }
 }
 
-// Generic: one wave per row; grid x = row l, y = batch b.
+// Generic: one wave per row; grid x = row l, y = batch b. The sum of squares
+// walks the row in stages of kStage elements: the wave reads a stage with
+// wave-contiguous loads (lane t takes elements 64e + t) into LDS, then lane j
+// adds up groups j, j + 64, ... of the stage from LDS, which keeps the fixed
+// order. The apply pass re-reads the row (mostly from L2), lane t taking
+// elements 64e + t of each span of 64 * kSpan.
 template <int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int64_t D)
 {
+    __shared__ float stage[kStage];
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
     const int64_t mrow = (MOD == kModToken) ? row : b * D;
-    const int64_t groups = (D + 7) / 8;
 
     float acc = 0.0f;
-    for (int64_t k = lane; k < groups; k += 64) {
-        for (int e = 0; e < 8; ++e) {
-            const int64_t d = 8 * k + e;
-            if (d < D) {
-                const float v = load_elem<DT>(x, row + d);
-                const float sv = v * v;
-                acc = acc + sv;
+    for (int64_t s0 = 0; s0 < D; s0 += kStage) {
+        float v[kStage / kBlock];
+#pragma unroll
+        for (int e = 0; e < kStage / kBlock; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
+            v[e] = d < D ? load_elem<DT>(x, row + d) : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kStage / kBlock; ++e)
+            stage[e * kBlock + lane] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kStage / 512; ++m) {
+            const int g0 = (lane + kBlock * m) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (s0 + g0 + e < D) {
+                    const float a = stage[g0 + e];
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
             }
         }
+        __syncthreads();
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1)
@@ -149,14 +173,26 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
     const float q = sqrtf(t);
     const float rr = 1.0f / q;
 
-    for (int64_t k = lane; k < groups; k += 64) {
-        for (int e = 0; e < 8; ++e) {
-            const int64_t d = 8 * k + e;
+    for (int64_t s0 = 0; s0 < D; s0 += kBlock * kSpan) {
+        float xv[kSpan], sv[kSpan], hv[kSpan];
+#pragma unroll
+        for (int e = 0; e < kSpan; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
+            const bool in = d < D;
+            xv[e] = in ? load_elem_stream<DT>(x, row + d) : 0.0f;
+            sv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(scale, mrow + d)
+                                           : load_elem<DT>(scale, mrow + d)) : 0.0f;
+            hv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(shift, mrow + d)
+                                           : load_elem<DT>(shift, mrow + d)) : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kSpan; ++e) {
+            const int64_t d = s0 + e * kBlock + lane;
             if (d < D) {
-                const float n = load_elem<DT>(x, row + d) * rr;
-                const float a = 1.0f + load_elem<DT>(scale, mrow + d);
+                const float n = xv[e] * rr;
+                const float a = 1.0f + sv[e];
                 const float m = n * a;
-                store_elem<DT>(out, row + d, m + load_elem<DT>(shift, mrow + d));
+                store_elem_stream<DT>(out, row + d, m + hv[e]);
             }
         }
     }

@@ -197,6 +197,30 @@ def rga_gate_add_rms_modulate_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tens
     return x_out, y
 
 
+def gelu_tanh(x: torch.Tensor, bias: torch.Tensor | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = gelu(x + bias) with the tanh approximation of GELU, over the last
+    dimension F of x (any leading shape); bias is an optional [F] row of the
+    same storage type (bf16, float16 or float32). ``out`` may be x."""
+    dt = _storage(x)
+    _require(x, "x", dtype=dt)
+    if x.dim() < 1:
+        raise ValueError("x needs at least one dimension")
+    F = x.shape[-1]
+    rows = x.numel() // F if F else 0
+    if bias is not None:
+        _require(bias, "bias", x.device, dt)
+        if tuple(bias.shape) != (F,):
+            raise ValueError(f"bias has shape {tuple(bias.shape)}, expected {(F,)}")
+    out = _output(out, "out", x)
+    st = library().rga_gelu_tanh(
+        x.data_ptr(), None if bias is None else bias.data_ptr(), out.data_ptr(),
+        rows, F, _DTYPES[dt], _stream_handle(x.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_gelu_tanh")
+    return out
+
+
 def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
     """Measurement helper: 128-bit device copy of src's bytes into dst."""
     if src.device.type != "cuda" or dst.device != src.device:

@@ -1,14 +1,16 @@
 /*
  * rga.h — C ABI of the MI355X (gfx950) elementwise library for video
- * diffusion transformer blocks: the gated residual add and the
- * weightless-RMSNorm adaLN modulation over contiguous bf16 [B, L, D].
+ * diffusion transformer blocks: the gated residual add, the weightless-RMSNorm
+ * adaLN modulation over contiguous [B, L, D] and the tanh-GELU of the FFN.
  *
  * Conventions shared by every call below:
  *   - Tensor pointers are DEVICE pointers (HIP device memory of the current
- *     device) to row-major contiguous bf16 values (bfloat16: sign, 8 exponent bits,
- *     7 fraction bits, the upper half of a binary32), passed as void*.
- *     Row (b, l) of a [B, L, D] tensor starts at element (b*L + l)*D; the
- *     broadcast row of batch b of a [B, 1, D] tensor starts at b*D.
+ *     device) to row-major contiguous values of the call's storage type,
+ *     passed as void*: bf16 (bfloat16: sign, 8 exponent bits, 7 fraction
+ *     bits, the upper half of a binary32) for the calls without a dtype
+ *     argument, RGA_DTYPE_* for the others (one type for every tensor of a
+ *     call). Row (b, l) of a [B, L, D] tensor starts at element (b*L + l)*D;
+ *     the broadcast row of batch b of a [B, 1, D] tensor starts at b*D.
  *   - Ownership: the caller allocates and owns every buffer. The library
  *     allocates nothing, keeps no pointer after a call returns and holds no
  *     state between calls. Calls are asynchronous: they validate on the host,
@@ -16,17 +18,19 @@
  *     synchronising; buffers must stay alive until that work completes.
  *     Calls may be made from several host threads at once.
  *   - Arithmetic: IEEE binary32 with round-to-nearest-even, no fused
- *     multiply-add, subnormals kept, then one rounding to bf16
+ *     multiply-add, subnormals kept, then one rounding to the storage type
  *     (round-to-nearest-even; a NaN stays a NaN, its payload unspecified).
  *   - Errors: every call returns an RGA_* status and never throws or aborts.
  *     Validation runs before anything is enqueued; on any non-zero status
  *     nothing was enqueued except for RGA_ERR_HIP, which reports the HIP
  *     error of the launch itself. There is no fallback path inside the
  *     library: a caller that wants one decides on a non-zero status.
- *   - Sizes: B, L, D >= 0; B*L*D == 0 is a valid no-op (RGA_OK, nothing
- *     enqueued, pointers may then be NULL). D must be a multiple of 8 and
- *     every pointer 16-byte aligned (one 128-bit access moves 8 elements),
- *     else RGA_ERR_UNSUPPORTED.
+ *   - Sizes: every dimension >= 0; an empty tensor is a valid no-op (RGA_OK,
+ *     nothing enqueued, pointers may then be NULL). The bf16 calls without a
+ *     dtype argument need D % 8 == 0 and 16-byte aligned pointers (one
+ *     128-bit access moves 8 elements), else RGA_ERR_UNSUPPORTED; the calls
+ *     with a dtype argument take any D and pointers aligned to the element
+ *     size, and run element-wise kernels where the 128-bit ones cannot.
  */
 #ifndef RGA_H
 #define RGA_H
@@ -176,6 +180,33 @@ int rga_gate_add_rms_modulate_ex(const void* x, const void* u, const void* g,
                                  int mod_mode, int dtype, hipStream_t stream);
 
 /*
+ * tanh-GELU over the FFN intermediate: out = gelu(x + bias), bias optional.
+ *
+ * Source: prhub summary of sglang PR #34172, "关键源码片段"
+ * (LTX2FeedForward.forward: the output of proj_in goes through a
+ * tanh-approximated GELU, there folded into the GEMM's epilogue) and "实现拆解"
+ * item 1 (the GELU is one of the element-wise chains torch.compile fuses).
+ * The pages name the function without printing it; the library takes the
+ * standard tanh approximation
+ *   gelu(h) = 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))).
+ *
+ *   x, out : [rows, F] (any leading shape flattened into rows), storage dtype
+ *   bias   : [F] or NULL; when given, h = x + bias in binary32 first
+ *   dtype  : RGA_DTYPE_*; pointers aligned to the element size
+ * Arithmetic: binary32 through the identity 0.5 (1 + tanh(a)) = 1 / (1 +
+ * e^-2a) with e^-|2a| (no overflow, no cancellation), then one
+ * round-to-nearest-even to storage. The result is within one ULP of the
+ * correctly rounded value for bf16 and binary16 storage; for binary32
+ * storage the relative error is at most (8 + 6|2a|) 2^-24 (plus 2^-146
+ * absolute for results near the subnormal range). +inf -> +inf, -inf -> -0,
+ * NaN -> NaN.
+ * Aliasing: out == x is allowed (in place); out must not overlap bias.
+ * Fast path: every pointer 16-byte aligned and (with a bias) F % 8 == 0.
+ */
+int rga_gelu_tanh(const void* x, const void* bias, void* out, int64_t rows,
+                  int64_t F, int dtype, hipStream_t stream);
+
+/*
  * Host-only validation of the arguments of the calls above, with the same
  * rules and the same status the call would return before launching.
  * Touches neither the device nor the pointed-to memory.
@@ -207,6 +238,9 @@ int rga_check_gate_add_rms_modulate_ex(const void* x, const void* u,
                                        int64_t B, int64_t L, int64_t D,
                                        int gate_mode, int mod_mode,
                                        int dtype);
+
+int rga_check_gelu_tanh(const void* x, const void* bias, const void* out,
+                        int64_t rows, int64_t F, int dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rga_status_string(int status);

@@ -76,6 +76,10 @@ def _load():
     lib.oracle_f16_from_f32.restype = None
     lib.oracle_f32_from_f16.argtypes = [p, p, i64]
     lib.oracle_f32_from_f16.restype = None
+    lib.oracle_gelu_tanh_f64.argtypes = [ctypes.c_double]
+    lib.oracle_gelu_tanh_f64.restype = ctypes.c_double
+    lib.oracle_gelu_tanh.argtypes = [p, p, p, i64, i64, ctypes.c_int]
+    lib.oracle_gelu_tanh.restype = ctypes.c_int
     lib.oracle_contraction_probe.argtypes = []
     lib.oracle_contraction_probe.restype = ctypes.c_float
     _LIB = lib
@@ -279,6 +283,29 @@ def f32_from_f16(a):
     a = np.ascontiguousarray(a, dtype=np.uint16)
     out = np.empty(a.shape, dtype=np.float32)
     _load().oracle_f32_from_f16(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def gelu_tanh_f64(h: float) -> float:
+    """The oracle's binary64 tanh-GELU of one value (before any rounding)."""
+    return float(_load().oracle_gelu_tanh_f64(float(h)))
+
+
+def gelu_tanh(x, dtype, bias=None, out=None):
+    """gelu(x (+ bias)) over [..., F], rounded once to the storage type."""
+    x = _typed(x, "x", dtype)
+    F = x.shape[-1] if x.ndim else 1
+    rows = x.size // F if F else 0
+    if bias is not None:
+        bias = _typed(bias, "bias", dtype)
+        if bias.shape != (F,):
+            raise ValueError("bias must be [F]")
+    if out is None:
+        out = np.empty_like(x)
+    rc = _load().oracle_gelu_tanh(_ptr(x), None if bias is None else _ptr(bias), _ptr(out),
+                                  rows, F, dtype)
+    if rc:
+        raise ValueError("oracle_gelu_tanh: bad dtype")
     return out
 
 

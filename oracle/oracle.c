@@ -1,6 +1,7 @@
 /*
- * CPU oracle for the gated residual add and the weightless-RMSNorm adaLN
- * modulation of LTX-2-style video diffusion transformer blocks.
+ * CPU oracle for the gated residual add, the weightless-RMSNorm adaLN
+ * modulation and the tanh-GELU of LTX-2-style video diffusion transformer
+ * blocks.
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the bench's CPU
  * baseline leg may load this library. The product path (the HIP library and
@@ -489,6 +490,79 @@ int oracle_gate_add_rms_modulate_ex(const void* x, const void* u,
     oracle_gate_add_ex(x, u, g, x_out, B, L, D, gate_mode, dtype);
     return oracle_rms_modulate_ex(x_out, scale, shift, eps, y, B, L, D,
                                   mod_mode, dtype, P);
+}
+
+/* ---- tanh-GELU on the FFN intermediate ----------------------------------
+ *
+ * Source: prhub summary of sglang PR #34172, "关键源码片段"
+ * (LTX2FeedForward.forward): the output of the FFN's proj_in goes through a
+ * tanh-approximated GELU, which that change folds into the GEMM's epilogue;
+ * "实现拆解" item 1 lists the GELU among the element-wise chains that
+ * torch.compile fuses. The pages name the function without printing it; the
+ * reading taken here is the standard tanh approximation of GELU,
+ *   gelu(h) = 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))).
+ *
+ * It is evaluated in binary64 through the identity
+ *   0.5 (1 + tanh(a)) = 1 / (1 + exp(-2a)),
+ * i.e. gelu(h) = h / (1 + exp(-2a)), which keeps full relative accuracy where
+ * 1 + tanh(a) cancels (h below about -6 in binary64), and then rounded once
+ * to the storage type. Limits: gelu(+inf) = +inf, gelu(-inf) = -0, NaN stays
+ * NaN. With a bias row, h = fl32(x + bias) first (the bias add of a GEMM
+ * epilogue, one binary32 addition).
+ */
+double oracle_gelu_tanh_f64(double h)
+{
+    if (isnan(h))
+        return h;
+    if (isinf(h))
+        return h > 0 ? h : -0.0;
+    const double c = sqrt(2.0 / acos(-1.0));
+    const double a = c * (h + 0.044715 * (h * h * h));
+    return h / (1.0 + exp(-2.0 * a));
+}
+
+/*
+ * binary64 -> binary32 rounded to odd: the neighbour toward zero with its
+ * last significand bit forced to 1 when the value is not exact. Rounding
+ * that binary32 value to nearest-even at 8 or 11 significand bits then gives
+ * the correctly rounded bf16 or binary16 value of d (binary32 keeps well over
+ * two extra bits at every magnitude those formats reach).
+ */
+static float round_to_odd_f32(double d)
+{
+    float f = (float)d;
+    if (isnan(d) || (double)f == d)
+        return f;
+    if (fabs((double)f) > fabs(d))
+        f = nextafterf(f, 0.0f);
+    uint32_t w;
+    memcpy(&w, &f, sizeof w);
+    w |= 1u;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+/* out[r, f] = gelu(x[r, f] (+ bias[f])) over rows x F for any storage type;
+ * bias may be NULL. */
+int oracle_gelu_tanh(const void* x, const void* bias, void* out, int64_t rows,
+                     int64_t F, int dtype)
+{
+    if (bad_dtype(dtype))
+        return 1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t f = 0; f < F; ++f) {
+            const int64_t i = r * F + f;
+            float h = load_elem(x, i, dtype);
+            if (bias)
+                h = h + load_elem(bias, f, dtype);
+            const double y = oracle_gelu_tanh_f64((double)h);
+            if (dtype == ORACLE_F32)
+                ((float*)out)[i] = (float)y;
+            else
+                store_elem(out, i, round_to_odd_f32(y), dtype);
+        }
+    }
+    return 0;
 }
 
 /* ---- build self-check ------------------------------------------------------

@@ -312,3 +312,42 @@ def test_ex_validation_rules(dte):
     assert call(scale=y + 2 * 5 * 4100 * 2 - 2 * 4100 * 2, mod_mode=ROW) == ali
     assert call(scale=y - 2 * 5 * 4100 * 2, mod_mode=TOK) == ok
     assert call(scale=y - 2 * 5 * 4100 * 2 + 2, mod_mode=TOK) == ali
+
+
+def test_gelu_validation_rules(dte):
+    ok, bad, uns, ali = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED, dte.RGA_ERR_ALIAS
+    BF, F16, F32 = dte.DTYPE_BF16, dte.DTYPE_F16, dte.DTYPE_F32
+    ck = dte.check_gelu_tanh
+    GB = 1024 * MB
+    assert ck(A, 0, A + 2 * GB, 32640, 16384, BF) == ok          # 1 GiB tensors
+    assert ck(A, A + 4 * GB, A + 2 * GB, 32640, 16384, BF) == ok
+    assert ck(A, 0, A + GB // 2, 32640, 16384, BF) == ali
+    x, b, o = A, A + 64 * MB, A + 128 * MB
+    assert ck(x, b, o, 3, 13, F16) == ok                 # element path
+    assert ck(x + 2, 0, o, 3, 16, BF) == ok
+    assert ck(x + 2, 0, o, 3, 16, F32) == uns
+    assert ck(x, b + 2, o, 3, 16, F32) == uns
+    assert ck(x, 0, o, -1, 16, BF) == bad
+    assert ck(x, 0, o, 1, -16, BF) == bad
+    assert ck(x, 0, o, 1, 16, 3) == bad
+    assert ck(0, 0, o, 1, 16, BF) == bad
+    assert ck(x, 0, 0, 1, 16, BF) == bad
+    assert ck(0, 0, 0, 0, 16, BF) == ok                  # empty
+    assert ck(0, 0, 0, 5, 0, F32) == ok
+    assert ck(x, 0, x, 7, 16, BF) == ok                  # in place
+    assert ck(x, 0, x + 2, 7, 16, BF) == ali
+    assert ck(x, o + 16, o, 7, 16, BF) == ali            # bias inside out
+    assert ck(x, o - 32, o, 7, 16, BF) == ok             # bias row just before out
+    assert ck(x, o - 30, o, 7, 16, BF) == ali
+    assert ck(x, 0, o, 1 << 40, 1 << 30, F32) == bad     # bytes overflow
+
+
+def test_gelu_isa_keeps_subnormals_and_no_contraction():
+    asm = _device_asm("gelu_tanh.hip")
+    bodies = _kernel_bodies(asm)
+    assert len(bodies) == 12, sorted(bodies)
+    assert asm.count(".amdhsa_float_denorm_mode_32 3") == len(bodies)
+    for name, body in bodies.items():
+        assert not re.search(r"\bv_(pk_)?(fma|fmac|fmamk|fmaak|mad|mac)(_mix\w*)?_f(16|32|64)", body), name
+        assert not re.search(r"\bv_pk_(add|mul|fma)_f32", body), name
+        assert "v_exp_f32" in body and "v_rcp_f32" in body, name
