@@ -23,9 +23,10 @@ Reported (one JSON line on stdout):
   variants     with --variants 1: the _ex calls at DiT shapes (binary16 and
                binary32 storage, per-token modulation, the element-wise paths
                for ragged D, element offsets and rows past the register
-               limit), the ideogram4 [1,4096,4608] bcast shape and the
-               tanh-GELU on the FFN intermediate [1,32640,16384]; cold and
-               back-to-back per-call time
+               limit), the ideogram4 [1,4096,4608] bcast shape, the
+               LayerNorm modulation at [2,32640,4096] and the tanh-GELU on
+               the FFN intermediate [1,32640,16384]; cold and back-to-back
+               per-call time
   small_configs with --small-configs 1: the other workload configurations
                (c1 full [1,126,2048] + rms_modulate, c2 bcast [1,L,3072] for
                L = 512, 4096, 4608): cold per-call time, and back-to-back
@@ -501,6 +502,22 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
          offset=1)
     rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
     rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
+    # LayerNorm modulation at the modulation shape
+    def ln(name, B, L, D, dt, mod):
+        mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
+        x = draw((B, L, D), dt, 2.0)
+        sc, sh = draw(mshape, dt, 0.1), draw(mshape, dt, 0.1)
+        o = torch.empty_like(x)
+        n = B * L * D
+        nbytes = (2 * n + 2 * (n if mod == dte.MOD_TOKEN else B * D)) * x.element_size()
+        log(f"variant {name}")
+        out[name] = cold_and_warm(
+            lambda: dte.rga_ln_modulate(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
+            "ln_modulate_kernel")
+
+    ln("bf16_ln_modulate_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW)
+    ln("f16_ln_modulate_token_[2,32640,4096]", 2, 32640, 4096, "f16", dte.MOD_TOKEN)
+
     # tanh-GELU on the FFN intermediate (video tokens x 4 hidden)
     def gelu(name, rows, F, dt, with_bias=False):
         x = draw((1, rows, F), dt, 2.0)

@@ -22,6 +22,11 @@ tensors starting at any element offset, and per-token scale/shift [B, L, D]:
     rga_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps=1e-6, x_out=None,
                                  y=None, gate_mode=None, mod_mode=None)
 
+Modulation after a weightless LayerNorm, with the same options as the _ex
+forms:
+
+    rga_ln_modulate(x, scale, shift, eps=1e-6, out=None, mod_mode=None)
+
 The FFN's tanh-GELU, any storage type, over the last dimension F:
 
     gelu_tanh(x, bias=None, out=None)   out = gelu(x + bias)
@@ -49,6 +54,7 @@ from ._lib import (  # noqa: F401
     check_residual_gate_add_ex,
     check_rms_modulate,
     check_gelu_tanh,
+    check_ln_modulate,
     check_rms_modulate_ex,
     library,
     library_path,
@@ -61,6 +67,7 @@ from .ops import (  # noqa: F401
     read_,
     rga_gate_add_rms_modulate,
     rga_gate_add_rms_modulate_ex,
+    rga_ln_modulate,
     rga_residual_gate_add,
     rga_residual_gate_add_ex,
     rga_rms_modulate_ex,
@@ -74,6 +81,7 @@ __all__ = [
     "rga_residual_gate_add_ex",
     "rga_rms_modulate_ex",
     "rga_gate_add_rms_modulate_ex",
+    "rga_ln_modulate",
     "gelu_tanh",
     "GATE_FULL",
     "GATE_BCAST",

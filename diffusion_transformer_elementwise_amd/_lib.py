@@ -86,6 +86,10 @@ def _load():
     lib.rga_check_gate_add_rms_modulate_ex.argtypes = [p, p, p, p, p, f32, p, p, i64, i64,
                                                        i64, i32, i32, i32]
     lib.rga_check_gate_add_rms_modulate_ex.restype = i32
+    lib.rga_ln_modulate.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, i32, p]
+    lib.rga_ln_modulate.restype = i32
+    lib.rga_check_ln_modulate.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, i32]
+    lib.rga_check_ln_modulate.restype = i32
     lib.rga_gelu_tanh.argtypes = [p, p, p, i64, i64, i32, p]
     lib.rga_gelu_tanh.restype = i32
     lib.rga_check_gelu_tanh.argtypes = [p, p, p, i64, i64, i32]
@@ -145,3 +149,7 @@ def check_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps, x_out, y, B, L, D
 
 def check_gelu_tanh(x, bias, out, rows, F, dtype) -> int:
     return _LIB.rga_check_gelu_tanh(x, bias, out, rows, F, dtype)
+
+
+def check_ln_modulate(x, scale, shift, eps, out, B, L, D, mod_mode, dtype) -> int:
+    return _LIB.rga_check_ln_modulate(x, scale, shift, eps, out, B, L, D, mod_mode, dtype)

@@ -379,6 +379,26 @@ int rga_rms_modulate_ex(const void* x, const void* scale, const void* shift,
                stream);
 }
 
+int rga_check_ln_modulate(const void* x, const void* scale, const void* shift,
+                          float eps, const void* out, int64_t B, int64_t L,
+                          int64_t D, int mod_mode, int dtype)
+{
+    bool fast = false;
+    return check_rms(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, false, &fast);
+}
+
+int rga_ln_modulate(const void* x, const void* scale, const void* shift,
+                    float eps, void* out, int64_t B, int64_t L, int64_t D,
+                    int mod_mode, int dtype, hipStream_t stream)
+{
+    bool fast = false;
+    const int st = check_rms(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, false, &fast);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return launched(rga::launch_ln_modulate(x, scale, shift, eps, out, B, L, D, mod_mode,
+                                            dtype, fast, stream));
+}
+
 static int fused(const void* x, const void* u, const void* g,
                  const void* scale, const void* shift, float eps, void* x_out,
                  void* y, int64_t B, int64_t L, int64_t D, int gate_mode,

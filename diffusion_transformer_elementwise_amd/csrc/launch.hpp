@@ -26,6 +26,13 @@ hipError_t launch_rms_modulate(const void* x, const void* scale,
                                int64_t B, int64_t L, int64_t D, int mod_mode,
                                int dtype, bool fast, hipStream_t stream);
 
+// modulation after a weightless LayerNorm (rms_modulate.hip); same grid
+// limits as rms_modulate_grid_fits
+hipError_t launch_ln_modulate(const void* x, const void* scale,
+                              const void* shift, float eps, void* out,
+                              int64_t B, int64_t L, int64_t D, int mod_mode,
+                              int dtype, bool fast, hipStream_t stream);
+
 // residual update then modulation, one pass (gate_add_rms_modulate.hip)
 bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D);
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,

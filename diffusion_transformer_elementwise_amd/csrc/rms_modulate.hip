@@ -1,18 +1,24 @@
-// adaLN modulation with a weightless RMSNorm,
-//   out = rms_norm(x, eps) * (1 + scale) + shift,
+// adaLN modulation of a normalized row,
+//   out = norm(x, eps) * (1 + scale) + shift,
 // over contiguous x [B, L, D] with scale and shift rows [B, 1, D] or per
-// token [B, L, D] (prhub summary of sglang PR #34172, "关键源码片段": the
-// expression and RMSNormNoWeight; "风险与影响": the fused kernel's one-ULP
-// allowance).
+// token [B, L, D], for two weightless norms:
+//   RMSNorm: norm(x) = x / sqrt(mean(x^2) + eps) (prhub summary of sglang PR
+//     #34172, "关键源码片段": the expression and RMSNormNoWeight; "风险与影响":
+//     the fused kernel's one-ULP allowance);
+//   LayerNorm: norm(x) = (x - mean) / sqrt(var + eps), biased variance (the
+//     LN+modulate family that summary lists beside it, "实现拆解" items 2 and 4;
+//     the pages do not describe it, the DiT adaLN form is taken).
 //
 // The fixed summation order: the row is cut into groups of 8 consecutive
 // elements (the last group may be shorter); one wave64 owns the row; lane j
-// accumulates the squares of groups j, j+64, ... in increasing group and
-// element order into one binary32 partial; the 64 partials are combined with
-// xor-distance lane exchanges 1, 2, ..., 32 (every lane ends with the same
-// sum, because a + b == b + a bit for bit). Then r = 1 / sqrt(ss / D + eps)
-// with IEEE division and square root, and each element becomes
-// ((x * r) * (1 + scale)) + shift, rounded once to the storage type.
+// accumulates groups j, j+64, ... in increasing group and element order into
+// one binary32 partial; the 64 partials are combined with xor-distance lane
+// exchanges 1, 2, ..., 32 (every lane ends with the same sum, because
+// a + b == b + a bit for bit). RMSNorm sums the squares; LayerNorm first sums
+// the values (mean = sum / D), then the squares of x - mean. Then
+// r = 1 / sqrt(ss / D + eps) with IEEE division and square root, and each
+// element becomes (((x or x - mean) * r) * (1 + scale)) + shift, rounded once
+// to the storage type.
 //
 // Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers): the
 // row stays in registers (G packs per lane), read once from HBM and written
@@ -20,10 +26,11 @@
 // per wave. With row modulation the packed 2-byte scale and shift rows stay
 // in registers across the wave's rows (the shape that measured fastest on
 // MI355X inside a chain of streaming kernels); per-token rows, and binary32
-// rows, are read in the apply phase instead.
+// rows, are read in the apply phase instead. The LayerNorm's second sum runs
+// over the registers, so it costs arithmetic, not memory traffic.
 //
-// Generic path (any D, element-aligned pointers): the same order in two
-// passes over the row with element loads (the second pass re-reads x).
+// Generic path (any D, element-aligned pointers): the same order, each sum
+// one pass over the row with element loads, then the apply pass.
 //
 // One wave per workgroup: nothing crosses a wave. The fast path uses no LDS;
 // the generic path stages the row through LDS to read it with contiguous
@@ -41,11 +48,33 @@ constexpr int kRowsPerWave = 2;
 constexpr int kStage = 2048;  // generic path: elements staged in LDS per step
 constexpr int kSpan = 8;      // generic path: elements per lane in the apply
 
-// G = packs per lane (at least ceil(D / 512)); lanes whose pack index is
-// past the row end hold zeros, which add +0 to a partial that is never -0,
-// so they change nothing. Grid: x = tile of kRowsPerWave rows, y = batch.
-template <int G, int DT, int MOD>
-__global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
+enum : int { kNormRms = 0, kNormLn = 1 };
+
+// The 64 lane partials combined by xor-distance exchanges 1, 2, ..., 32;
+// every lane ends with the same sum (a + b == b + a bit for bit).
+__device__ __forceinline__ float wave_sum(float acc)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        acc = acc + __shfl_xor(acc, m);
+    return acc;
+}
+
+__device__ __forceinline__ float inv_std(float ss, float d_float, float eps)
+{
+    const float ms = ss / d_float;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    return 1.0f / q;
+}
+
+// One wave modulates rows r0 .. r1-1 of batch b. G = packs per lane (at
+// least ceil(D / 512)); lanes whose pack index is past the row end hold
+// zeros, which add +0 to a partial that is never -0 (the RMS sum of squares
+// and the LayerNorm sum of x) and are left out of the LayerNorm sum of
+// squared deviations.
+template <int G, int DT, int MOD, int NORM>
+__device__ __forceinline__ void modulate_rows(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
@@ -74,24 +103,33 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
             xv[i] = (col < vpr) ? Pack<DT>::load_stream(x, row + col) : Pack<DT>::zero();
         }
 
+        float mu = 0.0f;
+        if constexpr (NORM == kNormLn) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc = acc + xv[i].get(e);
+            }
+            mu = wave_sum(acc) / d_float;
+        }
+
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
+            if (NORM == kNormLn && lane + 64 * i >= vpr)
+                continue;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float a = xv[i].get(e);
+                float a = xv[i].get(e);
+                if constexpr (NORM == kNormLn)
+                    a = a - mu;
                 const float sa = a * a;
                 acc = acc + sa;
             }
         }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1)
-            acc = acc + __shfl_xor(acc, m);
-
-        const float ms = acc / d_float;
-        const float t = ms + eps;
-        const float q = sqrtf(t);
-        const float rr = 1.0f / q;
+        const float rr = inv_std(wave_sum(acc), d_float, eps);
 
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -112,7 +150,10 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float n = xv[i].get(e) * rr;
+                float v = xv[i].get(e);
+                if constexpr (NORM == kNormLn)
+                    v = v - mu;
+                const float n = v * rr;
                 const float a = 1.0f + s_.get(e);
                 const float m = n * a;
                 o[e] = m + h_.get(e);
@@ -122,23 +163,33 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
     }
 }
 
-// Generic: one wave per row; grid x = row l, y = batch b. The sum of squares
-// walks the row in stages of kStage elements: the wave reads a stage with
-// wave-contiguous loads (lane t takes elements 64e + t) into LDS, then lane j
-// adds up groups j, j + 64, ... of the stage from LDS, which keeps the fixed
-// order. The apply pass re-reads the row (mostly from L2), lane t taking
-// elements 64e + t of each span of 64 * kSpan.
-template <int DT, int MOD>
-__global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
+// Grid: x = tile of kRowsPerWave rows, y = batch.
+template <int G, int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
-    float d_float, void* out, int64_t L, int64_t D)
+    float d_float, void* out, int64_t L, int vpr)
 {
-    __shared__ float stage[kStage];
-    const int lane = threadIdx.x;
-    const int64_t b = blockIdx.y;
-    const int64_t row = (b * L + blockIdx.x) * D;
-    const int64_t mrow = (MOD == kModToken) ? row : b * D;
+    modulate_rows<G, DT, MOD, kNormRms>(x, scale, shift, eps, d_float, out, L, vpr);
+}
 
+template <int G, int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void ln_modulate_kernel(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
+{
+    modulate_rows<G, DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, vpr);
+}
+
+// Generic path, one wave per row. A sum in the fixed order walks the row in
+// stages of kStage elements: the wave reads a stage with wave-contiguous
+// loads (lane t takes elements 64e + t) into LDS, then lane j adds up groups
+// j, j + 64, ... of the stage from LDS. WHAT: 0 the values, 1 their squares,
+// 2 the squares of value - mu.
+template <int DT, int WHAT>
+__device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t D,
+                                            float mu, float* stage)
+{
+    const int lane = threadIdx.x;
     float acc = 0.0f;
     for (int64_t s0 = 0; s0 < D; s0 += kStage) {
         float v[kStage / kBlock];
@@ -157,21 +208,40 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if (s0 + g0 + e < D) {
-                    const float a = stage[g0 + e];
-                    const float sa = a * a;
-                    acc = acc + sa;
+                    float a = stage[g0 + e];
+                    if constexpr (WHAT == 0) {
+                        acc = acc + a;
+                    } else {
+                        if constexpr (WHAT == 2)
+                            a = a - mu;
+                        const float sa = a * a;
+                        acc = acc + sa;
+                    }
                 }
             }
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-        acc = acc + __shfl_xor(acc, m);
-    const float ms = acc / d_float;
-    const float t = ms + eps;
-    const float q = sqrtf(t);
-    const float rr = 1.0f / q;
+    return wave_sum(acc);
+}
+
+// The apply pass re-reads the row (mostly from L2), lane t taking elements
+// 64e + t of each span of 64 * kSpan.
+template <int DT, int MOD, int NORM>
+__device__ __forceinline__ void modulate_row_generic(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int64_t D, float* stage)
+{
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t mrow = (MOD == kModToken) ? row : b * D;
+
+    float mu = 0.0f;
+    if constexpr (NORM == kNormLn)
+        mu = staged_sum<DT, 0>(x, row, D, 0.0f, stage) / d_float;
+    const float ss = staged_sum<DT, NORM == kNormLn ? 2 : 1>(x, row, D, mu, stage);
+    const float rr = inv_std(ss, d_float, eps);
 
     for (int64_t s0 = 0; s0 < D; s0 += kBlock * kSpan) {
         float xv[kSpan], sv[kSpan], hv[kSpan];
@@ -189,13 +259,35 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
         for (int e = 0; e < kSpan; ++e) {
             const int64_t d = s0 + e * kBlock + lane;
             if (d < D) {
-                const float n = xv[e] * rr;
+                float v = xv[e];
+                if constexpr (NORM == kNormLn)
+                    v = v - mu;
+                const float n = v * rr;
                 const float a = 1.0f + sv[e];
                 const float m = n * a;
                 store_elem_stream<DT>(out, row + d, m + hv[e]);
             }
         }
     }
+}
+
+// Grid: x = row l, y = batch b.
+template <int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int64_t D)
+{
+    __shared__ float stage[kStage];
+    modulate_row_generic<DT, MOD, kNormRms>(x, scale, shift, eps, d_float, out, L, D, stage);
+}
+
+template <int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int64_t D)
+{
+    __shared__ float stage[kStage];
+    modulate_row_generic<DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, D, stage);
 }
 
 typedef void (*rms_kernel_t)(const void*, const void*, const void*, float,
@@ -205,13 +297,19 @@ typedef void (*rms_kernel_t)(const void*, const void*, const void*, float,
 constexpr int kLadder[] = {1, 2, 4, 6, 8, 12, 16};
 static_assert(RGA_RMS_MAX_D / 512 == 16, "ladder tops out at RGA_RMS_MAX_D");
 
-template <int DT, int MOD>
+template <int NORM, int G, int DT, int MOD>
+constexpr rms_kernel_t fast_kernel()
+{
+    return NORM == kNormLn ? &ln_modulate_kernel<G, DT, MOD> : &rms_modulate_kernel<G, DT, MOD>;
+}
+
+template <int NORM, int DT, int MOD>
 rms_kernel_t pick(int groups)
 {
-    rms_kernel_t t[] = {&rms_modulate_kernel<1, DT, MOD>, &rms_modulate_kernel<2, DT, MOD>,
-                        &rms_modulate_kernel<4, DT, MOD>, &rms_modulate_kernel<6, DT, MOD>,
-                        &rms_modulate_kernel<8, DT, MOD>, &rms_modulate_kernel<12, DT, MOD>,
-                        &rms_modulate_kernel<16, DT, MOD>};
+    rms_kernel_t t[] = {fast_kernel<NORM, 1, DT, MOD>(), fast_kernel<NORM, 2, DT, MOD>(),
+                        fast_kernel<NORM, 4, DT, MOD>(), fast_kernel<NORM, 6, DT, MOD>(),
+                        fast_kernel<NORM, 8, DT, MOD>(), fast_kernel<NORM, 12, DT, MOD>(),
+                        fast_kernel<NORM, 16, DT, MOD>()};
     for (int i = 0; i < 7; ++i)
         if (groups <= kLadder[i])
             return t[i];
@@ -220,7 +318,7 @@ rms_kernel_t pick(int groups)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <int DT, int MOD>
+template <int NORM, int DT, int MOD>
 hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                         float eps, void* out, int64_t B, int64_t L, int64_t D,
                         bool fast, hipStream_t stream)
@@ -228,12 +326,13 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
     float d_float = (float)D;
     if (!fast) {
         void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &D};
-        return hipLaunchKernel(
-            reinterpret_cast<const void*>(&rms_modulate_generic_kernel<DT, MOD>),
-            dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
+        const void* k = NORM == kNormLn
+                            ? reinterpret_cast<const void*>(&ln_modulate_generic_kernel<DT, MOD>)
+                            : reinterpret_cast<const void*>(&rms_modulate_generic_kernel<DT, MOD>);
+        return hipLaunchKernel(k, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
     }
     int vpr = (int)(D / 8);
-    rms_kernel_t k = pick<DT, MOD>((int)ceil_div(vpr, 64));
+    rms_kernel_t k = pick<NORM, DT, MOD>((int)ceil_div(vpr, 64));
     if (k == nullptr)
         return hipErrorInvalidValue;
     void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &vpr};
@@ -242,14 +341,29 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                            dim3(kBlock), args, 0, stream);
 }
 
-template <int DT>
+template <int NORM, int DT>
 hipError_t launch_mod(const void* x, const void* scale, const void* shift,
                       float eps, void* out, int64_t B, int64_t L, int64_t D,
                       int mod_mode, bool fast, hipStream_t stream)
 {
     return mod_mode == RGA_MOD_TOKEN
-               ? launch_typed<DT, kModToken>(x, scale, shift, eps, out, B, L, D, fast, stream)
-               : launch_typed<DT, kModRow>(x, scale, shift, eps, out, B, L, D, fast, stream);
+               ? launch_typed<NORM, DT, kModToken>(x, scale, shift, eps, out, B, L, D, fast, stream)
+               : launch_typed<NORM, DT, kModRow>(x, scale, shift, eps, out, B, L, D, fast, stream);
+}
+
+template <int NORM>
+hipError_t launch_norm(const void* x, const void* scale, const void* shift, float eps,
+                       void* out, int64_t B, int64_t L, int64_t D, int mod_mode,
+                       int dtype, bool fast, hipStream_t stream)
+{
+    switch (dtype) {
+    case RGA_DTYPE_F16:
+        return launch_mod<NORM, kF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+    case RGA_DTYPE_F32:
+        return launch_mod<NORM, kF32>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+    default:
+        return launch_mod<NORM, kBF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+    }
 }
 
 }  // namespace
@@ -266,14 +380,17 @@ hipError_t launch_rms_modulate(const void* x, const void* scale,
                                int64_t B, int64_t L, int64_t D, int mod_mode,
                                int dtype, bool fast, hipStream_t stream)
 {
-    switch (dtype) {
-    case RGA_DTYPE_F16:
-        return launch_mod<kF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
-    case RGA_DTYPE_F32:
-        return launch_mod<kF32>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
-    default:
-        return launch_mod<kBF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
-    }
+    return launch_norm<kNormRms>(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, fast,
+                                 stream);
+}
+
+hipError_t launch_ln_modulate(const void* x, const void* scale,
+                              const void* shift, float eps, void* out,
+                              int64_t B, int64_t L, int64_t D, int mod_mode,
+                              int dtype, bool fast, hipStream_t stream)
+{
+    return launch_norm<kNormLn>(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, fast,
+                                stream);
 }
 
 }  // namespace rga

@@ -151,6 +151,24 @@ def rga_rms_modulate_ex(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tenso
     return out
 
 
+def rga_ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                    eps: float = 1e-6, out: torch.Tensor | None = None,
+                    mod_mode: int | None = None) -> torch.Tensor:
+    """out = layer_norm(x, eps) * (1 + scale) + shift with a weightless
+    LayerNorm (biased variance); bf16, float16 or float32, any D, scale/shift
+    per batch row [B, 1, D] or per token [B, L, D]. ``out`` may be x."""
+    dt = _storage(x)
+    B, L, D = _x_shape(x, dt)
+    mod_mode = _modulation(x, scale, shift, mod_mode, dt)
+    out = _output(out, "out", x)
+    st = library().rga_ln_modulate(
+        x.data_ptr(), scale.data_ptr(), shift.data_ptr(), float(eps),
+        out.data_ptr(), B, L, D, mod_mode, _DTYPES[dt], _stream_handle(x.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_ln_modulate")
+    return out
+
+
 def rga_gate_add_rms_modulate(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
                               scale: torch.Tensor, shift: torch.Tensor,
                               eps: float = 1e-6,

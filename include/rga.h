@@ -1,7 +1,8 @@
 /*
  * rga.h — C ABI of the MI355X (gfx950) elementwise library for video
- * diffusion transformer blocks: the gated residual add, the weightless-RMSNorm
- * adaLN modulation over contiguous [B, L, D] and the tanh-GELU of the FFN.
+ * diffusion transformer blocks: the gated residual add, the adaLN modulation
+ * after a weightless RMSNorm or LayerNorm over contiguous [B, L, D], and the
+ * tanh-GELU of the FFN.
  *
  * Conventions shared by every call below:
  *   - Tensor pointers are DEVICE pointers (HIP device memory of the current
@@ -180,6 +181,28 @@ int rga_gate_add_rms_modulate_ex(const void* x, const void* u, const void* g,
                                  int mod_mode, int dtype, hipStream_t stream);
 
 /*
+ * adaLN modulation with a weightless LayerNorm:
+ *   out = ((x - mean) / sqrt(var + eps)) * (1 + scale) + shift.
+ *
+ * Source: prhub summary of sglang PR #34172, "实现拆解" items 2 and 4: an
+ * LN+modulate fusion family (fused_ln_modulate) sits beside the
+ * RMSNorm+modulate one; the pages do not describe it, and the library takes
+ * the adaLN form of a DiT block with a LayerNorm without affine weight:
+ * mean = sum(x) / D, var = sum((x - mean)^2) / D (biased; the deviations from
+ * the binary32 mean).
+ *
+ * Same arguments, layouts, storage types, aliasing rules, status codes and
+ * kernels' launch shapes as rga_rms_modulate_ex. Both sums use the fixed
+ * order of the RMS sum of squares (groups of 8, partial k mod 64, pairwise by
+ * index distance 1..32); then r = 1 / sqrt(var + eps) and each element
+ * becomes (((x - mean) * r) * (1 + scale)) + shift, every step binary32, one
+ * rounding to storage. Results are reproducible bit for bit.
+ */
+int rga_ln_modulate(const void* x, const void* scale, const void* shift,
+                    float eps, void* out, int64_t B, int64_t L, int64_t D,
+                    int mod_mode, int dtype, hipStream_t stream);
+
+/*
  * tanh-GELU over the FFN intermediate: out = gelu(x + bias), bias optional.
  *
  * Source: prhub summary of sglang PR #34172, "关键源码片段"
@@ -239,6 +262,9 @@ int rga_check_gate_add_rms_modulate_ex(const void* x, const void* u,
                                        int gate_mode, int mod_mode,
                                        int dtype);
 
+int rga_check_ln_modulate(const void* x, const void* scale, const void* shift,
+                          float eps, const void* out, int64_t B, int64_t L,
+                          int64_t D, int mod_mode, int dtype);
 int rga_check_gelu_tanh(const void* x, const void* bias, const void* out,
                         int64_t rows, int64_t F, int dtype);
 

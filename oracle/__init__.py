@@ -76,6 +76,12 @@ def _load():
     lib.oracle_f16_from_f32.restype = None
     lib.oracle_f32_from_f16.argtypes = [p, p, i64]
     lib.oracle_f32_from_f16.restype = None
+    lib.oracle_ln_factors.argtypes = [p, p, p, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                      ctypes.c_int]
+    lib.oracle_ln_factors.restype = ctypes.c_int
+    lib.oracle_ln_modulate_ex.argtypes = [
+        p, p, p, ctypes.c_float, p, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_ln_modulate_ex.restype = ctypes.c_int
     lib.oracle_gelu_tanh_f64.argtypes = [ctypes.c_double]
     lib.oracle_gelu_tanh_f64.restype = ctypes.c_double
     lib.oracle_gelu_tanh.argtypes = [p, p, p, i64, i64, ctypes.c_int]
@@ -284,6 +290,37 @@ def f32_from_f16(a):
     out = np.empty(a.shape, dtype=np.float32)
     _load().oracle_f32_from_f16(_ptr(a), _ptr(out), a.size)
     return out
+
+
+def ln_modulate(x, scale, shift, eps, mod_mode, dtype, out=None, partials=64):
+    """((x - mean) / sqrt(var + eps)) * (1 + scale) + shift per row (weightless
+    LayerNorm, biased variance, both sums in the pinned order)."""
+    x = _typed(x, "x", dtype)
+    scale, shift = _typed(scale, "scale", dtype), _typed(shift, "shift", dtype)
+    B, L, D = x.shape
+    want = (B, 1, D) if mod_mode == MOD_ROW else (B, L, D)
+    if scale.shape != want or shift.shape != want:
+        raise ValueError("scale/shift shape does not fit the modulation layout")
+    if out is None:
+        out = np.empty_like(x)
+    rc = _load().oracle_ln_modulate_ex(_ptr(x), _ptr(scale), _ptr(shift), float(eps),
+                                       _ptr(out), B, L, D, mod_mode, dtype, partials)
+    if rc:
+        raise ValueError("oracle_ln_modulate_ex: bad dtype or partials")
+    return out
+
+
+def ln_factors(x, eps, dtype, partials=64):
+    """(mean, 1/sqrt(var + eps)) per row as float32 arrays [B, L]."""
+    x = _typed(x, "x", dtype)
+    B, L, D = x.shape
+    mean = np.empty((B, L), dtype=np.float32)
+    rstd = np.empty((B, L), dtype=np.float32)
+    rc = _load().oracle_ln_factors(_ptr(x), _ptr(mean), _ptr(rstd), B, L, D, float(eps),
+                                   dtype, partials)
+    if rc:
+        raise ValueError("oracle_ln_factors: bad dtype or partials")
+    return mean, rstd
 
 
 def gelu_tanh_f64(h: float) -> float:

@@ -492,6 +492,99 @@ int oracle_gate_add_rms_modulate_ex(const void* x, const void* u,
                                   mod_mode, dtype, P);
 }
 
+/* ---- weightless LayerNorm modulation --------------------------------------
+ *
+ * Source: prhub summary of sglang PR #34172, "实现拆解" items 2 and 4: an
+ * LN+modulate fusion family (fused_ln_modulate) sits beside the
+ * RMSNorm+modulate one among the quality-gated fusions; the pages do not
+ * describe it. Reading taken here: the adaLN form of a DiT block with a
+ * LayerNorm that has no affine weight,
+ *   y = ((x - mean) / sqrt(var + eps)) * (1 + scale) + shift,
+ *   mean = sum(x) / D,  var = sum((x - mean)^2) / D  (biased, two passes),
+ * the deviations taken from the binary32 mean. Both sums follow the RMS
+ * order: groups of 8 consecutive elements (the last may be shorter), group k
+ * into partial k mod P in increasing k and element order, then the
+ * xor-distance tree. Every step binary32, one rounding to storage at the end.
+ */
+static float pinned_sum(const void* x, int64_t row, int64_t D, int dtype,
+                        int P, int squares_of_deviation, float mean)
+{
+    float part[256];
+    float next[256];
+    for (int j = 0; j < P; ++j)
+        part[j] = 0.0f;
+    const int64_t groups = (D + 7) / 8;
+    for (int64_t k = 0; k < groups; ++k) {
+        const int j = (int)(k % P);
+        for (int64_t d = 8 * k; d < 8 * k + 8 && d < D; ++d) {
+            const float v = load_elem(x, row + d, dtype);
+            if (squares_of_deviation) {
+                const float dev = v - mean;
+                const float sq = dev * dev;
+                part[j] = part[j] + sq;
+            } else {
+                part[j] = part[j] + v;
+            }
+        }
+    }
+    for (int m = 1; m < P; m <<= 1) {
+        for (int j = 0; j < P; ++j)
+            next[j] = part[j] + part[j ^ m];
+        for (int j = 0; j < P; ++j)
+            part[j] = next[j];
+    }
+    return part[0];
+}
+
+/* mean and 1 / sqrt(var + eps) of one row, in the pinned order. */
+static void ln_row_factors(const void* x, int64_t row, int64_t D, float eps,
+                           int dtype, int P, float* mean, float* rstd)
+{
+    const float s1 = pinned_sum(x, row, D, dtype, P, 0, 0.0f);
+    const float mu = s1 / (float)D;
+    const float s2 = pinned_sum(x, row, D, dtype, P, 1, mu);
+    const float var = s2 / (float)D;
+    const float t = var + eps;
+    const float q = sqrtf(t);
+    *mean = mu;
+    *rstd = 1.0f / q;
+}
+
+int oracle_ln_factors(const void* x, float* mean, float* rstd, int64_t B,
+                      int64_t L, int64_t D, float eps, int dtype, int P)
+{
+    if (bad_partials(P) || bad_dtype(dtype))
+        return 1;
+    for (int64_t r = 0; r < B * L; ++r)
+        ln_row_factors(x, r * D, D, eps, dtype, P, &mean[r], &rstd[r]);
+    return 0;
+}
+
+int oracle_ln_modulate_ex(const void* x, const void* scale, const void* shift,
+                          float eps, void* out, int64_t B, int64_t L,
+                          int64_t D, int mod_mode, int dtype, int P)
+{
+    if (bad_partials(P) || bad_dtype(dtype))
+        return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t l = 0; l < L; ++l) {
+            const int64_t row = (b * L + l) * D;
+            const int64_t mrow = (mod_mode == ORACLE_MOD_TOKEN) ? row : b * D;
+            float mu, r;
+            ln_row_factors(x, row, D, eps, dtype, P, &mu, &r);
+            for (int64_t d = 0; d < D; ++d) {
+                const float dev = load_elem(x, row + d, dtype) - mu;
+                const float n = dev * r;
+                const float a = 1.0f + load_elem(scale, mrow + d, dtype);
+                const float m = n * a;
+                const float y = m + load_elem(shift, mrow + d, dtype);
+                store_elem(out, row + d, y, dtype);
+            }
+        }
+    }
+    return 0;
+}
+
 /* ---- tanh-GELU on the FFN intermediate ----------------------------------
  *
  * Source: prhub summary of sglang PR #34172, "关键源码片段"

@@ -351,3 +351,21 @@ def test_gelu_isa_keeps_subnormals_and_no_contraction():
         assert not re.search(r"\bv_(pk_)?(fma|fmac|fmamk|fmaak|mad|mac)(_mix\w*)?_f(16|32|64)", body), name
         assert not re.search(r"\bv_pk_(add|mul|fma)_f32", body), name
         assert "v_exp_f32" in body and "v_rcp_f32" in body, name
+
+
+def test_ln_modulate_validation_follows_the_ex_rules(dte):
+    ck, ref = dte.check_ln_modulate, dte.check_rms_modulate_ex
+    x, s, t, o = A, A + 64 * MB, A + 96 * MB, A + 128 * MB
+    cases = [
+        (x, s, t, 1e-6, o, 2, 3, 4096, 0, 0), (x, s, t, 1e-6, o, 1, 3, 4100, 1, 1),
+        (x, s, t, 1e-6, o, 1, 3, 20000, 0, 2), (x, s, t, -1.0, o, 1, 3, 8, 0, 0),
+        (x, s, t, 1e-6, o, 1, 3, 8, 2, 0), (x, s, t, 1e-6, o, 1, 3, 8, 0, 3),
+        (x + 2, s, t, 1e-6, o, 1, 3, 8, 0, 2), (x, s, t, 1e-6, x, 1, 3, 8, 1, 0),
+        (x, o - 16, t, 1e-6, o, 1, 3, 8, 0, 0), (x, o - 16, t, 1e-6, o, 1, 3, 8, 1, 0),
+        (0, 0, 0, 1e-6, 0, 0, 3, 8, 0, 0), (0, s, t, 1e-6, o, 1, 3, 8, 0, 0),
+    ]
+    want = [dte.RGA_OK, dte.RGA_OK, dte.RGA_OK, dte.RGA_ERR_INVALID_ARG,
+            dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED,
+            dte.RGA_OK, dte.RGA_OK, dte.RGA_ERR_ALIAS, dte.RGA_OK, dte.RGA_ERR_INVALID_ARG]
+    for c, w in zip(cases, want):
+        assert ck(*c) == w == ref(*c), c
