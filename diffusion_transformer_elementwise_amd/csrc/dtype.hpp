@@ -208,6 +208,98 @@ struct Interleaved<kF32> {
     }
 };
 
+// Grouped packs, for kernels where lane t must hold pack c0 + t of a chunk
+// of h <= 64 packs (a summation order fixes which elements a lane adds).
+// Packs past the chunk (t >= h, or h <= 0) load as zeros and are not
+// stored. For the 2-byte types a pack is one 16-byte word per lane. For
+// binary32 a pack is two words; lane t moves words wa(t) and 64 + wa(t) of
+// the chunk ("raw" order), wa(t) = 2t for t < 32 and 2(t - 32) + 1
+// otherwise, so that each of the two access instructions covers one
+// contiguous run, and one v_permlane32_swap per dword (lanes 32..63 of the
+// first register trade with lanes 0..31 of the second) turns raw order into
+// words 2t and 2t + 1 (group order). The swap is its own inverse. Element-wise
+// work can stay in raw order (load_raw / store_raw); only values that feed
+// an ordered sum need to_groups. Every call that swaps must be made with the
+// whole wave active: the swap reads other lanes' registers.
+template <int DT>
+struct Grouped {
+    __device__ __forceinline__ static Pack<DT> load_raw(const void* b, int64_t c0, int t, int h)
+    {
+        return t < h ? Pack<DT>::load(b, c0 + t) : Pack<DT>::zero();
+    }
+    __device__ __forceinline__ static Pack<DT> load_stream_raw(const void* b, int64_t c0, int t,
+                                                               int h)
+    {
+        return t < h ? Pack<DT>::load_stream(b, c0 + t) : Pack<DT>::zero();
+    }
+    __device__ __forceinline__ static void store_stream_raw(const Pack<DT>& p, void* b,
+                                                            int64_t c0, int t, int h)
+    {
+        if (t < h)
+            p.store_stream(b, c0 + t);
+    }
+    __device__ __forceinline__ static Pack<DT> to_groups(const Pack<DT>& p) { return p; }
+    __device__ __forceinline__ static Pack<DT> to_raw(const Pack<DT>& p) { return p; }
+    __device__ __forceinline__ static Pack<DT> load_stream(const void* b, int64_t c0, int t, int h)
+    {
+        return load_stream_raw(b, c0, t, h);
+    }
+};
+
+template <>
+struct Grouped<kF32> {
+    __device__ __forceinline__ static int wa(int t) { return t < 32 ? 2 * t : 2 * (t - 32) + 1; }
+    __device__ __forceinline__ static Pack<kF32> swapped(const Pack<kF32>& p)
+    {
+        Pack<kF32> q;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const auto r = __builtin_amdgcn_permlane32_swap(p.a[k], p.b[k], false, false);
+            q.a[k] = r[0];
+            q.b[k] = r[1];
+        }
+        return q;
+    }
+    template <bool STREAM>
+    __device__ __forceinline__ static Pack<kF32> load_any(const void* base, int64_t c0, int t,
+                                                          int h)
+    {
+        const u32x4* q = static_cast<const u32x4*>(base) + 2 * c0;
+        const int w = wa(t);
+        const u32x4 z = {0, 0, 0, 0};
+        Pack<kF32> p;
+        p.a = w < 2 * h ? (STREAM ? load16_stream(q + w) : load16(q + w)) : z;
+        p.b = 64 + w < 2 * h ? (STREAM ? load16_stream(q + 64 + w) : load16(q + 64 + w)) : z;
+        return p;
+    }
+    __device__ __forceinline__ static Pack<kF32> load_raw(const void* b, int64_t c0, int t, int h)
+    {
+        return load_any<false>(b, c0, t, h);
+    }
+    __device__ __forceinline__ static Pack<kF32> load_stream_raw(const void* b, int64_t c0, int t,
+                                                                 int h)
+    {
+        return load_any<true>(b, c0, t, h);
+    }
+    __device__ __forceinline__ static void store_stream_raw(const Pack<kF32>& p, void* base,
+                                                            int64_t c0, int t, int h)
+    {
+        u32x4* q = static_cast<u32x4*>(base) + 2 * c0;
+        const int w = wa(t);
+        if (w < 2 * h)
+            store16_stream(q + w, p.a);
+        if (64 + w < 2 * h)
+            store16_stream(q + 64 + w, p.b);
+    }
+    __device__ __forceinline__ static Pack<kF32> to_groups(const Pack<kF32>& p) { return swapped(p); }
+    __device__ __forceinline__ static Pack<kF32> to_raw(const Pack<kF32>& p) { return swapped(p); }
+    __device__ __forceinline__ static Pack<kF32> load_stream(const void* b, int64_t c0, int t,
+                                                             int h)
+    {
+        return swapped(load_any<true>(b, c0, t, h));
+    }
+};
+
 // Single elements, for the generic kernels (any D, element-aligned pointers).
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* base, int64_t i)

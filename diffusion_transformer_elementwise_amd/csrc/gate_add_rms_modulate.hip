@@ -67,20 +67,22 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * vpr;
 
+    // the residual update is element-wise: raw order (see Grouped); only the
+    // rounded x' that feeds the ordered sum goes to group order. Every lane
+    // runs every pack (binary32 packs trade data across lanes); packs past
+    // the row end load as zeros and are not stored.
+    using GP = Grouped<DT>;
     Pack<DT> xn[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        const int col = lane + 64 * i;
-        if (col < vpr) {
-            const Pack<DT> xv = Pack<DT>::load_stream(x, row + col);
-            const Pack<DT> uv = Pack<DT>::load_stream(u, row + col);
-            const Pack<DT> gv = FULL ? Pack<DT>::load_stream(g, row + col)
-                                     : Pack<DT>::load(g, b * vpr + col);
-            xn[i] = gate_add8<DT>(xv, uv, gv);
-            xn[i].store_stream(x_out, row + col);
-        } else {
-            xn[i] = Pack<DT>::zero();
-        }
+        const int h = vpr - 64 * i;
+        const Pack<DT> xv = GP::load_stream_raw(x, row + 64 * i, lane, h);
+        const Pack<DT> uv = GP::load_stream_raw(u, row + 64 * i, lane, h);
+        const Pack<DT> gv = FULL ? GP::load_stream_raw(g, row + 64 * i, lane, h)
+                                 : GP::load_raw(g, b * vpr + 64 * i, lane, h);
+        const Pack<DT> xr = gate_add8<DT>(xv, uv, gv);
+        GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
+        xn[i] = GP::to_groups(xr);
     }
 
     float acc = 0.0f;
@@ -103,22 +105,21 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
 
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        const int col = lane + 64 * i;
-        if (col >= vpr)
-            continue;
-        const Pack<DT> sc = MOD == kModToken ? Pack<DT>::load_stream(scale, row + col)
-                                             : Pack<DT>::load(scale, b * vpr + col);
-        const Pack<DT> sh = MOD == kModToken ? Pack<DT>::load_stream(shift, row + col)
-                                             : Pack<DT>::load(shift, b * vpr + col);
+        const int h = vpr - 64 * i;
+        const Pack<DT> xr = GP::to_raw(xn[i]);
+        const Pack<DT> sc = MOD == kModToken ? GP::load_stream_raw(scale, row + 64 * i, lane, h)
+                                             : GP::load_raw(scale, b * vpr + 64 * i, lane, h);
+        const Pack<DT> sh = MOD == kModToken ? GP::load_stream_raw(shift, row + 64 * i, lane, h)
+                                             : GP::load_raw(shift, b * vpr + 64 * i, lane, h);
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float n = xn[i].get(e) * rr;
+            const float n = xr.get(e) * rr;
             const float a = 1.0f + sc.get(e);
             const float m = n * a;
             o[e] = m + sh.get(e);
         }
-        Pack<DT>::make(o).store_stream(y, row + col);
+        GP::store_stream_raw(Pack<DT>::make(o), y, row + 64 * i, lane, h);
     }
 }
 

@@ -23,11 +23,15 @@
 // Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers): the
 // row stays in registers (G packs per lane), read once from HBM and written
 // once, with nontemporal loads and stores; one wave per workgroup, two rows
-// per wave. With row modulation the packed 2-byte scale and shift rows stay
-// in registers across the wave's rows (the shape that measured fastest on
-// MI355X inside a chain of streaming kernels); per-token rows, and binary32
-// rows, are read in the apply phase instead. The LayerNorm's second sum runs
-// over the registers, so it costs arithmetic, not memory traffic.
+// per wave. With row modulation the scale and shift rows stay in registers
+// across the wave's rows (the shape that measured fastest on MI355X inside a
+// chain of streaming kernels; for binary32 too, 8 % faster than re-reading
+// them from L2 per row despite the register cost); per-token rows are read in
+// the apply phase instead. The LayerNorm's second sum runs
+// over the registers, so it costs arithmetic, not memory traffic. A binary32
+// pack is two words; they are moved with contiguous wave-wide accesses and
+// one lane exchange (Grouped in dtype.hpp) rather than two adjacent words per
+// lane, which left every access instruction half a cache line per lane.
 //
 // Generic path (any D, element-aligned pointers): the same order, each sum
 // one pass over the row with element loads, then the apply pass.
@@ -78,7 +82,7 @@ __device__ __forceinline__ void modulate_rows(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
-    constexpr bool kHold = (MOD == kModRow) && (DT != kF32);
+    constexpr bool kHold = (MOD == kModRow);
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t r0 = (int64_t)blockIdx.x * kRowsPerWave;
@@ -88,9 +92,8 @@ __device__ __forceinline__ void modulate_rows(
     if constexpr (kHold) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int col = lane + 64 * i;
-            sc[i] = (col < vpr) ? Pack<DT>::load(scale, b * vpr + col) : Pack<DT>::zero();
-            sh[i] = (col < vpr) ? Pack<DT>::load(shift, b * vpr + col) : Pack<DT>::zero();
+            sc[i] = Grouped<DT>::load_raw(scale, b * vpr + 64 * i, lane, vpr - 64 * i);
+            sh[i] = Grouped<DT>::load_raw(shift, b * vpr + 64 * i, lane, vpr - 64 * i);
         }
     }
 
@@ -98,10 +101,8 @@ __device__ __forceinline__ void modulate_rows(
         const int64_t row = (b * L + r) * vpr;
         Pack<DT> xv[G];
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int col = lane + 64 * i;
-            xv[i] = (col < vpr) ? Pack<DT>::load_stream(x, row + col) : Pack<DT>::zero();
-        }
+        for (int i = 0; i < G; ++i)
+            xv[i] = Grouped<DT>::load_stream(x, row + 64 * i, lane, vpr - 64 * i);
 
         float mu = 0.0f;
         if constexpr (NORM == kNormLn) {
@@ -131,26 +132,28 @@ __device__ __forceinline__ void modulate_rows(
         }
         const float rr = inv_std(wave_sum(acc), d_float, eps);
 
+        // element-wise, so in raw order (binary32 rows are turned back from
+        // group order, which needs every lane: no lane skips a pack); packs
+        // past the row end are not stored
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int col = lane + 64 * i;
-            if (col >= vpr)
-                continue;
+            const int h = vpr - 64 * i;
+            const Pack<DT> xr = Grouped<DT>::to_raw(xv[i]);
             Pack<DT> s_, h_;
             if constexpr (kHold) {
                 s_ = sc[i];
                 h_ = sh[i];
             } else if constexpr (MOD == kModToken) {
-                s_ = Pack<DT>::load_stream(scale, row + col);
-                h_ = Pack<DT>::load_stream(shift, row + col);
+                s_ = Grouped<DT>::load_stream_raw(scale, row + 64 * i, lane, h);
+                h_ = Grouped<DT>::load_stream_raw(shift, row + 64 * i, lane, h);
             } else {
-                s_ = Pack<DT>::load(scale, b * vpr + col);
-                h_ = Pack<DT>::load(shift, b * vpr + col);
+                s_ = Grouped<DT>::load_raw(scale, b * vpr + 64 * i, lane, h);
+                h_ = Grouped<DT>::load_raw(shift, b * vpr + 64 * i, lane, h);
             }
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float v = xv[i].get(e);
+                float v = xr.get(e);
                 if constexpr (NORM == kNormLn)
                     v = v - mu;
                 const float n = v * rr;
@@ -158,7 +161,7 @@ __device__ __forceinline__ void modulate_rows(
                 const float m = n * a;
                 o[e] = m + h_.get(e);
             }
-            Pack<DT>::make(o).store_stream(out, row + col);
+            Grouped<DT>::store_stream_raw(Pack<DT>::make(o), out, row + 64 * i, lane, h);
         }
     }
 }
