@@ -1,9 +1,10 @@
 """torch integration: custom ops for torch.compile and a first-use check.
 
-Custom ops. The three entry points are registered as torch custom ops
+Custom ops. The entry points are registered as torch custom ops
 (``rga::residual_gate_add``, ``rga::rms_modulate``,
-``rga::gate_add_rms_modulate``), functional (they allocate their outputs),
-each with a fake implementation that only describes the output shapes. A
+``rga::gate_add_rms_modulate``, their ``_ex`` forms, ``rga::ln_modulate`` and
+``rga::gelu_tanh``), functional (they allocate their outputs), each with a
+fake implementation that only describes the output shapes. A
 ``torch.compile(fullgraph=True)`` trace then sees one opaque op instead of
 tracing into ctypes ("[KDA-Pilot] Add diffusion residual-gate CUDA fast path
 for LTX2", "Modifications": an eager custom op with a fake impl so direct
@@ -22,7 +23,7 @@ from __future__ import annotations
 
 import threading
 import warnings
-from typing import Callable
+from typing import Callable, Optional
 
 import torch
 
@@ -66,6 +67,65 @@ def gate_add_rms_modulate(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
 @gate_add_rms_modulate.register_fake
 def _gate_add_rms_modulate_fake(x, u, g, scale, shift, eps):
     return torch.empty_like(x), torch.empty_like(x)
+
+
+@torch.library.custom_op("rga::residual_gate_add_ex", mutates_args=())
+def residual_gate_add_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
+    """residual_gate_add for bf16, float16 or float32, any D, any offset."""
+    return ops.rga_residual_gate_add_ex(x, u, g)
+
+
+@residual_gate_add_ex.register_fake
+def _residual_gate_add_ex_fake(x, u, g):
+    return torch.empty_like(x)
+
+
+@torch.library.custom_op("rga::rms_modulate_ex", mutates_args=())
+def rms_modulate_ex(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                    eps: float) -> torch.Tensor:
+    """rms_modulate for any storage type; scale/shift [B, 1, D] or [B, L, D]."""
+    return ops.rga_rms_modulate_ex(x, scale, shift, eps)
+
+
+@rms_modulate_ex.register_fake
+def _rms_modulate_ex_fake(x, scale, shift, eps):
+    return torch.empty_like(x)
+
+
+@torch.library.custom_op("rga::gate_add_rms_modulate_ex", mutates_args=())
+def gate_add_rms_modulate_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
+                             scale: torch.Tensor, shift: torch.Tensor,
+                             eps: float) -> tuple[torch.Tensor, torch.Tensor]:
+    """gate_add_rms_modulate for any storage type and modulation layout."""
+    return ops.rga_gate_add_rms_modulate_ex(x, u, g, scale, shift, eps)
+
+
+@gate_add_rms_modulate_ex.register_fake
+def _gate_add_rms_modulate_ex_fake(x, u, g, scale, shift, eps):
+    return torch.empty_like(x), torch.empty_like(x)
+
+
+@torch.library.custom_op("rga::ln_modulate", mutates_args=())
+def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                eps: float) -> torch.Tensor:
+    """layer_norm(x, eps) * (1 + scale) + shift (weightless LayerNorm)."""
+    return ops.rga_ln_modulate(x, scale, shift, eps)
+
+
+@ln_modulate.register_fake
+def _ln_modulate_fake(x, scale, shift, eps):
+    return torch.empty_like(x)
+
+
+@torch.library.custom_op("rga::gelu_tanh", mutates_args=())
+def gelu_tanh(x: torch.Tensor, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gelu(x + bias), tanh approximation, over the last dimension."""
+    return ops.gelu_tanh(x, bias)
+
+
+@gelu_tanh.register_fake
+def _gelu_tanh_fake(x, bias=None):
+    return torch.empty_like(x)
 
 
 # ---- first-use check ------------------------------------------------------

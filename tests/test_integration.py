@@ -95,6 +95,28 @@ def test_ops_are_opaque_to_tracing():
     assert not any("ctypes" in t for t in targets)
 
 
+def test_extended_ops_are_opaque_to_tracing():
+    from torch.fx.experimental.proxy_tensor import make_fx
+    from torch._subclasses.fake_tensor import FakeTensorMode
+
+    def block(x, u, g, s, t, b):
+        x1 = torch.ops.rga.residual_gate_add_ex(x, u, g)
+        y = torch.ops.rga.ln_modulate(x1, s, t, 1e-6)
+        x2, y2 = torch.ops.rga.gate_add_rms_modulate_ex(x1, y, g, s, t, 1e-6)
+        y3 = torch.ops.rga.rms_modulate_ex(x2, s, t, 1e-6)
+        h = torch.ops.rga.gelu_tanh(y3, b)
+        return h, y2
+
+    with FakeTensorMode():
+        mk = lambda *shape: torch.empty(*shape, dtype=torch.float16, device="cuda")
+        args = (mk(2, 5, 24), mk(2, 5, 24), mk(2, 1, 24), mk(2, 5, 24), mk(2, 5, 24), mk(24))
+        gm = make_fx(block, tracing_mode="fake")(*args)
+    targets = {str(n.target) for n in gm.graph.nodes if n.op == "call_function"}
+    for name in ("residual_gate_add_ex", "ln_modulate", "gate_add_rms_modulate_ex",
+                 "rms_modulate_ex", "gelu_tanh"):
+        assert f"rga.{name}.default" in targets, (name, targets)
+
+
 # ---- GPU -------------------------------------------------------------------
 
 def _dev_inputs(seed, B=2, L=333, D=2048):
@@ -132,6 +154,27 @@ def test_compiled_block_matches_eager_and_oracle():
     x2, y2 = oracle.gate_add_rms_modulate(x1, y, h[2], h[3], h[4], 1e-6, oracle.GATE_BCAST)
     for a, w in zip(got, (x1, y, x2, y2)):
         assert np.array_equal(to_host(a), w)
+
+
+@pytest.mark.gpu
+def test_compiled_extended_block_matches_eager():
+    from tests.gpu_util import say
+
+    def block(x, u, g, s, t, b):
+        x1 = torch.ops.rga.residual_gate_add_ex(x, u, g)
+        y = torch.ops.rga.ln_modulate(x1, s, t, 1e-6)
+        x2, y2 = torch.ops.rga.gate_add_rms_modulate_ex(x1, y, g, s, t, 1e-6)
+        h = torch.ops.rga.gelu_tanh(torch.ops.rga.rms_modulate_ex(x2, s, t, 1e-6), b)
+        return x1, y, x2, y2, h
+
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    mk = lambda *shape: torch.randn(*shape, generator=gen, device="cuda").to(torch.float16)
+    args = (mk(2, 77, 1000), mk(2, 77, 1000), mk(2, 1, 1000), mk(2, 77, 1000) * 0.1,
+            mk(2, 77, 1000) * 0.1, mk(1000))
+    say("[compile] extended ops, float16, per-token modulation, D = 1000")
+    got = torch.compile(block, fullgraph=True, backend="aot_eager")(*args)
+    for a, b in zip(got, block(*args)):
+        assert I.bitwise_equal(a, b)
 
 
 @pytest.mark.gpu
