@@ -441,8 +441,10 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         n = B * L * D
         nbytes = (4 * n if mode == dte.GATE_FULL else 3 * n + B * D) * es
         fast = D % 8 == 0 and offset == 0
+        fast = fast or (mode == dte.GATE_FULL and offset == 0)  # a full add is one flat stream
         kern = ("gate_add_full_kernel" if mode == dte.GATE_FULL else "gate_add_bcast_kernel") \
-            if fast else "gate_add_generic_kernel"
+            if fast else ("gate_add_generic_full_kernel" if mode == dte.GATE_FULL
+                          else "gate_add_generic_bcast_kernel")
         log(f"variant {name}")
         out[name] = cold_and_warm(lambda: dte.rga_residual_gate_add_ex(x, u, g, out=o),
                                   nbytes, kern)

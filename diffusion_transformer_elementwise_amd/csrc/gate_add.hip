@@ -15,22 +15,23 @@
 // lane holds does not matter here, so binary32 packs are lane-interleaved
 // (Interleaved in dtype.hpp) for contiguous wave-wide accesses.
 //
-// Generic path (any D, pointers aligned to the element size): element
-// loads and stores with the same arithmetic, for shapes the fast path cannot
-// take.
+// Element path (any D, pointers aligned to the element size): the same
+// arithmetic on spans of elements staged through LDS with 16-byte accesses,
+// for shapes the pack path cannot take.
 //
 // Every thread reads its own elements before writing them and no element
 // depends on another, so out may alias x or u (and g in full mode).
 #include "dtype.hpp"
 #include "launch.hpp"
+#include "span.hpp"
 
 #include <rga.h>
 
 namespace rga {
 namespace {
 
-constexpr int kBlock = 64;  // one wave per workgroup
-constexpr int kSpan = 8;    // generic path: elements per lane
+constexpr int kBlock = 64;   // one wave per workgroup
+constexpr int kSpan = 512;   // element path: elements per workgroup
 
 template <int DT>
 __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
@@ -99,37 +100,53 @@ __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
     I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
 }
 
-// Generic path: each workgroup (one wave) takes a span of 64 * kSpan
-// elements, lane t the elements span_start + 64 e + t for e < kSpan, so that
-// every load and store instruction of the wave touches one contiguous run and
-// each lane keeps kSpan independent loads per stream in flight.
+// Element path: each workgroup (one wave) takes a span of up to kSpan
+// elements and moves it through LDS with 16-byte accesses (Span in
+// span.hpp), so any element alignment and any D run at near pack speed.
+template <int DT, bool G_STREAM>
+__device__ __forceinline__ void gate_add_span(const void* x, const void* u, const void* g,
+                                              void* out, int cnt)
+{
+    using S = Span<DT, kSpan>;
+    __shared__ u32x4 rx[S::kWords], ru[S::kWords], rg[S::kWords], ro[S::kWords];
+    S::template load<true>(x, cnt, rx);
+    S::template load<true>(u, cnt, ru);
+    S::template load<G_STREAM>(g, cnt, rg);
+    __syncthreads();
+    const int mx = S::offset(x), mu = S::offset(u), mg = S::offset(g), mo = S::offset(out);
+    for (int i = threadIdx.x; i < cnt; i += kBlock) {
+        const float p = S::get(ru, mu, i) * S::get(rg, mg, i);
+        S::put(ro, mo, i, S::get(rx, mx, i) + p);
+    }
+    __syncthreads();
+    S::template store<true>(out, cnt, ro);
+}
+
+template <int DT>
+__device__ __forceinline__ const void* elem_ptr(const void* p, int64_t i)
+{
+    return static_cast<const char*>(p) + i * (DT == kF32 ? 4 : 2);
+}
+
+template <int DT>
+__device__ __forceinline__ void* elem_ptr(void* p, int64_t i)
+{
+    return static_cast<char*>(p) + i * (DT == kF32 ? 4 : 2);
+}
+
 // Full gate: spans tile the flat B*L*D elements; grid x = span.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_generic_full_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t n)
 {
-    const int64_t s0 = (int64_t)blockIdx.x * (kBlock * kSpan) + threadIdx.x;
-    float xv[kSpan], uv[kSpan], gv[kSpan];
-#pragma unroll
-    for (int e = 0; e < kSpan; ++e) {
-        const int64_t i = s0 + (int64_t)e * kBlock;
-        const bool in = i < n;
-        xv[e] = in ? load_elem_stream<DT>(x, i) : 0.0f;
-        uv[e] = in ? load_elem_stream<DT>(u, i) : 0.0f;
-        gv[e] = in ? load_elem_stream<DT>(g, i) : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < kSpan; ++e) {
-        const int64_t i = s0 + (int64_t)e * kBlock;
-        if (i < n) {
-            const float p = uv[e] * gv[e];
-            store_elem_stream<DT>(out, i, xv[e] + p);
-        }
-    }
+    const int64_t e0 = (int64_t)blockIdx.x * kSpan;
+    const int cnt = (n - e0 < kSpan) ? (int)(n - e0) : kSpan;
+    gate_add_span<DT, true>(elem_ptr<DT>(x, e0), elem_ptr<DT>(u, e0), elem_ptr<DT>(g, e0),
+                            elem_ptr<DT>(out, e0), cnt);
 }
 
 // Broadcast gate: spans tile each row; grid x = (row l) * spans per row +
-// span, y = batch b; the gate element of column d is g[b*D + d].
+// span, y = batch b; the gate span is the same columns of g's row b.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_generic_bcast_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t L,
@@ -138,25 +155,11 @@ __global__ __launch_bounds__(kBlock) void gate_add_generic_bcast_kernel(
     const uint32_t l = blockIdx.x / spans;
     const uint32_t sp = blockIdx.x - l * spans;
     const int64_t b = blockIdx.y;
-    const int64_t d0 = (int64_t)sp * (kBlock * kSpan) + threadIdx.x;
-    const int64_t row = (b * L + l) * D;
-    float xv[kSpan], uv[kSpan], gv[kSpan];
-#pragma unroll
-    for (int e = 0; e < kSpan; ++e) {
-        const int64_t d = d0 + (int64_t)e * kBlock;
-        const bool in = d < D;
-        xv[e] = in ? load_elem_stream<DT>(x, row + d) : 0.0f;
-        uv[e] = in ? load_elem_stream<DT>(u, row + d) : 0.0f;
-        gv[e] = in ? load_elem<DT>(g, b * D + d) : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < kSpan; ++e) {
-        const int64_t d = d0 + (int64_t)e * kBlock;
-        if (d < D) {
-            const float p = uv[e] * gv[e];
-            store_elem_stream<DT>(out, row + d, xv[e] + p);
-        }
-    }
+    const int64_t d0 = (int64_t)sp * kSpan;
+    const int cnt = (D - d0 < kSpan) ? (int)(D - d0) : kSpan;
+    const int64_t e0 = (b * L + l) * D + d0;
+    gate_add_span<DT, false>(elem_ptr<DT>(x, e0), elem_ptr<DT>(u, e0),
+                             elem_ptr<DT>(g, b * D + d0), elem_ptr<DT>(out, e0), cnt);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -172,9 +175,9 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
             void* args[] = {&x, &u, &g, &out, &n};
             return hipLaunchKernel(
                 reinterpret_cast<const void*>(&gate_add_generic_full_kernel<DT>),
-                dim3((uint32_t)ceil_div(n, kBlock * kSpan)), dim3(kBlock), args, 0, stream);
+                dim3((uint32_t)ceil_div(n, kSpan)), dim3(kBlock), args, 0, stream);
         }
-        uint32_t spans = (uint32_t)ceil_div(D, kBlock * kSpan);
+        uint32_t spans = (uint32_t)ceil_div(D, kSpan);
         void* args[] = {&x, &u, &g, &out, &L, &D, &spans};
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_generic_bcast_kernel<DT>),
@@ -206,18 +209,14 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
 bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode,
                         bool fast)
 {
-    const int64_t max_x = (((int64_t)1 << 32) - 1);
-    if (gate_mode == RGA_GATE_FULL && fast)  // one flat grid dimension
-        return ceil_div(B * L * D / 8 + 1, kBlock) <= max_x / kBlock;
-    if (B > 65535)
+    const int64_t max_wg = (((int64_t)1 << 32) - 1) / kBlock;
+    if (gate_mode == RGA_GATE_FULL)  // one flat grid dimension, B plays no part
+        return fast ? ceil_div(B * L * D / 8 + 1, kBlock) <= max_wg
+                    : ceil_div(B * L * D, kSpan) <= max_wg;
+    if (B > 65535)  // grid y
         return false;
-    if (!fast) {
-        const int64_t span = kBlock * kSpan;
-        if (gate_mode == RGA_GATE_FULL)
-            return ceil_div(B * L * D, span) <= max_x / kBlock;
-        return L * ceil_div(D, span) <= max_x / kBlock;
-    }
-    return L * ceil_div(D / 8, kBlock) <= max_x / kBlock;
+    return fast ? L * ceil_div(D / 8, kBlock) <= max_wg
+                : L * ceil_div(D, kSpan) <= max_wg;
 }
 
 hipError_t launch_gate_add(const void* x, const void* u, const void* g,

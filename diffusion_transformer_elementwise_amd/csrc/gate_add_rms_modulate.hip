@@ -25,11 +25,12 @@
 // is read through the caches (it stays in L2), a full gate streams from HBM
 // like x and u.
 //
-// Generic path (any D, element-aligned pointers): the same operations in two
-// passes over the row with element loads; the second pass re-reads x_out,
-// which the same lane wrote in the first.
+// Element path (any D, element-aligned pointers): the same operations in two
+// passes over the row, moving spans of elements through LDS with 16-byte
+// accesses; the second pass re-reads x_out.
 #include "dtype.hpp"
 #include "launch.hpp"
+#include "span.hpp"
 
 #include <rga.h>
 
@@ -37,8 +38,7 @@ namespace rga {
 namespace {
 
 constexpr int kBlock = 64;
-constexpr int kStage = 2048;  // generic path: elements staged in LDS per step
-constexpr int kSpan = 8;      // generic path: elements per lane in pass 2
+constexpr int kStage = 1024;  // element path: elements per span
 
 template <int DT>
 __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
@@ -123,19 +123,32 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
     }
 }
 
-// Generic: one wave per row; grid x = row l, y = batch b. Pass 1 walks the
-// row in stages of kStage elements: wave-contiguous loads (lane t takes
-// elements 64e + t), x_out formed and stored, its rounded values staged in
-// LDS, from where lane j adds up groups j, j + 64, ... of the stage in the
-// fixed order. Pass 2 re-reads x_out (each lane the elements it wrote) and
-// writes y.
+template <int DT>
+__device__ __forceinline__ const void* elem_ptr(const void* p, int64_t i)
+{
+    return static_cast<const char*>(p) + i * (DT == kF32 ? 4 : 2);
+}
+
+template <int DT>
+__device__ __forceinline__ void* elem_ptr(void* p, int64_t i)
+{
+    return static_cast<char*>(p) + i * (DT == kF32 ? 4 : 2);
+}
+
+// Element path: one wave per row; grid x = row l, y = batch b. Spans of
+// kStage elements move through LDS with 16-byte accesses (span.hpp). Pass 1
+// forms x' for a span, stores it to x_out and, from its rounded value in
+// LDS, lane j adds up groups j, j + 64, ... of the span in the fixed order.
+// Pass 2 re-reads x_out (written by other lanes of this wave: the barrier
+// between the passes orders those writes before the reads) and writes y.
 template <bool FULL, int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     const void* x, const void* u, const void* g, const void* scale,
     const void* shift, float eps, float d_float, void* x_out, void* y,
     int64_t L, int64_t D)
 {
-    __shared__ float stage[kStage];
+    using S = Span<DT, kStage>;
+    __shared__ u32x4 r0[S::kWords], r1[S::kWords], r2[S::kWords], r3[S::kWords];
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
@@ -144,33 +157,29 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
 
     float acc = 0.0f;
     for (int64_t s0 = 0; s0 < D; s0 += kStage) {
-        float xv[kStage / kBlock], uv[kStage / kBlock], gv[kStage / kBlock];
-#pragma unroll
-        for (int e = 0; e < kStage / kBlock; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            const bool in = d < D;
-            xv[e] = in ? load_elem_stream<DT>(x, row + d) : 0.0f;
-            uv[e] = in ? load_elem_stream<DT>(u, row + d) : 0.0f;
-            gv[e] = in ? (FULL ? load_elem_stream<DT>(g, grow + d) : load_elem<DT>(g, grow + d))
-                       : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < kStage / kBlock; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            const float p = uv[e] * gv[e];
-            const float sum = xv[e] + p;
-            if (d < D)
-                store_elem<DT>(x_out, row + d, sum);
-            stage[e * kBlock + lane] = rounded<DT>(sum);
+        const int cnt = (D - s0 < kStage) ? (int)(D - s0) : kStage;
+        const void* px = elem_ptr<DT>(x, row + s0);
+        const void* pu = elem_ptr<DT>(u, row + s0);
+        const void* pg = elem_ptr<DT>(g, grow + s0);
+        void* po = elem_ptr<DT>(x_out, row + s0);
+        S::template load<true>(px, cnt, r0);
+        S::template load<true>(pu, cnt, r1);
+        S::template load<FULL>(pg, cnt, r2);
+        __syncthreads();
+        const int mx = S::offset(px), mu = S::offset(pu), mg = S::offset(pg), mo = S::offset(po);
+        for (int i = lane; i < cnt; i += kBlock) {
+            const float p = S::get(r1, mu, i) * S::get(r2, mg, i);
+            S::put(r3, mo, i, S::get(r0, mx, i) + p);
         }
         __syncthreads();
-#pragma unroll
-        for (int m = 0; m < kStage / 512; ++m) {
-            const int g0 = (lane + kBlock * m) * 8;
+        S::template store<true>(po, cnt, r3);
+#pragma unroll 1
+        for (int k = 0; k < kStage / 512; ++k) {
+            const int g0 = (lane + kBlock * k) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (s0 + g0 + e < D) {
-                    const float a = stage[g0 + e];
+                if (g0 + e < cnt) {
+                    const float a = S::get(r3, mo, g0 + e);  // the rounded x'
                     const float sa = a * a;
                     acc = acc + sa;
                 }
@@ -186,28 +195,26 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     const float q = sqrtf(t);
     const float rr = 1.0f / q;
 
-    for (int64_t s0 = 0; s0 < D; s0 += kBlock * kSpan) {
-        float xv[kSpan], sv[kSpan], hv[kSpan];
-#pragma unroll
-        for (int e = 0; e < kSpan; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            const bool in = d < D;
-            xv[e] = in ? load_elem<DT>(x_out, row + d) : 0.0f;
-            sv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(scale, mrow + d)
-                                           : load_elem<DT>(scale, mrow + d)) : 0.0f;
-            hv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(shift, mrow + d)
-                                           : load_elem<DT>(shift, mrow + d)) : 0.0f;
+    for (int64_t s0 = 0; s0 < D; s0 += kStage) {
+        const int cnt = (D - s0 < kStage) ? (int)(D - s0) : kStage;
+        const void* px = elem_ptr<DT>(x_out, row + s0);
+        const void* ps = elem_ptr<DT>(scale, mrow + s0);
+        const void* ph = elem_ptr<DT>(shift, mrow + s0);
+        void* py = elem_ptr<DT>(y, row + s0);
+        S::template load<false>(px, cnt, r0);
+        S::template load<MOD == kModToken>(ps, cnt, r1);
+        S::template load<MOD == kModToken>(ph, cnt, r2);
+        __syncthreads();
+        const int mx = S::offset(px), ms2 = S::offset(ps), mh = S::offset(ph), my = S::offset(py);
+        for (int i = lane; i < cnt; i += kBlock) {
+            const float n = S::get(r0, mx, i) * rr;
+            const float a = 1.0f + S::get(r1, ms2, i);
+            const float m = n * a;
+            S::put(r3, my, i, m + S::get(r2, mh, i));
         }
-#pragma unroll
-        for (int e = 0; e < kSpan; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            if (d < D) {
-                const float n = xv[e] * rr;
-                const float a = 1.0f + sv[e];
-                const float m = n * a;
-                store_elem_stream<DT>(y, row + d, m + hv[e]);
-            }
-        }
+        __syncthreads();
+        S::template store<true>(py, cnt, r3);
+        __syncthreads();
     }
 }
 

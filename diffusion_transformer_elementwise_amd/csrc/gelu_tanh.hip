@@ -33,9 +33,10 @@
 // one wave per workgroup, one 8-element pack per lane, nontemporal loads and
 // stores; without a bias the tensor is one flat stream (the last lane adds
 // the trailing rows*F % 8 elements), with a bias rows are cut into chunks of
-// up to 64 packs; other shapes take element-wise loads.
+// up to 64 packs; other layouts move spans of elements through LDS.
 #include "dtype.hpp"
 #include "launch.hpp"
+#include "span.hpp"
 
 #include <rga.h>
 
@@ -43,7 +44,7 @@ namespace rga {
 namespace {
 
 constexpr int kBlock = 64;
-constexpr int kSpan = 8;  // element path: elements per lane
+constexpr int kSpan = 512;  // element path: elements per workgroup
 
 // tl = t log2(e) = h (kC1 + kC2 h^2), t = 2 sqrt(2/pi) (h + 0.044715 h^3);
 // constants rounded to nearest binary32
@@ -158,34 +159,36 @@ __global__ __launch_bounds__(kBlock) void gelu_tanh_bias_kernel(
     I::store_stream(gelu8<DT, true>(xv, bv), out, c0, t, h);
 }
 
-// Element path: grid x = row * spans + span; lane t takes elements
-// span*64*kSpan + 64e + t of the row.
+// Element path: grid x = row * spans + span; a span of up to kSpan elements
+// of a row (and the same columns of the bias) moves through LDS with 16-byte
+// accesses (span.hpp).
 template <int DT, bool BIAS>
 __global__ __launch_bounds__(kBlock) void gelu_tanh_generic_kernel(
     const void* x, const void* bias, void* out, int64_t F, uint32_t spans)
 {
+    using S = Span<DT, kSpan>;
+    __shared__ u32x4 rx[S::kWords], rb[S::kWords], ro[S::kWords];
+    constexpr int es = DT == kF32 ? 4 : 2;
     const uint32_t r = blockIdx.x / spans;
     const uint32_t sp = blockIdx.x - r * spans;
-    const int64_t row = (int64_t)r * F;
-    const int64_t d0 = (int64_t)sp * (kBlock * kSpan) + threadIdx.x;
-    float hv[kSpan];
-#pragma unroll
-    for (int e = 0; e < kSpan; ++e) {
-        const int64_t d = d0 + (int64_t)e * kBlock;
-        float h = 0.0f;
-        if (d < F) {
-            h = load_elem_stream<DT>(x, row + d);
-            if constexpr (BIAS)
-                h = h + load_elem<DT>(bias, d);
-        }
-        hv[e] = h;
+    const int64_t d0 = (int64_t)sp * kSpan;
+    const int cnt = (F - d0 < kSpan) ? (int)(F - d0) : kSpan;
+    const void* px = static_cast<const char*>(x) + ((int64_t)r * F + d0) * es;
+    const void* pb = BIAS ? static_cast<const char*>(bias) + d0 * es : nullptr;
+    void* po = static_cast<char*>(out) + ((int64_t)r * F + d0) * es;
+    S::template load<true>(px, cnt, rx);
+    if constexpr (BIAS)
+        S::template load<false>(pb, cnt, rb);
+    __syncthreads();
+    const int mx = S::offset(px), mb = BIAS ? S::offset(pb) : 0, mo = S::offset(po);
+    for (int i = threadIdx.x; i < cnt; i += kBlock) {
+        float h = S::get(rx, mx, i);
+        if constexpr (BIAS)
+            h = h + S::get(rb, mb, i);
+        S::put(ro, mo, i, gelu1(h));
     }
-#pragma unroll
-    for (int e = 0; e < kSpan; ++e) {
-        const int64_t d = d0 + (int64_t)e * kBlock;
-        if (d < F)
-            store_elem_stream<DT>(out, row + d, gelu1(hv[e]));
-    }
+    __syncthreads();
+    S::template store<true>(po, cnt, ro);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -210,7 +213,7 @@ hipError_t launch_typed(const void* x, const void* bias, void* out, int64_t rows
         return hipLaunchKernel(reinterpret_cast<const void*>(&gelu_tanh_bias_kernel<DT>),
                                dim3((uint32_t)(rows * chunks)), dim3(kBlock), args, 0, stream);
     }
-    uint32_t spans = (uint32_t)ceil_div(F, kBlock * kSpan);
+    uint32_t spans = (uint32_t)ceil_div(F, kSpan);
     void* args[] = {&x, &bias, &out, &F, &spans};
     const void* k = bias ? reinterpret_cast<const void*>(&gelu_tanh_generic_kernel<DT, true>)
                          : reinterpret_cast<const void*>(&gelu_tanh_generic_kernel<DT, false>);
@@ -226,7 +229,7 @@ bool gelu_tanh_grid_fits(int64_t rows, int64_t F, bool has_bias, bool fast)
         return ceil_div(rows * F / 8 + 1, kBlock) <= max_wg;
     if (fast)
         return rows * ceil_div(F / 8, kBlock) <= max_wg;
-    return rows * ceil_div(F, kBlock * kSpan) <= max_wg;
+    return rows * ceil_div(F, kSpan) <= max_wg;
 }
 
 hipError_t launch_gelu_tanh(const void* x, const void* bias, void* out, int64_t rows,

@@ -33,14 +33,14 @@
 // one lane exchange (Grouped in dtype.hpp) rather than two adjacent words per
 // lane, which left every access instruction half a cache line per lane.
 //
-// Generic path (any D, element-aligned pointers): the same order, each sum
-// one pass over the row with element loads, then the apply pass.
+// Element path (any D, element-aligned pointers): the same order, each sum
+// one pass over the row, then the apply pass, all moving spans of elements
+// through LDS with 16-byte accesses (span.hpp).
 //
-// One wave per workgroup: nothing crosses a wave. The fast path uses no LDS;
-// the generic path stages the row through LDS to read it with contiguous
-// wave-wide loads and still add in the fixed order.
+// One wave per workgroup: nothing crosses a wave. The fast path uses no LDS.
 #include "dtype.hpp"
 #include "launch.hpp"
+#include "span.hpp"
 
 #include <rga.h>
 
@@ -49,8 +49,8 @@ namespace {
 
 constexpr int kBlock = 64;  // one wave per workgroup
 constexpr int kRowsPerWave = 2;
-constexpr int kStage = 2048;  // generic path: elements staged in LDS per step
-constexpr int kSpan = 8;      // generic path: elements per lane in the apply
+constexpr int kStage = 1024;  // element path: elements staged in LDS per sum step
+constexpr int kApply = 512;   // element path: elements per apply step
 
 enum : int { kNormRms = 0, kNormLn = 1 };
 
@@ -183,35 +183,43 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_kernel(
     modulate_rows<G, DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, vpr);
 }
 
-// Generic path, one wave per row. A sum in the fixed order walks the row in
-// stages of kStage elements: the wave reads a stage with wave-contiguous
-// loads (lane t takes elements 64e + t) into LDS, then lane j adds up groups
-// j, j + 64, ... of the stage from LDS. WHAT: 0 the values, 1 their squares,
-// 2 the squares of value - mu.
+template <int DT>
+__device__ __forceinline__ const void* elem_ptr(const void* p, int64_t i)
+{
+    return static_cast<const char*>(p) + i * (DT == kF32 ? 4 : 2);
+}
+
+template <int DT>
+__device__ __forceinline__ void* elem_ptr(void* p, int64_t i)
+{
+    return static_cast<char*>(p) + i * (DT == kF32 ? 4 : 2);
+}
+
+// Element path, one wave per row. A sum in the fixed order walks the row in
+// stages of kStage elements: the wave moves a stage into LDS with 16-byte
+// accesses (Span in span.hpp), then lane j adds up groups j, j + 64, ... of
+// the stage from LDS. WHAT: 0 the values, 1 their squares, 2 the squares of
+// value - mu.
 template <int DT, int WHAT>
 __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t D,
-                                            float mu, float* stage)
+                                            float mu, u32x4* raw)
 {
+    using S = Span<DT, kStage>;
     const int lane = threadIdx.x;
     float acc = 0.0f;
     for (int64_t s0 = 0; s0 < D; s0 += kStage) {
-        float v[kStage / kBlock];
-#pragma unroll
-        for (int e = 0; e < kStage / kBlock; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            v[e] = d < D ? load_elem<DT>(x, row + d) : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < kStage / kBlock; ++e)
-            stage[e * kBlock + lane] = v[e];
+        const int cnt = (D - s0 < kStage) ? (int)(D - s0) : kStage;
+        const void* p = elem_ptr<DT>(x, row + s0);
+        S::template load<false>(p, cnt, raw);
         __syncthreads();
-#pragma unroll
-        for (int m = 0; m < kStage / 512; ++m) {
-            const int g0 = (lane + kBlock * m) * 8;
+        const int m = S::offset(p);
+#pragma unroll 1
+        for (int k = 0; k < kStage / 512; ++k) {
+            const int g0 = (lane + kBlock * k) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (s0 + g0 + e < D) {
-                    float a = stage[g0 + e];
+                if (g0 + e < cnt) {
+                    float a = S::get(raw, m, g0 + e);
                     if constexpr (WHAT == 0) {
                         acc = acc + a;
                     } else {
@@ -228,14 +236,15 @@ __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t 
     return wave_sum(acc);
 }
 
-// The apply pass re-reads the row (mostly from L2), lane t taking elements
-// 64e + t of each span of 64 * kSpan.
+// The apply pass re-reads the row (mostly from L2) in spans of kApply
+// elements, with scale and shift spans beside it, and writes out spans.
 template <int DT, int MOD, int NORM>
 __device__ __forceinline__ void modulate_row_generic(
     const void* x, const void* scale, const void* shift, float eps,
-    float d_float, void* out, int64_t L, int64_t D, float* stage)
+    float d_float, void* out, int64_t L, int64_t D, u32x4* stage)
 {
-    const int lane = threadIdx.x;
+    using A = Span<DT, kApply>;
+    __shared__ u32x4 rx[A::kWords], rs[A::kWords], rh[A::kWords], ro[A::kWords];
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
     const int64_t mrow = (MOD == kModToken) ? row : b * D;
@@ -246,31 +255,28 @@ __device__ __forceinline__ void modulate_row_generic(
     const float ss = staged_sum<DT, NORM == kNormLn ? 2 : 1>(x, row, D, mu, stage);
     const float rr = inv_std(ss, d_float, eps);
 
-    for (int64_t s0 = 0; s0 < D; s0 += kBlock * kSpan) {
-        float xv[kSpan], sv[kSpan], hv[kSpan];
-#pragma unroll
-        for (int e = 0; e < kSpan; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            const bool in = d < D;
-            xv[e] = in ? load_elem_stream<DT>(x, row + d) : 0.0f;
-            sv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(scale, mrow + d)
-                                           : load_elem<DT>(scale, mrow + d)) : 0.0f;
-            hv[e] = in ? (MOD == kModToken ? load_elem_stream<DT>(shift, mrow + d)
-                                           : load_elem<DT>(shift, mrow + d)) : 0.0f;
+    for (int64_t s0 = 0; s0 < D; s0 += kApply) {
+        const int cnt = (D - s0 < kApply) ? (int)(D - s0) : kApply;
+        const void* px = elem_ptr<DT>(x, row + s0);
+        const void* ps = elem_ptr<DT>(scale, mrow + s0);
+        const void* ph = elem_ptr<DT>(shift, mrow + s0);
+        void* po = elem_ptr<DT>(out, row + s0);
+        A::template load<true>(px, cnt, rx);
+        A::template load<MOD == kModToken>(ps, cnt, rs);
+        A::template load<MOD == kModToken>(ph, cnt, rh);
+        __syncthreads();
+        const int mx = A::offset(px), ms = A::offset(ps), mh = A::offset(ph), mo = A::offset(po);
+        for (int i = threadIdx.x; i < cnt; i += kBlock) {
+            float v = A::get(rx, mx, i);
+            if constexpr (NORM == kNormLn)
+                v = v - mu;
+            const float n = v * rr;
+            const float a = 1.0f + A::get(rs, ms, i);
+            const float m = n * a;
+            A::put(ro, mo, i, m + A::get(rh, mh, i));
         }
-#pragma unroll
-        for (int e = 0; e < kSpan; ++e) {
-            const int64_t d = s0 + e * kBlock + lane;
-            if (d < D) {
-                float v = xv[e];
-                if constexpr (NORM == kNormLn)
-                    v = v - mu;
-                const float n = v * rr;
-                const float a = 1.0f + sv[e];
-                const float m = n * a;
-                store_elem_stream<DT>(out, row + d, m + hv[e]);
-            }
-        }
+        __syncthreads();
+        A::template store<true>(po, cnt, ro);
     }
 }
 
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int64_t D)
 {
-    __shared__ float stage[kStage];
+    __shared__ u32x4 stage[Span<DT, kStage>::kWords];
     modulate_row_generic<DT, MOD, kNormRms>(x, scale, shift, eps, d_float, out, L, D, stage);
 }
 
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int64_t D)
 {
-    __shared__ float stage[kStage];
+    __shared__ u32x4 stage[Span<DT, kStage>::kWords];
     modulate_row_generic<DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, D, stage);
 }
 

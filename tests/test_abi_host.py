@@ -369,3 +369,25 @@ def test_ln_modulate_validation_follows_the_ex_rules(dte):
             dte.RGA_OK, dte.RGA_OK, dte.RGA_ERR_ALIAS, dte.RGA_OK, dte.RGA_ERR_INVALID_ARG]
     for c, w in zip(cases, want):
         assert ck(*c) == w == ref(*c), c
+
+
+def test_grid_limits(dte):
+    # the broadcast add puts B on grid y (<= 65535); the full add is one flat
+    # stream, so any B fits while the pack grid does
+    ok, uns = dte.RGA_OK, dte.RGA_ERR_UNSUPPORTED
+    GB = 1024 * MB
+    x, u, g, o = A, A + 16 * GB, A + 32 * GB, A + 48 * GB
+    assert dte.check_residual_gate_add(x, u, g, o, 65535, 1, 8, dte.GATE_BCAST) == ok
+    assert dte.check_residual_gate_add(x, u, g, o, 65536, 1, 8, dte.GATE_BCAST) == uns
+    assert dte.check_residual_gate_add(x, u, g, o, 65536, 1, 8, dte.GATE_FULL) == ok
+    # element path of a full add (D % 8 != 0 on a misaligned pointer) keeps y = 1
+    assert dte.check_residual_gate_add_ex(x + 2, u, g, o, 65536, 1, 7, dte.GATE_FULL,
+                                          dte.DTYPE_BF16) == ok
+    assert dte.check_rms_modulate_ex(x, u, g, 1e-6, o, 65536, 1, 8, dte.MOD_ROW,
+                                     dte.DTYPE_BF16) == uns
+    # pack grid of the full add: ceil((n/8 + 1) / 64) workgroups of 64 lanes
+    # must stay below 2^32 work-items
+    n_max = (((1 << 32) - 1) // 64) * 64 * 8      # elements at the limit, roughly
+    x, u, g, o = (A + k * 256 * GB for k in range(4))  # room for 2 * n_max bf16 each
+    assert dte.check_residual_gate_add(x, u, g, o, 1, 1, n_max // 2, dte.GATE_FULL) == ok
+    assert dte.check_residual_gate_add(x, u, g, o, 1, 1, n_max * 2, dte.GATE_FULL) == uns
