@@ -207,12 +207,18 @@ __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t 
     using S = Span<DT, kStage>;
     const int lane = threadIdx.x;
     float acc = 0.0f;
+    // the next stage's loads are in flight while this one is summed
+    typename S::Words next = S::template fetch<false>(elem_ptr<DT>(x, row),
+                                                      D < kStage ? (int)D : kStage);
     for (int64_t s0 = 0; s0 < D; s0 += kStage) {
         const int cnt = (D - s0 < kStage) ? (int)(D - s0) : kStage;
-        const void* p = elem_ptr<DT>(x, row + s0);
-        S::template load<false>(p, cnt, raw);
+        const int m = S::offset(elem_ptr<DT>(x, row + s0));
+        S::commit(next, raw);
         __syncthreads();
-        const int m = S::offset(p);
+        const int64_t s1 = s0 + kStage;
+        if (s1 < D)
+            next = S::template fetch<false>(elem_ptr<DT>(x, row + s1),
+                                            (D - s1 < kStage) ? (int)(D - s1) : kStage);
 #pragma unroll 1
         for (int k = 0; k < kStage / 512; ++k) {
             const int g0 = (lane + kBlock * k) * 8;
@@ -237,7 +243,8 @@ __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t 
 }
 
 // The apply pass re-reads the row (mostly from L2) in spans of kApply
-// elements, with scale and shift spans beside it, and writes out spans.
+// elements, with scale and shift spans beside it, and writes out spans; the
+// next span's loads are in flight while this one is computed and stored.
 template <int DT, int MOD, int NORM>
 __device__ __forceinline__ void modulate_row_generic(
     const void* x, const void* scale, const void* shift, float eps,
@@ -255,17 +262,29 @@ __device__ __forceinline__ void modulate_row_generic(
     const float ss = staged_sum<DT, NORM == kNormLn ? 2 : 1>(x, row, D, mu, stage);
     const float rr = inv_std(ss, d_float, eps);
 
+    constexpr bool kTok = MOD == kModToken;
+    int cnt = D < kApply ? (int)D : kApply;
+    typename A::Words nx = A::template fetch<true>(elem_ptr<DT>(x, row), cnt);
+    typename A::Words ns = A::template fetch<kTok>(elem_ptr<DT>(scale, mrow), cnt);
+    typename A::Words nh = A::template fetch<kTok>(elem_ptr<DT>(shift, mrow), cnt);
     for (int64_t s0 = 0; s0 < D; s0 += kApply) {
-        const int cnt = (D - s0 < kApply) ? (int)(D - s0) : kApply;
-        const void* px = elem_ptr<DT>(x, row + s0);
-        const void* ps = elem_ptr<DT>(scale, mrow + s0);
-        const void* ph = elem_ptr<DT>(shift, mrow + s0);
+        cnt = (D - s0 < kApply) ? (int)(D - s0) : kApply;
+        const int mx = A::offset(elem_ptr<DT>(x, row + s0));
+        const int ms = A::offset(elem_ptr<DT>(scale, mrow + s0));
+        const int mh = A::offset(elem_ptr<DT>(shift, mrow + s0));
         void* po = elem_ptr<DT>(out, row + s0);
-        A::template load<true>(px, cnt, rx);
-        A::template load<MOD == kModToken>(ps, cnt, rs);
-        A::template load<MOD == kModToken>(ph, cnt, rh);
+        const int mo = A::offset(po);
+        A::commit(nx, rx);
+        A::commit(ns, rs);
+        A::commit(nh, rh);
         __syncthreads();
-        const int mx = A::offset(px), ms = A::offset(ps), mh = A::offset(ph), mo = A::offset(po);
+        const int64_t s1 = s0 + kApply;
+        if (s1 < D) {
+            const int c1 = (D - s1 < kApply) ? (int)(D - s1) : kApply;
+            nx = A::template fetch<true>(elem_ptr<DT>(x, row + s1), c1);
+            ns = A::template fetch<kTok>(elem_ptr<DT>(scale, mrow + s1), c1);
+            nh = A::template fetch<kTok>(elem_ptr<DT>(shift, mrow + s1), c1);
+        }
         for (int i = threadIdx.x; i < cnt; i += kBlock) {
             float v = A::get(rx, mx, i);
             if constexpr (NORM == kNormLn)

@@ -51,26 +51,45 @@ struct Span {
         return (int)(reinterpret_cast<uintptr_t>(p) & 15u);
     }
 
+    // words of a span in flight in registers (fetch), then written to LDS
+    // (commit): a caller can fetch the next span before working on this one
+    struct Words {
+        u32x4 v[kPerLane];
+        int count;
+    };
+
     template <bool STREAM>
-    __device__ __forceinline__ static void load(const void* p, int n, u32x4* raw)
+    __device__ __forceinline__ static Words fetch(const void* p, int n)
     {
         const int lane = threadIdx.x & 63;
         const uintptr_t a = reinterpret_cast<uintptr_t>(p);
         const u32x4* w0 = reinterpret_cast<const u32x4*>(a & ~(uintptr_t)15);
-        const int words = n > 0 ? ((int)(a & 15u) + n * kEs + 15) >> 4 : 0;
-        u32x4 v[kPerLane];
+        Words r;
+        r.count = n > 0 ? ((int)(a & 15u) + n * kEs + 15) >> 4 : 0;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int w = lane + 64 * k;
-            if (w < words)
-                v[k] = STREAM ? load16_stream(w0 + w) : load16(w0 + w);
+            if (w < r.count)
+                r.v[k] = STREAM ? load16_stream(w0 + w) : load16(w0 + w);
         }
+        return r;
+    }
+
+    __device__ __forceinline__ static void commit(const Words& r, u32x4* raw)
+    {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int w = lane + 64 * k;
-            if (w < words)
-                raw[w] = v[k];
+            if (w < r.count)
+                raw[w] = r.v[k];
         }
+    }
+
+    template <bool STREAM>
+    __device__ __forceinline__ static void load(const void* p, int n, u32x4* raw)
+    {
+        commit(fetch<STREAM>(p, n), raw);
     }
 
     __device__ __forceinline__ static float get(const u32x4* raw, int m, int i)
