@@ -61,10 +61,4 @@ __device__ __forceinline__ void store16_stream(u32x4* p, u32x4 v)
     __builtin_nontemporal_store(v, p);
 }
 
-// Wave-uniform value in a scalar register.
-__device__ __forceinline__ int wave_uniform(int v)
-{
-    return __builtin_amdgcn_readfirstlane(v);
-}
-
 }  // namespace rga

@@ -300,7 +300,8 @@ struct Grouped<kF32> {
     }
 };
 
-// Single elements, for the generic kernels (any D, element-aligned pointers).
+// Single elements: the trailing n % 8 elements of a flat pack stream, and the
+// narrowing of the span path (span.hpp).
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* base, int64_t i)
 {
@@ -310,19 +311,6 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t i)
         return (float)static_cast<const _Float16*>(base)[i];
     } else {
         return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ float load_elem_stream(const void* base, int64_t i)
-{
-    if constexpr (DT == kF32) {
-        return __builtin_nontemporal_load(static_cast<const float*>(base) + i);
-    } else if constexpr (DT == kF16) {
-        return (float)__builtin_nontemporal_load(static_cast<const _Float16*>(base) + i);
-    } else {
-        const uint16_t w = __builtin_nontemporal_load(static_cast<const uint16_t*>(base) + i);
-        return __uint_as_float((uint32_t)w << 16);
     }
 }
 
@@ -346,28 +334,6 @@ __device__ __forceinline__ void store_elem(void* base, int64_t i, float v)
         static_cast<float*>(base)[i] = v;
     else
         static_cast<uint16_t*>(base)[i] = (uint16_t)narrow_elem<DT>(v);
-}
-
-template <int DT>
-__device__ __forceinline__ void store_elem_stream(void* base, int64_t i, float v)
-{
-    if constexpr (DT == kF32)
-        __builtin_nontemporal_store(v, static_cast<float*>(base) + i);
-    else
-        __builtin_nontemporal_store((uint16_t)narrow_elem<DT>(v), static_cast<uint16_t*>(base) + i);
-}
-
-// binary32 value of v after one rounding to the storage type
-template <int DT>
-__device__ __forceinline__ float rounded(float v)
-{
-    if constexpr (DT == kF32) {
-        return v;
-    } else if constexpr (DT == kF16) {
-        return (float)(_Float16)v;
-    } else {
-        return __uint_as_float(pack_bf16(v, 0.0f) << 16);
-    }
 }
 
 }  // namespace rga
