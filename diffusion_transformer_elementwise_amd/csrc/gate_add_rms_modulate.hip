@@ -137,8 +137,9 @@ __device__ __forceinline__ void* elem_ptr(void* p, int64_t i)
 
 // Element path: one wave per row; grid x = row l, y = batch b. Spans of
 // kStage elements move through LDS with 16-byte accesses (span.hpp). Pass 1
-// forms x' for a span, stores it to x_out and, from its rounded value in
-// LDS, lane j adds up groups j, j + 64, ... of the span in the fixed order.
+// forms x' for a span, stores it to x_out and, from its rounded value put in
+// LDS at byte i * es (every group of 8 in whole 16-byte words), lane j adds
+// up groups j, j + 64, ... of the span in the fixed order.
 // Pass 2 re-reads x_out (written by other lanes of this wave: the barrier
 // between the passes orders those writes before the reads) and writes y.
 template <bool FULL, int DT, int MOD>
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
 {
     using S = Span<DT, kStage>;
     __shared__ u32x4 r0[S::kWords], r1[S::kWords], r2[S::kWords], r3[S::kWords];
+    __shared__ u32x4 ra[S::kWords];  // the rounded x' at byte i * es, for the sum
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
@@ -169,17 +171,22 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
         const int mx = S::offset(px), mu = S::offset(pu), mg = S::offset(pg), mo = S::offset(po);
         for (int i = lane; i < cnt; i += kBlock) {
             const float p = S::get(r1, mu, i) * S::get(r2, mg, i);
-            S::put(r3, mo, i, S::get(r0, mx, i) + p);
+            const float sum = S::get(r0, mx, i) + p;
+            S::put(r3, mo, i, sum);
+            S::put(ra, 0, i, sum);
         }
         __syncthreads();
         S::template store<true>(po, cnt, r3);
-#pragma unroll 1
+#pragma unroll
         for (int k = 0; k < kStage / 512; ++k) {
-            const int g0 = (lane + kBlock * k) * 8;
+            const int gi = lane + kBlock * k;
+            if (8 * gi >= cnt)
+                continue;
+            const Pack<DT> pk = S::group(ra, gi);  // the rounded x'
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (g0 + e < cnt) {
-                    const float a = S::get(r3, mo, g0 + e);  // the rounded x'
+                if (8 * gi + e < cnt) {
+                    const float a = pk.get(e);
                     const float sa = a * a;
                     acc = acc + sa;
                 }

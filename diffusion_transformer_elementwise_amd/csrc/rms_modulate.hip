@@ -197,9 +197,10 @@ __device__ __forceinline__ void* elem_ptr(void* p, int64_t i)
 
 // Element path, one wave per row. A sum in the fixed order walks the row in
 // stages of kStage elements: the wave moves a stage into LDS with 16-byte
-// accesses (Span in span.hpp), then lane j adds up groups j, j + 64, ... of
-// the stage from LDS. WHAT: 0 the values, 1 their squares, 2 the squares of
-// value - mu.
+// accesses, realigned so that every group of 8 starts a 16-byte word
+// (Span::commit_aligned in span.hpp), then lane j reads groups j, j + 64, ...
+// of the stage with 16-byte LDS reads and adds them up in order. WHAT: 0 the
+// values, 1 their squares, 2 the squares of value - mu.
 template <int DT, int WHAT>
 __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t D,
                                             float mu, u32x4* raw)
@@ -213,19 +214,22 @@ __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t 
     for (int64_t s0 = 0; s0 < D; s0 += kStage) {
         const int cnt = (D - s0 < kStage) ? (int)(D - s0) : kStage;
         const int m = S::offset(elem_ptr<DT>(x, row + s0));
-        S::commit(next, raw);
+        S::commit_aligned(next, m, cnt, raw);
         __syncthreads();
         const int64_t s1 = s0 + kStage;
         if (s1 < D)
             next = S::template fetch<false>(elem_ptr<DT>(x, row + s1),
                                             (D - s1 < kStage) ? (int)(D - s1) : kStage);
-#pragma unroll 1
+#pragma unroll
         for (int k = 0; k < kStage / 512; ++k) {
-            const int g0 = (lane + kBlock * k) * 8;
+            const int g = lane + kBlock * k;
+            if (8 * g >= cnt)
+                continue;
+            const Pack<DT> p = S::group(raw, g);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (g0 + e < cnt) {
-                    float a = S::get(raw, m, g0 + e);
+                if (8 * g + e < cnt) {
+                    float a = p.get(e);
                     if constexpr (WHAT == 0) {
                         acc = acc + a;
                     } else {

@@ -69,10 +69,76 @@ struct Span {
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int w = lane + 64 * k;
+            r.v[k] = u32x4{0, 0, 0, 0};
             if (w < r.count)
                 r.v[k] = STREAM ? load16_stream(w0 + w) : load16(w0 + w);
         }
         return r;
+    }
+
+    // Bytes Q*4 + sh .. of the 32-byte window (c, n), as one word.
+    template <int Q>
+    __device__ __forceinline__ static u32x4 cut(const u32x4& c, const u32x4& n, int sh)
+    {
+        const uint32_t w[8] = {c[0], c[1], c[2], c[3], n[0], n[1], n[2], n[3]};
+        u32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            o[d] = __builtin_amdgcn_alignbyte(w[Q + d + 1], w[Q + d], sh);
+        return o;
+    }
+
+    // Whole wave: write the span's words to LDS shifted so that element i
+    // sits at byte i * es, i.e. group g of 8 elements in word g (2-byte
+    // types) or words 2g, 2g + 1 (binary32), readable with aligned 16-byte
+    // LDS reads that touch every bank (the unshifted layout puts the groups
+    // of neighbouring lanes 16 bytes apart at one offset in their words: an
+    // 8-way bank conflict). m is the span's start offset (wave-uniform).
+    // Lane t's word w = t + 64k is joined with word w + 1, which lane t + 1
+    // holds (a DPP wave shift left by one lane) or, for lane 63, lane 0 in
+    // its next slot (a lane read into the shift's fill value). Bytes past
+    // the span's end are garbage and never read as elements.
+    __device__ __forceinline__ static void commit_aligned(const Words& r, int m, int n,
+                                                          u32x4* raw)
+    {
+        const int lane = threadIdx.x & 63;
+        const int na = (n * kEs + 15) >> 4;  // aligned words holding the span
+        const int sh = m & 3;
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            u32x4 nx;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int fill = (k + 1 < kPerLane)
+                                     ? __builtin_amdgcn_readlane((int)r.v[k + 1 < kPerLane ? k + 1 : k][d], 0)
+                                     : 0;
+                nx[d] = (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)r.v[k][d], 0x130, 0xF,
+                                                              0xF, false);
+            }
+            u32x4 o;
+            switch (m >> 2) {
+            case 0: o = cut<0>(r.v[k], nx, sh); break;
+            case 1: o = cut<1>(r.v[k], nx, sh); break;
+            case 2: o = cut<2>(r.v[k], nx, sh); break;
+            default: o = cut<3>(r.v[k], nx, sh); break;
+            }
+            const int w = lane + 64 * k;
+            if (w < na)
+                raw[w] = o;
+        }
+    }
+
+    // Group g (elements 8g .. 8g + 7) of a span committed with commit_aligned.
+    __device__ __forceinline__ static Pack<DT> group(const u32x4* raw, int g)
+    {
+        Pack<DT> p;
+        if constexpr (DT == kF32) {
+            p.a = raw[2 * g];
+            p.b = raw[2 * g + 1];
+        } else {
+            p.v = raw[g];
+        }
+        return p;
     }
 
     __device__ __forceinline__ static void commit(const Words& r, u32x4* raw)

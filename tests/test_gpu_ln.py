@@ -104,3 +104,25 @@ def test_video_scale_sampled_rows(dte):
         want = oracle.ln_modulate(xs, to_host_typed(s[b:b + 1]), to_host_typed(t[b:b + 1]),
                                   1e-6, ROW, BF16)
         _identical(to_host_typed(y[b:b + 1, rows]), want, BF16, f"video batch {b}")
+
+
+@pytest.mark.parametrize("D", [4096, 1003])
+def test_eps_zero_degenerate_rows(dte, D):
+    # eps = 0: an all-zero row has r = 1/sqrt(0) = inf and 0 * inf = NaN; a
+    # constant row (LayerNorm) the same. Both sides take IEEE's answer: NaN
+    # outputs match by class, everything else bit for bit. D = 1003 runs the
+    # element path, 4096 the pack path.
+    B, L = 1, 4
+    x = random_typed(13000 + D, (B, L, D), N02, BF16)
+    x[0, 0] = 0                                   # zero row
+    x[0, 1] = 0x3F80                              # constant 1.0 row
+    x[0, 2] = 0x8000                              # -0 row
+    s = random_typed(13001, (B, 1, D), N001, BF16)
+    t = random_typed(13002, (B, 1, D), N001, BF16)
+    say(f"[eps 0] D={D}")
+    for name, fn, ref in (
+            ("rms", dte.rga_rms_modulate_ex, lambda: oracle.rms_modulate_ex(x, s, t, 0.0, ROW, BF16)),
+            ("ln", dte.rga_ln_modulate, lambda: oracle.ln_modulate(x, s, t, 0.0, ROW, BF16))):
+        got = to_host_typed(fn(to_dev_typed(x, BF16), to_dev_typed(s, BF16), to_dev_typed(t, BF16),
+                               0.0))
+        _identical(got, ref(), BF16, f"eps 0 {name} D={D}")
