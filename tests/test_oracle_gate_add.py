@@ -276,10 +276,16 @@ def test_special_value_table():
 
 
 def test_subnormal_product_rounds_before_the_add():
-    # u*g = 2^-130 * (1 + 2^-7 + ...) is subnormal in binary32 and loses bits
-    # when rounded; a fused multiply-add would keep them. x = 2^-126 keeps the
-    # sum in range where the difference survives the bf16 rounding only
-    # through binary32 -> check against exact rationals element by element.
+    # u*g = -2^-132 * (1 + a/128)(1 + b/128) is subnormal in binary32 (exact
+    # there: its lowest bit, 2^-147, is above the subnormal quantum 2^-149)
+    # and x = 2^-126 puts the sum on the normal/subnormal boundary, where
+    # bf16 keeps bits of the product down to 2^-133: a product flushed to
+    # zero, or a sum on the wrong grid, shows. Checked against exact
+    # rationals element by element. (A fused multiply-add cannot show at a
+    # bf16 output: a product of two bf16 values has at most 16 significant
+    # bits, so only subnormal products round in binary32, and the bf16
+    # rounding of the sum never sees those bits; the build's probe pins the
+    # contraction instead.)
     vals = []
     for a in range(1, 128, 9):
         for b in range(1, 128, 11):

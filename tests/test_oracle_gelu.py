@@ -197,3 +197,47 @@ def test_exhaustive_cases_include_double_rounding_traps():
                 n += 1
         traps[dtype] = n
     assert traps[F16] >= 1, traps
+
+
+def _near_midpoint(y: np.ndarray, dtype: int, ulps: int = 2) -> np.ndarray:
+    """Mask of binary64 results whose nearest binary32 lies within `ulps`
+    binary32 ulps of a midpoint between two neighbours of the 2-byte format
+    (where a wrong last rounding step shows)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        f = y.astype(np.float32)
+        return _near_midpoint_bits(f, dtype, ulps)
+
+
+def _near_midpoint_bits(f: np.ndarray, dtype: int, ulps: int) -> np.ndarray:
+    w = f.view(np.uint32).astype(np.int64)
+    finite = np.isfinite(f)
+    if dtype == BF16:  # bf16 rounds binary32 at bit 16 at every magnitude
+        return finite & (np.abs((w & 0xFFFF) - 0x8000) <= ulps)
+    a = np.abs(f.astype(np.float64))
+    normal = finite & (a >= 2.0 ** -14) & (np.abs((w & 0x1FFF) - 0x1000) <= ulps)
+    # binary16 subnormals: midpoints are the odd multiples of 2^-25
+    r = a * 2.0 ** 25
+    k = np.rint(r)
+    ulp = np.spacing(np.abs(f)).astype(np.float64) * 2.0 ** 25
+    sub = finite & (a < 2.0 ** -14) & (k % 2 == 1) & (np.abs(r - k) <= ulps * ulp)
+    return normal | sub
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_results_near_midpoints_are_correctly_rounded(dtype):
+    # the inputs of the 2-byte format whose gelu lies next to a rounding
+    # midpoint of that format, chosen with numpy's float64 evaluation of the
+    # logistic form; the expected bits come from the tanh form at high
+    # precision
+    pats = np.arange(1 << 16, dtype=np.uint16)
+    vals = (pats.astype(np.uint32) << 16).view(np.float32) if dtype == BF16 \
+        else pats.view(np.float16).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = vals.astype(np.float64)
+        a = np.sqrt(2 / np.pi) * (h + 0.044715 * h ** 3)
+        y = h / (1.0 + np.exp(-2.0 * a))
+    pick = np.flatnonzero(_near_midpoint(y, dtype) & np.isfinite(h))
+    assert len(pick) >= (100 if dtype == BF16 else 20), len(pick)
+    got = oracle.gelu_tanh(pats[pick], dtype)
+    for j, i in enumerate(pick):
+        assert int(got[j]) == _exact_bits(float(vals[i]), dtype), (int(i), float(vals[i]))
