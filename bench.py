@@ -461,7 +461,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         log(f"variant {name}")
         out[name] = cold_and_warm(
             lambda: dte.rga_rms_modulate_ex(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
-            "rms_modulate_kernel" if fast else "rms_modulate_generic_kernel")
+            "rms_modulate_kernel" if fast else element_norm_kernel("rms", D, dt))
 
     def fused(name, B, L, D, dt, mode, mod):
         mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
@@ -478,6 +478,11 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
             lambda: dte.rga_gate_add_rms_modulate_ex(x, u, g, sc, sh, 1e-6, x_out=xo, y=y,
                                                      gate_mode=mode, mod_mode=mod),
             nbytes, "gate_add_rms_modulate_kernel")
+
+    def element_norm_kernel(norm, D, dt):
+        # 2-byte rows of up to 16 slots of 64 groups sit in registers
+        regs = dt != "f32" and -(-(-(-D // 8)) // 64) <= 16
+        return "modulate_regs_kernel" if regs else f"{norm}_modulate_generic_kernel"
 
     # the ideogram4 shape of the residual-gate page's table, bf16, its seeded case
     c = EXTRA_CASES["ideogram4"]
@@ -504,6 +509,10 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
          offset=1)
     rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
     rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
+    rms("bf16_rms_modulate_offset1_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW,
+        offset=1)
+    gate("f32_bcast_gate_add_offset1_[1,8160,4096]", 1, 8160, 4096, "f32", dte.GATE_BCAST,
+         offset=1)
     # LayerNorm modulation at the modulation shape
     def ln(name, B, L, D, dt, mod):
         mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
@@ -515,10 +524,11 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         log(f"variant {name}")
         out[name] = cold_and_warm(
             lambda: dte.rga_ln_modulate(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
-            "ln_modulate_kernel")
+            "ln_modulate_kernel" if D % 8 == 0 else element_norm_kernel("ln", D, dt))
 
     ln("bf16_ln_modulate_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW)
     ln("f16_ln_modulate_token_[2,32640,4096]", 2, 32640, 4096, "f16", dte.MOD_TOKEN)
+    ln("bf16_ln_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
 
     # tanh-GELU on the FFN intermediate (video tokens x 4 hidden)
     def gelu(name, rows, F, dt, with_bias=False):
@@ -530,12 +540,13 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         log(f"variant {name}")
         out[name] = cold_and_warm(lambda: dte.gelu_tanh(x, b, out=o), nbytes,
                                   ("gelu_tanh_bias_kernel" if with_bias else "gelu_tanh_flat_kernel")
-                                  if fast else "gelu_tanh_generic_kernel")
+                                  if fast else "gelu_tanh_generic_bias_kernel")
 
     gelu("bf16_gelu_tanh_[1,32640,16384]", 32640, 16384, "bf16")
     gelu("bf16_gelu_tanh_bias_[1,32640,16384]", 32640, 16384, "bf16", with_bias=True)
     gelu("f16_gelu_tanh_[1,32640,16384]", 32640, 16384, "f16")
     gelu("f32_gelu_tanh_[1,8160,16384]", 8160, 16384, "f32")
+    gelu("bf16_gelu_tanh_bias_ragged_[1,32640,16380]", 32640, 16380, "bf16", with_bias=True)
     torch.cuda.synchronize()
     return out
 

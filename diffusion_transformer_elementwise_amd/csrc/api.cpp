@@ -119,7 +119,7 @@ int check_gate_add(const void* x, const void* u, const void* g,
     // lane adds the trailing B*L*D % 8 elements)
     if (!strict && gate_mode == RGA_GATE_FULL)
         *fast = aligned16(x) && aligned16(u) && aligned16(g) && aligned16(out);
-    if (!rga::gate_add_grid_fits(B, L, D, gate_mode, *fast))
+    if (!rga::gate_add_grid_fits(B, L, D, gate_mode, es, *fast))
         return RGA_ERR_UNSUPPORTED;
 
     const bool full = gate_mode == RGA_GATE_FULL;
@@ -243,7 +243,7 @@ int check_gelu(const void* x, const void* bias, const void* out, int64_t rows,
     if (!aligned_to(x, es) || !aligned_to(out, es) || (bias && !aligned_to(bias, es)))
         return RGA_ERR_UNSUPPORTED;
     *fast = aligned16(x) && aligned16(out) && (!bias || (aligned16(bias) && F % 8 == 0));
-    if (!rga::gelu_tanh_grid_fits(rows, F, bias != nullptr, *fast))
+    if (!rga::gelu_tanh_grid_fits(rows, F, bias != nullptr, es, *fast))
         return RGA_ERR_UNSUPPORTED;
     const Range o = range_of(out, bytes);
     if (overlaps(o, range_of(x, bytes)) && out != x)

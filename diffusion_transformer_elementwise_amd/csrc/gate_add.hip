@@ -16,14 +16,15 @@
 // (Interleaved in dtype.hpp) for contiguous wave-wide accesses.
 //
 // Element path (any D, pointers aligned to the element size): the same
-// arithmetic on spans of elements staged through LDS with 16-byte accesses,
-// for shapes the pack path cannot take.
+// arithmetic over chunks of the output's aligned 16-byte words, every input
+// realigned to the output in registers (realign.hpp), for shapes the pack
+// path cannot take.
 //
 // Every thread reads its own elements before writing them and no element
 // depends on another, so out may alias x or u (and g in full mode).
 #include "dtype.hpp"
 #include "launch.hpp"
-#include "span.hpp"
+#include "realign.hpp"
 
 #include <rga.h>
 
@@ -31,7 +32,6 @@ namespace rga {
 namespace {
 
 constexpr int kBlock = 64;   // one wave per workgroup
-constexpr int kSpan = 512;   // element path: elements per workgroup
 
 template <int DT>
 __device__ __forceinline__ Pack<DT> gate_add8(const Pack<DT>& x,
@@ -100,26 +100,34 @@ __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
     I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
 }
 
-// Element path: each workgroup (one wave) takes a span of up to kSpan
-// elements and moves it through LDS with 16-byte accesses (Span in
-// span.hpp), so any element alignment and any D run at near pack speed.
-template <int DT, bool G_STREAM>
-__device__ __forceinline__ void gate_add_span(const void* x, const void* u, const void* g,
-                                              void* out, int cnt)
+template <int DT>
+__device__ __forceinline__ u32x4 gate_add_word(const u32x4& x, const u32x4& u, const u32x4& g)
 {
-    using S = Span<DT, kSpan>;
-    __shared__ u32x4 rx[S::kWords], ru[S::kWords], rg[S::kWords], ro[S::kWords];
-    S::template load<true>(x, cnt, rx);
-    S::template load<true>(u, cnt, ru);
-    S::template load<G_STREAM>(g, cnt, rg);
-    __syncthreads();
-    const int mx = S::offset(x), mu = S::offset(u), mg = S::offset(g), mo = S::offset(out);
-    for (int i = threadIdx.x; i < cnt; i += kBlock) {
-        const float p = S::get(ru, mu, i) * S::get(rg, mg, i);
-        S::put(ro, mo, i, S::get(rx, mx, i) + p);
+    using W = Word<DT>;
+    float o[W::kN];
+#pragma unroll
+    for (int e = 0; e < W::kN; ++e) {
+        const float p = W::get(u, e) * W::get(g, e);
+        o[e] = W::get(x, e) + p;
     }
-    __syncthreads();
-    S::template store<true>(out, cnt, ro);
+    return W::make(o);
+}
+
+// Element path (realign.hpp): a run of elements is cut into chunks of 64
+// 16-byte words of the output's aligned window, one chunk per workgroup;
+// each input is read realigned to the output's byte positions, so a lane
+// computes the elements of exactly one output word.
+template <int DT, bool G_STREAM>
+__device__ __forceinline__ void gate_add_chunk(const void* x, const void* u, const void* g,
+                                               void* out, int64_t nbytes, int64_t j)
+{
+    const int mo = start_offset(out);
+    if (64 * j >= window_words(out, nbytes))
+        return;
+    const u32x4 xv = load_for_chunk<true>(x, nbytes, mo, j);
+    const u32x4 uv = load_for_chunk<true>(u, nbytes, mo, j);
+    const u32x4 gv = load_for_chunk<G_STREAM>(g, nbytes, mo, j);
+    store_chunk<true>(out, nbytes, j, gate_add_word<DT>(xv, uv, gv));
 }
 
 template <int DT>
@@ -134,54 +142,54 @@ __device__ __forceinline__ void* elem_ptr(void* p, int64_t i)
     return static_cast<char*>(p) + i * (DT == kF32 ? 4 : 2);
 }
 
-// Full gate: spans tile the flat B*L*D elements; grid x = span.
+// Full gate: the flat B*L*D elements are one run; grid x = chunk.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_generic_full_kernel(
-    const void* x, const void* u, const void* g, void* out, int64_t n)
+    const void* x, const void* u, const void* g, void* out, int64_t nbytes)
 {
-    const int64_t e0 = (int64_t)blockIdx.x * kSpan;
-    const int cnt = (n - e0 < kSpan) ? (int)(n - e0) : kSpan;
-    gate_add_span<DT, true>(elem_ptr<DT>(x, e0), elem_ptr<DT>(u, e0), elem_ptr<DT>(g, e0),
-                            elem_ptr<DT>(out, e0), cnt);
+    gate_add_chunk<DT, true>(x, u, g, out, nbytes, blockIdx.x);
 }
 
-// Broadcast gate: spans tile each row; grid x = (row l) * spans per row +
-// span, y = batch b; the gate span is the same columns of g's row b.
+// Broadcast gate: each row is a run, with row b of g as its gate run; grid
+// x = (row l) * chunks per row + chunk, y = batch b.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_generic_bcast_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t L,
-    int64_t D, uint32_t spans)
+    int64_t D, uint32_t chunks)
 {
-    const uint32_t l = blockIdx.x / spans;
-    const uint32_t sp = blockIdx.x - l * spans;
+    const uint32_t l = blockIdx.x / chunks;
+    const uint32_t j = blockIdx.x - l * chunks;
     const int64_t b = blockIdx.y;
-    const int64_t d0 = (int64_t)sp * kSpan;
-    const int cnt = (D - d0 < kSpan) ? (int)(D - d0) : kSpan;
-    const int64_t e0 = (b * L + l) * D + d0;
-    gate_add_span<DT, false>(elem_ptr<DT>(x, e0), elem_ptr<DT>(u, e0),
-                             elem_ptr<DT>(g, b * D + d0), elem_ptr<DT>(out, e0), cnt);
+    const int64_t e0 = (b * L + l) * D;
+    gate_add_chunk<DT, false>(elem_ptr<DT>(x, e0), elem_ptr<DT>(u, e0), elem_ptr<DT>(g, b * D),
+                              elem_ptr<DT>(out, e0), D * (DT == kF32 ? 4 : 2), j);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Chunks of 64 output words that cover a run of nbytes at any start offset
+// (at most 14 bytes into its first word).
+int64_t element_chunks(int64_t nbytes) { return ceil_div(ceil_div(14 + nbytes, 16), 64); }
 
 template <int DT>
 hipError_t launch_typed(const void* x, const void* u, const void* g,
                         void* out, int64_t B, int64_t L, int64_t D,
                         int gate_mode, bool fast, hipStream_t stream)
 {
+    constexpr int es = DT == kF32 ? 4 : 2;
     if (!fast) {
         if (gate_mode == RGA_GATE_FULL) {
-            int64_t n = B * L * D;
-            void* args[] = {&x, &u, &g, &out, &n};
+            int64_t nbytes = B * L * D * es;
+            void* args[] = {&x, &u, &g, &out, &nbytes};
             return hipLaunchKernel(
                 reinterpret_cast<const void*>(&gate_add_generic_full_kernel<DT>),
-                dim3((uint32_t)ceil_div(n, kSpan)), dim3(kBlock), args, 0, stream);
+                dim3((uint32_t)element_chunks(nbytes)), dim3(kBlock), args, 0, stream);
         }
-        uint32_t spans = (uint32_t)ceil_div(D, kSpan);
-        void* args[] = {&x, &u, &g, &out, &L, &D, &spans};
+        uint32_t chunks = (uint32_t)element_chunks(D * es);
+        void* args[] = {&x, &u, &g, &out, &L, &D, &chunks};
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_generic_bcast_kernel<DT>),
-            dim3((uint32_t)(L * spans), (uint32_t)B), dim3(kBlock), args, 0, stream);
+            dim3((uint32_t)(L * chunks), (uint32_t)B), dim3(kBlock), args, 0, stream);
     }
     if (gate_mode == RGA_GATE_FULL) {
         const int64_t n = B * L * D;
@@ -206,17 +214,17 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
 
 // AMD dispatch packets carry the grid size in work-items per dimension as
 // 32-bit numbers; HIP grids stop at 65535 workgroups in y.
-bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode,
+bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode, int es,
                         bool fast)
 {
     const int64_t max_wg = (((int64_t)1 << 32) - 1) / kBlock;
     if (gate_mode == RGA_GATE_FULL)  // one flat grid dimension, B plays no part
         return fast ? ceil_div(B * L * D / 8 + 1, kBlock) <= max_wg
-                    : ceil_div(B * L * D, kSpan) <= max_wg;
+                    : element_chunks(B * L * D * es) <= max_wg;
     if (B > 65535)  // grid y
         return false;
     return fast ? L * ceil_div(D / 8, kBlock) <= max_wg
-                : L * ceil_div(D, kSpan) <= max_wg;
+                : L * element_chunks(D * es) <= max_wg;
 }
 
 hipError_t launch_gate_add(const void* x, const void* u, const void* g,

@@ -33,10 +33,11 @@
 // one wave per workgroup, one 8-element pack per lane, nontemporal loads and
 // stores; without a bias the tensor is one flat stream (the last lane adds
 // the trailing rows*F % 8 elements), with a bias rows are cut into chunks of
-// up to 64 packs; other layouts move spans of elements through LDS.
+// up to 64 packs; other layouts run over chunks of the output's aligned
+// 16-byte words with the inputs realigned in registers (realign.hpp).
 #include "dtype.hpp"
 #include "launch.hpp"
-#include "span.hpp"
+#include "realign.hpp"
 
 #include <rga.h>
 
@@ -44,7 +45,6 @@ namespace rga {
 namespace {
 
 constexpr int kBlock = 64;
-constexpr int kSpan = 512;  // element path: elements per workgroup
 
 // tl = t log2(e) = h (kC1 + kC2 h^2), t = 2 sqrt(2/pi) (h + 0.044715 h^3);
 // constants rounded to nearest binary32
@@ -159,39 +159,72 @@ __global__ __launch_bounds__(kBlock) void gelu_tanh_bias_kernel(
     I::store_stream(gelu8<DT, true>(xv, bv), out, c0, t, h);
 }
 
-// Element path: grid x = row * spans + span; a span of up to kSpan elements
-// of a row (and the same columns of the bias) moves through LDS with 16-byte
-// accesses (span.hpp).
+// gelu8 for one 16-byte word of any storage type (8 or 4 elements).
 template <int DT, bool BIAS>
-__global__ __launch_bounds__(kBlock) void gelu_tanh_generic_kernel(
-    const void* x, const void* bias, void* out, int64_t F, uint32_t spans)
+__device__ __forceinline__ u32x4 gelu_word(const u32x4& x, const u32x4& b)
 {
-    using S = Span<DT, kSpan>;
-    __shared__ u32x4 rx[S::kWords], rb[S::kWords], ro[S::kWords];
-    constexpr int es = DT == kF32 ? 4 : 2;
-    const uint32_t r = blockIdx.x / spans;
-    const uint32_t sp = blockIdx.x - r * spans;
-    const int64_t d0 = (int64_t)sp * kSpan;
-    const int cnt = (F - d0 < kSpan) ? (int)(F - d0) : kSpan;
-    const void* px = static_cast<const char*>(x) + ((int64_t)r * F + d0) * es;
-    const void* pb = BIAS ? static_cast<const char*>(bias) + d0 * es : nullptr;
-    void* po = static_cast<char*>(out) + ((int64_t)r * F + d0) * es;
-    S::template load<true>(px, cnt, rx);
-    if constexpr (BIAS)
-        S::template load<false>(pb, cnt, rb);
-    __syncthreads();
-    const int mx = S::offset(px), mb = BIAS ? S::offset(pb) : 0, mo = S::offset(po);
-    for (int i = threadIdx.x; i < cnt; i += kBlock) {
-        float h = S::get(rx, mx, i);
+    using W = Word<DT>;
+    float h[W::kN], tl[W::kN], o[W::kN];
+    bool tiny = false;
+#pragma unroll
+    for (int e = 0; e < W::kN; ++e) {
+        h[e] = W::get(x, e);
         if constexpr (BIAS)
-            h = h + S::get(rb, mb, i);
-        S::put(ro, mo, i, gelu1(h));
+            h[e] = h[e] + W::get(b, e);
+        tl[e] = exp_arg(h[e]);
+        tiny = tiny || (tl[e] < kTinyExp);
     }
-    __syncthreads();
-    S::template store<true>(po, cnt, ro);
+    if (__any(tiny)) {
+#pragma unroll
+        for (int e = 0; e < W::kN; ++e)
+            o[e] = gelu_general(h[e], tl[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < W::kN; ++e)
+            o[e] = gelu_common(h[e], tl[e]);
+    }
+    return W::make(o);
+}
+
+// Element path (realign.hpp): chunks of 64 16-byte words of the output's
+// aligned window, the input (and bias) read realigned to the output.
+// Without a bias the rows * F elements are one run, grid x = chunk.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gelu_tanh_generic_flat_kernel(
+    const void* x, void* out, int64_t nbytes)
+{
+    const int64_t j = blockIdx.x;
+    const int mo = start_offset(out);
+    if (64 * j >= window_words(out, nbytes))
+        return;
+    const u32x4 xv = load_for_chunk<true>(x, nbytes, mo, j);
+    store_chunk<true>(out, nbytes, j, gelu_word<DT, false>(xv, xv));
+}
+
+// With a bias each row is a run, with the bias row beside it; grid x =
+// row * chunks per row + chunk.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gelu_tanh_generic_bias_kernel(
+    const void* x, const void* bias, void* out, int64_t F, uint32_t chunks)
+{
+    constexpr int es = DT == kF32 ? 4 : 2;
+    const uint32_t r = blockIdx.x / chunks;
+    const int64_t j = blockIdx.x - r * chunks;
+    const int64_t nbytes = F * es;
+    const void* px = static_cast<const char*>(x) + (int64_t)r * nbytes;
+    void* po = static_cast<char*>(out) + (int64_t)r * nbytes;
+    const int mo = start_offset(po);
+    if (64 * j >= window_words(po, nbytes))
+        return;
+    const u32x4 xv = load_for_chunk<true>(px, nbytes, mo, j);
+    const u32x4 bv = load_for_chunk<false>(bias, nbytes, mo, j);
+    store_chunk<true>(po, nbytes, j, gelu_word<DT, true>(xv, bv));
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Chunks of 64 output words that cover a run of nbytes at any start offset.
+int64_t element_chunks(int64_t nbytes) { return ceil_div(ceil_div(14 + nbytes, 16), 64); }
 
 template <int DT>
 hipError_t launch_typed(const void* x, const void* bias, void* out, int64_t rows, int64_t F,
@@ -213,23 +246,32 @@ hipError_t launch_typed(const void* x, const void* bias, void* out, int64_t rows
         return hipLaunchKernel(reinterpret_cast<const void*>(&gelu_tanh_bias_kernel<DT>),
                                dim3((uint32_t)(rows * chunks)), dim3(kBlock), args, 0, stream);
     }
-    uint32_t spans = (uint32_t)ceil_div(F, kSpan);
-    void* args[] = {&x, &bias, &out, &F, &spans};
-    const void* k = bias ? reinterpret_cast<const void*>(&gelu_tanh_generic_kernel<DT, true>)
-                         : reinterpret_cast<const void*>(&gelu_tanh_generic_kernel<DT, false>);
-    return hipLaunchKernel(k, dim3((uint32_t)(rows * spans)), dim3(kBlock), args, 0, stream);
+    constexpr int es = DT == kF32 ? 4 : 2;
+    if (bias == nullptr) {
+        int64_t nbytes = rows * F * es;
+        void* args[] = {&x, &out, &nbytes};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&gelu_tanh_generic_flat_kernel<DT>),
+                               dim3((uint32_t)element_chunks(nbytes)), dim3(kBlock), args, 0,
+                               stream);
+    }
+    uint32_t chunks = (uint32_t)element_chunks(F * es);
+    void* args[] = {&x, &bias, &out, &F, &chunks};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gelu_tanh_generic_bias_kernel<DT>),
+                           dim3((uint32_t)(rows * chunks)), dim3(kBlock), args, 0, stream);
 }
 
 }  // namespace
 
-bool gelu_tanh_grid_fits(int64_t rows, int64_t F, bool has_bias, bool fast)
+bool gelu_tanh_grid_fits(int64_t rows, int64_t F, bool has_bias, int es, bool fast)
 {
     const int64_t max_wg = (((int64_t)1 << 32) - 1) / kBlock;
     if (fast && !has_bias)
         return ceil_div(rows * F / 8 + 1, kBlock) <= max_wg;
     if (fast)
         return rows * ceil_div(F / 8, kBlock) <= max_wg;
-    return rows * ceil_div(F, kSpan) <= max_wg;
+    if (!has_bias)
+        return element_chunks(rows * F * es) <= max_wg;
+    return rows * element_chunks(F * es) <= max_wg;
 }
 
 hipError_t launch_gelu_tanh(const void* x, const void* bias, void* out, int64_t rows,

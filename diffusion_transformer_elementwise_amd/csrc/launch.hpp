@@ -12,7 +12,7 @@
 namespace rga {
 
 // gated residual add (gate_add.hip)
-bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode,
+bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode, int es,
                         bool fast);
 hipError_t launch_gate_add(const void* x, const void* u, const void* g,
                            void* out, int64_t B, int64_t L, int64_t D,
@@ -45,7 +45,7 @@ hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
 
 // tanh-GELU over [rows, F] with an optional bias row (gelu_tanh.hip); fast:
 // every pointer 16-byte aligned and, with a bias, F % 8 == 0
-bool gelu_tanh_grid_fits(int64_t rows, int64_t F, bool has_bias, bool fast);
+bool gelu_tanh_grid_fits(int64_t rows, int64_t F, bool has_bias, int es, bool fast);
 hipError_t launch_gelu_tanh(const void* x, const void* bias, void* out,
                             int64_t rows, int64_t F, int dtype, bool fast,
                             hipStream_t stream);

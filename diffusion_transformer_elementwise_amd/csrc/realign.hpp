@@ -1,0 +1,298 @@
+// Runs of 2-byte elements at any element alignment, realigned in registers.
+//
+// A run of n elements starting at address p (start offset m = p mod 16) is
+// read as the aligned 16-byte words that hold its bytes: lane t, slot k
+// holds word t + 64k of that window (one contiguous wave-wide access per
+// slot); word 64K, which only a run of exactly 64K groups can reach with
+// m > 0, is held by every lane. realign_in then turns the words into
+// groups: lane t, slot k holds elements 8(t + 64k) .. 8(t + 64k) + 7 of the
+// run, by joining its word with the next one (which lane t + 1 holds: a DPP
+// wave shift left by one lane, lane 63 taking lane 0 of the next slot) and
+// cutting 16 bytes at offset m (alignbyte). store_run does the reverse for
+// an output at its own start offset: word w of the output window joins
+// groups w - 1 (a DPP wave shift right) and w, interior words go out with
+// 16-byte stores and the two partial edge words element by element, so no
+// byte outside the run is written.
+//
+// Every word read holds at least one byte of the run, so it lies in memory
+// the caller owns pages of; the other bytes are read and ignored. Groups
+// past the run's end hold garbage that callers neither store nor sum.
+//
+// Every function is called by the whole wave with wave-uniform arguments.
+#pragma once
+
+#include "dtype.hpp"
+
+namespace rga {
+
+// One of four values by a wave-uniform index (q1, q2 its bits), as selects
+// on values: indexing a local array with a select would put the array in
+// scratch memory.
+__device__ __forceinline__ uint32_t pick4(bool q1, bool q2, uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3)
+{
+    const uint32_t lo = q1 ? a1 : a0;
+    const uint32_t hi = q1 ? a3 : a2;
+    return q2 ? hi : lo;
+}
+
+// Bytes o .. o + 15 of the 32-byte window (c, n), 0 <= o < 16, o
+// wave-uniform: the dword shift o >> 2 picks dwords with selects on a
+// uniform condition (no branches), then alignbyte shifts by o & 3 bytes.
+__device__ __forceinline__ u32x4 window_at(const u32x4& c, const u32x4& n, int o)
+{
+    const bool q1 = (o & 4) != 0, q2 = (o & 8) != 0;
+    const int sh = o & 3;
+    const uint32_t s0 = pick4(q1, q2, c[0], c[1], c[2], c[3]);
+    const uint32_t s1 = pick4(q1, q2, c[1], c[2], c[3], n[0]);
+    const uint32_t s2 = pick4(q1, q2, c[2], c[3], n[0], n[1]);
+    const uint32_t s3 = pick4(q1, q2, c[3], n[0], n[1], n[2]);
+    const uint32_t s4 = pick4(q1, q2, n[0], n[1], n[2], n[3]);
+    return u32x4{__builtin_amdgcn_alignbyte(s1, s0, sh), __builtin_amdgcn_alignbyte(s2, s1, sh),
+                 __builtin_amdgcn_alignbyte(s3, s2, sh), __builtin_amdgcn_alignbyte(s4, s3, sh)};
+}
+
+// DPP wave shifts by one lane; a lane with no source keeps `fill`.
+__device__ __forceinline__ u32x4 lane_from_next(const u32x4& v, const u32x4& fill)
+{
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        o[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)fill[d], (int)v[d], 0x130 /* wave_shl1 */,
+                                                     0xF, 0xF, false);
+    return o;
+}
+
+__device__ __forceinline__ u32x4 lane_from_prev(const u32x4& v, const u32x4& fill)
+{
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        o[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)fill[d], (int)v[d], 0x138 /* wave_shr1 */,
+                                                     0xF, 0xF, false);
+    return o;
+}
+
+__device__ __forceinline__ u32x4 read_lane(const u32x4& v, int lane)
+{
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        o[d] = (uint32_t)__builtin_amdgcn_readlane((int)v[d], lane);
+    return o;
+}
+
+__device__ __forceinline__ int start_offset(const void* p)
+{
+    return (int)(reinterpret_cast<uintptr_t>(p) & 15u);
+}
+
+// The 16-byte word holding p's first byte. Derived from p by pointer
+// arithmetic (not through an integer) so the compiler keeps the global
+// address space and emits global rather than flat accesses.
+__device__ __forceinline__ const u32x4* aligned_down(const void* p)
+{
+    return reinterpret_cast<const u32x4*>(static_cast<const char*>(p) - start_offset(p));
+}
+
+__device__ __forceinline__ u32x4* aligned_down(void* p)
+{
+    return reinterpret_cast<u32x4*>(static_cast<char*>(p) - start_offset(p));
+}
+
+// Words of a run of n >= 1 2-byte elements at p into w[0..K) and extra.
+template <int K, bool STREAM>
+__device__ __forceinline__ void load_run(const void* p, int n, u32x4 (&w)[K], u32x4& extra)
+{
+    const int lane = threadIdx.x & 63;
+    const int m = start_offset(p);
+    const u32x4* w0 = aligned_down(p);
+    const int count = (m + 2 * n + 15) >> 4;  // n >= 1
+    // lanes past the window re-read its last word (an index clamp rather
+    // than a branch, which would wait for each load before the next): those
+    // values only reach elements past the run, never summed nor stored
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = lane + 64 * k;
+        const int ic = i < count ? i : count - 1;
+        w[k] = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
+    }
+    extra = load16(w0 + (count > 64 * K ? 64 * K : count - 1));
+}
+
+// Words -> groups, in place (m = the run's start offset).
+template <int K>
+__device__ __forceinline__ void realign_in(u32x4 (&w)[K], const u32x4& extra, int m)
+{
+    if (m == 0)
+        return;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const u32x4 fill = (k + 1 < K) ? read_lane(w[k + 1 < K ? k + 1 : k], 0) : extra;
+        w[k] = window_at(w[k], lane_from_next(w[k], fill), m);
+    }
+}
+
+template <int K, bool STREAM>
+__device__ __forceinline__ void load_groups(const void* p, int n, u32x4 (&g)[K])
+{
+    u32x4 extra;
+    load_run<K, STREAM>(p, n, g, extra);
+    realign_in<K>(g, extra, start_offset(p));
+}
+
+// The bytes of output word i inside the run [mo, end) of the window at
+// w0, as 2-byte stores (every element size here is a multiple of 2 and
+// every run boundary a multiple of the element size).
+__device__ __forceinline__ void put_partial(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
+                                            int64_t end)
+{
+    const int64_t lo = 16 * i;
+    unsigned char* gb = reinterpret_cast<unsigned char*>(w0);
+    const int b0 = (int)((lo > mo ? lo : mo) - lo);
+    const int b1 = (int)((lo + 16 < end ? lo + 16 : end) - lo);
+    for (int j = b0; j < b1; j += 2) {
+        const uint32_t dw = j < 8 ? (j < 4 ? v[0] : v[1]) : (j < 12 ? v[2] : v[3]);
+        *reinterpret_cast<uint16_t*>(gb + lo + j) = (uint16_t)(dw >> (8 * (j & 2)));
+    }
+}
+
+// Output word i of the run [mo, end): one 16-byte store when it lies wholly
+// inside the run, else its bytes inside the run.
+template <bool STREAM>
+__device__ __forceinline__ void put_word(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
+                                         int64_t end)
+{
+    const int64_t lo = 16 * i;
+    if (lo >= end)
+        return;
+    if (lo >= mo && lo + 16 <= end) {
+        if (STREAM)
+            store16_stream(w0 + i, v);
+        else
+            w0[i] = v;
+        return;
+    }
+    put_partial(w0, i, v, mo, end);
+}
+
+// Groups -> the n elements of a run at p: output word w joins groups w - 1
+// and w (cut at 16 - mo). Whole words are stored in the slot loop; the
+// run's first word (when mo > 0) and last word (when the run does not end
+// on a word boundary) are the only partial ones and are written after it.
+template <int K, bool STREAM>
+__device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K])
+{
+    if (n <= 0)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int mo = start_offset(p);
+    u32x4* w0 = aligned_down(p);
+    const int end = mo + 2 * n;
+    const int words = (end + 15) >> 4;
+    u32x4 fill = u32x4{0, 0, 0, 0};
+    u32x4 first = u32x4{0, 0, 0, 0}, last = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const u32x4 v = mo == 0 ? g[k] : window_at(lane_from_prev(g[k], fill), g[k], 16 - mo);
+        fill = read_lane(g[k], 63);
+        const int w = lane + 64 * k;
+        if (16 * w >= mo && 16 * w + 16 <= end) {
+            if (STREAM)
+                store16_stream(w0 + w, v);
+            else
+                w0[w] = v;
+        }
+        if (k == 0)
+            first = v;
+        if (w == words - 1)
+            last = v;
+    }
+    // word 64K (only reached when mo > 0): the tail of group 64K - 1
+    if (words - 1 == 64 * K)
+        last = window_at(fill, u32x4{0, 0, 0, 0}, 16 - mo);
+    const int wl = words - 1;
+    const bool last_partial = (end & 15) != 0;
+    if (lane == 0 && mo != 0)
+        put_partial(w0, 0, first, mo, end);
+    if (last_partial && lane == (wl & 63) && !(wl == 0 && mo != 0))
+        put_partial(w0, wl, last, mo, end);
+}
+
+// ---- Output-aligned chunks -----------------------------------------------
+//
+// An element-wise result over a run of nbytes bytes written at po is cut
+// into chunks of 64 words of po's aligned window: lane t of chunk j owns
+// output word 64j + t. Only the window's first and last words can be
+// partial, so only they are written element by element, every other word
+// is one 16-byte store, and no two waves write the same word. An input run
+// at its own start offset mi is read so that each lane gets the input bytes
+// that line up with its output word: for d = mi - mo, output bytes
+// [16w - mo, 16w - mo + 16) of the run are input window bytes
+// [16w + d, 16w + d + 16), i.e. words w + floor(d / 16) and the next one
+// (a DPP shift brings the next lane's word; lane 63 takes one more word
+// loaded by every lane), cut at d mod 16. Indexes outside the input's
+// window are clamped to its first or last word; the bytes they supply fall
+// outside the run.
+// The same byte-level realignment serves every element size.
+
+__device__ __forceinline__ int64_t window_words(const void* p, int64_t nbytes)
+{
+    return nbytes > 0 ? (start_offset(p) + nbytes + 15) >> 4 : 0;
+}
+
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load_for_chunk(const void* p, int64_t nbytes, int mo, int64_t j)
+{
+    const int lane = threadIdx.x & 63;
+    const int mi = start_offset(p);
+    const u32x4* w0 = aligned_down(p);
+    const int64_t count = window_words(p, nbytes);
+    const int d = mi - mo;
+    const int64_t q0 = 64 * j + (d < 0 ? -1 : 0);
+    const int sh = d < 0 ? d + 16 : d;
+    // indexes clamped into the input's window (no branch around the loads);
+    // a clamped word only supplies bytes outside the run
+    const int64_t i = q0 + lane;
+    const int64_t ic = i < 0 ? 0 : (i < count ? i : count - 1);
+    const u32x4 cur = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
+    if (sh == 0)
+        return cur;
+    const int64_t ie = q0 + 64;
+    const u32x4 extra = load16(w0 + (ie < 0 ? 0 : (ie < count ? ie : count - 1)));
+    return window_at(cur, lane_from_next(cur, extra), sh);
+}
+
+template <bool STREAM>
+__device__ __forceinline__ void store_chunk(void* p, int64_t nbytes, int64_t j, const u32x4& v)
+{
+    const int lane = threadIdx.x & 63;
+    const int mo = start_offset(p);
+    put_word<STREAM>(aligned_down(p), 64 * j + lane, v, mo, mo + nbytes);
+}
+
+// Elements of a 16-byte word: 8 of a 2-byte type, 4 binary32.
+template <int DT>
+struct Word {
+    static constexpr int kN = DT == kF32 ? 4 : 8;
+    __device__ __forceinline__ static float get(const u32x4& w, int e)
+    {
+        if constexpr (DT == kF32) {
+            return __uint_as_float(w[e]);
+        } else {
+            Pack<DT> p;
+            p.v = w;
+            return p.get(e);
+        }
+    }
+    __device__ __forceinline__ static u32x4 make(const float* f)
+    {
+        if constexpr (DT == kF32)
+            return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                         __float_as_uint(f[3])};
+        else
+            return Pack<DT>::make(f).v;
+    }
+};
+
+}  // namespace rga

@@ -24,6 +24,7 @@
 #pragma once
 
 #include "dtype.hpp"
+#include "realign.hpp"
 
 namespace rga {
 
@@ -62,10 +63,9 @@ struct Span {
     __device__ __forceinline__ static Words fetch(const void* p, int n)
     {
         const int lane = threadIdx.x & 63;
-        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-        const u32x4* w0 = reinterpret_cast<const u32x4*>(a & ~(uintptr_t)15);
+        const u32x4* w0 = aligned_down(p);
         Words r;
-        r.count = n > 0 ? ((int)(a & 15u) + n * kEs + 15) >> 4 : 0;
+        r.count = n > 0 ? (start_offset(p) + n * kEs + 15) >> 4 : 0;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int w = lane + 64 * k;
@@ -74,18 +74,6 @@ struct Span {
                 r.v[k] = STREAM ? load16_stream(w0 + w) : load16(w0 + w);
         }
         return r;
-    }
-
-    // Bytes Q*4 + sh .. of the 32-byte window (c, n), as one word.
-    template <int Q>
-    __device__ __forceinline__ static u32x4 cut(const u32x4& c, const u32x4& n, int sh)
-    {
-        const uint32_t w[8] = {c[0], c[1], c[2], c[3], n[0], n[1], n[2], n[3]};
-        u32x4 o;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-            o[d] = __builtin_amdgcn_alignbyte(w[Q + d + 1], w[Q + d], sh);
-        return o;
     }
 
     // Whole wave: write the span's words to LDS shifted so that element i
@@ -103,25 +91,12 @@ struct Span {
     {
         const int lane = threadIdx.x & 63;
         const int na = (n * kEs + 15) >> 4;  // aligned words holding the span
-        const int sh = m & 3;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
-            u32x4 nx;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const int fill = (k + 1 < kPerLane)
-                                     ? __builtin_amdgcn_readlane((int)r.v[k + 1 < kPerLane ? k + 1 : k][d], 0)
-                                     : 0;
-                nx[d] = (uint32_t)__builtin_amdgcn_update_dpp(fill, (int)r.v[k][d], 0x130, 0xF,
-                                                              0xF, false);
-            }
-            u32x4 o;
-            switch (m >> 2) {
-            case 0: o = cut<0>(r.v[k], nx, sh); break;
-            case 1: o = cut<1>(r.v[k], nx, sh); break;
-            case 2: o = cut<2>(r.v[k], nx, sh); break;
-            default: o = cut<3>(r.v[k], nx, sh); break;
-            }
+            const u32x4 fill = (k + 1 < kPerLane) ? read_lane(r.v[k + 1 < kPerLane ? k + 1 : k], 0)
+                                                  : u32x4{0, 0, 0, 0};
+            const u32x4 nx = lane_from_next(r.v[k], fill);
+            const u32x4 o = window_at(r.v[k], nx, m);
             const int w = lane + 64 * k;
             if (w < na)
                 raw[w] = o;
@@ -180,9 +155,8 @@ struct Span {
     __device__ __forceinline__ static void store(void* p, int n, const u32x4* raw)
     {
         const int lane = threadIdx.x & 63;
-        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-        u32x4* w0 = reinterpret_cast<u32x4*>(a & ~(uintptr_t)15);
-        const int m = (int)(a & 15u);
+        u32x4* w0 = aligned_down(p);
+        const int m = start_offset(p);
         const int end = m + n * kEs;  // span bytes [m, end) of the raw buffer
         const int words = n > 0 ? (end + 15) >> 4 : 0;
 #pragma unroll

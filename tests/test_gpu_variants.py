@@ -15,6 +15,7 @@ import torch
 import oracle
 from synth_inputs import (BF16, EXTRA_CASES, F16, F32, GATE_BCAST, GATE_FULL, N001, N01, N02,
                           U11, make_inputs, random_typed)
+from tests.test_gpu_gelu import _check as gelu_check, _values as gelu_inputs
 from tests.gpu_util import (first_mismatch_typed, same_bits_typed, say, to_dev, to_dev_typed,
                             to_host, to_host_typed, ulp_diff_typed)
 
@@ -128,6 +129,58 @@ def test_element_offsets(dte, D, dtype):
     dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6, x_out=xo, y=yo)
     _bit_exact(to_host_typed(xo), wx, dtype, "fused x_out")
     _zero_ulp(to_host_typed(yo), wy, dtype, "fused y")
+
+
+def _empty_at(shape, like, offset):
+    n = int(np.prod(shape))
+    return torch.empty(n + offset, dtype=like.dtype, device=like.device)[offset:].view(shape)
+
+
+# each entry of the element path's slot ladder (ceil(ceil(D / 8) / 64) slots
+# of 8-element groups per lane: 1, 2, 4, 6, 8, 9, 12, 16) and rows past it
+MIXED_D = [1, 100, 1000, 1500, 2500, 4000, 4500, 6000, 8191, 8193]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=NAMES.get)
+@pytest.mark.parametrize("D", MIXED_D)
+def test_mixed_offsets(dte, D, dtype):
+    # every operand at its own element offset (so the realignment into and
+    # out of registers differs per operand), outputs too
+    B, L = 2, 6
+    say(f"[mixed offsets] {NAMES[dtype]} B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(5000 + D, B, L, D, GATE_BCAST, dtype)
+    s, t = _mod_inputs(5100 + D, B, L, D, MOD_ROW, dtype)
+    ts, tt = _mod_inputs(5200 + D, B, L, D, MOD_TOKEN, dtype)
+    dx, du, dg = to_dev_typed(x, dtype, 1), to_dev_typed(u, dtype, 2), to_dev_typed(g, dtype, 3)
+    ds, dt = to_dev_typed(s, dtype, 5), to_dev_typed(t, dtype, 6)
+    dts, dtt = to_dev_typed(ts, dtype, 7), to_dev_typed(tt, dtype, 3)
+    for off in (0, 5):
+        out = _empty_at((B, L, D), dx, off)
+        dte.rga_residual_gate_add_ex(dx, du, dg, out=out)
+        _bit_exact(to_host_typed(out), oracle.gate_add_ex(x, u, g, GATE_BCAST, dtype), dtype,
+                   f"gate bcast out+{off}")
+        gf = random_typed(5300 + D, (B, L, D), U11, dtype)
+        dte.rga_residual_gate_add_ex(dx, du, to_dev_typed(gf, dtype, 4), out=out,
+                                     gate_mode=GATE_FULL)
+        _bit_exact(to_host_typed(out), oracle.gate_add_ex(x, u, gf, GATE_FULL, dtype), dtype,
+                   f"gate full out+{off}")
+        dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6, out=out)
+        _zero_ulp(to_host_typed(out), oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_ROW, dtype),
+                  dtype, f"rms row out+{off}")
+        dte.rga_rms_modulate_ex(dx, dts, dtt, 1e-6, out=out, mod_mode=MOD_TOKEN)
+        _zero_ulp(to_host_typed(out), oracle.rms_modulate_ex(x, ts, tt, 1e-6, MOD_TOKEN, dtype),
+                  dtype, f"rms token out+{off}")
+        dte.rga_ln_modulate(dx, ds, dt, 1e-6, out=out)
+        _zero_ulp(to_host_typed(out), oracle.ln_modulate(x, s, t, 1e-6, MOD_ROW, dtype),
+                  dtype, f"ln row out+{off}")
+        yo = _empty_at((B, L, D), dx, off + 2)
+        dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6, x_out=out, y=yo)
+        wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_BCAST, MOD_ROW, dtype)
+        _bit_exact(to_host_typed(out), wx, dtype, f"fused x_out+{off}")
+        _zero_ulp(to_host_typed(yo), wy, dtype, f"fused y+{off + 2}")
+        dte.gelu_tanh(dx, out=out)
+        gelu_check(to_host_typed(out), oracle.gelu_tanh(x, dtype), gelu_inputs(x, dtype), dtype,
+                   f"gelu out+{off}")
 
 
 def test_bf16_ex_runs_the_same_kernels_as_the_bf16_calls(dte):
