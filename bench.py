@@ -477,7 +477,9 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         out[name] = cold_and_warm(
             lambda: dte.rga_gate_add_rms_modulate_ex(x, u, g, sc, sh, 1e-6, x_out=xo, y=y,
                                                      gate_mode=mode, mod_mode=mod),
-            nbytes, "gate_add_rms_modulate_kernel")
+            nbytes, "gate_add_rms_modulate_kernel" if D % 8 == 0 else (
+                "gate_add_rms_modulate_regs_kernel" if dt != "f32" and D <= 8192
+                else "gate_add_rms_modulate_generic_kernel"))
 
     def element_norm_kernel(norm, D, dt):
         # 2-byte rows of up to 16 slots of 64 groups sit in registers
@@ -508,6 +510,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
     gate("bf16_bcast_gate_add_offset1_[1,32640,4096]", 1, 32640, 4096, "bf16", dte.GATE_BCAST,
          offset=1)
     rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
+    fused("bf16_fused_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.GATE_BCAST, dte.MOD_ROW)
     rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
     rms("bf16_rms_modulate_offset1_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW,
         offset=1)

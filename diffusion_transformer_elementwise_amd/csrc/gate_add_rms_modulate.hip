@@ -25,11 +25,14 @@
 // is read through the caches (it stays in L2), a full gate streams from HBM
 // like x and u.
 //
-// Element path (any D, element-aligned pointers): the same operations in two
-// passes over the row, moving spans of elements through LDS with 16-byte
-// accesses; the second pass re-reads x_out.
+// Element path (any D, element-aligned pointers): for 2-byte rows of up to
+// 8192 elements, one pass with the row realigned in registers (x_out is
+// never read back); otherwise (binary32, longer rows) two passes over the
+// row, moving spans of elements through LDS with 16-byte accesses, the
+// second pass re-reading x_out.
 #include "dtype.hpp"
 #include "launch.hpp"
+#include "row_regs.hpp"
 #include "span.hpp"
 
 #include <rga.h>
@@ -225,6 +228,70 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     }
 }
 
+// Element path for 2-byte types with D <= 512 * K: one wave per row. x, u
+// and g are read once and realigned in registers (realign.hpp) to groups,
+// x' is formed there, written to x_out realigned to its offset, and the
+// rounded x' groups stay in registers for the modulation (row_regs.hpp), so
+// x_out is never read back.
+template <int K, bool FULL, int DT, int MOD>
+__global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_regs_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int64_t D)
+{
+    const int64_t b = blockIdx.y;
+    const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t grow = FULL ? row : b * D;
+    const int64_t mrow = (MOD == kModToken) ? row : b * D;
+    const int n = (int)D;
+
+    u32x4 xv[K];
+    {
+        u32x4 uv[K], gv[K];
+        load_groups<K, true>(elem_ptr<DT>(x, row), n, xv);
+        load_groups<K, true>(elem_ptr<DT>(u, row), n, uv);
+        load_groups<K, FULL>(elem_ptr<DT>(g, grow), n, gv);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            Pack<DT> a, c, e;
+            a.v = xv[k];
+            c.v = uv[k];
+            e.v = gv[k];
+            xv[k] = gate_add8<DT>(a, c, e).v;
+        }
+    }
+    store_run<K, true>(elem_ptr<DT>(x_out, row), n, xv);
+    float mu, rr;
+    regs::row_factors<K, DT, regs::kRms>(xv, n, d_float, eps, &mu, &rr);
+    regs::apply_store<K, DT, MOD == kModToken, regs::kRms>(xv, elem_ptr<DT>(scale, mrow),
+                                                            elem_ptr<DT>(shift, mrow), n, mu, rr,
+                                                            elem_ptr<DT>(y, row));
+}
+
+typedef void (*regs_kernel_t)(const void*, const void*, const void*, const void*, const void*,
+                              float, float, void*, void*, int64_t, int64_t);
+
+// Slots per lane for the register-resident element path: the smallest entry
+// >= ceil(ceil(D / 8) / 64); longer rows (and binary32) take the LDS path.
+constexpr int kRegsLadder[] = {1, 2, 4, 6, 8, 9, 12, 16};
+
+template <bool FULL, int DT, int MOD>
+regs_kernel_t pick_regs(int64_t slots)
+{
+    regs_kernel_t t[] = {&gate_add_rms_modulate_regs_kernel<1, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<2, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<4, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<6, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<8, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<9, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<12, FULL, DT, MOD>,
+                         &gate_add_rms_modulate_regs_kernel<16, FULL, DT, MOD>};
+    for (int i = 0; i < 8; ++i)
+        if (slots <= kRegsLadder[i])
+            return t[i];
+    return nullptr;
+}
+
 typedef void (*fused_kernel_t)(const void*, const void*, const void*,
                                const void*, const void*, float, float, void*,
                                void*, int64_t, int);
@@ -259,6 +326,13 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
     float d_float = (float)D;
     if (!fast) {
         void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &D};
+        if constexpr (DT != kF32) {
+            regs_kernel_t rk = pick_regs<FULL, DT, MOD>(ceil_div(ceil_div(D, 8), 64));
+            if (rk != nullptr)
+                return hipLaunchKernel(reinterpret_cast<const void*>(rk),
+                                       dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
+                                       stream);
+        }
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
             dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);

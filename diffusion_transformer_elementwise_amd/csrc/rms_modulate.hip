@@ -40,7 +40,7 @@
 // One wave per workgroup: nothing crosses a wave. The fast path uses no LDS.
 #include "dtype.hpp"
 #include "launch.hpp"
-#include "realign.hpp"
+#include "row_regs.hpp"
 #include "span.hpp"
 
 #include <rga.h>
@@ -325,96 +325,27 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
 
 // Element path for 2-byte types with D <= 512 * K: one wave per row, the
 // row read once and realigned in registers (realign.hpp) so lane t, slot k
-// holds group t + 64k, which is the fixed order's assignment; the sums skip
-// the elements of the last group past D. Scale and shift are realigned the
-// same way and the result is realigned to the output's offset.
+// holds group t + 64k, which is the fixed order's assignment (row_regs.hpp).
+// Scale and shift are realigned the same way and the result is realigned
+// to the output's offset.
 template <int K, int DT, int MOD, int NORM>
 __global__ __launch_bounds__(kBlock) void modulate_regs_kernel(
     const void* x, const void* scale, const void* shift, float eps, float d_float,
     void* out, int64_t L, int64_t D)
 {
-    const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
     const int64_t mrow = (MOD == kModToken) ? row : b * D;
     const int n = (int)D;
-    constexpr bool kTok = MOD == kModToken;
+    constexpr int kNorm = NORM == kNormLn ? regs::kLn : regs::kRms;
 
     u32x4 xv[K];
     load_groups<K, true>(elem_ptr<DT>(x, row), n, xv);
-
-    // a slot whose 64 groups all lie inside the row (wave-uniform test) is
-    // summed without per-element masks; only the row's last slot needs them
-    float mu = 0.0f;
-    if constexpr (NORM == kNormLn) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            Pack<DT> p;
-            p.v = xv[k];
-            const int e0 = 8 * (lane + 64 * k);
-            if (512 * (k + 1) <= n) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc = acc + p.get(e);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (e0 + e < n)
-                        acc = acc + p.get(e);
-                }
-            }
-        }
-        mu = wave_sum(acc) / d_float;
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        Pack<DT> p;
-        p.v = xv[k];
-        const int e0 = 8 * (lane + 64 * k);
-        const bool whole = 512 * (k + 1) <= n;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (whole || e0 + e < n) {
-                float a = p.get(e);
-                if constexpr (NORM == kNormLn)
-                    a = a - mu;
-                const float sa = a * a;
-                acc = acc + sa;
-            }
-        }
-    }
-    const float rr = inv_std(wave_sum(acc), d_float, eps);
-    // keep the row packed across the reduction: the apply widens it again
-    // (a few shifts) instead of holding 8 widened values per group
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        __asm__ volatile("" : "+v"(xv[k]));
-
-    u32x4 sv[K], hv[K];
-    load_groups<K, kTok>(elem_ptr<DT>(scale, mrow), n, sv);
-    load_groups<K, kTok>(elem_ptr<DT>(shift, mrow), n, hv);
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        Pack<DT> xp, sp, hp;
-        xp.v = xv[k];
-        sp.v = sv[k];
-        hp.v = hv[k];
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = xp.get(e);
-            if constexpr (NORM == kNormLn)
-                v = v - mu;
-            const float nv = v * rr;
-            const float a = 1.0f + sp.get(e);
-            const float m = nv * a;
-            o[e] = m + hp.get(e);
-        }
-        xv[k] = Pack<DT>::make(o).v;
-    }
-    store_run<K, true>(elem_ptr<DT>(out, row), n, xv);
+    float mu, rr;
+    regs::row_factors<K, DT, kNorm>(xv, n, d_float, eps, &mu, &rr);
+    regs::apply_store<K, DT, MOD == kModToken, kNorm>(xv, elem_ptr<DT>(scale, mrow),
+                                                      elem_ptr<DT>(shift, mrow), n, mu, rr,
+                                                      elem_ptr<DT>(out, row));
 }
 
 typedef void (*rms_kernel_t)(const void*, const void*, const void*, float,

@@ -1,0 +1,114 @@
+// The modulation of one row of a 2-byte type held in registers as groups
+// (realign.hpp: lane t, slot k holds elements 8(t + 64k) .. 8(t + 64k) + 7,
+// the last group possibly past the row end), shared by the element paths of
+// the modulation and of the fused residual update.
+//
+// Sums follow the library's fixed order: lane j accumulates groups j,
+// j + 64, ... in increasing group and element order, then xor-distance lane
+// exchanges 1, 2, ..., 32 combine the 64 partials; elements past the row end
+// are skipped. A slot whose 64 groups all lie inside the row (a wave-uniform
+// test) is summed without per-element masks.
+//
+// Called by the whole wave.
+#pragma once
+
+#include "realign.hpp"
+
+namespace rga {
+namespace regs {
+
+enum : int { kRms = 0, kLn = 1 };
+
+__device__ __forceinline__ float wave_sum(float acc)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        acc = acc + __shfl_xor(acc, m);
+    return acc;
+}
+
+// sum over the row of x (WHAT 0), x^2 (1) or (x - mu)^2 (2)
+template <int K, int DT, int WHAT>
+__device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu)
+{
+    const int lane = threadIdx.x & 63;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        Pack<DT> p;
+        p.v = xv[k];
+        const int e0 = 8 * (lane + 64 * k);
+        const bool whole = 512 * (k + 1) <= n;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (whole || e0 + e < n) {
+                float a = p.get(e);
+                if constexpr (WHAT == 0) {
+                    acc = acc + a;
+                } else {
+                    if constexpr (WHAT == 2)
+                        a = a - mu;
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
+            }
+        }
+    }
+    return wave_sum(acc);
+}
+
+// mean (LayerNorm; 0 for RMSNorm) and 1 / sqrt(mean square + eps)
+template <int K, int DT, int NORM>
+__device__ __forceinline__ void row_factors(const u32x4 (&xv)[K], int n, float d_float, float eps,
+                                            float* mu, float* rr)
+{
+    float m = 0.0f;
+    if constexpr (NORM == kLn)
+        m = row_sum<K, DT, 0>(xv, n, 0.0f) / d_float;
+    const float ss = row_sum<K, DT, NORM == kLn ? 2 : 1>(xv, n, m);
+    const float ms = ss / d_float;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    *mu = m;
+    *rr = 1.0f / q;
+}
+
+// out = ((x - mu) * rr) * (1 + scale) + shift over the row, written at out
+// realigned to its offset; scale and shift rows are read realigned to
+// groups (streamed when per token). xv is overwritten.
+template <int K, int DT, bool STREAM_MOD, int NORM>
+__device__ __forceinline__ void apply_store(u32x4 (&xv)[K], const void* scale, const void* shift,
+                                            int n, float mu, float rr, void* out)
+{
+    // keep the row packed across the reduction: the apply widens it again
+    // (a few shifts) instead of holding 8 widened values per group
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        __asm__ volatile("" : "+v"(xv[k]));
+    u32x4 sv[K], hv[K];
+    load_groups<K, STREAM_MOD>(scale, n, sv);
+    load_groups<K, STREAM_MOD>(shift, n, hv);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        Pack<DT> xp, sp, hp;
+        xp.v = xv[k];
+        sp.v = sv[k];
+        hp.v = hv[k];
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = xp.get(e);
+            if constexpr (NORM == kLn)
+                v = v - mu;
+            const float nv = v * rr;
+            const float a = 1.0f + sp.get(e);
+            const float m = nv * a;
+            o[e] = m + hp.get(e);
+        }
+        xv[k] = Pack<DT>::make(o).v;
+    }
+    store_run<K, true>(out, n, xv);
+}
+
+}  // namespace regs
+}  // namespace rga
