@@ -32,6 +32,14 @@
  *     128-bit access moves 8 elements), else RGA_ERR_UNSUPPORTED; the calls
  *     with a dtype argument take any D and pointers aligned to the element
  *     size, and run element-wise kernels where the 128-bit ones cannot.
+ *   - Memory touched: every kernel reads and writes with aligned 128-bit
+ *     accesses. For a tensor that does not start or end on a 16-byte
+ *     boundary, the element-wise kernels also READ the bytes of the first
+ *     and last 16-byte words that lie outside the tensor (those words hold
+ *     at least one of its elements, so they sit in pages the caller owns);
+ *     they never WRITE a byte outside an output tensor (partial words are
+ *     written element by element). Concurrent writers of those neighbouring
+ *     bytes are therefore safe.
  */
 #ifndef RGA_H
 #define RGA_H
