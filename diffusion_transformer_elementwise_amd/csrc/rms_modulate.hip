@@ -33,8 +33,10 @@
 // one lane exchange (Grouped in dtype.hpp) rather than two adjacent words per
 // lane, which left every access instruction half a cache line per lane.
 //
-// Element path (any D, element-aligned pointers): the same order, each sum
-// one pass over the row, then the apply pass, all moving spans of elements
+// Element path (any D, element-aligned pointers), the same order: 2-byte
+// rows of up to 8192 elements are read once and realigned in registers
+// (realign.hpp, row_regs.hpp); binary32 rows and longer rows take each sum
+// as one pass over the row, then the apply pass, moving spans of elements
 // through LDS with 16-byte accesses (span.hpp).
 //
 // One wave per workgroup: nothing crosses a wave. The fast path uses no LDS.

@@ -1,8 +1,10 @@
-// Element spans at any element alignment, moved with 16-byte accesses.
+// Element spans at any element alignment, staged through LDS with 16-byte
+// accesses.
 //
-// The element-wise kernels serve layouts the pack kernels cannot take (D not
-// a multiple of 8, pointers aligned only to the element size). Accessing such
-// a span element by element is bound by the access issue rate on MI355X
+// Used by the modulations' element kernels where a row does not fit the
+// register-resident path (binary32 rows, rows longer than 8192 elements);
+// every other element path realigns in registers (realign.hpp). Accessing a
+// span element by element is bound by the access issue rate on MI355X
 // (2-byte accesses measured at 2.4 TB/s, 16-byte ones at 6.6), so a wave
 // moves a span of n elements through LDS instead:
 //
