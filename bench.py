@@ -482,9 +482,15 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
                 else "gate_add_rms_modulate_generic_kernel"))
 
     def element_norm_kernel(norm, D, dt):
-        # 2-byte rows of up to 16 slots of 64 groups sit in registers
-        regs = dt != "f32" and -(-(-(-D // 8)) // 64) <= 16
-        return "modulate_regs_kernel" if regs else f"{norm}_modulate_generic_kernel"
+        # 2-byte rows of up to 16 slots of 64 groups sit in registers; other
+        # rows up to 64 KB (with two spare words, less 256 B of static LDS)
+        # are staged in LDS once
+        if dt != "f32" and -(-(-(-D // 8)) // 64) <= 16:
+            return "modulate_regs_kernel"
+        es = 4 if dt == "f32" else 2
+        if (-(-D * es // 16) + 2) * 16 <= 65536 - 256:
+            return "modulate_lds_kernel"
+        return f"{norm}_modulate_generic_kernel"
 
     # the ideogram4 shape of the residual-gate page's table, bf16, its seeded case
     c = EXTRA_CASES["ideogram4"]
@@ -512,6 +518,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
     rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
     fused("bf16_fused_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.GATE_BCAST, dte.MOD_ROW)
     rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
+    rms("f32_rms_modulate_ragged_[1,32640,4100]", 1, 32640, 4100, "f32", dte.MOD_ROW)
     rms("bf16_rms_modulate_offset1_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW,
         offset=1)
     gate("f32_bcast_gate_add_offset1_[1,8160,4096]", 1, 8160, 4096, "f32", dte.GATE_BCAST,

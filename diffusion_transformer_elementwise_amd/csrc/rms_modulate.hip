@@ -325,6 +325,132 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
     modulate_row_generic<DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, D, stage);
 }
 
+// Element path for rows that fit in LDS but not in registers (binary32
+// rows; 2-byte rows over 8192 elements): one workgroup of kRowWaves waves per
+// row, the row read from HBM once. The waves stage it into a dynamic LDS
+// buffer (stage i by wave i mod kRowWaves, the wave's next stage in flight
+// while one is committed), realigned so that element i sits at byte i * es
+// (Span::commit_aligned); wave 0 takes the sums from LDS in the fixed order
+// (lane j: groups j, j + 64, ...); all waves then apply over chunks of the
+// output's aligned 16-byte words (realign.hpp), x taken from LDS at the
+// output's byte positions (two aligned LDS words and a cut), scale and shift
+// read realigned to them.
+constexpr int kRowStage = 1024;  // elements staged per step
+constexpr int kRowWaves = 8;
+constexpr int64_t kMaxRowLds = 65536 - 256;  // 64 KB per workgroup, less the static LDS
+
+// LDS bytes the staged row needs: its aligned words plus two words that a
+// cut at the row's end may touch (their bytes are never used).
+int64_t row_lds_bytes(int64_t D, int es) { return ((D * es + 15) / 16 + 2) * 16; }
+
+// sum over the staged row of x (what 0), x^2 (1) or (x - mu)^2 (2), by one wave
+template <int DT>
+__device__ __forceinline__ float lds_row_sum(const u32x4* rowbuf, int n, float mu, int what)
+{
+    const int lane = threadIdx.x & 63;
+    const int groups = (n + 7) >> 3;
+    float acc = 0.0f;
+    for (int g = lane; g < groups; g += kBlock) {
+        const Pack<DT> p = Span<DT, kRowStage>::group(rowbuf, g);
+        const bool whole = 8 * g + 8 <= n;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (whole || 8 * g + e < n) {
+                float a = p.get(e);
+                if (what == 0) {
+                    acc = acc + a;
+                } else {
+                    if (what == 2)
+                        a = a - mu;
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
+            }
+        }
+    }
+    return wave_sum(acc);
+}
+
+template <int DT, int MOD, int NORM>
+__global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
+    const void* x, const void* scale, const void* shift, float eps, float d_float,
+    void* out, int64_t L, int64_t D)
+{
+    extern __shared__ u32x4 rowbuf[];
+    __shared__ float factors[2];
+    using S = Span<DT, kRowStage>;
+    constexpr int es = DT == kF32 ? 4 : 2;
+    constexpr bool kTok = MOD == kModToken;
+    constexpr int kStride = kRowStage * kRowWaves;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.y;
+    const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t mrow = kTok ? row : b * D;
+    const int n = (int)D;
+
+    const int first = wave * kRowStage;
+    if (first < n) {
+        typename S::Words next = S::template fetch<true>(
+            elem_ptr<DT>(x, row + first), (n - first < kRowStage) ? n - first : kRowStage);
+        for (int s0 = first; s0 < n; s0 += kStride) {
+            const int cnt = (n - s0 < kRowStage) ? n - s0 : kRowStage;
+            const int m = S::offset(elem_ptr<DT>(x, row + s0));
+            const typename S::Words cur = next;
+            const int s1 = s0 + kStride;
+            if (s1 < n)
+                next = S::template fetch<true>(elem_ptr<DT>(x, row + s1),
+                                               (n - s1 < kRowStage) ? n - s1 : kRowStage);
+            S::commit_aligned(cur, m, cnt, rowbuf + s0 * es / 16);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float mu = 0.0f;
+        if constexpr (NORM == kNormLn)
+            mu = lds_row_sum<DT>(rowbuf, n, 0.0f, 0) / d_float;
+        const float rr =
+            inv_std(lds_row_sum<DT>(rowbuf, n, mu, NORM == kNormLn ? 2 : 1), d_float, eps);
+        if (lane == 0) {
+            factors[0] = mu;
+            factors[1] = rr;
+        }
+    }
+    __syncthreads();
+    const float mu = factors[0];
+    const float rr = factors[1];
+
+    void* po = elem_ptr<DT>(out, row);
+    const int mo = start_offset(po);
+    const int64_t nbytes = D * es;
+    const int64_t words = window_words(po, nbytes);
+    const int sh = (16 - mo) & 15;
+    // rowbuf holds (nbytes + 15) / 16 + 2 words: q and q + 1 stay inside for
+    // q <= qmax; lanes past the row's last word are clamped (not stored)
+    const int qmax = (int)((nbytes + 15) / 16);
+    for (int64_t c = wave; 64 * c < words; c += kRowWaves) {
+        // output word w holds row bytes [16w - mo, 16w - mo + 16)
+        int q = (int)((16 * (64 * c + lane) - mo) >> 4);
+        q = q < qmax ? q : qmax;
+        const u32x4 xw = sh == 0 ? rowbuf[q] : window_at(rowbuf[q < 0 ? 0 : q], rowbuf[q + 1], sh);
+        const u32x4 sw = load_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, c);
+        const u32x4 hw = load_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, c);
+        using W = Word<DT>;
+        float o[W::kN];
+#pragma unroll
+        for (int e = 0; e < W::kN; ++e) {
+            float v = W::get(xw, e);
+            if constexpr (NORM == kNormLn)
+                v = v - mu;
+            const float nv = v * rr;
+            const float a = 1.0f + W::get(sw, e);
+            const float mm = nv * a;
+            o[e] = mm + W::get(hw, e);
+        }
+        store_chunk<true>(po, nbytes, c, W::make(o));
+    }
+}
+
 // Element path for 2-byte types with D <= 512 * K: one wave per row, the
 // row read once and realigned in registers (realign.hpp) so lane t, slot k
 // holds group t + 64k, which is the fixed order's assignment (row_regs.hpp).
@@ -415,6 +541,12 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
             if (rk != nullptr)
                 return hipLaunchKernel(rk, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
                                        stream);
+        }
+        const int64_t lds = row_lds_bytes(D, DT == kF32 ? 4 : 2);
+        if (lds <= kMaxRowLds) {
+            const void* lk = reinterpret_cast<const void*>(&modulate_lds_kernel<DT, MOD, NORM>);
+            return hipLaunchKernel(lk, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock * kRowWaves),
+                                   args, (size_t)lds, stream);
         }
         const void* k = NORM == kNormLn
                             ? reinterpret_cast<const void*>(&ln_modulate_generic_kernel<DT, MOD>)

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from synth_inputs import BF16, GATE_BCAST, N001, N01, N02, U11, random_typed
+from synth_inputs import BF16, F32, GATE_BCAST, N001, N01, N02, U11, random_typed
 from tests.gpu_util import say, to_dev_typed, to_host_typed, ulp_diff_typed
 
 pytestmark = pytest.mark.gpu
@@ -79,6 +79,23 @@ def test_modulations(dte, norm, L, D, offset):
     else:
         want = oracle.ln_modulate(_sample(x, rows), s, t, 1e-6, MOD_ROW, BF16)
     _zero_ulp(_sample(got, rows), want, f"{norm} D={D} offset={offset}")
+
+
+@pytest.mark.parametrize("dtype,L,D", [(BF16, 8160, 16384), (F32, 32640, 4100)])
+def test_modulation_staged_in_lds(dte, dtype, L, D):
+    # rows past the register-resident limit and binary32 rows: the row staged
+    # in LDS once
+    B = 1
+    say(f"[element rms lds] dtype={dtype} B={B} L={L} D={D}: inputs")
+    x = random_typed(7401, (B, L, D), N02, dtype)
+    s = random_typed(7402, (B, 1, D), N001, dtype)
+    t = random_typed(7403, (B, 1, D), N001, dtype)
+    got = to_host_typed(dte.rga_rms_modulate_ex(*(to_dev_typed(a, dtype) for a in (x, s, t)), 1e-6))
+    rows = _rows(L, seed=4)
+    want = oracle.rms_modulate_ex(_sample(x, rows), s, t, 1e-6, MOD_ROW, dtype)
+    d = ulp_diff_typed(_sample(got, rows), want, dtype)
+    say(f"[element rms lds] max ULP {int(d.max())} over {d.size} elements")
+    assert d.max() == 0
 
 
 def test_fused_ragged(dte):

@@ -137,8 +137,10 @@ def _empty_at(shape, like, offset):
 
 
 # each entry of the element path's slot ladder (ceil(ceil(D / 8) / 64) slots
-# of 8-element groups per lane: 1, 2, 4, 6, 8, 9, 12, 16) and rows past it
-MIXED_D = [1, 100, 1000, 1500, 2500, 4000, 4500, 6000, 8191, 8193]
+# of 8-element groups per lane: 1, 2, 4, 6, 8, 9, 12, 16), rows past it
+# (staged in LDS: binary32 rows and 2-byte rows up to 64 KB) and rows past
+# the LDS limit (two passes)
+MIXED_D = [1, 100, 1000, 1500, 2500, 4000, 4500, 6000, 8191, 8193, 16370, 33001]
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=NAMES.get)
