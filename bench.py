@@ -477,9 +477,17 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         out[name] = cold_and_warm(
             lambda: dte.rga_gate_add_rms_modulate_ex(x, u, g, sc, sh, 1e-6, x_out=xo, y=y,
                                                      gate_mode=mode, mod_mode=mod),
-            nbytes, "gate_add_rms_modulate_kernel" if D % 8 == 0 else (
-                "gate_add_rms_modulate_regs_kernel" if dt != "f32" and D <= 8192
-                else "gate_add_rms_modulate_generic_kernel"))
+            nbytes, "gate_add_rms_modulate_kernel" if D % 8 == 0 and D <= 8192
+            else element_fused_kernel(D, dt))
+
+    def element_fused_kernel(D, dt):
+        # as element_norm_kernel; the fused call's LDS buffer has one more word
+        if dt != "f32" and -(-(-(-D // 8)) // 64) <= 16:
+            return "gate_add_rms_modulate_regs_kernel"
+        es = 4 if dt == "f32" else 2
+        if (-(-D * es // 16) + 3) * 16 <= 65536 - 256:
+            return "gate_add_rms_modulate_lds_kernel"
+        return "gate_add_rms_modulate_generic_kernel"
 
     def element_norm_kernel(norm, D, dt):
         # 2-byte rows of up to 16 slots of 64 groups sit in registers; other
@@ -517,6 +525,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
          offset=1)
     rms("bf16_rms_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
     fused("bf16_fused_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.GATE_BCAST, dte.MOD_ROW)
+    fused("f32_fused_ragged_[1,32640,4100]", 1, 32640, 4100, "f32", dte.GATE_BCAST, dte.MOD_ROW)
     rms("bf16_rms_modulate_wide_[1,8160,16384]", 1, 8160, 16384, "bf16", dte.MOD_ROW)
     rms("f32_rms_modulate_ragged_[1,32640,4100]", 1, 32640, 4100, "f32", dte.MOD_ROW)
     rms("bf16_rms_modulate_offset1_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW,

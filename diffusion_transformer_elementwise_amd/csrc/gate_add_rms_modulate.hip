@@ -228,6 +228,133 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     }
 }
 
+// 16 bytes of an LDS row buffer starting at byte pos, pos mod 16 = sh the
+// same in every lane; word indexes are clamped to [0, qmax] (the clamped
+// bytes are never used).
+__device__ __forceinline__ u32x4 lds_bytes16(const u32x4* buf, int pos, int sh, int qmax)
+{
+    int q = pos >> 4;
+    q = q < qmax ? q : qmax;
+    if (sh == 0)
+        return buf[q < 0 ? 0 : q];
+    return window_at(buf[q < 0 ? 0 : q], buf[q + 1 < 0 ? 0 : q + 1], sh);
+}
+
+// Element path for rows that fit in LDS but not in registers (binary32
+// rows; 2-byte rows over 8192 elements): one workgroup of kRowWaves waves per
+// row, x, u and g read once. The waves form x' over chunks of x_out's aligned
+// 16-byte words (each input read realigned to x_out, realign.hpp), store it
+// and keep the words in a dynamic LDS buffer; wave 0 takes the fixed-order
+// sum from LDS (group g is the 16 or 32 bytes at x_out's offset + g * 8 *
+// es); all waves then write y over chunks of y's aligned words, x' taken
+// from LDS realigned to y. x_out is never read back.
+constexpr int kRowWaves = 8;
+constexpr int64_t kMaxRowLds = 65536 - 256;  // 64 KB per workgroup, less the static LDS
+
+// LDS bytes of the row buffer: x_out's window words (at most one more than
+// the row's aligned words) and two spare words a cut may touch.
+int64_t row_lds_bytes(int64_t D, int es) { return ((D * es + 15) / 16 + 3) * 16; }
+
+template <bool FULL, int DT, int MOD>
+__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int64_t D)
+{
+    extern __shared__ u32x4 rowbuf[];
+    __shared__ float factor;
+    constexpr int es = DT == kF32 ? 4 : 2;
+    constexpr bool kTok = MOD == kModToken;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.y;
+    const int64_t row = (b * L + blockIdx.x) * D;
+    const int64_t grow = FULL ? row : b * D;
+    const int64_t mrow = kTok ? row : b * D;
+    const int n = (int)D;
+    const int64_t nbytes = D * es;
+    using W = Word<DT>;
+
+    void* pxo = elem_ptr<DT>(x_out, row);
+    const int mxo = start_offset(pxo);
+    const int64_t words_xo = window_words(pxo, nbytes);
+    for (int64_t c = wave; 64 * c < words_xo; c += kRowWaves) {
+        const u32x4 xw = load_for_chunk<true>(elem_ptr<DT>(x, row), nbytes, mxo, c);
+        const u32x4 uw = load_for_chunk<true>(elem_ptr<DT>(u, row), nbytes, mxo, c);
+        const u32x4 gw = load_for_chunk<FULL>(elem_ptr<DT>(g, grow), nbytes, mxo, c);
+        float o[W::kN];
+#pragma unroll
+        for (int e = 0; e < W::kN; ++e) {
+            const float p = W::get(uw, e) * W::get(gw, e);
+            o[e] = W::get(xw, e) + p;
+        }
+        const u32x4 v = W::make(o);
+        store_chunk<true>(pxo, nbytes, c, v);
+        const int64_t w = 64 * c + lane;
+        if (w < words_xo)
+            rowbuf[w] = v;
+    }
+    __syncthreads();
+
+    // the buffer's row starts at byte mxo; it holds (nbytes + 15) / 16 + 3
+    // words, so reading words q and q + 1 with q <= words_xo stays inside
+    // (words past words_xo - 1 only supply bytes past the row)
+    const int qmax = (int)words_xo;
+    if (wave == 0) {
+        const int groups = (n + 7) >> 3;
+        float acc = 0.0f;
+        for (int gi = lane; gi < groups; gi += kBlock) {
+            Pack<DT> p;
+            if constexpr (DT == kF32) {
+                p.a = lds_bytes16(rowbuf, mxo + 32 * gi, mxo, qmax);
+                p.b = lds_bytes16(rowbuf, mxo + 32 * gi + 16, mxo, qmax);
+            } else {
+                p.v = lds_bytes16(rowbuf, mxo + 16 * gi, mxo, qmax);
+            }
+            const bool whole = 8 * gi + 8 <= n;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (whole || 8 * gi + e < n) {
+                    const float a = p.get(e);
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1)
+            acc = acc + __shfl_xor(acc, m);
+        const float ms = acc / d_float;
+        const float t = ms + eps;
+        const float q = sqrtf(t);
+        if (lane == 0)
+            factor = 1.0f / q;
+    }
+    __syncthreads();
+    const float rr = factor;
+
+    void* py = elem_ptr<DT>(y, row);
+    const int my = start_offset(py);
+    const int64_t words_y = window_words(py, nbytes);
+    const int sh = (mxo - my) & 15;
+    for (int64_t c = wave; 64 * c < words_y; c += kRowWaves) {
+        // y word w holds row bytes [16w - my, +16): buffer bytes from 16w - my + mxo
+        const int pos = (int)(16 * (64 * c + lane)) - my + mxo;
+        const u32x4 xw = lds_bytes16(rowbuf, pos, sh, qmax);
+        const u32x4 sw = load_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, c);
+        const u32x4 hw = load_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, c);
+        float o[W::kN];
+#pragma unroll
+        for (int e = 0; e < W::kN; ++e) {
+            const float nv = W::get(xw, e) * rr;
+            const float a = 1.0f + W::get(sw, e);
+            const float m = nv * a;
+            o[e] = m + W::get(hw, e);
+        }
+        store_chunk<true>(py, nbytes, c, W::make(o));
+    }
+}
+
 // Element path for 2-byte types with D <= 512 * K: one wave per row. x, u
 // and g are read once and realigned in registers (realign.hpp) to groups,
 // x' is formed there, written to x_out realigned to its offset, and the
@@ -333,6 +460,12 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
                                        dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
                                        stream);
         }
+        const int64_t lds = row_lds_bytes(D, DT == kF32 ? 4 : 2);
+        if (lds <= kMaxRowLds)
+            return hipLaunchKernel(
+                reinterpret_cast<const void*>(&gate_add_rms_modulate_lds_kernel<FULL, DT, MOD>),
+                dim3((uint32_t)L, (uint32_t)B), dim3(kBlock * kRowWaves), args, (size_t)lds,
+                stream);
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
             dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
