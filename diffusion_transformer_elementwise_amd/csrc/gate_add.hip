@@ -124,10 +124,11 @@ __device__ __forceinline__ void gate_add_chunk(const void* x, const void* u, con
     const int mo = start_offset(out);
     if (64 * j >= window_words(out, nbytes))
         return;
-    const u32x4 xv = load_for_chunk<true>(x, nbytes, mo, j);
-    const u32x4 uv = load_for_chunk<true>(u, nbytes, mo, j);
-    const u32x4 gv = load_for_chunk<G_STREAM>(g, nbytes, mo, j);
-    store_chunk<true>(out, nbytes, j, gate_add_word<DT>(xv, uv, gv));
+    const ChunkWords fx = fetch_for_chunk<true>(x, nbytes, mo, j);
+    const ChunkWords fu = fetch_for_chunk<true>(u, nbytes, mo, j);
+    const ChunkWords fg = fetch_for_chunk<G_STREAM>(g, nbytes, mo, j);
+    store_chunk<true>(out, nbytes, j,
+                      gate_add_word<DT>(chunk_word(fx), chunk_word(fu), chunk_word(fg)));
 }
 
 template <int DT>
@@ -151,7 +152,10 @@ __global__ __launch_bounds__(kBlock) void gate_add_generic_full_kernel(
 }
 
 // Broadcast gate: each row is a run, with row b of g as its gate run; grid
-// x = (row l) * chunks per row + chunk, y = batch b.
+// x = (row l) * chunks per row + chunk, y = batch b. (Folding a ragged row's
+// last word or two into another workgroup's loop measured slower: that
+// workgroup then waits out two load-to-store latencies while holding its
+// slot.)
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_generic_bcast_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t L,

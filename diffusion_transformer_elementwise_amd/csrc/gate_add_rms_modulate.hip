@@ -279,9 +279,12 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
     const int mxo = start_offset(pxo);
     const int64_t words_xo = window_words(pxo, nbytes);
     for (int64_t c = wave; 64 * c < words_xo; c += kRowWaves) {
-        const u32x4 xw = load_for_chunk<true>(elem_ptr<DT>(x, row), nbytes, mxo, c);
-        const u32x4 uw = load_for_chunk<true>(elem_ptr<DT>(u, row), nbytes, mxo, c);
-        const u32x4 gw = load_for_chunk<FULL>(elem_ptr<DT>(g, grow), nbytes, mxo, c);
+        const ChunkWords fxw = fetch_for_chunk<true>(elem_ptr<DT>(x, row), nbytes, mxo, c);
+        const ChunkWords fuw = fetch_for_chunk<true>(elem_ptr<DT>(u, row), nbytes, mxo, c);
+        const ChunkWords fgw = fetch_for_chunk<FULL>(elem_ptr<DT>(g, grow), nbytes, mxo, c);
+        const u32x4 xw = chunk_word(fxw);
+        const u32x4 uw = chunk_word(fuw);
+        const u32x4 gw = chunk_word(fgw);
         float o[W::kN];
 #pragma unroll
         for (int e = 0; e < W::kN; ++e) {
@@ -341,8 +344,10 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
         // y word w holds row bytes [16w - my, +16): buffer bytes from 16w - my + mxo
         const int pos = (int)(16 * (64 * c + lane)) - my + mxo;
         const u32x4 xw = lds_bytes16(rowbuf, pos, sh, qmax);
-        const u32x4 sw = load_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, c);
-        const u32x4 hw = load_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, c);
+        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, c);
+        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, c);
+        const u32x4 sw = chunk_word(fsw);
+        const u32x4 hw = chunk_word(fhw);
         float o[W::kN];
 #pragma unroll
         for (int e = 0; e < W::kN; ++e) {

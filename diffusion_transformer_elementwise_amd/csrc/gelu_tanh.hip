@@ -216,9 +216,9 @@ __global__ __launch_bounds__(kBlock) void gelu_tanh_generic_bias_kernel(
     const int mo = start_offset(po);
     if (64 * j >= window_words(po, nbytes))
         return;
-    const u32x4 xv = load_for_chunk<true>(px, nbytes, mo, j);
-    const u32x4 bv = load_for_chunk<false>(bias, nbytes, mo, j);
-    store_chunk<true>(po, nbytes, j, gelu_word<DT, true>(xv, bv));
+    const ChunkWords fx = fetch_for_chunk<true>(px, nbytes, mo, j);
+    const ChunkWords fb = fetch_for_chunk<false>(bias, nbytes, mo, j);
+    store_chunk<true>(po, nbytes, j, gelu_word<DT, true>(chunk_word(fx), chunk_word(fb)));
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

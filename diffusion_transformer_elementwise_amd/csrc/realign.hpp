@@ -241,8 +241,18 @@ __device__ __forceinline__ int64_t window_words(const void* p, int64_t nbytes)
     return nbytes > 0 ? (start_offset(p) + nbytes + 15) >> 4 : 0;
 }
 
+// The words an input supplies to lane t of chunk j, fetched (every load
+// issued, none waited on) so that a caller can fetch all its inputs before
+// realigning any: a branch between fetches made the compiler wait for each
+// input's loads before issuing the next input's.
+struct ChunkWords {
+    u32x4 cur, extra;
+    int sh;
+};
+
 template <bool STREAM>
-__device__ __forceinline__ u32x4 load_for_chunk(const void* p, int64_t nbytes, int mo, int64_t j)
+__device__ __forceinline__ ChunkWords fetch_for_chunk(const void* p, int64_t nbytes, int mo,
+                                                      int64_t j)
 {
     const int lane = threadIdx.x & 63;
     const int mi = start_offset(p);
@@ -250,17 +260,27 @@ __device__ __forceinline__ u32x4 load_for_chunk(const void* p, int64_t nbytes, i
     const int64_t count = window_words(p, nbytes);
     const int d = mi - mo;
     const int64_t q0 = 64 * j + (d < 0 ? -1 : 0);
-    const int sh = d < 0 ? d + 16 : d;
     // indexes clamped into the input's window (no branch around the loads);
     // a clamped word only supplies bytes outside the run
     const int64_t i = q0 + lane;
     const int64_t ic = i < 0 ? 0 : (i < count ? i : count - 1);
-    const u32x4 cur = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
-    if (sh == 0)
-        return cur;
     const int64_t ie = q0 + 64;
-    const u32x4 extra = load16(w0 + (ie < 0 ? 0 : (ie < count ? ie : count - 1)));
-    return window_at(cur, lane_from_next(cur, extra), sh);
+    ChunkWords r;
+    r.cur = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
+    r.extra = load16(w0 + (ie < 0 ? 0 : (ie < count ? ie : count - 1)));
+    r.sh = d < 0 ? d + 16 : d;
+    return r;
+}
+
+__device__ __forceinline__ u32x4 chunk_word(const ChunkWords& w)
+{
+    return w.sh == 0 ? w.cur : window_at(w.cur, lane_from_next(w.cur, w.extra), w.sh);
+}
+
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load_for_chunk(const void* p, int64_t nbytes, int mo, int64_t j)
+{
+    return chunk_word(fetch_for_chunk<STREAM>(p, nbytes, mo, j));
 }
 
 template <bool STREAM>

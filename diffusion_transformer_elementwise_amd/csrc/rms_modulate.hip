@@ -433,8 +433,10 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
         int q = (int)((16 * (64 * c + lane) - mo) >> 4);
         q = q < qmax ? q : qmax;
         const u32x4 xw = sh == 0 ? rowbuf[q] : window_at(rowbuf[q < 0 ? 0 : q], rowbuf[q + 1], sh);
-        const u32x4 sw = load_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, c);
-        const u32x4 hw = load_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, c);
+        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, c);
+        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, c);
+        const u32x4 sw = chunk_word(fsw);
+        const u32x4 hw = chunk_word(fhw);
         using W = Word<DT>;
         float o[W::kN];
 #pragma unroll
