@@ -379,10 +379,17 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_regs_kernel(
 
     u32x4 xv[K];
     {
-        u32x4 uv[K], gv[K];
-        load_groups<K, true>(elem_ptr<DT>(x, row), n, xv);
-        load_groups<K, true>(elem_ptr<DT>(u, row), n, uv);
-        load_groups<K, FULL>(elem_ptr<DT>(g, grow), n, gv);
+        // every input's loads issued before any is realigned
+        u32x4 uv[K], gv[K], xe, ue, ge;
+        const void* px = elem_ptr<DT>(x, row);
+        const void* pu = elem_ptr<DT>(u, row);
+        const void* pg = elem_ptr<DT>(g, grow);
+        load_run<K, true>(px, n, xv, xe);
+        load_run<K, true>(pu, n, uv, ue);
+        load_run<K, FULL>(pg, n, gv, ge);
+        realign_in<K>(xv, xe, start_offset(px));
+        realign_in<K>(uv, ue, start_offset(pu));
+        realign_in<K>(gv, ge, start_offset(pg));
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             Pack<DT> a, c, e;

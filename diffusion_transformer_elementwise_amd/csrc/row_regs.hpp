@@ -85,9 +85,12 @@ __device__ __forceinline__ void apply_store(u32x4 (&xv)[K], const void* scale, c
 #pragma unroll
     for (int k = 0; k < K; ++k)
         __asm__ volatile("" : "+v"(xv[k]));
-    u32x4 sv[K], hv[K];
-    load_groups<K, STREAM_MOD>(scale, n, sv);
-    load_groups<K, STREAM_MOD>(shift, n, hv);
+    // both rows' loads issued before either is realigned
+    u32x4 sv[K], hv[K], se, he;
+    load_run<K, STREAM_MOD>(scale, n, sv, se);
+    load_run<K, STREAM_MOD>(shift, n, hv, he);
+    realign_in<K>(sv, se, start_offset(scale));
+    realign_in<K>(hv, he, start_offset(shift));
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         Pack<DT> xp, sp, hp;
