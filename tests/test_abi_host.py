@@ -5,7 +5,9 @@ the arithmetic it promises."""
 import glob
 import os
 import re
+import shutil
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -391,3 +393,18 @@ def test_grid_limits(dte):
     x, u, g, o = (A + k * 256 * GB for k in range(4))  # room for 2 * n_max bf16 each
     assert dte.check_residual_gate_add(x, u, g, o, 1, 1, n_max // 2, dte.GATE_FULL) == ok
     assert dte.check_residual_gate_add(x, u, g, o, 1, 1, n_max * 2, dte.GATE_FULL) == uns
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    # a copy of the Python package without librga.so must refuse to import
+    # (no CPU fallback anywhere)
+    dst = tmp_path / "diffusion_transformer_elementwise_amd"
+    dst.mkdir()
+    for name in os.listdir(PKG):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(PKG, name), dst / name)
+    r = subprocess.run([sys.executable, "-c", "import diffusion_transformer_elementwise_amd"],
+                       cwd=tmp_path, capture_output=True, text=True,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "no CPU fallback" in r.stderr, r.stderr[-2000:]
