@@ -114,7 +114,8 @@ __device__ __forceinline__ u32x4 gate_add_word(const u32x4& x, const u32x4& u, c
 }
 
 // Element path (realign.hpp): a run of elements is cut into chunks of 64
-// 16-byte words of the output's aligned window, one chunk per workgroup;
+// 16-byte words of the output's aligned window (whole 128-byte lines), one
+// chunk per workgroup;
 // each input is read realigned to the output's byte positions, so a lane
 // computes the elements of exactly one output word.
 template <int DT, bool G_STREAM>
@@ -122,12 +123,13 @@ __device__ __forceinline__ void gate_add_chunk(const void* x, const void* u, con
                                                void* out, int64_t nbytes, int64_t j)
 {
     const int mo = start_offset(out);
-    if (64 * j >= window_words(out, nbytes))
+    const int64_t wbase = 64 * j - line_lead(out);
+    if (wbase >= window_words(out, nbytes))
         return;
-    const ChunkWords fx = fetch_for_chunk<true>(x, nbytes, mo, j);
-    const ChunkWords fu = fetch_for_chunk<true>(u, nbytes, mo, j);
-    const ChunkWords fg = fetch_for_chunk<G_STREAM>(g, nbytes, mo, j);
-    store_chunk<true>(out, nbytes, j,
+    const ChunkWords fx = fetch_for_chunk<true>(x, nbytes, mo, wbase);
+    const ChunkWords fu = fetch_for_chunk<true>(u, nbytes, mo, wbase);
+    const ChunkWords fg = fetch_for_chunk<G_STREAM>(g, nbytes, mo, wbase);
+    store_chunk<true>(out, nbytes, wbase,
                       gate_add_word<DT>(chunk_word(fx), chunk_word(fu), chunk_word(fg)));
 }
 
@@ -172,8 +174,9 @@ __global__ __launch_bounds__(kBlock) void gate_add_generic_bcast_kernel(
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Chunks of 64 output words that cover a run of nbytes at any start offset
-// (at most 14 bytes into its first word).
-int64_t element_chunks(int64_t nbytes) { return ceil_div(ceil_div(14 + nbytes, 16), 64); }
+// (at most 14 bytes into its first word), the first chunk starting up to 7
+// words early (line_lead in realign.hpp).
+int64_t element_chunks(int64_t nbytes) { return ceil_div(ceil_div(14 + nbytes, 16) + 7, 64); }
 
 template <int DT>
 hipError_t launch_typed(const void* x, const void* u, const void* g,

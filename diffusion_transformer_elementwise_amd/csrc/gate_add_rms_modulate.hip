@@ -278,10 +278,12 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
     void* pxo = elem_ptr<DT>(x_out, row);
     const int mxo = start_offset(pxo);
     const int64_t words_xo = window_words(pxo, nbytes);
-    for (int64_t c = wave; 64 * c < words_xo; c += kRowWaves) {
-        const ChunkWords fxw = fetch_for_chunk<true>(elem_ptr<DT>(x, row), nbytes, mxo, c);
-        const ChunkWords fuw = fetch_for_chunk<true>(elem_ptr<DT>(u, row), nbytes, mxo, c);
-        const ChunkWords fgw = fetch_for_chunk<FULL>(elem_ptr<DT>(g, grow), nbytes, mxo, c);
+    const int lead_xo = line_lead(pxo);
+    for (int64_t c = wave; 64 * c - lead_xo < words_xo; c += kRowWaves) {
+        const int64_t wbase = 64 * c - lead_xo;  // chunks of whole 128-byte lines
+        const ChunkWords fxw = fetch_for_chunk<true>(elem_ptr<DT>(x, row), nbytes, mxo, wbase);
+        const ChunkWords fuw = fetch_for_chunk<true>(elem_ptr<DT>(u, row), nbytes, mxo, wbase);
+        const ChunkWords fgw = fetch_for_chunk<FULL>(elem_ptr<DT>(g, grow), nbytes, mxo, wbase);
         const u32x4 xw = chunk_word(fxw);
         const u32x4 uw = chunk_word(fuw);
         const u32x4 gw = chunk_word(fgw);
@@ -292,9 +294,9 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
             o[e] = W::get(xw, e) + p;
         }
         const u32x4 v = W::make(o);
-        store_chunk<true>(pxo, nbytes, c, v);
-        const int64_t w = 64 * c + lane;
-        if (w < words_xo)
+        store_chunk<true>(pxo, nbytes, wbase, v);
+        const int64_t w = wbase + lane;
+        if (w >= 0 && w < words_xo)
             rowbuf[w] = v;
     }
     __syncthreads();
@@ -340,12 +342,14 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
     const int my = start_offset(py);
     const int64_t words_y = window_words(py, nbytes);
     const int sh = (mxo - my) & 15;
-    for (int64_t c = wave; 64 * c < words_y; c += kRowWaves) {
+    const int lead_y = line_lead(py);
+    for (int64_t c = wave; 64 * c - lead_y < words_y; c += kRowWaves) {
+        const int64_t wbase = 64 * c - lead_y;
         // y word w holds row bytes [16w - my, +16): buffer bytes from 16w - my + mxo
-        const int pos = (int)(16 * (64 * c + lane)) - my + mxo;
+        const int pos = (int)(16 * (wbase + lane)) - my + mxo;
         const u32x4 xw = lds_bytes16(rowbuf, pos, sh, qmax);
-        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, c);
-        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, c);
+        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, wbase);
+        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, wbase);
         const u32x4 sw = chunk_word(fsw);
         const u32x4 hw = chunk_word(fhw);
         float o[W::kN];
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
             const float m = nv * a;
             o[e] = m + W::get(hw, e);
         }
-        store_chunk<true>(py, nbytes, c, W::make(o));
+        store_chunk<true>(py, nbytes, wbase, W::make(o));
     }
 }
 

@@ -193,12 +193,12 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void gelu_tanh_generic_flat_kernel(
     const void* x, void* out, int64_t nbytes)
 {
-    const int64_t j = blockIdx.x;
     const int mo = start_offset(out);
-    if (64 * j >= window_words(out, nbytes))
+    const int64_t wbase = 64 * (int64_t)blockIdx.x - line_lead(out);
+    if (wbase >= window_words(out, nbytes))
         return;
-    const u32x4 xv = load_for_chunk<true>(x, nbytes, mo, j);
-    store_chunk<true>(out, nbytes, j, gelu_word<DT, false>(xv, xv));
+    const u32x4 xv = load_for_chunk<true>(x, nbytes, mo, wbase);
+    store_chunk<true>(out, nbytes, wbase, gelu_word<DT, false>(xv, xv));
 }
 
 // With a bias each row is a run, with the bias row beside it; grid x =
@@ -214,17 +214,19 @@ __global__ __launch_bounds__(kBlock) void gelu_tanh_generic_bias_kernel(
     const void* px = static_cast<const char*>(x) + (int64_t)r * nbytes;
     void* po = static_cast<char*>(out) + (int64_t)r * nbytes;
     const int mo = start_offset(po);
-    if (64 * j >= window_words(po, nbytes))
+    const int64_t wbase = 64 * j - line_lead(po);
+    if (wbase >= window_words(po, nbytes))
         return;
-    const ChunkWords fx = fetch_for_chunk<true>(px, nbytes, mo, j);
-    const ChunkWords fb = fetch_for_chunk<false>(bias, nbytes, mo, j);
-    store_chunk<true>(po, nbytes, j, gelu_word<DT, true>(chunk_word(fx), chunk_word(fb)));
+    const ChunkWords fx = fetch_for_chunk<true>(px, nbytes, mo, wbase);
+    const ChunkWords fb = fetch_for_chunk<false>(bias, nbytes, mo, wbase);
+    store_chunk<true>(po, nbytes, wbase, gelu_word<DT, true>(chunk_word(fx), chunk_word(fb)));
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Chunks of 64 output words that cover a run of nbytes at any start offset.
-int64_t element_chunks(int64_t nbytes) { return ceil_div(ceil_div(14 + nbytes, 16), 64); }
+// Chunks of 64 output words that cover a run of nbytes at any start offset,
+// the first chunk starting up to 7 words early (line_lead in realign.hpp).
+int64_t element_chunks(int64_t nbytes) { return ceil_div(ceil_div(14 + nbytes, 16) + 7, 64); }
 
 template <int DT>
 hipError_t launch_typed(const void* x, const void* bias, void* out, int64_t rows, int64_t F,

@@ -158,7 +158,7 @@ __device__ __forceinline__ void put_partial(u32x4* w0, int64_t i, const u32x4& v
 }
 
 // Output word i of the run [mo, end): one 16-byte store when it lies wholly
-// inside the run, else its bytes inside the run.
+// inside the run, else its bytes inside the run (none for i < 0).
 template <bool STREAM>
 __device__ __forceinline__ void put_word(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
                                          int64_t end)
@@ -222,8 +222,9 @@ __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K])
 // ---- Output-aligned chunks -----------------------------------------------
 //
 // An element-wise result over a run of nbytes bytes written at po is cut
-// into chunks of 64 words of po's aligned window: lane t of chunk j owns
-// output word 64j + t. Only the window's first and last words can be
+// into chunks of 64 words of po's aligned window: lane t of the chunk that
+// starts at window word wbase owns output word wbase + t (words before the
+// window's start are owned by no one and not written). Only the window's first and last words can be
 // partial, so only they are written element by element, every other word
 // is one 16-byte store, and no two waves write the same word. An input run
 // at its own start offset mi is read so that each lane gets the input bytes
@@ -241,6 +242,16 @@ __device__ __forceinline__ int64_t window_words(const void* p, int64_t nbytes)
     return nbytes > 0 ? (start_offset(p) + nbytes + 15) >> 4 : 0;
 }
 
+// Words of p's aligned window that precede the first 128-byte line boundary
+// at or after its start (0..7). Chunks start at window word 64j - lead, so
+// every chunk covers whole 128-byte lines of the output: chunks that split
+// lines had neighbouring workgroups (often on different XCDs, with their
+// own L2s) fetch the shared lines twice.
+__device__ __forceinline__ int line_lead(const void* p)
+{
+    return (int)((reinterpret_cast<uintptr_t>(p) >> 4) & 7u);
+}
+
 // The words an input supplies to lane t of chunk j, fetched (every load
 // issued, none waited on) so that a caller can fetch all its inputs before
 // realigning any: a branch between fetches made the compiler wait for each
@@ -252,14 +263,14 @@ struct ChunkWords {
 
 template <bool STREAM>
 __device__ __forceinline__ ChunkWords fetch_for_chunk(const void* p, int64_t nbytes, int mo,
-                                                      int64_t j)
+                                                      int64_t wbase)
 {
     const int lane = threadIdx.x & 63;
     const int mi = start_offset(p);
     const u32x4* w0 = aligned_down(p);
     const int64_t count = window_words(p, nbytes);
     const int d = mi - mo;
-    const int64_t q0 = 64 * j + (d < 0 ? -1 : 0);
+    const int64_t q0 = wbase + (d < 0 ? -1 : 0);
     // indexes clamped into the input's window (no branch around the loads);
     // a clamped word only supplies bytes outside the run
     const int64_t i = q0 + lane;
@@ -278,17 +289,18 @@ __device__ __forceinline__ u32x4 chunk_word(const ChunkWords& w)
 }
 
 template <bool STREAM>
-__device__ __forceinline__ u32x4 load_for_chunk(const void* p, int64_t nbytes, int mo, int64_t j)
+__device__ __forceinline__ u32x4 load_for_chunk(const void* p, int64_t nbytes, int mo,
+                                                int64_t wbase)
 {
-    return chunk_word(fetch_for_chunk<STREAM>(p, nbytes, mo, j));
+    return chunk_word(fetch_for_chunk<STREAM>(p, nbytes, mo, wbase));
 }
 
 template <bool STREAM>
-__device__ __forceinline__ void store_chunk(void* p, int64_t nbytes, int64_t j, const u32x4& v)
+__device__ __forceinline__ void store_chunk(void* p, int64_t nbytes, int64_t wbase, const u32x4& v)
 {
     const int lane = threadIdx.x & 63;
     const int mo = start_offset(p);
-    put_word<STREAM>(aligned_down(p), 64 * j + lane, v, mo, mo + nbytes);
+    put_word<STREAM>(aligned_down(p), wbase + lane, v, mo, mo + nbytes);
 }
 
 // Elements of a 16-byte word: 8 of a 2-byte type, 4 binary32.

@@ -428,13 +428,16 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
     // rowbuf holds (nbytes + 15) / 16 + 2 words: q and q + 1 stay inside for
     // q <= qmax; lanes past the row's last word are clamped (not stored)
     const int qmax = (int)((nbytes + 15) / 16);
-    for (int64_t c = wave; 64 * c < words; c += kRowWaves) {
-        // output word w holds row bytes [16w - mo, 16w - mo + 16)
-        int q = (int)((16 * (64 * c + lane) - mo) >> 4);
-        q = q < qmax ? q : qmax;
+    const int lead = line_lead(po);
+    for (int64_t c = wave; 64 * c - lead < words; c += kRowWaves) {
+        const int64_t wbase = 64 * c - lead;  // chunks of whole 128-byte output lines
+        // output word w holds row bytes [16w - mo, 16w - mo + 16); words
+        // before the row (w < 0) read clamped words and are not stored
+        int q = (int)((16 * (wbase + lane) - mo) >> 4);
+        q = q < -1 ? -1 : (q < qmax ? q : qmax);
         const u32x4 xw = sh == 0 ? rowbuf[q] : window_at(rowbuf[q < 0 ? 0 : q], rowbuf[q + 1], sh);
-        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, c);
-        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, c);
+        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, wbase);
+        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, wbase);
         const u32x4 sw = chunk_word(fsw);
         const u32x4 hw = chunk_word(fhw);
         using W = Word<DT>;
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
             const float mm = nv * a;
             o[e] = mm + W::get(hw, e);
         }
-        store_chunk<true>(po, nbytes, c, W::make(o));
+        store_chunk<true>(po, nbytes, wbase, W::make(o));
     }
 }
 
