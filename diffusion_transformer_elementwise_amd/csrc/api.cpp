@@ -158,7 +158,7 @@ int check_rms(const void* x, const void* scale, const void* shift, float eps,
     int st = layout(ptrs, 4, D, es, strict, RGA_RMS_MAX_D, fast);
     if (st != RGA_OK)
         return st;
-    if (!rga::rms_modulate_grid_fits(B, L, D, *fast))
+    if (!rga::rms_modulate_grid_fits(B, L, D, es, *fast))
         return RGA_ERR_UNSUPPORTED;
 
     const int64_t mod_bytes = mod_mode == RGA_MOD_TOKEN ? bytes : B * D * es;
@@ -200,7 +200,7 @@ int check_fused(const void* x, const void* u, const void* g,
     int st = layout(ptrs, 7, D, es, strict, RGA_RMS_MAX_D, fast);
     if (st != RGA_OK)
         return st;
-    if (!rga::gate_add_rms_modulate_grid_fits(B, L, D))
+    if (!rga::gate_add_rms_modulate_grid_fits(B, L, D, es, *fast))
         return RGA_ERR_UNSUPPORTED;
 
     const bool full = gate_mode == RGA_GATE_FULL;

@@ -515,10 +515,16 @@ hipError_t launch_dt(const void* x, const void* u, const void* g,
 
 }  // namespace
 
-bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D)
+// Grid x is L workgroups of 64 lanes, or of kBlock * kRowWaves lanes for the
+// LDS-staged rows; its size in work-items must fit 32 bits.
+bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast)
 {
-    (void)D;
-    return L <= (((int64_t)1 << 32) - 1) / kBlock && B <= 65535;
+    if (B > 65535)
+        return false;
+    const bool regs = es == 2 && ceil_div(ceil_div(D, 8), 64) <= kRegsLadder[7];
+    const bool lds = !fast && !regs && row_lds_bytes(D, es) <= kMaxRowLds;
+    const int64_t wg = lds ? kBlock * kRowWaves : kBlock;
+    return L <= (((int64_t)1 << 32) - 1) / wg;
 }
 
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,

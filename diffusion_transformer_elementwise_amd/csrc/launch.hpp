@@ -20,7 +20,7 @@ hipError_t launch_gate_add(const void* x, const void* u, const void* g,
                            hipStream_t stream);
 
 // modulation (rms_modulate.hip)
-bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, bool fast);
+bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast);
 hipError_t launch_rms_modulate(const void* x, const void* scale,
                                const void* shift, float eps, void* out,
                                int64_t B, int64_t L, int64_t D, int mod_mode,
@@ -34,7 +34,7 @@ hipError_t launch_ln_modulate(const void* x, const void* scale,
                               int dtype, bool fast, hipStream_t stream);
 
 // residual update then modulation, one pass (gate_add_rms_modulate.hip)
-bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D);
+bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast);
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
                                         const void* g, const void* scale,
                                         const void* shift, float eps,

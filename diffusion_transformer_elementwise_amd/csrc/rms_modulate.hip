@@ -51,7 +51,15 @@ namespace rga {
 namespace {
 
 constexpr int kBlock = 64;  // one wave per workgroup
-constexpr int kRowsPerWave = 2;
+// Rows per wave of the fast path: two with row modulation (the scale and
+// shift rows held in registers serve both), one with per-token modulation
+// (nothing to share, and two rows would put 64 KB of traffic through one
+// wave).
+template <int MOD>
+constexpr int rows_per_wave()
+{
+    return MOD == kModToken ? 1 : 2;
+}
 constexpr int kStage = 1024;  // element path: elements staged in LDS per sum step
 constexpr int kApply = 512;   // element path: elements per apply step
 
@@ -88,8 +96,9 @@ __device__ __forceinline__ void modulate_rows(
     constexpr bool kHold = (MOD == kModRow);
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
-    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerWave;
-    const int64_t r1 = (r0 + kRowsPerWave < L) ? r0 + kRowsPerWave : L;
+    constexpr int kRows = rows_per_wave<MOD>();
+    const int64_t r0 = (int64_t)blockIdx.x * kRows;
+    const int64_t r1 = (r0 + kRows < L) ? r0 + kRows : L;
 
     Pack<DT> sc[kHold ? G : 1], sh[kHold ? G : 1];
     if constexpr (kHold) {
@@ -169,7 +178,7 @@ __device__ __forceinline__ void modulate_rows(
     }
 }
 
-// Grid: x = tile of kRowsPerWave rows, y = batch.
+// Grid: x = tile of rows_per_wave<MOD>() rows, y = batch.
 template <int G, int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
@@ -564,7 +573,7 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
         return hipErrorInvalidValue;
     void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &vpr};
     return hipLaunchKernel(reinterpret_cast<const void*>(k),
-                           dim3((uint32_t)ceil_div(L, kRowsPerWave), (uint32_t)B),
+                           dim3((uint32_t)ceil_div(L, rows_per_wave<MOD>()), (uint32_t)B),
                            dim3(kBlock), args, 0, stream);
 }
 
@@ -595,11 +604,19 @@ hipError_t launch_norm(const void* x, const void* scale, const void* shift, floa
 
 }  // namespace
 
-bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, bool fast)
+// Grid x holds at most L workgroups (one or two rows each on the fast path,
+// one row on the element paths); its size in work-items, L times the
+// workgroup size, must fit 32 bits: 64 lanes, or kBlock * kRowWaves for the
+// LDS-staged rows (binary32 rows and 2-byte rows over the register limit
+// that fit the LDS buffer).
+bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast)
 {
-    (void)D;
-    const int64_t rows = fast ? ceil_div(L, kRowsPerWave) : L;
-    return rows <= (((int64_t)1 << 32) - 1) / kBlock && B <= 65535;
+    if (B > 65535)
+        return false;
+    const bool regs = es == 2 && ceil_div(ceil_div(D, 8), 64) <= kRegsLadder[7];
+    const bool lds = !fast && !regs && row_lds_bytes(D, es) <= kMaxRowLds;
+    const int64_t wg = lds ? kBlock * kRowWaves : kBlock;
+    return L <= (((int64_t)1 << 32) - 1) / wg;
 }
 
 hipError_t launch_rms_modulate(const void* x, const void* scale,

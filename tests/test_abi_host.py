@@ -395,6 +395,27 @@ def test_grid_limits(dte):
     assert dte.check_residual_gate_add(x, u, g, o, 1, 1, n_max * 2, dte.GATE_FULL) == uns
 
 
+def test_grid_limit_of_the_lds_staged_rows(dte):
+    # binary32 rows of the element path are staged in LDS by workgroups of 8
+    # waves (512 work-items), one per row: L * 512 must stay below 2^32, a
+    # tighter limit than the 64-lane kernels' (rows of 2-byte elements in
+    # registers); the fused call has the same limit
+    ok, uns = dte.RGA_OK, dte.RGA_ERR_UNSUPPORTED
+    GB = 1024 * MB
+    L_max = ((1 << 32) - 1) // 512
+    D = 100  # D % 8 != 0: element path
+    ts = [A + k * 8 * GB for k in range(8)]  # each > L_max * D * 4 bytes apart
+    for L, want in ((L_max, ok), (L_max + 1, uns)):
+        assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L, D,
+                                         dte.MOD_ROW, dte.DTYPE_F32) == want, L
+        assert dte.check_gate_add_rms_modulate_ex(ts[0], ts[1], ts[2], ts[3], ts[4], 1e-6,
+                                                  ts[5], ts[6], 1, L, D, dte.GATE_FULL,
+                                                  dte.MOD_TOKEN, dte.DTYPE_F32) == want, L
+    # the same L with 2-byte rows runs the 64-lane register kernels
+    assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L_max + 1, D,
+                                     dte.MOD_ROW, dte.DTYPE_BF16) == ok
+
+
 def test_package_fails_loudly_without_the_library(tmp_path):
     # a copy of the Python package without librga.so must refuse to import
     # (no CPU fallback anywhere)
