@@ -257,11 +257,14 @@ def test_token_modulation_at_video_scale(dte, dtype):
     _zero_ulp(to_host_typed(y), wy, dtype, "token fused y")
 
 
-def test_in_place_ex(dte):
-    # element path in place: out == x for the gate-add and the modulation,
-    # x_out == x and y == u for the fused call (D % 8 != 0)
-    B, L, D, dtype = 2, 11, 1003, F16
-    say(f"[in place ex] B={B} L={L} D={D}")
+@pytest.mark.parametrize("dtype,D", [(F16, 1003), (F32, 1003), (BF16, 16390), (BF16, 33001)],
+                         ids=["regs", "lds-f32", "lds-wide", "two-pass"])
+def test_in_place_ex(dte, dtype, D):
+    # element paths in place: out == x for the gate-add and the modulation,
+    # x_out == x and y == u for the fused call (D % 8 != 0); rows held in
+    # registers, staged in LDS (binary32, long rows) and over 64 KB
+    B, L = 2, 11
+    say(f"[in place ex] {NAMES[dtype]} B={B} L={L} D={D}")
     x, u, g = _gate_inputs(8000, B, L, D, GATE_FULL, dtype)
     s, t = _mod_inputs(8003, B, L, D, MOD_TOKEN, dtype)
     dx = to_dev_typed(x, dtype)
