@@ -8,7 +8,15 @@ from ._lib import (DTYPE_BF16, DTYPE_F16, DTYPE_F32, GATE_BCAST, GATE_FULL, MOD_
                    MOD_TOKEN, RGA_OK, RGAError, library)
 
 
+# torch's raw accessor of the current stream (what its own compiled kernels
+# use) costs ~0.1 us against ~2 us for building a torch.cuda.Stream object;
+# builds without it take the public API
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device: torch.device) -> int:
+    if _raw_stream is not None and device.index is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -17,13 +25,15 @@ _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: 
 
 
 def _require(t: torch.Tensor, name: str, device=None, dtype=torch.bfloat16) -> None:
+    # dtype by identity and device by index: building torch.device objects
+    # for every check was a measurable part of a small call's host time
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
+    if t.dtype is not dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a HIP device, got {t.device}")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -44,10 +54,10 @@ def _storage(x) -> torch.dtype:
     return x.dtype
 
 
-def _gate(x, u, g, gate_mode, dtype) -> int:
+def _gate(x, u, g, gate_mode, dtype, dev) -> int:
     B, L, D = x.shape
-    _require(u, "u", x.device, dtype)
-    _require(g, "g", x.device, dtype)
+    _require(u, "u", dev, dtype)
+    _require(g, "g", dev, dtype)
     if u.shape != x.shape:
         raise ValueError(f"u has shape {tuple(u.shape)}, expected {tuple(x.shape)}")
     if gate_mode is None:
@@ -58,22 +68,22 @@ def _gate(x, u, g, gate_mode, dtype) -> int:
     return int(gate_mode)
 
 
-def _modulation(x, scale, shift, mod_mode, dtype) -> int:
+def _modulation(x, scale, shift, mod_mode, dtype, dev) -> int:
     B, L, D = x.shape
     if mod_mode is None:
         mod_mode = MOD_TOKEN if (L != 1 and tuple(scale.shape) == (B, L, D)) else MOD_ROW
     want = (B, L, D) if mod_mode == MOD_TOKEN else (B, 1, D)
     for name, t in (("scale", scale), ("shift", shift)):
-        _require(t, name, x.device, dtype)
+        _require(t, name, dev, dtype)
         if mod_mode in (MOD_ROW, MOD_TOKEN) and tuple(t.shape) != want:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
     return int(mod_mode)
 
 
-def _output(t, name, x):
+def _output(t, name, x, dev):
     if t is None:
         return torch.empty_like(x)
-    _require(t, name, x.device, x.dtype)
+    _require(t, name, dev, x.dtype)
     if t.shape != x.shape:
         raise ValueError(f"{name} must have x's shape")
     return t
@@ -88,11 +98,12 @@ def rga_residual_gate_add(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
     gate_mode is inferred from g's shape when None. ``out`` may be x or u
     (in place), or g in full mode. Enqueued on the current stream."""
     B, L, D = _x_shape(x, torch.bfloat16)
-    gate_mode = _gate(x, u, g, gate_mode, torch.bfloat16)
-    out = _output(out, "out", x)
+    dev = x.device
+    gate_mode = _gate(x, u, g, gate_mode, torch.bfloat16, dev)
+    out = _output(out, "out", x, dev)
     st = library().rga_residual_gate_add(
         x.data_ptr(), u.data_ptr(), g.data_ptr(), out.data_ptr(), B, L, D,
-        gate_mode, _stream_handle(x.device))
+        gate_mode, _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_residual_gate_add")
     return out
@@ -105,11 +116,12 @@ def rga_residual_gate_add_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
     type), any D, and tensors that start at any element offset."""
     dt = _storage(x)
     B, L, D = _x_shape(x, dt)
-    gate_mode = _gate(x, u, g, gate_mode, dt)
-    out = _output(out, "out", x)
+    dev = x.device
+    gate_mode = _gate(x, u, g, gate_mode, dt, dev)
+    out = _output(out, "out", x, dev)
     st = library().rga_residual_gate_add_ex(
         x.data_ptr(), u.data_ptr(), g.data_ptr(), out.data_ptr(), B, L, D,
-        gate_mode, _DTYPES[dt], _stream_handle(x.device))
+        gate_mode, _DTYPES[dt], _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_residual_gate_add_ex")
     return out
@@ -123,11 +135,12 @@ def rms_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     x: [B, L, D]; scale, shift: [B, 1, D]; ``out`` may be x (in place).
     eps is passed as binary32. Enqueued on the current stream."""
     B, L, D = _x_shape(x, torch.bfloat16)
-    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16)
-    out = _output(out, "out", x)
+    dev = x.device
+    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16, dev)
+    out = _output(out, "out", x, dev)
     st = library().rms_modulate(
         x.data_ptr(), scale.data_ptr(), shift.data_ptr(), float(eps),
-        out.data_ptr(), B, L, D, _stream_handle(x.device))
+        out.data_ptr(), B, L, D, _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rms_modulate")
     return out
@@ -141,11 +154,12 @@ def rga_rms_modulate_ex(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tenso
     ([B, 1, D], MOD_ROW); mod_mode is inferred from scale's shape when None."""
     dt = _storage(x)
     B, L, D = _x_shape(x, dt)
-    mod_mode = _modulation(x, scale, shift, mod_mode, dt)
-    out = _output(out, "out", x)
+    dev = x.device
+    mod_mode = _modulation(x, scale, shift, mod_mode, dt, dev)
+    out = _output(out, "out", x, dev)
     st = library().rga_rms_modulate_ex(
         x.data_ptr(), scale.data_ptr(), shift.data_ptr(), float(eps),
-        out.data_ptr(), B, L, D, mod_mode, _DTYPES[dt], _stream_handle(x.device))
+        out.data_ptr(), B, L, D, mod_mode, _DTYPES[dt], _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_rms_modulate_ex")
     return out
@@ -159,11 +173,12 @@ def rga_ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     per batch row [B, 1, D] or per token [B, L, D]. ``out`` may be x."""
     dt = _storage(x)
     B, L, D = _x_shape(x, dt)
-    mod_mode = _modulation(x, scale, shift, mod_mode, dt)
-    out = _output(out, "out", x)
+    dev = x.device
+    mod_mode = _modulation(x, scale, shift, mod_mode, dt, dev)
+    out = _output(out, "out", x, dev)
     st = library().rga_ln_modulate(
         x.data_ptr(), scale.data_ptr(), shift.data_ptr(), float(eps),
-        out.data_ptr(), B, L, D, mod_mode, _DTYPES[dt], _stream_handle(x.device))
+        out.data_ptr(), B, L, D, mod_mode, _DTYPES[dt], _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_ln_modulate")
     return out
@@ -178,14 +193,15 @@ def rga_gate_add_rms_modulate(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
     """x_out = x + u * g, then y = rms_norm(x_out, eps) * (1 + scale) + shift,
     in one pass. Returns (x_out, y). x_out and y may each be x or u."""
     B, L, D = _x_shape(x, torch.bfloat16)
-    gate_mode = _gate(x, u, g, gate_mode, torch.bfloat16)
-    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16)
-    x_out = _output(x_out, "x_out", x)
-    y = _output(y, "y", x)
+    dev = x.device
+    gate_mode = _gate(x, u, g, gate_mode, torch.bfloat16, dev)
+    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16, dev)
+    x_out = _output(x_out, "x_out", x, dev)
+    y = _output(y, "y", x, dev)
     st = library().rga_gate_add_rms_modulate(
         x.data_ptr(), u.data_ptr(), g.data_ptr(), scale.data_ptr(),
         shift.data_ptr(), float(eps), x_out.data_ptr(), y.data_ptr(), B, L, D,
-        gate_mode, _stream_handle(x.device))
+        gate_mode, _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_gate_add_rms_modulate")
     return x_out, y
@@ -202,14 +218,15 @@ def rga_gate_add_rms_modulate_ex(x: torch.Tensor, u: torch.Tensor, g: torch.Tens
     element offset, and per-token or per-batch-row scale/shift."""
     dt = _storage(x)
     B, L, D = _x_shape(x, dt)
-    gate_mode = _gate(x, u, g, gate_mode, dt)
-    mod_mode = _modulation(x, scale, shift, mod_mode, dt)
-    x_out = _output(x_out, "x_out", x)
-    y = _output(y, "y", x)
+    dev = x.device
+    gate_mode = _gate(x, u, g, gate_mode, dt, dev)
+    mod_mode = _modulation(x, scale, shift, mod_mode, dt, dev)
+    x_out = _output(x_out, "x_out", x, dev)
+    y = _output(y, "y", x, dev)
     st = library().rga_gate_add_rms_modulate_ex(
         x.data_ptr(), u.data_ptr(), g.data_ptr(), scale.data_ptr(),
         shift.data_ptr(), float(eps), x_out.data_ptr(), y.data_ptr(), B, L, D,
-        gate_mode, mod_mode, _DTYPES[dt], _stream_handle(x.device))
+        gate_mode, mod_mode, _DTYPES[dt], _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_gate_add_rms_modulate_ex")
     return x_out, y
@@ -226,14 +243,15 @@ def gelu_tanh(x: torch.Tensor, bias: torch.Tensor | None = None,
         raise ValueError("x needs at least one dimension")
     F = x.shape[-1]
     rows = x.numel() // F if F else 0
+    dev = x.device
     if bias is not None:
-        _require(bias, "bias", x.device, dt)
+        _require(bias, "bias", dev, dt)
         if tuple(bias.shape) != (F,):
             raise ValueError(f"bias has shape {tuple(bias.shape)}, expected {(F,)}")
-    out = _output(out, "out", x)
+    out = _output(out, "out", x, dev)
     st = library().rga_gelu_tanh(
         x.data_ptr(), None if bias is None else bias.data_ptr(), out.data_ptr(),
-        rows, F, _DTYPES[dt], _stream_handle(x.device))
+        rows, F, _DTYPES[dt], _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_gelu_tanh")
     return out
