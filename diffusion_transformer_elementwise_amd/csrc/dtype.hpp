@@ -238,6 +238,21 @@ struct Grouped {
         if (t < h)
             p.store_stream(b, c0 + t);
     }
+    // load_raw / load_stream_raw without a branch around the load: the index
+    // is clamped to the row's last pack (c0 + h - 1, which every row has) and
+    // the zeros are selected afterwards. A branch per load made the compiler
+    // wait for one pack's loads before issuing the next pack's.
+    template <bool STREAM>
+    __device__ __forceinline__ static Pack<DT> load_clamped(const void* b, int64_t c0, int t, int h)
+    {
+        const int tc = t < h ? t : h - 1;
+        Pack<DT> p = STREAM ? Pack<DT>::load_stream(b, c0 + tc) : Pack<DT>::load(b, c0 + tc);
+        const bool in = t < h;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            p.v[d] = in ? p.v[d] : 0u;
+        return p;
+    }
     __device__ __forceinline__ static Pack<DT> to_groups(const Pack<DT>& p) { return p; }
     __device__ __forceinline__ static Pack<DT> to_raw(const Pack<DT>& p) { return p; }
     __device__ __forceinline__ static Pack<DT> load_stream(const void* b, int64_t c0, int t, int h)
@@ -270,6 +285,28 @@ struct Grouped<kF32> {
         Pack<kF32> p;
         p.a = w < 2 * h ? (STREAM ? load16_stream(q + w) : load16(q + w)) : z;
         p.b = 64 + w < 2 * h ? (STREAM ? load16_stream(q + 64 + w) : load16(q + 64 + w)) : z;
+        return p;
+    }
+    // load_any without branches: word indexes clamped to the row's last word
+    // (2(c0 + h) - 1), zeros selected afterwards
+    template <bool STREAM>
+    __device__ __forceinline__ static Pack<kF32> load_clamped(const void* base, int64_t c0, int t,
+                                                              int h)
+    {
+        const u32x4* q = static_cast<const u32x4*>(base) + 2 * c0;
+        const int w = wa(t);
+        const int wb = 64 + w;
+        const int last = 2 * h - 1;
+        Pack<kF32> p;
+        p.a = STREAM ? load16_stream(q + (w < 2 * h ? w : last)) : load16(q + (w < 2 * h ? w : last));
+        p.b = STREAM ? load16_stream(q + (wb < 2 * h ? wb : last))
+                     : load16(q + (wb < 2 * h ? wb : last));
+        const bool ia = w < 2 * h, ib = wb < 2 * h;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            p.a[d] = ia ? p.a[d] : 0u;
+            p.b[d] = ib ? p.b[d] : 0u;
+        }
         return p;
     }
     __device__ __forceinline__ static Pack<kF32> load_raw(const void* b, int64_t c0, int t, int h)

@@ -74,16 +74,23 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
     // rounded x' that feeds the ordered sum goes to group order. Every lane
     // runs every pack (binary32 packs trade data across lanes); packs past
     // the row end load as zeros and are not stored.
+    // every pack's loads are issued before the first add (no branch around a
+    // load), so a wave keeps its whole row of x, u and g in flight
     using GP = Grouped<DT>;
+    Pack<DT> xv[G], uv[G], gv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
+        uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
+        gv[i] = FULL ? GP::template load_clamped<true>(g, row + 64 * i, lane, h)
+                     : GP::template load_clamped<false>(g, b * vpr + 64 * i, lane, h);
+    }
     Pack<DT> xn[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int h = vpr - 64 * i;
-        const Pack<DT> xv = GP::load_stream_raw(x, row + 64 * i, lane, h);
-        const Pack<DT> uv = GP::load_stream_raw(u, row + 64 * i, lane, h);
-        const Pack<DT> gv = FULL ? GP::load_stream_raw(g, row + 64 * i, lane, h)
-                                 : GP::load_raw(g, b * vpr + 64 * i, lane, h);
-        const Pack<DT> xr = gate_add8<DT>(xv, uv, gv);
+        const Pack<DT> xr = gate_add8<DT>(xv[i], uv[i], gv[i]);
         GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
         xn[i] = GP::to_groups(xr);
     }
@@ -106,14 +113,22 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
     const float q = sqrtf(t);
     const float rr = 1.0f / q;
 
+    // the scale and shift rows likewise, before the first apply
+    Pack<DT> scs[G], shs[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        scs[i] = MOD == kModToken ? GP::template load_clamped<true>(scale, row + 64 * i, lane, h)
+                                  : GP::template load_clamped<false>(scale, b * vpr + 64 * i, lane, h);
+        shs[i] = MOD == kModToken ? GP::template load_clamped<true>(shift, row + 64 * i, lane, h)
+                                  : GP::template load_clamped<false>(shift, b * vpr + 64 * i, lane, h);
+    }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int h = vpr - 64 * i;
         const Pack<DT> xr = GP::to_raw(xn[i]);
-        const Pack<DT> sc = MOD == kModToken ? GP::load_stream_raw(scale, row + 64 * i, lane, h)
-                                             : GP::load_raw(scale, b * vpr + 64 * i, lane, h);
-        const Pack<DT> sh = MOD == kModToken ? GP::load_stream_raw(shift, row + 64 * i, lane, h)
-                                             : GP::load_raw(shift, b * vpr + 64 * i, lane, h);
+        const Pack<DT>& sc = scs[i];
+        const Pack<DT>& sh = shs[i];
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

@@ -52,6 +52,60 @@ __device__ __forceinline__ u32x4 window_at(const u32x4& c, const u32x4& n, int o
                  __builtin_amdgcn_alignbyte(s3, s2, sh), __builtin_amdgcn_alignbyte(s4, s3, sh)};
 }
 
+// The same cut for a compile-time O: fixed dword picks, and alignbyte only
+// when O is not a multiple of 4 (2-byte elements at an odd element offset).
+template <int O>
+__device__ __forceinline__ u32x4 window_c(const u32x4& c, const u32x4& n)
+{
+    static_assert(O >= 0 && O < 16, "byte offset inside a word");
+    const uint32_t s[8] = {c[0], c[1], c[2], c[3], n[0], n[1], n[2], n[3]};
+    constexpr int q = O >> 2, sh = O & 3;
+    if constexpr (sh == 0)
+        return u32x4{s[q], s[q + 1], s[q + 2], s[q + 3]};
+    else
+        return u32x4{__builtin_amdgcn_alignbyte(s[q + 1], s[q], sh),
+                     __builtin_amdgcn_alignbyte(s[q + 2], s[q + 1], sh),
+                     __builtin_amdgcn_alignbyte(s[q + 3], s[q + 2], sh),
+                     __builtin_amdgcn_alignbyte(s[q + 4], s[q + 3], sh)};
+}
+
+// A byte offset as a type: O in 0..15, or -1 for one known only at run time.
+template <int O>
+struct Offset {
+    static constexpr int value = O;
+};
+
+// window_c<O> where the offset is fixed, else window_at with the run-time o.
+template <int O>
+__device__ __forceinline__ u32x4 window_o(const u32x4& c, const u32x4& n, int o)
+{
+    if constexpr (O >= 0)
+        return window_c<O>(c, n);
+    else
+        return window_at(c, n, o);
+}
+
+// f(Offset<o>{}) for a wave-uniform byte offset o: one scalar branch, then
+// straight-line code for that offset, where window_at spends 15 selects
+// per word on an offset known only at run time. Runs of 2- and 4-byte
+// elements at element-aligned addresses have even offsets; an odd one
+// (not reachable through the library's calls) takes the run-time form.
+template <typename F>
+__device__ __forceinline__ void dispatch_offset(int o, F&& f)
+{
+    switch (o) {
+    case 0: f(Offset<0>{}); break;
+    case 2: f(Offset<2>{}); break;
+    case 4: f(Offset<4>{}); break;
+    case 6: f(Offset<6>{}); break;
+    case 8: f(Offset<8>{}); break;
+    case 10: f(Offset<10>{}); break;
+    case 12: f(Offset<12>{}); break;
+    case 14: f(Offset<14>{}); break;
+    default: f(Offset<-1>{}); break;
+    }
+}
+
 // DPP wave shifts by one lane; a lane with no source keeps `fill`.
 __device__ __forceinline__ u32x4 lane_from_next(const u32x4& v, const u32x4& fill)
 {
@@ -124,13 +178,16 @@ __device__ __forceinline__ void load_run(const void* p, int n, u32x4 (&w)[K], u3
 template <int K>
 __device__ __forceinline__ void realign_in(u32x4 (&w)[K], const u32x4& extra, int m)
 {
-    if (m == 0)
-        return;
+    dispatch_offset(m, [&](auto off) {
+        constexpr int O = decltype(off)::value;
+        if constexpr (O != 0) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const u32x4 fill = (k + 1 < K) ? read_lane(w[k + 1 < K ? k + 1 : k], 0) : extra;
-        w[k] = window_at(w[k], lane_from_next(w[k], fill), m);
-    }
+            for (int k = 0; k < K; ++k) {
+                const u32x4 fill = (k + 1 < K) ? read_lane(w[k + 1 < K ? k + 1 : k], 0) : extra;
+                w[k] = window_o<O>(w[k], lane_from_next(w[k], fill), m);
+            }
+        }
+    });
 }
 
 template <int K, bool STREAM>
@@ -190,27 +247,35 @@ __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K])
     u32x4* w0 = aligned_down(p);
     const int end = mo + 2 * n;
     const int words = (end + 15) >> 4;
-    u32x4 fill = u32x4{0, 0, 0, 0};
     u32x4 first = u32x4{0, 0, 0, 0}, last = u32x4{0, 0, 0, 0};
+    dispatch_offset(mo, [&](auto off) {
+        constexpr int O = decltype(off)::value;
+        // the cut at 16 - mo, fixed with mo
+        constexpr int C = O > 0 ? 16 - O : -1;
+        u32x4 fill = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const u32x4 v = mo == 0 ? g[k] : window_at(lane_from_prev(g[k], fill), g[k], 16 - mo);
-        fill = read_lane(g[k], 63);
-        const int w = lane + 64 * k;
-        if (16 * w >= mo && 16 * w + 16 <= end) {
-            if (STREAM)
-                store16_stream(w0 + w, v);
-            else
-                w0[w] = v;
+        for (int k = 0; k < K; ++k) {
+            u32x4 v = g[k];
+            if constexpr (O != 0)
+                v = window_o<C>(lane_from_prev(g[k], fill), g[k], 16 - mo);
+            fill = read_lane(g[k], 63);
+            const int w = lane + 64 * k;
+            if (16 * w >= mo && 16 * w + 16 <= end) {
+                if (STREAM)
+                    store16_stream(w0 + w, v);
+                else
+                    w0[w] = v;
+            }
+            if (k == 0)
+                first = v;
+            if (w == words - 1)
+                last = v;
         }
-        if (k == 0)
-            first = v;
-        if (w == words - 1)
-            last = v;
-    }
-    // word 64K (only reached when mo > 0): the tail of group 64K - 1
-    if (words - 1 == 64 * K)
-        last = window_at(fill, u32x4{0, 0, 0, 0}, 16 - mo);
+        // word 64K (only reached when mo > 0): the tail of group 64K - 1
+        if constexpr (O != 0)
+            if (words - 1 == 64 * K)
+                last = window_o<C>(fill, u32x4{0, 0, 0, 0}, 16 - mo);
+    });
     const int wl = words - 1;
     const bool last_partial = (end & 15) != 0;
     if (lane == 0 && mo != 0)
@@ -283,6 +348,8 @@ __device__ __forceinline__ ChunkWords fetch_for_chunk(const void* p, int64_t nby
     return r;
 }
 
+// One word per lane: the run-time cut (selects) measured faster here than a
+// branch to code for the offset, which slowed a chunked gated add by half.
 __device__ __forceinline__ u32x4 chunk_word(const ChunkWords& w)
 {
     return w.sh == 0 ? w.cur : window_at(w.cur, lane_from_next(w.cur, w.extra), w.sh);
