@@ -322,8 +322,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
     const int qmax = (int)words_xo;
     if (wave == 0) {
         const int groups = (n + 7) >> 3;
-        float acc = 0.0f;
-        for (int gi = lane; gi < groups; gi += kBlock) {
+        auto group_at = [&](int gi) {
             Pack<DT> p;
             if constexpr (DT == kF32) {
                 p.a = lds_bytes16(rowbuf, mxo + 32 * gi, mxo, qmax);
@@ -331,6 +330,32 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
             } else {
                 p.v = lds_bytes16(rowbuf, mxo + 16 * gi, mxo, qmax);
             }
+            return p;
+        };
+        float acc = 0.0f;
+        // batches of U groups wholly inside the row: the U reads are issued
+        // before any is added (one LDS round trip per batch); the additions
+        // keep the fixed order. The rest, masked, below.
+        constexpr int U = DT == kF32 ? 4 : 8;
+        const int n_whole = n >> 3;
+        int gi = lane;
+        for (; gi + kBlock * (U - 1) < n_whole; gi += kBlock * U) {
+            Pack<DT> p[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                p[u] = group_at(gi + kBlock * u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a = p[u].get(e);
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
+            }
+        }
+        for (; gi < groups; gi += kBlock) {
+            const Pack<DT> p = group_at(gi);
             const bool whole = 8 * gi + 8 <= n;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {

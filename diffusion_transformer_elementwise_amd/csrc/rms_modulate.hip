@@ -359,7 +359,34 @@ __device__ __forceinline__ float lds_row_sum(const u32x4* rowbuf, int n, float m
     const int lane = threadIdx.x & 63;
     const int groups = (n + 7) >> 3;
     float acc = 0.0f;
-    for (int g = lane; g < groups; g += kBlock) {
+    // batches of U groups wholly inside the row: the U reads are issued
+    // before any is added (one LDS round trip per batch rather than per
+    // group); the additions keep the fixed order. The rest, masked, below.
+    constexpr int U = DT == kF32 ? 4 : 8;
+    const int n_whole = n >> 3;
+    int g = lane;
+    for (; g + kBlock * (U - 1) < n_whole; g += kBlock * U) {
+        Pack<DT> p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            p[u] = Span<DT, kRowStage>::group(rowbuf, g + kBlock * u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = p[u].get(e);
+                if (what == 0) {
+                    acc = acc + a;
+                } else {
+                    if (what == 2)
+                        a = a - mu;
+                    const float sa = a * a;
+                    acc = acc + sa;
+                }
+            }
+        }
+    }
+    for (; g < groups; g += kBlock) {
         const Pack<DT> p = Span<DT, kRowStage>::group(rowbuf, g);
         const bool whole = 8 * g + 8 <= n;
 #pragma unroll
