@@ -185,6 +185,52 @@ def test_mixed_offsets(dte, D, dtype):
                    f"gelu out+{off}")
 
 
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=NAMES.get)
+@pytest.mark.parametrize("D", [1000, 4100])
+def test_every_offset_of_every_operand(dte, D, dtype):
+    # the register-resident rows realign each operand with code for its byte
+    # offset inside a 16-byte word (8 even offsets for a 2-byte type): each
+    # operand is moved through all 8 element offsets, every operand at a
+    # different one. D = 1000 keeps an operand's rows at one offset, D = 4100
+    # alternates two.
+    B, L = 2, 3
+    x, u, g = _gate_inputs(5400 + D, B, L, D, GATE_BCAST, dtype)
+    gf = random_typed(5401 + D, (B, L, D), U11, dtype)
+    s, t = _mod_inputs(5402 + D, B, L, D, MOD_ROW, dtype)
+    ts, tt = _mod_inputs(5403 + D, B, L, D, MOD_TOKEN, dtype)
+    want_gate = oracle.gate_add_ex(x, u, g, GATE_BCAST, dtype)
+    want_rms = oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_ROW, dtype)
+    want_rms_tok = oracle.rms_modulate_ex(x, ts, tt, 1e-6, MOD_TOKEN, dtype)
+    want_ln = oracle.ln_modulate(x, s, t, 1e-6, MOD_ROW, dtype)
+    want_ln_tok = oracle.ln_modulate(x, ts, tt, 1e-6, MOD_TOKEN, dtype)
+    wbx, wby = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_BCAST, MOD_ROW, dtype)
+    wfx, wfy = oracle.gate_add_rms_modulate_ex(x, u, gf, ts, tt, 1e-6, GATE_FULL, MOD_TOKEN,
+                                               dtype)
+    for o in range(8):
+        say(f"[every offset] {NAMES[dtype]} D={D} rotation {o}")
+        dx, du, dg, dgf, ds, dt, dts, dtt = (
+            to_dev_typed(a, dtype, (o + k) % 8) for k, a in enumerate((x, u, g, gf, s, t, ts, tt)))
+        out = _empty_at((B, L, D), dx, (o + 3) % 8)
+        yo = _empty_at((B, L, D), dx, (o + 6) % 8)
+        dte.rga_residual_gate_add_ex(dx, du, dg, out=out)
+        _bit_exact(to_host_typed(out), want_gate, dtype, f"gate, rotation {o}")
+        dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6, out=out)
+        _zero_ulp(to_host_typed(out), want_rms, dtype, f"rms row, rotation {o}")
+        dte.rga_rms_modulate_ex(dx, dts, dtt, 1e-6, out=out, mod_mode=MOD_TOKEN)
+        _zero_ulp(to_host_typed(out), want_rms_tok, dtype, f"rms token, rotation {o}")
+        dte.rga_ln_modulate(dx, ds, dt, 1e-6, out=out)
+        _zero_ulp(to_host_typed(out), want_ln, dtype, f"ln row, rotation {o}")
+        dte.rga_ln_modulate(dx, dts, dtt, 1e-6, out=out, mod_mode=MOD_TOKEN)
+        _zero_ulp(to_host_typed(out), want_ln_tok, dtype, f"ln token, rotation {o}")
+        dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6, x_out=out, y=yo)
+        _bit_exact(to_host_typed(out), wbx, dtype, f"fused bcast x_out, rotation {o}")
+        _zero_ulp(to_host_typed(yo), wby, dtype, f"fused bcast y, rotation {o}")
+        dte.rga_gate_add_rms_modulate_ex(dx, du, dgf, dts, dtt, 1e-6, x_out=out, y=yo,
+                                         gate_mode=GATE_FULL, mod_mode=MOD_TOKEN)
+        _bit_exact(to_host_typed(out), wfx, dtype, f"fused full x_out, rotation {o}")
+        _zero_ulp(to_host_typed(yo), wfy, dtype, f"fused full y, rotation {o}")
+
+
 def test_bf16_ex_runs_the_same_kernels_as_the_bf16_calls(dte):
     # with bf16, row modulation, D % 8 == 0 and aligned tensors the _ex calls
     # take the pack path: identical results to the original calls
