@@ -256,22 +256,23 @@ __device__ __forceinline__ u32x4 lds_bytes16(const u32x4* buf, int pos, int sh, 
 }
 
 // Element path for rows that fit in LDS but not in registers (binary32
-// rows; 2-byte rows over 8192 elements): one workgroup of kRowWaves waves per
-// row, x, u and g read once. The waves form x' over chunks of x_out's aligned
+// rows; 2-byte rows over 8192 elements): one workgroup of NW waves per row
+// (lds_row_waves: about one per 4 KB of row), x, u and g read once. The waves form x' over chunks of x_out's aligned
 // 16-byte words (each input read realigned to x_out, realign.hpp), store it
 // and keep the words in a dynamic LDS buffer; wave 0 takes the fixed-order
 // sum from LDS (group g is the 16 or 32 bytes at x_out's offset + g * 8 *
 // es); all waves then write y over chunks of y's aligned words, x' taken
 // from LDS realigned to y. x_out is never read back.
-constexpr int kRowWaves = 8;
-constexpr int64_t kMaxRowLds = 65536 - 256;  // 64 KB per workgroup, less the static LDS
+// dynamic LDS per workgroup (the compiler also places the two-pass kernel's
+// static buffers here; a gfx950 workgroup may use more than 64 KB in all)
+constexpr int64_t kMaxRowLds = 65536 - 256;
 
 // LDS bytes of the row buffer: x_out's window words (at most one more than
 // the row's aligned words) and two spare words a cut may touch.
 int64_t row_lds_bytes(int64_t D, int es) { return ((D * es + 15) / 16 + 3) * 16; }
 
-template <bool FULL, int DT, int MOD>
-__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_kernel(
+template <bool FULL, int DT, int MOD, int NW>
+__global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
     const void* x, const void* u, const void* g, const void* scale,
     const void* shift, float eps, float d_float, void* x_out, void* y,
     int64_t L, int64_t D)
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
     const int mxo = start_offset(pxo);
     const int64_t words_xo = window_words(pxo, nbytes);
     const int lead_xo = line_lead(pxo);
-    for (int64_t c = wave; 64 * c - lead_xo < words_xo; c += kRowWaves) {
+    for (int64_t c = wave; 64 * c - lead_xo < words_xo; c += NW) {
         const int64_t wbase = 64 * c - lead_xo;  // chunks of whole 128-byte lines
         const ChunkWords fxw = fetch_for_chunk<true>(elem_ptr<DT>(x, row), nbytes, mxo, wbase);
         const ChunkWords fuw = fetch_for_chunk<true>(elem_ptr<DT>(u, row), nbytes, mxo, wbase);
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_lds_
     const int64_t words_y = window_words(py, nbytes);
     const int sh = (mxo - my) & 15;
     const int lead_y = line_lead(py);
-    for (int64_t c = wave; 64 * c - lead_y < words_y; c += kRowWaves) {
+    for (int64_t c = wave; 64 * c - lead_y < words_y; c += NW) {
         const int64_t wbase = 64 * c - lead_y;
         // y word w holds row bytes [16w - my, +16): buffer bytes from 16w - my + mxo
         const int pos = (int)(16 * (wbase + lane)) - my + mxo;
@@ -501,6 +502,16 @@ fused_kernel_t pick(int groups)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <bool FULL, int DT, int MOD>
+const void* lds_kernel(int w)
+{
+    switch (w) {
+    case 2: return reinterpret_cast<const void*>(&gate_add_rms_modulate_lds_kernel<FULL, DT, MOD, 2>);
+    case 4: return reinterpret_cast<const void*>(&gate_add_rms_modulate_lds_kernel<FULL, DT, MOD, 4>);
+    default: return reinterpret_cast<const void*>(&gate_add_rms_modulate_lds_kernel<FULL, DT, MOD, 8>);
+    }
+}
+
+template <bool FULL, int DT, int MOD>
 hipError_t launch_typed(const void* x, const void* u, const void* g,
                         const void* scale, const void* shift, float eps,
                         void* x_out, void* y, int64_t B, int64_t L, int64_t D,
@@ -517,11 +528,11 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
                                        stream);
         }
         const int64_t lds = row_lds_bytes(D, DT == kF32 ? 4 : 2);
-        if (lds <= kMaxRowLds)
-            return hipLaunchKernel(
-                reinterpret_cast<const void*>(&gate_add_rms_modulate_lds_kernel<FULL, DT, MOD>),
-                dim3((uint32_t)L, (uint32_t)B), dim3(kBlock * kRowWaves), args, (size_t)lds,
-                stream);
+        if (lds <= kMaxRowLds) {
+            const int w = lds_row_waves(D * (DT == kF32 ? 4 : 2));
+            return hipLaunchKernel(lds_kernel<FULL, DT, MOD>(w), dim3((uint32_t)L, (uint32_t)B),
+                                   dim3(kBlock * w), args, (size_t)lds, stream);
+        }
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
             dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
@@ -555,7 +566,7 @@ hipError_t launch_dt(const void* x, const void* u, const void* g,
 
 }  // namespace
 
-// Grid x is L workgroups of 64 lanes, or of kBlock * kRowWaves lanes for the
+// Grid x is L workgroups of 64 lanes, or of 64 lds_row_waves(D * es) lanes for the
 // LDS-staged rows; its size in work-items must fit 32 bits.
 bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast)
 {
@@ -563,7 +574,7 @@ bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bo
         return false;
     const bool regs = es == 2 && ceil_div(ceil_div(D, 8), 64) <= kRegsLadder[7];
     const bool lds = !fast && !regs && row_lds_bytes(D, es) <= kMaxRowLds;
-    const int64_t wg = lds ? kBlock * kRowWaves : kBlock;
+    const int64_t wg = lds ? kBlock * lds_row_waves(D * es) : kBlock;
     return L <= (((int64_t)1 << 32) - 1) / wg;
 }
 

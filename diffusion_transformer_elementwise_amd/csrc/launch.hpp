@@ -33,6 +33,20 @@ hipError_t launch_ln_modulate(const void* x, const void* scale,
                               int64_t B, int64_t L, int64_t D, int mod_mode,
                               int dtype, bool fast, hipStream_t stream);
 
+// Waves per workgroup of the kernels that stage one row in LDS (binary32
+// rows, long 2-byte rows; rms_modulate.hip, gate_add_rms_modulate.hip): the
+// power of two from 2 to 8 nearest to one wave per 4 KB of row. Measured on
+// MI355X over rows of 8 to 64 KB: fewer waves leave too few loads in flight
+// per row, more leave too few rows in flight per CU (16 waves on 64 KB rows
+// measured slower than 8 for binary32 rows and the fused call).
+inline int lds_row_waves(int64_t row_bytes)
+{
+    int w = 2;
+    while (w < 8 && row_bytes > 6144 * (int64_t)w)  // > 1.5 w times 4 KB
+        w *= 2;
+    return w;
+}
+
 // residual update then modulation, one pass (gate_add_rms_modulate.hip)
 bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast);
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,

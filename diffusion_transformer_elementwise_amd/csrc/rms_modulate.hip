@@ -335,9 +335,10 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
 }
 
 // Element path for rows that fit in LDS but not in registers (binary32
-// rows; 2-byte rows over 8192 elements): one workgroup of kRowWaves waves per
-// row, the row read from HBM once. The waves stage it into a dynamic LDS
-// buffer (stage i by wave i mod kRowWaves, the wave's next stage in flight
+// rows; 2-byte rows over 8192 elements): one workgroup of NW waves per row
+// (lds_row_waves: about one per 4 KB of row), the row read from HBM once.
+// The waves stage it into a dynamic LDS buffer (stage i by wave i mod NW, the
+// wave's next stage in flight
 // while one is committed), realigned so that element i sits at byte i * es
 // (Span::commit_aligned); wave 0 takes the sums from LDS in the fixed order
 // (lane j: groups j, j + 64, ...); all waves then apply over chunks of the
@@ -345,8 +346,10 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
 // output's byte positions (two aligned LDS words and a cut), scale and shift
 // read realigned to them.
 constexpr int kRowStage = 1024;  // elements staged per step
-constexpr int kRowWaves = 8;
-constexpr int64_t kMaxRowLds = 65536 - 256;  // 64 KB per workgroup, less the static LDS
+// dynamic LDS per workgroup (the compiler also places the two-pass kernels'
+// static buffers in these kernels, 6-12 KB; a gfx950 workgroup may use more
+// than 64 KB in all)
+constexpr int64_t kMaxRowLds = 65536 - 256;
 
 // LDS bytes the staged row needs: its aligned words plus two words that a
 // cut at the row's end may touch (their bytes are never used).
@@ -407,8 +410,8 @@ __device__ __forceinline__ float lds_row_sum(const u32x4* rowbuf, int n, float m
     return wave_sum(acc);
 }
 
-template <int DT, int MOD, int NORM>
-__global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
+template <int DT, int MOD, int NORM, int NW>
+__global__ __launch_bounds__(kBlock * NW) void modulate_lds_kernel(
     const void* x, const void* scale, const void* shift, float eps, float d_float,
     void* out, int64_t L, int64_t D)
 {
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
     using S = Span<DT, kRowStage>;
     constexpr int es = DT == kF32 ? 4 : 2;
     constexpr bool kTok = MOD == kModToken;
-    constexpr int kStride = kRowStage * kRowWaves;
+    constexpr int kStride = kRowStage * NW;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_lds_kernel(
     // q <= qmax; lanes past the row's last word are clamped (not stored)
     const int qmax = (int)((nbytes + 15) / 16);
     const int lead = line_lead(po);
-    for (int64_t c = wave; 64 * c - lead < words; c += kRowWaves) {
+    for (int64_t c = wave; 64 * c - lead < words; c += NW) {
         const int64_t wbase = 64 * c - lead;  // chunks of whole 128-byte output lines
         // output word w holds row bytes [16w - mo, 16w - mo + 16); words
         // before the row (w < 0) read clamped words and are not stored
@@ -569,6 +572,16 @@ const void* pick_regs(int64_t slots)
     return nullptr;
 }
 
+template <int DT, int MOD, int NORM>
+const void* lds_kernel(int w)
+{
+    switch (w) {
+    case 2: return reinterpret_cast<const void*>(&modulate_lds_kernel<DT, MOD, NORM, 2>);
+    case 4: return reinterpret_cast<const void*>(&modulate_lds_kernel<DT, MOD, NORM, 4>);
+    default: return reinterpret_cast<const void*>(&modulate_lds_kernel<DT, MOD, NORM, 8>);
+    }
+}
+
 template <int NORM, int DT, int MOD>
 hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                         float eps, void* out, int64_t B, int64_t L, int64_t D,
@@ -585,9 +598,9 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
         }
         const int64_t lds = row_lds_bytes(D, DT == kF32 ? 4 : 2);
         if (lds <= kMaxRowLds) {
-            const void* lk = reinterpret_cast<const void*>(&modulate_lds_kernel<DT, MOD, NORM>);
-            return hipLaunchKernel(lk, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock * kRowWaves),
-                                   args, (size_t)lds, stream);
+            const int w = lds_row_waves(D * (DT == kF32 ? 4 : 2));
+            return hipLaunchKernel(lds_kernel<DT, MOD, NORM>(w), dim3((uint32_t)L, (uint32_t)B),
+                                   dim3(kBlock * w), args, (size_t)lds, stream);
         }
         const void* k = NORM == kNormLn
                             ? reinterpret_cast<const void*>(&ln_modulate_generic_kernel<DT, MOD>)
@@ -633,16 +646,16 @@ hipError_t launch_norm(const void* x, const void* scale, const void* shift, floa
 
 // Grid x holds at most L workgroups (one or two rows each on the fast path,
 // one row on the element paths); its size in work-items, L times the
-// workgroup size, must fit 32 bits: 64 lanes, or kBlock * kRowWaves for the
-// LDS-staged rows (binary32 rows and 2-byte rows over the register limit
-// that fit the LDS buffer).
+// workgroup size, must fit 32 bits: 64 lanes, or 64 lds_row_waves(D * es)
+// for the LDS-staged rows (binary32 rows and 2-byte rows over the register
+// limit that fit the LDS buffer).
 bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast)
 {
     if (B > 65535)
         return false;
     const bool regs = es == 2 && ceil_div(ceil_div(D, 8), 64) <= kRegsLadder[7];
     const bool lds = !fast && !regs && row_lds_bytes(D, es) <= kMaxRowLds;
-    const int64_t wg = lds ? kBlock * kRowWaves : kBlock;
+    const int64_t wg = lds ? kBlock * lds_row_waves(D * es) : kBlock;
     return L <= (((int64_t)1 << 32) - 1) / wg;
 }
 

@@ -396,23 +396,29 @@ def test_grid_limits(dte):
 
 
 def test_grid_limit_of_the_lds_staged_rows(dte):
-    # binary32 rows of the element path are staged in LDS by workgroups of 8
-    # waves (512 work-items), one per row: L * 512 must stay below 2^32, a
-    # tighter limit than the 64-lane kernels' (rows of 2-byte elements in
+    # binary32 rows of the element path are staged in LDS by one workgroup
+    # per row of about one wave per 4 KB of row (a power of two from 2 to
+    # 8): 400-byte rows take 2 waves (128 work-items), 64000-byte rows 8
+    # (512). L times the workgroup size must stay below 2^32, a tighter
+    # limit than the 64-lane kernels' (rows of 2-byte elements in
     # registers); the fused call has the same limit
     ok, uns = dte.RGA_OK, dte.RGA_ERR_UNSUPPORTED
     GB = 1024 * MB
-    L_max = ((1 << 32) - 1) // 512
-    D = 100  # D % 8 != 0: element path
-    ts = [A + k * 8 * GB for k in range(8)]  # each > L_max * D * 4 bytes apart
-    for L, want in ((L_max, ok), (L_max + 1, uns)):
-        assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L, D,
-                                         dte.MOD_ROW, dte.DTYPE_F32) == want, L
-        assert dte.check_gate_add_rms_modulate_ex(ts[0], ts[1], ts[2], ts[3], ts[4], 1e-6,
-                                                  ts[5], ts[6], 1, L, D, dte.GATE_FULL,
-                                                  dte.MOD_TOKEN, dte.DTYPE_F32) == want, L
-    # the same L with 2-byte rows runs the 64-lane register kernels
-    assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L_max + 1, D,
+    for D, lanes in ((100, 128), (16000, 512)):
+        L_max = ((1 << 32) - 1) // lanes
+        gap = 1 << ((L_max * D * 4).bit_length() + 1)  # tensors far apart
+        ts = [A + k * gap for k in range(8)]
+        for L, want in ((L_max, ok), (L_max + 1, uns)):
+            assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L, D,
+                                             dte.MOD_ROW, dte.DTYPE_F32) == want, (D, L)
+            assert dte.check_gate_add_rms_modulate_ex(ts[0], ts[1], ts[2], ts[3], ts[4], 1e-6,
+                                                      ts[5], ts[6], 1, L, D, dte.GATE_FULL,
+                                                      dte.MOD_TOKEN, dte.DTYPE_F32) == want, (D, L)
+    # a length past the 128-lane limit with 2-byte rows runs the 64-lane
+    # register kernels
+    L = ((1 << 32) - 1) // 128 + 1
+    ts = [A + k * 64 * GB for k in range(8)]
+    assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L, 100,
                                      dte.MOD_ROW, dte.DTYPE_BF16) == ok
 
 
