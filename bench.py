@@ -45,6 +45,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -570,14 +571,47 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
     return out
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with its comments removed and whitespace runs collapsed
+    (string and character literals kept as they are): what the compiler
+    sees, so an edit to comments alone keeps the digest."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_digest() -> str:
+    """Digest of the library's sources as code: comments and layout do not
+    count, so the committed counters stay valid across comment edits."""
     csrc = os.path.join(ROOT, "diffusion_transformer_elementwise_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if not name.endswith((".hip", ".hpp", ".cpp", ".py")):
             continue
         with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+            data = f.read()
+        if not name.endswith(".py"):
+            data = _code_only(data.decode("utf-8")).encode("utf-8")
+        h.update(name.encode() + b"\0" + data)
     return h.hexdigest()[:16]
 
 

@@ -18,12 +18,14 @@
 //
 // Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers),
 // launch shape measured on MI355X: one wave per workgroup and one row per
-// wave, nontemporal loads and stores; each x_out pack is stored as soon as it
-// is formed, and scale and shift are read only in the apply phase (through
-// the caches for row modulation, streamed for per-token modulation), which
-// keeps the wave at 79 registers for bf16 and D = 4096. A broadcast gate row
-// is read through the caches (it stays in L2), a full gate streams from HBM
-// like x and u.
+// wave, nontemporal loads and stores. Every pack's x, u and g loads are
+// issued before the first add, with no branch around a load (a branch per
+// bounded load made the wave wait for each pack before issuing the next);
+// each x_out pack is stored as soon as it is formed; scale and shift are read
+// only for the apply phase, all packs before the first (through the caches
+// for row modulation, streamed for per-token modulation). A broadcast gate
+// row is read through the caches (it stays in L2), a full gate streams from
+// HBM like x and u.
 //
 // Element path (any D, element-aligned pointers): for 2-byte rows of up to
 // 8192 elements, one pass with the row realigned in registers (x_out is
