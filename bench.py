@@ -630,10 +630,24 @@ def load_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def _row_ranges(B, n, parts):
+    """(b, first, end) row ranges: each batch's first n rows cut into
+    contiguous pieces, about `parts` in all."""
+    per = max(1, -(-parts // B))
+    step = -(-n // per)
+    return [(b, a, min(a + step, n)) for b in range(B) for a in range(0, n, step)]
+
+
 def cpu_baseline(host, fraction, min_seconds, log):
-    """The oracle (single-threaded C, as it stands) on the first `fraction` of
-    each launch's rows, same launch mix as one step, repeated until at least
-    `min_seconds` have passed."""
+    """The oracle (the C oracle as it stands) on the first `fraction` of each
+    launch's rows, same launch mix as one step, repeated until at least
+    `min_seconds` have passed: once on one thread, once with every launch's
+    rows cut into contiguous ranges over the host's cores (one oracle call per
+    range on a thread pool; the C calls run outside the GIL). The two are
+    checked bit-identical on one pass from the same inputs. `value` is the
+    all-cores rate."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -654,26 +668,77 @@ def cpu_baseline(host, fraction, min_seconds, log):
               + 6 * c4.B * n4 * c4.D + 2 * c4.B * c4.D
               + 4 * c5.B * n5 * c5.D + 4 * c5.B * c5.D
               + 6 * c5.B * n5 * c5.D + 2 * c5.B * c5.D)
-    log(f"cpu baseline: oracle on {fraction:.2f} of every launch's rows, "
-        f"repeated for at least {min_seconds:.0f} s")
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def one_thread(x4, x5, out3, y5):
         oracle.gate_add(x3, u3, g3, GATE_FULL, out=out3)
         oracle.gate_add(x4, u4, h4["g"], GATE_BCAST, out=x4)
         oracle.rms_modulate(x5, h5["scale"], h5["shift"], c5.eps, out=y5)
         oracle.gate_add(x5, u5, h5["g"], GATE_BCAST, out=x5)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    total = sample * reps
-    log(f"cpu baseline: {total / 1e9:.2f} GB in {dt:.1f} s ({reps} passes)")
-    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    pool = ThreadPoolExecutor(max_workers=threads)
+    r3 = _row_ranges(c3.B, n3, threads)
+    r4 = _row_ranges(c4.B, n4, threads)
+    r5 = _row_ranges(c5.B, n5, threads)
+
+    def launch(fn, ranges):
+        for f in [pool.submit(fn, *r) for r in ranges]:
+            f.result()
+
+    def all_cores(x4, x5, out3, y5):
+        launch(lambda b, a, e: oracle.gate_add(
+            x3[b:b + 1, a:e], u3[b:b + 1, a:e], g3[b:b + 1, a:e], GATE_FULL,
+            out=out3[b:b + 1, a:e]), r3)
+        launch(lambda b, a, e: oracle.gate_add(
+            x4[b:b + 1, a:e], u4[b:b + 1, a:e], h4["g"][b:b + 1], GATE_BCAST,
+            out=x4[b:b + 1, a:e]), r4)
+        launch(lambda b, a, e: oracle.rms_modulate(
+            x5[b:b + 1, a:e], h5["scale"][b:b + 1], h5["shift"][b:b + 1], c5.eps,
+            out=y5[b:b + 1, a:e]), r5)
+        launch(lambda b, a, e: oracle.gate_add(
+            x5[b:b + 1, a:e], u5[b:b + 1, a:e], h5["g"][b:b + 1], GATE_BCAST,
+            out=x5[b:b + 1, a:e]), r5)
+
+    # one pass each from the same inputs: the partitioned run must give the
+    # single-threaded bits
+    s_out = [x4.copy(), x5.copy(), np.empty_like(out3), np.empty_like(y5)]
+    p_out = [x4.copy(), x5.copy(), np.empty_like(out3), np.empty_like(y5)]
+    one_thread(*s_out)
+    all_cores(*p_out)
+    same = all(np.array_equal(a, b) for a, b in zip(s_out, p_out))
+    del s_out, p_out
+    if not same:
+        pool.shutdown()
+        raise RuntimeError("row-partitioned oracle differs from the single-threaded one")
+
+    def timed(run):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            run(x4, x5, out3, y5)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                return reps, dt
+
+    log(f"cpu baseline: oracle on {fraction:.2f} of every launch's rows, one thread "
+        f"then {threads}, each for at least {min_seconds:.0f} s")
+    reps1, dt1 = timed(one_thread)
+    log(f"cpu baseline: 1 thread {sample * reps1 / 1e9:.2f} GB in {dt1:.1f} s ({reps1} passes)")
+    repsn, dtn = timed(all_cores)
+    pool.shutdown()
+    log(f"cpu baseline: {threads} threads {sample * repsn / 1e9:.2f} GB in {dtn:.1f} s "
+        f"({repsn} passes)")
+    return {"value": round(sample * repsn / dtn / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} passes over the first {fraction:.2f} of the rows of each of "
-                      f"the step's 4 launches ({total} algorithmic bytes in {dt:.1f} s, "
-                      "single-threaded C oracle)",
+            "sample": f"{repsn} passes over the first {fraction:.2f} of the rows of each of "
+                      f"the step's 4 launches ({sample * repsn} algorithmic bytes in "
+                      f"{dtn:.1f} s), the C oracle called on contiguous row ranges from "
+                      f"{threads} threads; bit-identical to one thread on one pass",
+            "single_thread": {"value": round(sample * reps1 / dt1 / 1e9, 3), "unit": "GB/s",
+                              "cores": 1,
+                              "sample": f"{reps1} passes, {sample * reps1} algorithmic "
+                                        f"bytes in {dt1:.1f} s"},
             "host_cpus": os.cpu_count()}
 
 
