@@ -231,6 +231,31 @@ def test_every_offset_of_every_operand(dte, D, dtype):
         _zero_ulp(to_host_typed(yo), wfy, dtype, f"fused full y, rotation {o}")
 
 
+# rows staged in LDS run with 2, 4 or 8 waves per row, switching at 12288
+# and 24576 bytes of row: binary32 rows on both sides of each switch, 2-byte
+# rows (staged from 8193 elements on) on both sides of the second
+LDS_SIZES = [(F32, 3072), (F32, 3073), (F32, 6144), (F32, 6145), (BF16, 8193),
+             (BF16, 12288), (BF16, 12289)]
+
+
+@pytest.mark.parametrize("dtype,D", LDS_SIZES, ids=[f"{NAMES[t]}-{d}" for t, d in LDS_SIZES])
+def test_lds_rows_at_the_wave_count_switches(dte, dtype, D):
+    B, L = 2, 5
+    say(f"[lds row sizes] {NAMES[dtype]} B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(5600 + D, B, L, D, GATE_BCAST, dtype)
+    s, t = _mod_inputs(5601 + D, B, L, D, MOD_ROW, dtype)
+    dx, du, dg = to_dev_typed(x, dtype, 1), to_dev_typed(u, dtype), to_dev_typed(g, dtype)
+    ds, dt = to_dev_typed(s, dtype), to_dev_typed(t, dtype, 3)
+    _zero_ulp(to_host_typed(dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6)),
+              oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_ROW, dtype), dtype, "rms")
+    _zero_ulp(to_host_typed(dte.rga_ln_modulate(dx, ds, dt, 1e-6)),
+              oracle.ln_modulate(x, s, t, 1e-6, MOD_ROW, dtype), dtype, "ln")
+    wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_BCAST, MOD_ROW, dtype)
+    xo, yo = dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6)
+    _bit_exact(to_host_typed(xo), wx, dtype, "fused x_out")
+    _zero_ulp(to_host_typed(yo), wy, dtype, "fused y")
+
+
 def test_bf16_ex_runs_the_same_kernels_as_the_bf16_calls(dte):
     # with bf16, row modulation, D % 8 == 0 and aligned tensors the _ex calls
     # take the pack path: identical results to the original calls
