@@ -14,6 +14,13 @@
 // 16-byte stores and the two partial edge words element by element, so no
 // byte outside the run is written.
 //
+// Two forms of the cut: window_at takes the offset at run time (selects pick
+// the dwords), window_c<O> has it fixed (the picks are free). realign_in and
+// store_run branch once per run on the wave-uniform offset (dispatch_offset)
+// to code for that offset, which pays off over a row's many slots; the
+// chunked kernels cut one word per lane and keep window_at, where a branch
+// between the loads and their use cost more than the selects.
+//
 // Every word read holds at least one byte of the run, so it lies in memory
 // the caller owns pages of; the other bytes are read and ignored. Groups
 // past the run's end hold garbage that callers neither store nor sum.
