@@ -169,8 +169,14 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
     int64_t L, int64_t D)
 {
     using S = Span<DT, kStage>;
-    __shared__ u32x4 r0[S::kWords], r1[S::kWords], r2[S::kWords], r3[S::kWords];
-    __shared__ u32x4 ra[S::kWords];  // the rounded x' at byte i * es, for the sum
+    // five spans from the launch's dynamic LDS (5 * kWords words): a static
+    // buffer would also be placed, unused, in this file's LDS-staged kernel
+    extern __shared__ u32x4 rowbuf[];
+    u32x4* r0 = rowbuf;
+    u32x4* r1 = r0 + S::kWords;
+    u32x4* r2 = r1 + S::kWords;
+    u32x4* r3 = r2 + S::kWords;
+    u32x4* ra = r3 + S::kWords;  // the rounded x' at byte i * es, for the sum
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
@@ -265,8 +271,7 @@ __device__ __forceinline__ u32x4 lds_bytes16(const u32x4* buf, int pos, int sh, 
 // sum from LDS (group g is the 16 or 32 bytes at x_out's offset + g * 8 *
 // es); all waves then write y over chunks of y's aligned words, x' taken
 // from LDS realigned to y. x_out is never read back.
-// dynamic LDS per workgroup (the compiler also places the two-pass kernel's
-// static buffers here; a gfx950 workgroup may use more than 64 KB in all)
+// dynamic LDS per workgroup, less room for the few static bytes
 constexpr int64_t kMaxRowLds = 65536 - 256;
 
 // LDS bytes of the row buffer: x_out's window words (at most one more than
@@ -537,7 +542,8 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
         }
         return hipLaunchKernel(
             reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
-            dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
+            dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args,
+            (size_t)(5 * 16 * Span<DT, kStage>::kWords), stream);
     }
     int vpr = (int)(D / 8);
     fused_kernel_t k = pick<FULL, DT, MOD>((int)ceil_div(vpr, 64));

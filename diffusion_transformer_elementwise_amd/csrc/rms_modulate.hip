@@ -258,6 +258,17 @@ __device__ __forceinline__ float staged_sum(const void* x, int64_t row, int64_t 
     return wave_sum(acc);
 }
 
+// LDS of the two-pass kernels, taken from the launch's dynamic LDS: the
+// staged-sum span, then the apply pass's x, scale, shift and out spans. (A
+// static buffer would also be placed, unused, in every kernel of this file
+// that uses dynamic LDS, 6-12 KB that limited the rows the LDS-staged
+// kernels keep per CU.)
+template <int DT>
+constexpr int64_t generic_lds_bytes()
+{
+    return 16 * ((int64_t)Span<DT, kStage>::kWords + 4 * (int64_t)Span<DT, kApply>::kWords);
+}
+
 // The apply pass re-reads the row (mostly from L2) in spans of kApply
 // elements, with scale and shift spans beside it, and writes out spans; the
 // next span's loads are in flight while this one is computed and stored.
@@ -267,7 +278,10 @@ __device__ __forceinline__ void modulate_row_generic(
     float d_float, void* out, int64_t L, int64_t D, u32x4* stage)
 {
     using A = Span<DT, kApply>;
-    __shared__ u32x4 rx[A::kWords], rs[A::kWords], rh[A::kWords], ro[A::kWords];
+    u32x4* rx = stage + Span<DT, kStage>::kWords;
+    u32x4* rs = rx + A::kWords;
+    u32x4* rh = rs + A::kWords;
+    u32x4* ro = rh + A::kWords;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
     const int64_t mrow = (MOD == kModToken) ? row : b * D;
@@ -321,8 +335,8 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_generic_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int64_t D)
 {
-    __shared__ u32x4 stage[Span<DT, kStage>::kWords];
-    modulate_row_generic<DT, MOD, kNormRms>(x, scale, shift, eps, d_float, out, L, D, stage);
+    extern __shared__ u32x4 rowbuf[];  // generic_lds_bytes<DT>()
+    modulate_row_generic<DT, MOD, kNormRms>(x, scale, shift, eps, d_float, out, L, D, rowbuf);
 }
 
 template <int DT, int MOD>
@@ -330,8 +344,8 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int64_t D)
 {
-    __shared__ u32x4 stage[Span<DT, kStage>::kWords];
-    modulate_row_generic<DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, D, stage);
+    extern __shared__ u32x4 rowbuf[];  // generic_lds_bytes<DT>()
+    modulate_row_generic<DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, D, rowbuf);
 }
 
 // Element path for rows that fit in LDS but not in registers (binary32
@@ -346,9 +360,7 @@ __global__ __launch_bounds__(kBlock) void ln_modulate_generic_kernel(
 // output's byte positions (two aligned LDS words and a cut), scale and shift
 // read realigned to them.
 constexpr int kRowStage = 1024;  // elements staged per step
-// dynamic LDS per workgroup (the compiler also places the two-pass kernels'
-// static buffers in these kernels, 6-12 KB; a gfx950 workgroup may use more
-// than 64 KB in all)
+// dynamic LDS per workgroup, less room for the few static bytes
 constexpr int64_t kMaxRowLds = 65536 - 256;
 
 // LDS bytes the staged row needs: its aligned words plus two words that a
@@ -605,7 +617,8 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
         const void* k = NORM == kNormLn
                             ? reinterpret_cast<const void*>(&ln_modulate_generic_kernel<DT, MOD>)
                             : reinterpret_cast<const void*>(&rms_modulate_generic_kernel<DT, MOD>);
-        return hipLaunchKernel(k, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0, stream);
+        return hipLaunchKernel(k, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args,
+                               (size_t)generic_lds_bytes<DT>(), stream);
     }
     int vpr = (int)(D / 8);
     rms_kernel_t k = pick<NORM, DT, MOD>((int)ceil_div(vpr, 64));
