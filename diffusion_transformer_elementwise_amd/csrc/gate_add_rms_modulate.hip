@@ -464,7 +464,7 @@ typedef void (*regs_kernel_t)(const void*, const void*, const void*, const void*
 
 // Slots per lane for the register-resident element path: the smallest entry
 // >= ceil(ceil(D / 8) / 64); longer rows (and binary32) take the LDS path.
-constexpr int kRegsLadder[] = {1, 2, 4, 6, 8, 9, 12, 16};
+using regs::kRegsLadder;
 
 template <bool FULL, int DT, int MOD>
 regs_kernel_t pick_regs(int64_t slots)

@@ -563,7 +563,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Element-path slots per lane for 2-byte rows held in registers: the
 // smallest entry >= ceil(ceil(D / 8) / 64); rows past the last entry (and
 // binary32 rows) take the LDS-staged kernels.
-constexpr int kRegsLadder[] = {1, 2, 4, 6, 8, 9, 12, 16};
+using regs::kRegsLadder;
 
 template <int NORM, int K, int DT, int MOD>
 const void* regs_kernel()

@@ -6,8 +6,8 @@
 // Sums follow the library's fixed order: lane j accumulates groups j,
 // j + 64, ... in increasing group and element order, then xor-distance lane
 // exchanges 1, 2, ..., 32 combine the 64 partials; elements past the row end
-// are skipped. A slot whose 64 groups all lie inside the row (a wave-uniform
-// test) is summed without per-element masks.
+// are skipped. Slots that every row of the instance fills (whole_slots) are
+// summed without per-element masks.
 //
 // Called by the whole wave.
 #pragma once
@@ -19,6 +19,26 @@ namespace regs {
 
 enum : int { kRms = 0, kLn = 1 };
 
+// The slot ladder of the register-resident rows: a row of n 2-byte elements
+// runs with the smallest K here of at least ceil(ceil(n / 8) / 64) slots;
+// longer rows are staged in LDS.
+constexpr int kRegsLadder[] = {1, 2, 4, 6, 8, 9, 12, 16};
+
+// Slots that every row run with K slots fills with whole groups: such a row
+// has more than 512 times the ladder's previous entry elements (it would
+// run with that entry otherwise), so its slots below that entry are whole.
+template <int K>
+constexpr int whole_slots()
+{
+    int prev = 0;
+    for (const int k : kRegsLadder) {
+        if (k == K)
+            return prev;
+        prev = k;
+    }
+    return 0;
+}
+
 __device__ __forceinline__ float wave_sum(float acc)
 {
 #pragma unroll
@@ -27,10 +47,14 @@ __device__ __forceinline__ float wave_sum(float acc)
     return acc;
 }
 
-// sum over the row of x (WHAT 0), x^2 (1) or (x - mu)^2 (2)
+// sum over the row of x (WHAT 0), x^2 (1) or (x - mu)^2 (2). Slots below
+// whole_slots<K>() are summed without masks: known whole at compile time,
+// where a run-time test left a compare and a select on every element (the
+// compiler turned the branch into selects).
 template <int K, int DT, int WHAT>
 __device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu)
 {
+    constexpr int kWhole = whole_slots<K>();
     const int lane = threadIdx.x & 63;
     float acc = 0.0f;
 #pragma unroll
@@ -38,7 +62,7 @@ __device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu)
         Pack<DT> p;
         p.v = xv[k];
         const int e0 = 8 * (lane + 64 * k);
-        const bool whole = 512 * (k + 1) <= n;
+        const bool whole = k < kWhole || 512 * (k + 1) <= n;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if (whole || e0 + e < n) {

@@ -231,6 +231,33 @@ def test_every_offset_of_every_operand(dte, D, dtype):
         _zero_ulp(to_host_typed(yo), wfy, dtype, f"fused full y, rotation {o}")
 
 
+# register-resident rows run with K slots from the ladder 1, 2, 4, 6, 8, 9,
+# 12, 16; an instance sums the slots below the previous entry without
+# masks, so each K is checked on the shortest row it serves (512 times the
+# previous entry, plus one) and the longest (512 K)
+LADDER_D = [1, 512, 513, 1024, 1025, 2048, 2049, 3072, 3073, 4096, 4097, 4608, 4609, 6144,
+            6145, 8192]
+
+
+@pytest.mark.parametrize("D", LADDER_D)
+def test_register_rows_across_the_slot_ladder(dte, D):
+    B, L = 2, 3
+    dtype = BF16
+    say(f"[slot ladder] bf16 B={B} L={L} D={D}")
+    x, u, g = _gate_inputs(5700 + D, B, L, D, GATE_BCAST, dtype)
+    s, t = _mod_inputs(5701 + D, B, L, D, MOD_ROW, dtype)
+    dx, du, dg = to_dev_typed(x, dtype, 1), to_dev_typed(u, dtype), to_dev_typed(g, dtype, 2)
+    ds, dt = to_dev_typed(s, dtype, 3), to_dev_typed(t, dtype)
+    _zero_ulp(to_host_typed(dte.rga_rms_modulate_ex(dx, ds, dt, 1e-6)),
+              oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_ROW, dtype), dtype, "rms")
+    _zero_ulp(to_host_typed(dte.rga_ln_modulate(dx, ds, dt, 1e-6)),
+              oracle.ln_modulate(x, s, t, 1e-6, MOD_ROW, dtype), dtype, "ln")
+    wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, GATE_BCAST, MOD_ROW, dtype)
+    xo, yo = dte.rga_gate_add_rms_modulate_ex(dx, du, dg, ds, dt, 1e-6)
+    _bit_exact(to_host_typed(xo), wx, dtype, "fused x_out")
+    _zero_ulp(to_host_typed(yo), wy, dtype, "fused y")
+
+
 # rows staged in LDS run with 2, 4 or 8 waves per row, switching at 12288
 # and 24576 bytes of row: binary32 rows on both sides of each switch, 2-byte
 # rows (staged from 8193 elements on) on both sides of the second
