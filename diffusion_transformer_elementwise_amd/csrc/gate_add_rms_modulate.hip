@@ -253,14 +253,17 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_generic_kernel(
 
 // 16 bytes of an LDS row buffer starting at byte pos, pos mod 16 = sh the
 // same in every lane; word indexes are clamped to [0, qmax] (the clamped
-// bytes are never used).
+// bytes are never used). O: sh fixed at compile time (0..15), or -1.
+template <int O>
 __device__ __forceinline__ u32x4 lds_bytes16(const u32x4* buf, int pos, int sh, int qmax)
 {
     int q = pos >> 4;
     q = q < qmax ? q : qmax;
-    if (sh == 0)
-        return buf[q < 0 ? 0 : q];
-    return window_at(buf[q < 0 ? 0 : q], buf[q + 1 < 0 ? 0 : q + 1], sh);
+    const u32x4 c = buf[q < 0 ? 0 : q];
+    if constexpr (O == 0)
+        return c;
+    else
+        return window_o<O>(c, buf[q + 1 < 0 ? 0 : q + 1], sh);
 }
 
 // Element path for rows that fit in LDS but not in registers (binary32
@@ -330,50 +333,55 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
     const int qmax = (int)words_xo;
     if (wave == 0) {
         const int groups = (n + 7) >> 3;
-        auto group_at = [&](int gi) {
-            Pack<DT> p;
-            if constexpr (DT == kF32) {
-                p.a = lds_bytes16(rowbuf, mxo + 32 * gi, mxo, qmax);
-                p.b = lds_bytes16(rowbuf, mxo + 32 * gi + 16, mxo, qmax);
-            } else {
-                p.v = lds_bytes16(rowbuf, mxo + 16 * gi, mxo, qmax);
-            }
-            return p;
-        };
         float acc = 0.0f;
-        // batches of U groups wholly inside the row: the U reads are issued
-        // before any is added (one LDS round trip per batch); the additions
-        // keep the fixed order. The rest, masked, below.
-        constexpr int U = DT == kF32 ? 4 : 8;
-        const int n_whole = n >> 3;
-        int gi = lane;
-        for (; gi + kBlock * (U - 1) < n_whole; gi += kBlock * U) {
-            Pack<DT> p[U];
+        // one branch on the buffer's offset (uniform) around the sum, so each
+        // group read is cut with fixed dword picks
+        dispatch_offset(mxo, [&](auto off) {
+            constexpr int O = decltype(off)::value;
+            auto group_at = [&](int gi) {
+                Pack<DT> p;
+                if constexpr (DT == kF32) {
+                    p.a = lds_bytes16<O>(rowbuf, mxo + 32 * gi, mxo, qmax);
+                    p.b = lds_bytes16<O>(rowbuf, mxo + 32 * gi + 16, mxo, qmax);
+                } else {
+                    p.v = lds_bytes16<O>(rowbuf, mxo + 16 * gi, mxo, qmax);
+                }
+                return p;
+            };
+            // batches of U groups wholly inside the row: the U reads are issued
+            // before any is added (one LDS round trip per batch); the additions
+            // keep the fixed order. The rest, masked, below.
+            constexpr int U = DT == kF32 ? 4 : 8;
+            const int n_whole = n >> 3;
+            int gi = lane;
+            for (; gi + kBlock * (U - 1) < n_whole; gi += kBlock * U) {
+                Pack<DT> p[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                p[u] = group_at(gi + kBlock * u);
+                for (int u = 0; u < U; ++u)
+                    p[u] = group_at(gi + kBlock * u);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float a = p[u].get(e);
+                        const float sa = a * a;
+                        acc = acc + sa;
+                    }
+                }
+            }
+            for (; gi < groups; gi += kBlock) {
+                const Pack<DT> p = group_at(gi);
+                const bool whole = 8 * gi + 8 <= n;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float a = p[u].get(e);
-                    const float sa = a * a;
-                    acc = acc + sa;
+                    if (whole || 8 * gi + e < n) {
+                        const float a = p.get(e);
+                        const float sa = a * a;
+                        acc = acc + sa;
+                    }
                 }
             }
-        }
-        for (; gi < groups; gi += kBlock) {
-            const Pack<DT> p = group_at(gi);
-            const bool whole = 8 * gi + 8 <= n;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (whole || 8 * gi + e < n) {
-                    const float a = p.get(e);
-                    const float sa = a * a;
-                    acc = acc + sa;
-                }
-            }
-        }
+        });
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1)
             acc = acc + __shfl_xor(acc, m);
@@ -391,25 +399,31 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
     const int64_t words_y = window_words(py, nbytes);
     const int sh = (mxo - my) & 15;
     const int lead_y = line_lead(py);
-    for (int64_t c = wave; 64 * c - lead_y < words_y; c += NW) {
-        const int64_t wbase = 64 * c - lead_y;
-        // y word w holds row bytes [16w - my, +16): buffer bytes from 16w - my + mxo
-        const int pos = (int)(16 * (wbase + lane)) - my + mxo;
-        const u32x4 xw = lds_bytes16(rowbuf, pos, sh, qmax);
-        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, wbase);
-        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, wbase);
-        const u32x4 sw = chunk_word(fsw);
-        const u32x4 hw = chunk_word(fhw);
-        float o[W::kN];
+    // one branch on the row's LDS cut (uniform) around the y loop
+    dispatch_offset(sh, [&](auto off) {
+        constexpr int O = decltype(off)::value;
+        for (int64_t c = wave; 64 * c - lead_y < words_y; c += NW) {
+            const int64_t wbase = 64 * c - lead_y;
+            // y word w holds row bytes [16w - my, +16): buffer bytes from 16w - my + mxo
+            const int pos = (int)(16 * (wbase + lane)) - my + mxo;
+            const u32x4 xw = lds_bytes16<O>(rowbuf, pos, sh, qmax);
+            const ChunkWords fsw =
+                fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, my, wbase);
+            const ChunkWords fhw =
+                fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, my, wbase);
+            const u32x4 sw = chunk_word(fsw);
+            const u32x4 hw = chunk_word(fhw);
+            float o[W::kN];
 #pragma unroll
-        for (int e = 0; e < W::kN; ++e) {
-            const float nv = W::get(xw, e) * rr;
-            const float a = 1.0f + W::get(sw, e);
-            const float m = nv * a;
-            o[e] = m + W::get(hw, e);
+            for (int e = 0; e < W::kN; ++e) {
+                const float nv = W::get(xw, e) * rr;
+                const float a = 1.0f + W::get(sw, e);
+                const float m = nv * a;
+                o[e] = m + W::get(hw, e);
+            }
+            store_chunk<true>(py, nbytes, wbase, W::make(o));
         }
-        store_chunk<true>(py, nbytes, wbase, W::make(o));
-    }
+    });
 }
 
 // Element path for 2-byte types with D <= 512 * K: one wave per row. x, u

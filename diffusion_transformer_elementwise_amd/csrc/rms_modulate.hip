@@ -480,31 +480,40 @@ __global__ __launch_bounds__(kBlock * NW) void modulate_lds_kernel(
     // q <= qmax; lanes past the row's last word are clamped (not stored)
     const int qmax = (int)((nbytes + 15) / 16);
     const int lead = line_lead(po);
-    for (int64_t c = wave; 64 * c - lead < words; c += NW) {
-        const int64_t wbase = 64 * c - lead;  // chunks of whole 128-byte output lines
-        // output word w holds row bytes [16w - mo, 16w - mo + 16); words
-        // before the row (w < 0) read clamped words and are not stored
-        int q = (int)((16 * (wbase + lane) - mo) >> 4);
-        q = q < -1 ? -1 : (q < qmax ? q : qmax);
-        const u32x4 xw = sh == 0 ? rowbuf[q] : window_at(rowbuf[q < 0 ? 0 : q], rowbuf[q + 1], sh);
-        const ChunkWords fsw = fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, wbase);
-        const ChunkWords fhw = fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, wbase);
-        const u32x4 sw = chunk_word(fsw);
-        const u32x4 hw = chunk_word(fhw);
-        using W = Word<DT>;
-        float o[W::kN];
+    // one branch on the row's LDS cut (uniform for the row) around the whole
+    // apply loop, so the x words are cut with fixed dword picks
+    dispatch_offset(sh, [&](auto off) {
+        constexpr int O = decltype(off)::value;
+        for (int64_t c = wave; 64 * c - lead < words; c += NW) {
+            const int64_t wbase = 64 * c - lead;  // chunks of whole 128-byte output lines
+            // output word w holds row bytes [16w - mo, 16w - mo + 16); words
+            // before the row (w < 0) read clamped words and are not stored
+            int q = (int)((16 * (wbase + lane) - mo) >> 4);
+            q = q < -1 ? -1 : (q < qmax ? q : qmax);
+            u32x4 xw = rowbuf[q < 0 ? 0 : q];
+            if constexpr (O != 0)
+                xw = window_o<O>(xw, rowbuf[q + 1], sh);
+            const ChunkWords fsw =
+                fetch_for_chunk<kTok>(elem_ptr<DT>(scale, mrow), nbytes, mo, wbase);
+            const ChunkWords fhw =
+                fetch_for_chunk<kTok>(elem_ptr<DT>(shift, mrow), nbytes, mo, wbase);
+            const u32x4 sw = chunk_word(fsw);
+            const u32x4 hw = chunk_word(fhw);
+            using W = Word<DT>;
+            float o[W::kN];
 #pragma unroll
-        for (int e = 0; e < W::kN; ++e) {
-            float v = W::get(xw, e);
-            if constexpr (NORM == kNormLn)
-                v = v - mu;
-            const float nv = v * rr;
-            const float a = 1.0f + W::get(sw, e);
-            const float mm = nv * a;
-            o[e] = mm + W::get(hw, e);
+            for (int e = 0; e < W::kN; ++e) {
+                float v = W::get(xw, e);
+                if constexpr (NORM == kNormLn)
+                    v = v - mu;
+                const float nv = v * rr;
+                const float a = 1.0f + W::get(sw, e);
+                const float mm = nv * a;
+                o[e] = mm + W::get(hw, e);
+            }
+            store_chunk<true>(po, nbytes, wbase, W::make(o));
         }
-        store_chunk<true>(po, nbytes, wbase, W::make(o));
-    }
+    });
 }
 
 // Element path for 2-byte types with D <= 512 * K: one wave per row, the
