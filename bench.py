@@ -199,6 +199,14 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 10 * 2 * FLUSH_BYTES / (hev.ms(ev[0], ev[1]) * 1e-3) / 1e9
     log(f"copy ceiling {copy_gbps:.0f} GB/s")
+    # read-only ceiling: the same 1 GiB read by the flush kernel
+    hev.record(ev[0], stream)
+    for _ in range(10):
+        dte.read_(src, sink)
+    hev.record(ev[1], stream)
+    torch.cuda.synchronize()
+    read_gbps = 10 * FLUSH_BYTES / (hev.ms(ev[0], ev[1]) * 1e-3) / 1e9
+    log(f"read ceiling {read_gbps:.0f} GB/s")
 
     def run_step(events=None):
         for i, l in enumerate(launches):
@@ -401,6 +409,7 @@ def main():
         "variants": variants,
         "fused": fused,
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "read_ceiling_GBps": round(read_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

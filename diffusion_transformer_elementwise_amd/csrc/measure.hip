@@ -18,7 +18,8 @@ namespace {
 constexpr int kCopyBlock = 64;
 constexpr int kBlock = 256;
 constexpr int kFillUnroll = 4;
-constexpr int kReadGrid = 256 * 16;  // workgroups of the grid-stride read
+constexpr int kReadBlock = 1024;  // lanes per workgroup of the grid-stride read
+constexpr int kReadGrid = 256;    // its workgroups: one per CU
 
 __global__ __launch_bounds__(kCopyBlock) void copy_kernel(const u32x4* src,
                                                           u32x4* dst,
@@ -43,25 +44,45 @@ __global__ __launch_bounds__(kBlock) void fill_kernel(u32x4* dst, int64_t n16,
     }
 }
 
-__global__ __launch_bounds__(kBlock) void read_kernel(const u32x4* src,
+__global__ __launch_bounds__(kReadBlock) void read_kernel(const u32x4* src,
                                                       int64_t n16,
                                                       uint32_t* sink)
 {
-    u32x4 acc = {0, 0, 0, 0};
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16;
-         i += stride)
-        acc ^= load16(src + i);
+    // four independent accumulators, so each thread keeps four loads in
+    // flight (one load per iteration left the stream latency-bound); the
+    // XOR of all words does not depend on the grouping
+    u32x4 a[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    const int64_t stride = (int64_t)gridDim.x * kReadBlock;
+    int64_t i = (int64_t)blockIdx.x * kReadBlock + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            a[k] ^= load16(src + i + k * stride);
+    }
+    for (; i < n16; i += stride)
+        a[0] ^= load16(src + i);
+    u32x4 acc = (a[0] ^ a[1]) ^ (a[2] ^ a[3]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
 #pragma unroll
         for (int w = 0; w < 4; ++w)
             acc[w] ^= (uint32_t)__shfl_xor((int)acc[w], m);
     }
-    if ((threadIdx.x & 63) == 0) {
+    // the workgroup's waves combine through LDS, then one atomic per dword
+    // per workgroup: atomics on one address serialize in L2, and one set
+    // per wave made them the kernel's limit
+    __shared__ u32x4 part[kReadBlock / 64];
+    if ((threadIdx.x & 63) == 0)
+        part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        u32x4 t = part[0];
+#pragma unroll
+        for (int w = 1; w < kReadBlock / 64; ++w)
+            t ^= part[w];
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-            atomicXor(sink + w, acc[w]);
+            atomicXor(sink + w, t[w]);
     }
 }
 
@@ -101,9 +122,10 @@ hipError_t launch_read(const void* src, int64_t n16, void* sink,
     const u32x4* s = static_cast<const u32x4*>(src);
     uint32_t* k = static_cast<uint32_t*>(sink);
     void* args[] = {&s, &n16, &k};
-    const int64_t blocks = ceil_div(n16, kBlock) < kReadGrid ? ceil_div(n16, kBlock) : kReadGrid;
+    const int64_t blocks =
+        ceil_div(n16, kReadBlock) < kReadGrid ? ceil_div(n16, kReadBlock) : kReadGrid;
     return hipLaunchKernel(reinterpret_cast<const void*>(&read_kernel),
-                           dim3((uint32_t)blocks), dim3(kBlock), args, 0,
+                           dim3((uint32_t)blocks), dim3(kReadBlock), args, 0,
                            stream);
 }
 

@@ -267,8 +267,12 @@ def test_copy_and_fill_helpers(dte):
     assert bool((dst == 0x12345678).all())
 
 
-def test_read_helper_folds_every_word(dte):
-    src = torch.arange(1 << 18, dtype=torch.int32, device="cuda:0")
+@pytest.mark.parametrize("words", [1 << 16, 5 * 256 * 1024 + 12345])
+def test_read_helper_folds_every_word(dte, words):
+    # one grid pass, and five passes of the 256 x 1024-lane grid plus a
+    # ragged remainder (the four-load loop, then the one-load tail)
+    src = torch.arange(4 * words, dtype=torch.int32, device="cuda:0")
+    src = src * 2654435761 % (1 << 31)
     sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
     dte.read_(src, sink)
     want = np.bitwise_xor.reduce(src.cpu().numpy().reshape(-1, 4), axis=0)
