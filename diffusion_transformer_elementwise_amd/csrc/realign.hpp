@@ -181,10 +181,47 @@ __device__ __forceinline__ void load_run(const void* p, int n, u32x4 (&w)[K], u3
     extra = load16(w0 + (count > 64 * K ? 64 * K : count - 1));
 }
 
+// Slots of a run from which realign_in uses the run-time cut (register use;
+// measured on MI355X at 12 and 16 slots: only 16 gained).
+constexpr int kRealignRuntimeSlots = 16;
+
+// Words of slots k0 .. k0 + KB - 1 of the run into w[0..KB) (as load_run),
+// and in extra the word that completes the last of them: slot k0 + KB's
+// first word, or the window's last word.
+template <int KB, bool STREAM>
+__device__ __forceinline__ void load_run_at(const void* p, int n, int k0, u32x4 (&w)[KB],
+                                            u32x4& extra)
+{
+    const int lane = threadIdx.x & 63;
+    const int m = start_offset(p);
+    const u32x4* w0 = aligned_down(p);
+    const int count = (m + 2 * n + 15) >> 4;  // n >= 1
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        const int i = lane + 64 * (k0 + j);
+        const int ic = i < count ? i : count - 1;
+        w[j] = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
+    }
+    const int ie = 64 * (k0 + KB);
+    extra = load16(w0 + (ie < count ? ie : count - 1));
+}
+
 // Words -> groups, in place (m = the run's start offset).
 template <int K>
 __device__ __forceinline__ void realign_in(u32x4 (&w)[K], const u32x4& extra, int m)
 {
+    // at 16 slots the run-time cut: the branch to code for each offset held
+    // ~60 more registers there (1 wave per SIMD instead of 2, 17-22 % slower)
+    if constexpr (K >= kRealignRuntimeSlots) {
+        if (m == 0)
+            return;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const u32x4 fill = (k + 1 < K) ? read_lane(w[k + 1 < K ? k + 1 : k], 0) : extra;
+            w[k] = window_at(w[k], lane_from_next(w[k], fill), m);
+        }
+        return;
+    }
     dispatch_offset(m, [&](auto off) {
         constexpr int O = decltype(off)::value;
         if constexpr (O != 0) {
