@@ -2,6 +2,7 @@
 function the public headers declare, validates arguments by the documented
 rules (host-only check entry points, no kernel launch), and its build keeps
 the arithmetic it promises."""
+import concurrent.futures
 import glob
 import os
 import re
@@ -193,8 +194,11 @@ def test_gate_add_isa_has_no_fused_multiply_add():
 
 
 def test_device_code_keeps_subnormals_and_ieee_sqrt_div():
-    for src in ("rms_modulate.hip", "gate_add_rms_modulate.hip"):
-        asm = _device_asm(src)
+    srcs = ("rms_modulate.hip", "gate_add_rms_modulate.hip")
+    # the two device compiles are the slowest step of the host suite: run them side by side
+    with concurrent.futures.ThreadPoolExecutor(len(srcs)) as pool:
+        asms = list(pool.map(_device_asm, srcs))
+    for src, asm in zip(srcs, asms):
         assert ".amdhsa_float_denorm_mode_32 0" not in asm, src
         bodies = _kernel_bodies(asm)
         assert asm.count(".amdhsa_float_denorm_mode_32 3") == len(bodies), src
