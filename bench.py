@@ -342,7 +342,7 @@ def main():
         # and rms_modulate launches (same kernels, shapes and bytes)
         pair = per_launch["c5_bcast_gate_add_inplace"]["us"] + per_launch["c5_rms_modulate"]["us"]
         fused = {"shape": "[2,32640,4096] bcast gate, x_out in place",
-                 "kernel": "gate_add_rms_modulate_kernel",
+                 "kernel": "gate_add_rms_modulate_regs_kernel",
                  "bytes": fused_bytes, "us": round(fus, 2),
                  "GBps": round(fused_bytes / (fus * 1e-6) / 1e9, 1),
                  "frac_of_hbm_peak": round(fused_bytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -487,7 +487,8 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         out[name] = cold_and_warm(
             lambda: dte.rga_gate_add_rms_modulate_ex(x, u, g, sc, sh, 1e-6, x_out=xo, y=y,
                                                      gate_mode=mode, mod_mode=mod),
-            nbytes, "gate_add_rms_modulate_kernel" if D % 8 == 0 and D <= 8192
+            nbytes, "gate_add_rms_modulate_kernel"
+            if D % 8 == 0 and D <= 8192 and (mod == dte.MOD_TOKEN or dt == "f32")
             else element_fused_kernel(D, dt))
 
     def element_fused_kernel(D, dt):

@@ -16,7 +16,8 @@
 // The _ex calls take the 16-byte-pack kernels when every pointer is 16-byte
 // aligned and D % 8 == 0 (any D for a full-gate add, which is one flat
 // stream) and, for the modulation, D <= RGA_RMS_MAX_D; the element-wise
-// kernels otherwise.
+// kernels otherwise. The fused call with 2-byte rows and row modulation
+// always takes its register-row element kernel (the faster one there).
 // The gate-add rejection of unsupported inputs mirrors the residual-gate
 // page's test list ("unsupported input rejection"); the bf16-only contract
 // mirrors the modulation page's guard that admits only bf16 tensors.

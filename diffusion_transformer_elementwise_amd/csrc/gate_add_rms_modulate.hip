@@ -16,8 +16,11 @@
 // outputs are bit-identical to rga_residual_gate_add followed by
 // rms_modulate.
 //
-// Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers),
-// launch shape measured on MI355X: one wave per workgroup and one row per
+// Pack path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers, with
+// per-token modulation or binary32 storage; 2-byte rows with row modulation
+// take the register-row kernel of the element path at any alignment, which
+// measured faster there), launch shape measured on MI355X: one wave per
+// workgroup and one row per
 // wave, nontemporal loads and stores. Every pack's x, u and g loads are
 // issued before the first add, with no branch around a load (a branch per
 // bounded load made the wave wait for each pack before issuing the next);
@@ -532,41 +535,62 @@ const void* lds_kernel(int w)
     }
 }
 
+// Element path: register rows for 2-byte rows of up to 8192 elements, then
+// the LDS-staged rows, then the two-pass kernel.
+template <bool FULL, int DT, int MOD>
+hipError_t launch_element(const void* x, const void* u, const void* g,
+                          const void* scale, const void* shift, float eps,
+                          void* x_out, void* y, int64_t B, int64_t L, int64_t D,
+                          hipStream_t stream)
+{
+    float d_float = (float)D;
+    void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &D};
+    if constexpr (DT != kF32) {
+        regs_kernel_t rk = pick_regs<FULL, DT, MOD>(ceil_div(ceil_div(D, 8), 64));
+        if (rk != nullptr)
+            return hipLaunchKernel(reinterpret_cast<const void*>(rk),
+                                   dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
+                                   stream);
+    }
+    const int64_t lds = row_lds_bytes(D, DT == kF32 ? 4 : 2);
+    if (lds <= kMaxRowLds) {
+        const int w = lds_row_waves(D * (DT == kF32 ? 4 : 2));
+        return hipLaunchKernel(lds_kernel<FULL, DT, MOD>(w), dim3((uint32_t)L, (uint32_t)B),
+                               dim3(kBlock * w), args, (size_t)lds, stream);
+    }
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
+        dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args,
+        (size_t)(5 * 16 * Span<DT, kStage>::kWords), stream);
+}
+
 template <bool FULL, int DT, int MOD>
 hipError_t launch_typed(const void* x, const void* u, const void* g,
                         const void* scale, const void* shift, float eps,
                         void* x_out, void* y, int64_t B, int64_t L, int64_t D,
                         bool fast, hipStream_t stream)
 {
-    float d_float = (float)D;
-    if (!fast) {
-        void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &D};
-        if constexpr (DT != kF32) {
-            regs_kernel_t rk = pick_regs<FULL, DT, MOD>(ceil_div(ceil_div(D, 8), 64));
-            if (rk != nullptr)
-                return hipLaunchKernel(reinterpret_cast<const void*>(rk),
-                                       dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
-                                       stream);
-        }
-        const int64_t lds = row_lds_bytes(D, DT == kF32 ? 4 : 2);
-        if (lds <= kMaxRowLds) {
-            const int w = lds_row_waves(D * (DT == kF32 ? 4 : 2));
-            return hipLaunchKernel(lds_kernel<FULL, DT, MOD>(w), dim3((uint32_t)L, (uint32_t)B),
-                                   dim3(kBlock * w), args, (size_t)lds, stream);
-        }
-        return hipLaunchKernel(
-            reinterpret_cast<const void*>(&gate_add_rms_modulate_generic_kernel<FULL, DT, MOD>),
-            dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args,
-            (size_t)(5 * 16 * Span<DT, kStage>::kWords), stream);
+    // 2-byte rows with row modulation take the register-row kernel also when
+    // aligned (its realignment is then a no-op): on MI355X it ran 1-3 %
+    // faster than the pack kernel there, and 1-3 % slower with per-token
+    // modulation, which keeps the pack kernel, as binary32 does
+    if constexpr (DT != kF32 && MOD == kModRow) {
+        return launch_element<FULL, DT, MOD>(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                                             stream);
+    } else {
+        if (!fast)
+            return launch_element<FULL, DT, MOD>(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                                                 stream);
+        float d_float = (float)D;
+        int vpr = (int)(D / 8);
+        fused_kernel_t k = pick<FULL, DT, MOD>((int)ceil_div(vpr, 64));
+        if (k == nullptr)
+            return hipErrorInvalidValue;
+        void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k),
+                               dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
+                               stream);
     }
-    int vpr = (int)(D / 8);
-    fused_kernel_t k = pick<FULL, DT, MOD>((int)ceil_div(vpr, 64));
-    if (k == nullptr)
-        return hipErrorInvalidValue;
-    void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
-    return hipLaunchKernel(reinterpret_cast<const void*>(k),
-                           dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
-                           stream);
 }
 
 template <int DT>
