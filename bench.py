@@ -19,19 +19,30 @@ Reported (one JSON line on stdout):
   cold         per-call microseconds with the caches flushed before each call
                (a 1 GiB read with cache-allocating loads pushes earlier data
                out of the L2s and the 256 MB memory-side cache and leaves
-               only clean lines), median of repetitions
-  variants     with --variants 1: the _ex calls at DiT shapes (binary16 and
-               binary32 storage, per-token modulation, the element-wise paths
-               for ragged D, element offsets and rows past the register
-               limit), the ideogram4 [1,4096,4608] bcast shape, the
-               LayerNorm modulation at [2,32640,4096] and the tanh-GELU on
-               the FFN intermediate [1,32640,16384]; cold and back-to-back
-               per-call time
-  small_configs with --small-configs 1: the other workload configurations
-               (c1 full [1,126,2048] + rms_modulate, c2 bcast [1,L,3072] for
-               L = 512, 4096, 4608): cold per-call time, and back-to-back
-               per-call time (launch overhead and cache-resident inputs
-               dominate at these sizes)
+               only clean lines), median of repetitions; frac_of_hbm_peak
+               and frac_of_mix_ceiling of every launch come from it
+  mix_ceilings the read:write mixes of the step's launches on their own
+               (rga_stream: the gate-add kernels' access shape with an XOR for
+               arithmetic), timed by the same cold protocol on buffers of the
+               launches' sizes: 3 reads + 1 write at [1,8160,4096] (c3's mix),
+               2 reads + 1 write in place at [1,32640,4096] (c4's) and at
+               [2,32640,4096] (c5's gate-add), 1 read + 1 write at
+               [2,32640,4096] (the modulation's), and a read-only stream
+  small_configs the other workload configurations (c1 full [1,126,2048] +
+               rms_modulate, c2 bcast [1,L,3072] for L = 512, 4096, 4608):
+               cold per-call time, and back-to-back per-call time (launch
+               overhead and cache-resident inputs dominate at these sizes)
+  variants     a compact set by default (the ideogram4 [1,4096,4608] bcast
+               shape, binary16 rms_modulate and bf16 LayerNorm modulation at
+               [2,32640,4096], the tanh-GELU on the FFN intermediate
+               [1,32640,16384]); with --variants 1 every _ex variant as
+               well (binary16 and binary32 storage, per-token modulation, the
+               element-wise paths for ragged D, element offsets and rows past
+               the register limit); cold and back-to-back per-call time
+  ablations    with --ablations 1: the broadcast-gate add at c4 in the
+               shapes the library does not use (rows per wave with the gate
+               held, store cache policies), cold, and the store policies
+               inside a chain of kernels on rotating buffers
   fused        the residual update + next modulation fused into one pass
                (rga_gate_add_rms_modulate) at the [2,32640,4096] shapes,
                against the step's own separate launches of the two kernels
@@ -118,12 +129,17 @@ def parse_args():
                    help="repetitions per launch of the cache-flushed timing (0: skip)")
     p.add_argument("--cpu-fraction", type=float, default=1.0,
                    help="fraction of each launch's rows the CPU oracle runs on (0: skip)")
-    p.add_argument("--small-configs", type=int, default=0,
-                   help="1: also time the c1/c2 configurations (kept out of the default "
-                        "run so a profile of it averages the step's launches only)")
+    p.add_argument("--small-configs", type=int, default=1,
+                   help="1: also time the c1/c2 configurations (0: skip)")
     p.add_argument("--variants", type=int, default=0,
-                   help="1: also time the _ex variants (storage types, per-token "
-                        "modulation, element-wise paths) and the ideogram4 shape")
+                   help="0: the compact variant set; 1: every _ex variant as well "
+                        "(storage types, per-token modulation, element-wise paths); "
+                        "-1: none")
+    p.add_argument("--mix-ceilings", type=int, default=1,
+                   help="1: time the read:write mix ceilings of the step's launches")
+    p.add_argument("--ablations", type=int, default=0,
+                   help="1: time the broadcast-gate add in the shapes the library does "
+                        "not use (row tiles, store policies)")
     p.add_argument("--fused-reps", type=int, default=30,
                    help="repetitions of the fused-vs-separate comparison (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -199,14 +215,33 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 10 * 2 * FLUSH_BYTES / (hev.ms(ev[0], ev[1]) * 1e-3) / 1e9
     log(f"copy ceiling {copy_gbps:.0f} GB/s")
-    # read-only ceiling: the same 1 GiB read by the flush kernel
+    # the cache flush's own rate: cache-allocating loads, not a ceiling
     hev.record(ev[0], stream)
     for _ in range(10):
         dte.read_(src, sink)
     hev.record(ev[1], stream)
     torch.cuda.synchronize()
-    read_gbps = 10 * FLUSH_BYTES / (hev.ms(ev[0], ev[1]) * 1e-3) / 1e9
-    log(f"read ceiling {read_gbps:.0f} GB/s")
+    flush_gbps = 10 * FLUSH_BYTES / (hev.ms(ev[0], ev[1]) * 1e-3) / 1e9
+    log(f"flush read {flush_gbps:.0f} GB/s")
+    del dst
+    torch.cuda.empty_cache()
+
+    e0, e1 = hev.new(), hev.new()
+
+    def cold_times(fn, reps, before=None):
+        """Per-call microseconds, each call after a 1 GiB cache-allocating read
+        (and after `before`, untimed, when given)."""
+        ts = []
+        for _ in range(reps):
+            if before is not None:
+                before()
+            dte.read_(src, sink)
+            hev.record(e0, stream)
+            fn()
+            hev.record(e1, stream)
+            hev.sync(e1)
+            ts.append(hev.ms(e0, e1) * 1e3)
+        return ts
 
     def run_step(events=None):
         for i, l in enumerate(launches):
@@ -250,33 +285,31 @@ def main():
     cold = {}
     if args.cold_reps > 0:
         log(f"cold timing, {args.cold_reps} reps per launch")
-        e0, e1 = hev.new(), hev.new()
         for name, kernel, nbytes, fn in launches:
-            ts = []
-            for _ in range(args.cold_reps):
-                dte.read_(src, sink)
-                hev.record(e0, stream)
-                fn()
-                hev.record(e1, stream)
-                hev.sync(e1)
-                ts.append(hev.ms(e0, e1) * 1e3)
+            ts = cold_times(fn, args.cold_reps)
             med = statistics.median(ts)
             cold[name] = {"us_median": round(med, 2),
                           "us_p10": round(float(np.percentile(ts, 10)), 2),
                           "us_p90": round(float(np.percentile(ts, 90)), 2),
-                          "GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}
+                          "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                          "frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
-    e0, e1 = hev.new(), hev.new()
+    # the read:write mix of each launch on its own, same buffer sizes, same protocol
+    mixes = {}
+    if args.mix_ceilings and args.cold_reps > 0:
+        log("mix ceilings")
+        mixes = mix_ceilings(dte, torch, dev, cold_times, args.cold_reps, log)
+        for name, m in mixes.items():
+            for launch in m.get("compares_with", []):
+                if launch in cold:
+                    cold[launch]["mix"] = name
+                    cold[launch]["mix_ceiling_us"] = m["cold_us_median"]
+                    cold[launch]["frac_of_mix_ceiling"] = round(
+                        m["cold_us_median"] / cold[launch]["us_median"], 4)
+        torch.cuda.empty_cache()
 
     def cold_and_warm(fn, nbytes, kernel):
-        ts = []
-        for _ in range(args.cold_reps):
-            dte.read_(src, sink)
-            hev.record(e0, stream)
-            fn()
-            hev.record(e1, stream)
-            hev.sync(e1)
-            ts.append(hev.ms(e0, e1) * 1e3)
+        ts = cold_times(fn, args.cold_reps)
         hev.record(e0, stream)
         for _ in range(100):
             fn()
@@ -284,12 +317,15 @@ def main():
         hev.sync(e1)
         warm = hev.ms(e0, e1) * 1e3 / 100
         med = statistics.median(ts)
+        # the cold median is the measurement; back to back, inputs that fit
+        # the 256 MB memory-side cache are served from it (context only)
         return {"kernel": kernel, "bytes": nbytes, "cold_us_median": round(med, 2),
+                "cold_us_p10": round(float(np.percentile(ts, 10)), 2),
+                "cold_us_p90": round(float(np.percentile(ts, 90)), 2),
                 "cold_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                 "back_to_back_us": round(warm, 2),
-                "back_to_back_GBps": round(nbytes / (warm * 1e-6) / 1e9, 1),
-                "frac_of_hbm_peak": round(max(nbytes / (med * 1e-6), nbytes / (warm * 1e-6))
-                                          / 1e9 / HBM_PEAK_GBPS, 4)}
+                "back_to_back_GBps": round(nbytes / (warm * 1e-6) / 1e9, 1)}
 
     small = {}
     if args.small_configs and args.cold_reps > 0:
@@ -302,16 +338,24 @@ def main():
             small[c.name + "_gate_add"] = cold_and_warm(
                 lambda: dte.rga_residual_gate_add(d["x"], d["u"], d["g"], out=o, gate_mode=c.gate),
                 gate_bytes(c), "gate_add_full_kernel" if c.gate == GATE_FULL else "gate_add_bcast_kernel")
+            small[c.name + "_gate_add"]["shape"] = [c.B, c.L, c.D]
             if c.rms:
                 small[c.name + "_rms_modulate"] = cold_and_warm(
                     lambda: dte.rms_modulate(d["x"], d["scale"], d["shift"], c.eps, out=o),
                     (2 * c.elems + 2 * c.B * c.D) * 2, "rms_modulate_kernel")
+                small[c.name + "_rms_modulate"]["shape"] = [c.B, c.L, c.D]
             del d, o
 
     variants = {}
-    if args.variants and args.cold_reps > 0:
-        log("variants: storage types, per-token modulation, element-wise paths, ideogram4")
-        variants = run_variants(dte, torch, dev, cold_and_warm, log)
+    if args.variants >= 0 and args.cold_reps > 0:
+        log("variants" + (": every _ex variant" if args.variants else ": compact set"))
+        variants = run_variants(dte, torch, dev, cold_and_warm, log, full=bool(args.variants))
+        torch.cuda.empty_cache()
+
+    ablations = {}
+    if args.ablations and args.cold_reps > 0:
+        log("ablations: broadcast-gate add shapes and store policies at c4")
+        ablations = run_ablations(dte, torch, dev, d4, cold_times, hev, stream, args.cold_reps, log)
         torch.cuda.empty_cache()
 
     fused = {}
@@ -351,7 +395,8 @@ def main():
                  "separate_pair_from": "per_launch c5_bcast_gate_add_inplace + c5_rms_modulate",
                  "speedup_vs_separate": round(pair / fus, 3)}
 
-    # roofline of the kernel with the largest share of the step
+    # roofline of the kernel with the largest share of the step, from the
+    # step's own launches (the other shapes above do not enter it)
     by_kernel = {}
     for name, kernel, nbytes, _ in launches:
         agg = by_kernel.setdefault(kernel, {"bytes": 0, "us": 0.0, "launches": 0})
@@ -374,9 +419,21 @@ def main():
     hev.close()
     cpu = None
     if host is not None:
-        del d3, d4, d5, out3, y5, src, dst
+        del d3, d4, d5, out3, y5, src
         torch.cuda.empty_cache()
         cpu = cpu_baseline(host, args.cpu_fraction, args.cpu_seconds, log)
+
+    headline = {}
+    for key, launch in (("bcast_[1,32640,4096]", "c4_bcast_gate_add_inplace"),
+                        ("full_[1,8160,4096]", "c3_full_gate_add")):
+        headline[key] = {k: per_launch[launch][k] for k in ("us", "GBps")}
+        if launch in cold:
+            headline[key]["cold_us"] = cold[launch]["us_median"]
+            headline[key]["cold_GBps"] = cold[launch]["GBps"]
+            headline[key]["cold_frac_of_hbm_peak"] = cold[launch]["frac_of_hbm_peak"]
+            if "frac_of_mix_ceiling" in cold[launch]:
+                headline[key]["mix"] = cold[launch]["mix"]
+                headline[key]["cold_frac_of_mix_ceiling"] = cold[launch]["frac_of_mix_ceiling"]
 
     result = {
         "metric": METRIC,
@@ -398,27 +455,131 @@ def main():
                         "bcast gate-add in place [2,32640,4096]",
             "step_bytes": step_bytes,
             "gpu_time_per_step_ms": round(gpu_step_ms, 4),
-            "headline": {
-                "bcast_[1,32640,4096]": {k: per_launch["c4_bcast_gate_add_inplace"][k] for k in ("us", "GBps")},
-                "full_[1,8160,4096]": {k: per_launch["c3_full_gate_add"][k] for k in ("us", "GBps")},
-            },
+            "headline": headline,
         },
         "per_launch": per_launch,
         "cold": cold,
+        "mix_ceilings": mixes,
         "small_configs": small,
         "variants": variants,
         "fused": fused,
+        "ablations": ablations,
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        "read_ceiling_GBps": round(read_gbps, 1),
+        "flush_read_GBps": round(flush_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
 
 
-def run_variants(dte, torch, dev, cold_and_warm, log):
+def mix_ceilings(dte, torch, dev, cold_times, reps, log):
+    """rga_stream at the step's read:write mixes and sizes, cold protocol.
+    Each entry names the launches it bounds (compares_with)."""
+    import numpy as np
+    e3 = 8160 * 4096 * 2          # bytes of one [1,8160,4096] bf16 tensor
+    e4 = 32640 * 4096 * 2         # [1,32640,4096]
+    e5 = 2 * e4                   # [2,32640,4096]
+    specs = [
+        # name, sources, write (None / "new" / "inplace"), bytes per stream, words/lane, bounds
+        ("3R:1W [1,8160,4096]", 3, "new", e3, 1, ["c3_full_gate_add"]),
+        ("2R:1W in place [1,32640,4096]", 2, "inplace", e4, 1, ["c4_bcast_gate_add_inplace"]),
+        ("2R:1W in place [2,32640,4096]", 2, "inplace", e5, 1, ["c5_bcast_gate_add_inplace"]),
+        ("1R:1W [2,32640,4096]", 1, "new", e5, 1, ["c5_rms_modulate"]),
+        ("R [2,32640,4096], 1 word per lane", 1, None, e5, 1, []),
+        ("R [2,32640,4096], 2 words per lane", 1, None, e5, 2, []),
+    ]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nsrc, write, nbytes, wpl, bounds in specs:
+        srcs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(nsrc)]
+        for k, t in enumerate(srcs):
+            dte.fill_(t, 0x3F803F80 + k)
+        dst = None
+        if write == "new":
+            dst = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+        elif write == "inplace":
+            dst = srcs[0]
+        fn = lambda: dte.stream_(srcs, dst, words_per_lane=wpl, sink=sink)
+        fn()
+        ts = cold_times(fn, reps)
+        med = statistics.median(ts)
+        total = nbytes * (nsrc + (1 if dst is not None else 0))
+        out[name] = {"reads": nsrc, "writes": 0 if dst is None else 1,
+                     "in_place": write == "inplace", "words_per_lane": wpl,
+                     "bytes": total, "cold_us_median": round(med, 2),
+                     "cold_us_p10": round(float(np.percentile(ts, 10)), 2),
+                     "cold_us_p90": round(float(np.percentile(ts, 90)), 2),
+                     "GBps": round(total / (med * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_peak": round(total / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "compares_with": bounds}
+        log(f"mix {name}: {med:.2f} us, {total / (med * 1e-6) / 1e9:.0f} GB/s")
+        del srcs, dst
+    return out
+
+
+def run_ablations(dte, torch, dev, d4, cold_times, hev, stream, reps, log):
+    """The c4 broadcast-gate add (in place, [1,32640,4096]) in the shapes and
+    store policies the library does not use (rga_gate_add_variant), cold; and
+    each store policy inside a chain that leaves nothing to reuse from the
+    caches: the gate-add on one of four rotating (x, u) sets, then a 1 GiB
+    nontemporal copy, repeated; per-kernel and chain time from HIP events."""
+    B, L, D = 1, 32640, 4096
+    nbytes = (3 * B * L * D + B * D) * 2
+    x, u, g = d4["x"], d4["u"], d4["g"]
+    pol = {"nt": dte.STORE_NT, "plain": dte.STORE_PLAIN, "device": dte.STORE_DEVICE}
+    out = {"shape": [B, L, D], "bytes": nbytes, "cold": {}, "chain": {}}
+    for T in (1, 2, 4, 8):
+        for pname, sp in pol.items():
+            if T != 1 and pname != "nt":
+                continue
+            fn = lambda: dte.gate_add_variant(x, u, g, out=x, rows_per_wave=T, store_policy=sp)
+            fn()
+            ts = cold_times(fn, reps)
+            med = statistics.median(ts)
+            key = f"rows_per_wave={T} store={pname}"
+            out["cold"][key] = {"us_median": round(med, 2),
+                                "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                "frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            log(f"ablation {key}: {med:.2f} us")
+    # chain on rotating buffers: nothing a kernel reads was touched by the
+    # previous few kernels, so a store policy that parks lines in a cache
+    # pays their write-back inside the chain
+    sets = [(torch.empty_like(x), torch.empty_like(u)) for _ in range(4)]
+    for xs, us_ in sets:
+        xs.copy_(x)
+        us_.copy_(u)
+    csrc = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    cdst = torch.empty_like(csrc)
+    dte.fill_(csrc, 0x3F803F80)
+    steps = 16
+    for pname, sp in pol.items():
+        evs = [hev.new() for _ in range(2 * steps + 1)]
+        for k in range(4):
+            xs, us_ = sets[k % 4]
+            dte.gate_add_variant(xs, us_, g, out=xs, rows_per_wave=1, store_policy=sp)
+            dte.copy_(cdst, csrc)
+        torch.cuda.synchronize()
+        for k in range(steps):
+            xs, us_ = sets[k % 4]
+            hev.record(evs[2 * k], stream)
+            dte.gate_add_variant(xs, us_, g, out=xs, rows_per_wave=1, store_policy=sp)
+            hev.record(evs[2 * k + 1], stream)
+            dte.copy_(cdst, csrc)
+        hev.record(evs[-1], stream)
+        torch.cuda.synchronize()
+        tg = statistics.mean(hev.ms(evs[2 * k], evs[2 * k + 1]) * 1e3 for k in range(steps))
+        tc = statistics.mean(hev.ms(evs[2 * k + 1], evs[2 * k + 2]) * 1e3 for k in range(steps))
+        out["chain"][f"store={pname}"] = {"gate_add_us": round(tg, 2), "copy_1GiB_us": round(tc, 2),
+                                          "pair_us": round(tg + tc, 2)}
+        log(f"ablation chain store={pname}: gate {tg:.2f} us, copy {tc:.2f} us")
+    del sets, csrc, cdst
+    return out
+
+
+def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
     """The _ex variants at DiT shapes, each timed cold (caches flushed) and
-    back to back. Inputs: seeded normal draws on the device (x N(0,2), u
+    back to back; with full=False only a compact set (ideogram4, binary16
+    rms_modulate, bf16 LayerNorm modulation, bf16 tanh-GELU). Inputs: seeded normal draws on the device (x N(0,2), u
     N(0,1), gate uniform(-1,1), scale/shift N(0,0.1)), out of place.
     Algorithmic bytes: every input element read once (a broadcast row once
     per call), every output element written once, at the storage size."""
@@ -523,10 +684,44 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         (3 * c.elems + c.B * c.D) * 2, "gate_add_bcast_kernel")
     del dx, du, dg, do
 
-    for dt in ("f16", "f32"):
-        gate(f"{dt}_bcast_gate_add_[1,32640,4096]", 1, 32640, 4096, dt, dte.GATE_BCAST)
-        gate(f"{dt}_full_gate_add_[1,8160,4096]", 1, 8160, 4096, dt, dte.GATE_FULL)
-        rms(f"{dt}_rms_modulate_[2,32640,4096]", 2, 32640, 4096, dt, dte.MOD_ROW)
+    # LayerNorm modulation at the modulation shape
+    def ln(name, B, L, D, dt, mod):
+        mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
+        x = draw((B, L, D), dt, 2.0)
+        sc, sh = draw(mshape, dt, 0.1), draw(mshape, dt, 0.1)
+        o = torch.empty_like(x)
+        n = B * L * D
+        nbytes = (2 * n + 2 * (n if mod == dte.MOD_TOKEN else B * D)) * x.element_size()
+        log(f"variant {name}")
+        out[name] = cold_and_warm(
+            lambda: dte.rga_ln_modulate(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
+            "ln_modulate_kernel" if D % 8 == 0 else element_norm_kernel("ln", D, dt))
+
+    # tanh-GELU on the FFN intermediate (video tokens x 4 hidden)
+    def gelu(name, rows, F, dt, with_bias=False):
+        x = draw((1, rows, F), dt, 2.0)
+        b = draw((F,), dt) if with_bias else None
+        o = torch.empty_like(x)
+        nbytes = (2 * rows * F + (F if with_bias else 0)) * x.element_size()
+        fast = (F % 8 == 0) if with_bias else True
+        log(f"variant {name}")
+        out[name] = cold_and_warm(lambda: dte.gelu_tanh(x, b, out=o), nbytes,
+                                  ("gelu_tanh_bias_kernel" if with_bias else "gelu_tanh_flat_kernel")
+                                  if fast else "gelu_tanh_generic_bias_kernel")
+
+    # the compact set (default run)
+    rms("f16_rms_modulate_[2,32640,4096]", 2, 32640, 4096, "f16", dte.MOD_ROW)
+    ln("bf16_ln_modulate_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW)
+    gelu("bf16_gelu_tanh_[1,32640,16384]", 32640, 16384, "bf16")
+    if not full:
+        torch.cuda.synchronize()
+        return out
+
+    gate("f16_bcast_gate_add_[1,32640,4096]", 1, 32640, 4096, "f16", dte.GATE_BCAST)
+    gate("f16_full_gate_add_[1,8160,4096]", 1, 8160, 4096, "f16", dte.GATE_FULL)
+    gate("f32_bcast_gate_add_[1,32640,4096]", 1, 32640, 4096, "f32", dte.GATE_BCAST)
+    gate("f32_full_gate_add_[1,8160,4096]", 1, 8160, 4096, "f32", dte.GATE_FULL)
+    rms("f32_rms_modulate_[2,32640,4096]", 2, 32640, 4096, "f32", dte.MOD_ROW)
     rms("bf16_rms_modulate_token_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_TOKEN)
     fused("bf16_fused_token_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.GATE_BCAST, dte.MOD_TOKEN)
     fused("f16_fused_[2,32640,4096]", 2, 32640, 4096, "f16", dte.GATE_BCAST, dte.MOD_ROW)
@@ -543,36 +738,8 @@ def run_variants(dte, torch, dev, cold_and_warm, log):
         offset=1)
     gate("f32_bcast_gate_add_offset1_[1,8160,4096]", 1, 8160, 4096, "f32", dte.GATE_BCAST,
          offset=1)
-    # LayerNorm modulation at the modulation shape
-    def ln(name, B, L, D, dt, mod):
-        mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
-        x = draw((B, L, D), dt, 2.0)
-        sc, sh = draw(mshape, dt, 0.1), draw(mshape, dt, 0.1)
-        o = torch.empty_like(x)
-        n = B * L * D
-        nbytes = (2 * n + 2 * (n if mod == dte.MOD_TOKEN else B * D)) * x.element_size()
-        log(f"variant {name}")
-        out[name] = cold_and_warm(
-            lambda: dte.rga_ln_modulate(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
-            "ln_modulate_kernel" if D % 8 == 0 else element_norm_kernel("ln", D, dt))
-
-    ln("bf16_ln_modulate_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_ROW)
     ln("f16_ln_modulate_token_[2,32640,4096]", 2, 32640, 4096, "f16", dte.MOD_TOKEN)
     ln("bf16_ln_modulate_ragged_[2,32640,4100]", 2, 32640, 4100, "bf16", dte.MOD_ROW)
-
-    # tanh-GELU on the FFN intermediate (video tokens x 4 hidden)
-    def gelu(name, rows, F, dt, with_bias=False):
-        x = draw((1, rows, F), dt, 2.0)
-        b = draw((F,), dt) if with_bias else None
-        o = torch.empty_like(x)
-        nbytes = (2 * rows * F + (F if with_bias else 0)) * x.element_size()
-        fast = (F % 8 == 0) if with_bias else True
-        log(f"variant {name}")
-        out[name] = cold_and_warm(lambda: dte.gelu_tanh(x, b, out=o), nbytes,
-                                  ("gelu_tanh_bias_kernel" if with_bias else "gelu_tanh_flat_kernel")
-                                  if fast else "gelu_tanh_generic_bias_kernel")
-
-    gelu("bf16_gelu_tanh_[1,32640,16384]", 32640, 16384, "bf16")
     gelu("bf16_gelu_tanh_bias_[1,32640,16384]", 32640, 16384, "bf16", with_bias=True)
     gelu("f16_gelu_tanh_[1,32640,16384]", 32640, 16384, "f16")
     gelu("f32_gelu_tanh_[1,8160,16384]", 8160, 16384, "f32")

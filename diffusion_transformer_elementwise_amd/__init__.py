@@ -30,6 +30,10 @@ forms:
 The FFN's tanh-GELU, any storage type, over the last dimension F:
 
     gelu_tanh(x, bias=None, out=None)   out = gelu(x + bias)
+
+Measurement helpers (include/rga_measure.h): copy_, fill_, read_ (cache
+flush), stream_ (read:write mix ceilings) and gate_add_variant (the
+broadcast-gate add in the shapes the library does not use).
 """
 from __future__ import annotations
 
@@ -47,13 +51,18 @@ from ._lib import (  # noqa: F401
     RGA_ERR_UNSUPPORTED,
     RGA_OK,
     RGA_RMS_MAX_D,
+    STORE_DEVICE,
+    STORE_NT,
+    STORE_PLAIN,
     RGAError,
     check_gate_add_rms_modulate,
     check_gate_add_rms_modulate_ex,
     check_residual_gate_add,
     check_residual_gate_add_ex,
     check_rms_modulate,
+    check_gate_add_variant,
     check_gelu_tanh,
+    check_stream,
     check_ln_modulate,
     check_rms_modulate_ex,
     library,
@@ -63,6 +72,8 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     copy_,
     fill_,
+    gate_add_variant,
+    stream_,
     gelu_tanh,
     read_,
     rga_gate_add_rms_modulate,

@@ -38,6 +38,10 @@ RGA_ERR_HIP = 4
 
 RGA_RMS_MAX_D = 8192
 
+STORE_NT = 0
+STORE_PLAIN = 1
+STORE_DEVICE = 2
+
 
 class RGAError(RuntimeError):
     def __init__(self, status: int, call: str):
@@ -102,6 +106,15 @@ def _load():
     lib.rga_fill.restype = i32
     lib.rga_read.argtypes = [p, i64, p, p]
     lib.rga_read.restype = i32
+    pp = ctypes.POINTER(p)
+    lib.rga_stream.argtypes = [pp, i32, p, i64, i32, p, p]
+    lib.rga_stream.restype = i32
+    lib.rga_check_stream.argtypes = [pp, i32, p, i64, i32, p]
+    lib.rga_check_stream.restype = i32
+    lib.rga_gate_add_variant.argtypes = [p, p, p, p, i64, i64, i64, i32, i32, p]
+    lib.rga_gate_add_variant.restype = i32
+    lib.rga_check_gate_add_variant.argtypes = [p, p, p, p, i64, i64, i64, i32, i32]
+    lib.rga_check_gate_add_variant.restype = i32
     return lib
 
 
@@ -153,3 +166,21 @@ def check_gelu_tanh(x, bias, out, rows, F, dtype) -> int:
 
 def check_ln_modulate(x, scale, shift, eps, out, B, L, D, mod_mode, dtype) -> int:
     return _LIB.rga_check_ln_modulate(x, scale, shift, eps, out, B, L, D, mod_mode, dtype)
+
+
+def pointer_array(ptrs):
+    """A C array of device addresses (for rga_stream's source list)."""
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))()
+    for i, a in enumerate(ptrs):
+        arr[i] = a
+    return arr
+
+
+def check_stream(srcs, dst, nbytes, words_per_lane, sink) -> int:
+    return _LIB.rga_check_stream(pointer_array(srcs) if srcs else None, len(srcs), dst,
+                                 nbytes, words_per_lane, sink)
+
+
+def check_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave, store_policy) -> int:
+    return _LIB.rga_check_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave,
+                                           store_policy)

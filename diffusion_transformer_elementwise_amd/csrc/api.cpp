@@ -7,16 +7,16 @@
 //      int64;
 //   2. RGA_OK without a launch when B*L*D == 0 (pointers may be NULL);
 //   3. RGA_ERR_INVALID_ARG: a NULL pointer;
-//   4. RGA_ERR_UNSUPPORTED: for the original calls D % 8 != 0, a pointer not
-//      16-byte aligned or D above RGA_RMS_MAX_D (modulation); for the _ex
-//      calls a pointer not aligned to the element size; a grid beyond the
-//      dispatch limit;
+//   4. RGA_ERR_UNSUPPORTED: for the original calls D % 8 != 0 or a pointer
+//      not 16-byte aligned; for the _ex calls a pointer not aligned to the
+//      element size; a grid beyond the dispatch limit;
 //   5. RGA_ERR_ALIAS: an output overlapping an input other than the exact
 //      in-place aliases each call allows.
-// The _ex calls take the 16-byte-pack kernels when every pointer is 16-byte
+// Every call takes the 16-byte-pack kernels when every pointer is 16-byte
 // aligned and D % 8 == 0 (any D for a full-gate add, which is one flat
 // stream) and, for the modulation, D <= RGA_RMS_MAX_D; the element-wise
-// kernels otherwise. The fused call with 2-byte rows and row modulation
+// kernels otherwise (for the original calls: modulation rows above
+// RGA_RMS_MAX_D, staged in LDS). The fused call with 2-byte rows and row modulation
 // always takes its register-row element kernel (the faster one there).
 // The gate-add rejection of unsupported inputs mirrors the residual-gate
 // page's test list ("unsupported input rejection"); the bf16-only contract
@@ -75,10 +75,10 @@ bool aligned_to(const void* p, int n)
 
 // Layout rule shared by the three operations. strict: the original calls
 // (bf16 only, D % 8 == 0 and 16-byte alignment or RGA_ERR_UNSUPPORTED);
-// otherwise pointers need only element alignment and *fast tells whether the
-// 16-byte-pack kernels can run. max_d > 0 caps the fast path's D (the
-// modulation holds a row in registers); in strict mode a larger D is
-// unsupported.
+// otherwise pointers need only element alignment. *fast tells whether the
+// 16-byte-pack kernels can run; max_d > 0 caps their D (the modulation holds
+// a row in registers). A row above that cap is not an unsupported input: it
+// runs the kernels that stage the row in LDS, in the same summation order.
 int layout(const void* const* ptrs, int nptr, int64_t D, int es, bool strict,
            int64_t max_d, bool* fast)
 {
@@ -88,9 +88,9 @@ int layout(const void* const* ptrs, int nptr, int64_t D, int es, bool strict,
             return RGA_ERR_UNSUPPORTED;
         all16 = all16 && aligned16(ptrs[i]);
     }
-    *fast = all16 && D % 8 == 0 && (max_d <= 0 || D <= max_d);
-    if (strict && !*fast)
+    if (strict && !(all16 && D % 8 == 0))
         return RGA_ERR_UNSUPPORTED;
+    *fast = all16 && D % 8 == 0 && (max_d <= 0 || D <= max_d);
     return RGA_OK;
 }
 
@@ -507,6 +507,98 @@ int rga_read(const void* src, int64_t nbytes, void* sink, hipStream_t stream)
                : RGA_ERR_HIP;
 }
 
+static int check_stream(const void* const* src, int nsrc, const void* dst, int64_t nbytes,
+                        int words_per_lane, const void* sink)
+{
+    if (nsrc < 0 || nsrc > 3 || nbytes < 0)
+        return RGA_ERR_INVALID_ARG;
+    if (words_per_lane != 1 && words_per_lane != 2 && words_per_lane != 4)
+        return RGA_ERR_INVALID_ARG;
+    if (nsrc == 0 && dst == nullptr)
+        return RGA_ERR_INVALID_ARG;
+    if (nbytes == 0)
+        return RGA_OK;
+    if (nsrc > 0 && src == nullptr)
+        return RGA_ERR_INVALID_ARG;
+    for (int k = 0; k < nsrc; ++k)
+        if (src[k] == nullptr)
+            return RGA_ERR_INVALID_ARG;
+    if (dst == nullptr && sink == nullptr)
+        return RGA_ERR_INVALID_ARG;
+    if (nbytes % 16 != 0 || (dst && !aligned16(dst)) || (!dst && !aligned16(sink)))
+        return RGA_ERR_UNSUPPORTED;
+    for (int k = 0; k < nsrc; ++k)
+        if (!aligned16(src[k]))
+            return RGA_ERR_UNSUPPORTED;
+    if (!rga::stream_grid_fits(nbytes / 16))
+        return RGA_ERR_UNSUPPORTED;
+    if (dst) {
+        const Range d = range_of(dst, nbytes);
+        for (int k = 0; k < nsrc; ++k)
+            if (overlaps(d, range_of(src[k], nbytes)) && !(k == 0 && dst == src[0]))
+                return RGA_ERR_ALIAS;
+    } else {
+        const Range s = range_of(sink, 16);
+        for (int k = 0; k < nsrc; ++k)
+            if (overlaps(s, range_of(src[k], nbytes)))
+                return RGA_ERR_ALIAS;
+    }
+    return RGA_OK;
+}
+
+int rga_check_stream(const void* const* src, int nsrc, const void* dst, int64_t nbytes,
+                     int words_per_lane, const void* sink)
+{
+    return check_stream(src, nsrc, dst, nbytes, words_per_lane, sink);
+}
+
+int rga_stream(const void* const* src, int nsrc, void* dst, int64_t nbytes,
+               int words_per_lane, void* sink, hipStream_t stream)
+{
+    const int st = check_stream(src, nsrc, dst, nbytes, words_per_lane, sink);
+    if (st != RGA_OK || nbytes == 0)
+        return st;
+    return launched(rga::launch_stream(src, nsrc, dst, nbytes / 16, words_per_lane, sink,
+                                       stream));
+}
+
+static int check_gate_add_variant(const void* x, const void* u, const void* g,
+                                  const void* out, int64_t B, int64_t L, int64_t D,
+                                  int rows_per_wave, int store_policy)
+{
+    if (rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4 && rows_per_wave != 8)
+        return RGA_ERR_INVALID_ARG;
+    if (store_policy != RGA_STORE_NT && store_policy != RGA_STORE_PLAIN &&
+        store_policy != RGA_STORE_DEVICE)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    const int st = check_gate_add(x, u, g, out, B, L, D, RGA_GATE_BCAST, RGA_DTYPE_BF16,
+                                  true, &fast);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    if (!rga::gate_add_variant_grid_fits(B, L, D, rows_per_wave))
+        return RGA_ERR_UNSUPPORTED;
+    return RGA_OK;
+}
+
+int rga_check_gate_add_variant(const void* x, const void* u, const void* g, const void* out,
+                               int64_t B, int64_t L, int64_t D, int rows_per_wave,
+                               int store_policy)
+{
+    return check_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave, store_policy);
+}
+
+int rga_gate_add_variant(const void* x, const void* u, const void* g, void* out,
+                         int64_t B, int64_t L, int64_t D, int rows_per_wave,
+                         int store_policy, hipStream_t stream)
+{
+    const int st = check_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave, store_policy);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return launched(rga::launch_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave,
+                                                 store_policy, stream));
+}
+
 const char* rga_status_string(int status)
 {
     switch (status) {
@@ -516,8 +608,9 @@ const char* rga_status_string(int status)
         return "invalid argument (negative or overflowing size, bad gate "
                "mode or eps, NULL pointer)";
     case RGA_ERR_UNSUPPORTED:
-        return "unsupported input (D not a multiple of 8, pointer not "
-               "16-byte aligned, D too large, or grid too large)";
+        return "unsupported input (D not a multiple of 8 or pointer not "
+               "16-byte aligned for a call without a storage type, pointer "
+               "not aligned to the element size, or grid too large)";
     case RGA_ERR_ALIAS:
         return "output overlaps an input other than as an allowed in-place "
                "alias";

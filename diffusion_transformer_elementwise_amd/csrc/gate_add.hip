@@ -27,6 +27,7 @@
 #include "realign.hpp"
 
 #include <rga.h>
+#include <rga_measure.h>
 
 namespace rga {
 namespace {
@@ -98,6 +99,65 @@ __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
     const Pack<DT> uv = I::load_stream(u, c0, t, h);
     const Pack<DT> gv = I::load(g, b * vpr + col0, t, h);
     I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
+}
+
+// Measurement variants of the bf16 broadcast-gate add (rga_gate_add_variant
+// in rga_measure.h), same arithmetic and result as gate_add_bcast_kernel:
+//   T rows per wave: the wave takes one 64-pack column chunk of T consecutive
+//     rows and loads its gate pack once for all of them (the row tile of the
+//     residual-gate page's Nsight Compute check); T = 1 is the library's
+//     shape. Grid: x = (row tile) * chunks + chunk, y = batch.
+//   SP, the stores' cache policy: RGA_STORE_NT (nontemporal, the library's),
+//     RGA_STORE_PLAIN (default policy: lines stay dirty in the L2) or
+//     RGA_STORE_DEVICE (device scope: written through the L2 into the
+//     memory-side cache, which may keep them; a buffer store with the SC1
+//     bit, whose descriptor covers exactly the chunk's valid bytes).
+template <int SP>
+__device__ __forceinline__ void store_with_policy(void* out, int64_t c0, int t, int h,
+                                                  const u32x4& v)
+{
+    u32x4* p = static_cast<u32x4*>(out) + c0;
+    if constexpr (SP == RGA_STORE_NT) {
+        store16_stream(p + t, v);
+    } else if constexpr (SP == RGA_STORE_PLAIN) {
+        store16(p + t, v);
+    } else {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(p, (short)0, h * 16, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, t * 16, 0, 16 /* SC1 */);
+    }
+}
+
+template <int T, int SP>
+__global__ __launch_bounds__(kBlock) void gate_add_bcast_rows_kernel(
+    const void* x, const void* u, const void* g, void* out, int64_t L,
+    uint32_t vpr, uint32_t chunks)
+{
+    const uint32_t tile = blockIdx.x / chunks;
+    const uint32_t chunk = blockIdx.x - tile * chunks;
+    const uint32_t col0 = chunk * kBlock;
+    const int t = threadIdx.x;
+    const int h = (vpr - col0 < (uint32_t)kBlock) ? (int)(vpr - col0) : kBlock;
+    if (t >= h)
+        return;
+    const int64_t b = blockIdx.y;
+    const int64_t l0 = (int64_t)tile * T;
+    const Pack<kBF16> gv = Pack<kBF16>::load(g, b * vpr + col0 + t);
+    Pack<kBF16> xv[T], uv[T];
+#pragma unroll
+    for (int r = 0; r < T; ++r) {
+        if (l0 + r < L) {
+            const int64_t c0 = (b * L + l0 + r) * vpr + col0;
+            xv[r] = Pack<kBF16>::load_stream(x, c0 + t);
+            uv[r] = Pack<kBF16>::load_stream(u, c0 + t);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < T; ++r) {
+        if (l0 + r < L)
+            store_with_policy<SP>(out, (b * L + l0 + r) * vpr + col0, t, h,
+                                  gate_add8<kBF16>(xv[r], uv[r], gv).v);
+    }
 }
 
 template <int DT>
@@ -232,6 +292,40 @@ bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode, int es,
         return false;
     return fast ? L * ceil_div(D / 8, kBlock) <= max_wg
                 : L * element_chunks(D * es) <= max_wg;
+}
+
+bool gate_add_variant_grid_fits(int64_t B, int64_t L, int64_t D, int rows_per_wave)
+{
+    const int64_t max_wg = (((int64_t)1 << 32) - 1) / kBlock;
+    return B <= 65535 && ceil_div(L, rows_per_wave) * ceil_div(D / 8, kBlock) <= max_wg;
+}
+
+template <int T>
+const void* variant_kernel(int store_policy)
+{
+    switch (store_policy) {
+    case RGA_STORE_PLAIN:
+        return reinterpret_cast<const void*>(&gate_add_bcast_rows_kernel<T, RGA_STORE_PLAIN>);
+    case RGA_STORE_DEVICE:
+        return reinterpret_cast<const void*>(&gate_add_bcast_rows_kernel<T, RGA_STORE_DEVICE>);
+    default:
+        return reinterpret_cast<const void*>(&gate_add_bcast_rows_kernel<T, RGA_STORE_NT>);
+    }
+}
+
+hipError_t launch_gate_add_variant(const void* x, const void* u, const void* g, void* out,
+                                   int64_t B, int64_t L, int64_t D, int rows_per_wave,
+                                   int store_policy, hipStream_t stream)
+{
+    const void* k = rows_per_wave == 8   ? variant_kernel<8>(store_policy)
+                    : rows_per_wave == 4 ? variant_kernel<4>(store_policy)
+                    : rows_per_wave == 2 ? variant_kernel<2>(store_policy)
+                                         : variant_kernel<1>(store_policy);
+    uint32_t vpr = (uint32_t)(D / 8);
+    uint32_t chunks = (uint32_t)ceil_div(vpr, kBlock);
+    void* args[] = {&x, &u, &g, &out, &L, &vpr, &chunks};
+    return hipLaunchKernel(k, dim3((uint32_t)(ceil_div(L, rows_per_wave) * chunks), (uint32_t)B),
+                           dim3(kBlock), args, 0, stream);
 }
 
 hipError_t launch_gate_add(const void* x, const void* u, const void* g,

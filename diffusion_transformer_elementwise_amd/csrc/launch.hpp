@@ -72,5 +72,17 @@ hipError_t launch_fill(void* dst, int64_t n16, uint32_t value,
                        hipStream_t stream);
 hipError_t launch_read(const void* src, int64_t n16, void* sink,
                        hipStream_t stream);
+// nsrc in 0..3 source streams, dst NULL for a read-only stream (then sink is
+// the 16-byte word the fold may reach), words_per_lane 1, 2 or 4
+hipError_t launch_stream(const void* const* src, int nsrc, void* dst, int64_t n16,
+                         int words_per_lane, void* sink, hipStream_t stream);
+
+// bf16 broadcast-gate add in a chosen shape, for measurement (gate_add.hip):
+// rows_per_wave 1, 2, 4 or 8 with the gate pack held across them, and the
+// store's cache policy (RGA_STORE_* of rga_measure.h)
+bool gate_add_variant_grid_fits(int64_t B, int64_t L, int64_t D, int rows_per_wave);
+hipError_t launch_gate_add_variant(const void* x, const void* u, const void* g, void* out,
+                                   int64_t B, int64_t L, int64_t D, int rows_per_wave,
+                                   int store_policy, hipStream_t stream);
 
 }  // namespace rga

@@ -9,6 +9,14 @@
 //         only clean lines, i.e. a cache flush that bills no write-back to
 //         the next kernel; the words are XOR-folded into a 16-byte sink so
 //         the loads cannot be dropped.
+//   stream: the read:write mixes of the gated adds on their own. 0 to 3
+//         source streams and at most one destination stream of the same
+//         size, the gate-add kernels' access shape (64-lane workgroups,
+//         nontemporal 16-byte loads and stores, consecutive lanes on
+//         consecutive words) with the arithmetic replaced by an XOR, and 1,
+//         2 or 4 words per lane (a read-only stream needs two words per lane
+//         to reach its own limit: with one, the many very short waves leave
+//         the dispatcher as the bound).
 #include "bf16x8.hpp"
 #include "launch.hpp"
 
@@ -86,6 +94,61 @@ __global__ __launch_bounds__(kReadBlock) void read_kernel(const u32x4* src,
     }
 }
 
+// NSRC source streams XORed into the destination (WRITE) or, without one,
+// folded into a per-lane value that reaches sink only when it equals a
+// pattern that must never occur in practice (kNever): the compiler has to keep
+// every load. dst may be s0 (in place): each word is read before it is
+// written, by the same lane. Lanes past n16 do nothing.
+constexpr uint32_t kNever[4] = {0x9E3779B9u, 0x7F4A7C15u, 0xF39CC060u, 0x5CEDC834u};
+
+template <int NSRC, bool WRITE, int WPL>
+__global__ __launch_bounds__(kCopyBlock) void stream_kernel(const u32x4* s0, const u32x4* s1,
+                                                            const u32x4* s2, u32x4* dst,
+                                                            int64_t n16, u32x4* sink)
+{
+    const int64_t base = (int64_t)blockIdx.x * (kCopyBlock * WPL) + threadIdx.x;
+    u32x4 v[WPL];
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) {
+        const int64_t i = base + (int64_t)k * kCopyBlock;
+        v[k] = u32x4{(uint32_t)i, 0x3F80u, 0u, 0u};
+        if (i < n16) {
+            if constexpr (NSRC > 0)
+                v[k] = load16_stream(s0 + i);
+            if constexpr (NSRC > 1)
+                v[k] ^= load16_stream(s1 + i);
+            if constexpr (NSRC > 2)
+                v[k] ^= load16_stream(s2 + i);
+        }
+    }
+    u32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) {
+        const int64_t i = base + (int64_t)k * kCopyBlock;
+        if (i < n16) {
+            if constexpr (WRITE)
+                store16_stream(dst + i, v[k]);
+            else
+                acc ^= v[k];
+        }
+    }
+    if constexpr (!WRITE) {
+        if (acc[0] == kNever[0] && acc[1] == kNever[1] && acc[2] == kNever[2] &&
+            acc[3] == kNever[3])
+            *sink = acc;
+    }
+}
+
+template <int NSRC, bool WRITE>
+const void* stream_kernel_for(int wpl)
+{
+    switch (wpl) {
+    case 1: return reinterpret_cast<const void*>(&stream_kernel<NSRC, WRITE, 1>);
+    case 2: return reinterpret_cast<const void*>(&stream_kernel<NSRC, WRITE, 2>);
+    default: return reinterpret_cast<const void*>(&stream_kernel<NSRC, WRITE, 4>);
+    }
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
@@ -114,6 +177,27 @@ hipError_t launch_fill(void* dst, int64_t n16, uint32_t value,
     return hipLaunchKernel(reinterpret_cast<const void*>(&fill_kernel),
                            dim3((uint32_t)ceil_div(n16, (int64_t)kBlock * kFillUnroll)),
                            dim3(kBlock), args, 0, stream);
+}
+
+hipError_t launch_stream(const void* const* src, int nsrc, void* dst, int64_t n16,
+                         int words_per_lane, void* sink, hipStream_t stream)
+{
+    const u32x4* s[3] = {nullptr, nullptr, nullptr};
+    for (int k = 0; k < nsrc && k < 3; ++k)
+        s[k] = static_cast<const u32x4*>(src[k]);
+    u32x4* d = static_cast<u32x4*>(dst);
+    u32x4* k = static_cast<u32x4*>(sink);
+    const bool w = dst != nullptr;
+    const void* f = nullptr;
+    switch (nsrc) {
+    case 0: f = stream_kernel_for<0, true>(words_per_lane); break;
+    case 1: f = w ? stream_kernel_for<1, true>(words_per_lane) : stream_kernel_for<1, false>(words_per_lane); break;
+    case 2: f = w ? stream_kernel_for<2, true>(words_per_lane) : stream_kernel_for<2, false>(words_per_lane); break;
+    default: f = w ? stream_kernel_for<3, true>(words_per_lane) : stream_kernel_for<3, false>(words_per_lane); break;
+    }
+    void* args[] = {&s[0], &s[1], &s[2], &d, &n16, &k};
+    return hipLaunchKernel(f, dim3((uint32_t)ceil_div(n16, (int64_t)kCopyBlock * words_per_lane)),
+                           dim3(kCopyBlock), args, 0, stream);
 }
 
 hipError_t launch_read(const void* src, int64_t n16, void* sink,

@@ -5,7 +5,7 @@ from __future__ import annotations
 import torch
 
 from ._lib import (DTYPE_BF16, DTYPE_F16, DTYPE_F32, GATE_BCAST, GATE_FULL, MOD_ROW,
-                   MOD_TOKEN, RGA_OK, RGAError, library)
+                   MOD_TOKEN, RGA_OK, STORE_NT, RGAError, library, pointer_array)
 
 
 # torch's raw accessor of the current stream (what its own compiled kernels
@@ -298,3 +298,46 @@ def read_(src: torch.Tensor, sink: torch.Tensor) -> torch.Tensor:
     if st != RGA_OK:
         raise RGAError(st, "rga_read")
     return sink
+
+
+def stream_(srcs, dst: torch.Tensor | None = None, words_per_lane: int = 1,
+            sink: torch.Tensor | None = None) -> None:
+    """Measurement helper (rga_stream): reads every source tensor in full and,
+    with ``dst``, writes dst = XOR of the sources (a read:write mix with no
+    arithmetic). Sources and dst have one byte size; dst may be srcs[0] (in
+    place). Without dst the stream is read-only and ``sink`` (16 bytes) is
+    required."""
+    srcs = list(srcs)
+    ref = dst if dst is not None else srcs[0]
+    n = ref.numel() * ref.element_size()
+    for t in srcs + ([dst] if dst is not None else []) + ([sink] if sink is not None else []):
+        if t.device.type != "cuda" or t.device != ref.device or not t.is_contiguous():
+            raise ValueError("stream_ needs contiguous tensors on one HIP device")
+    for t in srcs:
+        if t.numel() * t.element_size() != n:
+            raise ValueError("stream_ needs sources of the destination's byte size")
+    st = library().rga_stream(pointer_array([t.data_ptr() for t in srcs]) if srcs else None,
+                              len(srcs), dst.data_ptr() if dst is not None else None, n,
+                              int(words_per_lane),
+                              sink.data_ptr() if sink is not None else None,
+                              _stream_handle(ref.device))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_stream")
+
+
+def gate_add_variant(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
+                     out: torch.Tensor | None = None, rows_per_wave: int = 1,
+                     store_policy: int = STORE_NT) -> torch.Tensor:
+    """Measurement helper (rga_gate_add_variant): the bf16 broadcast-gate add
+    of rga_residual_gate_add in another kernel shape (rows per wave with the
+    gate held, store cache policy); same result bit for bit."""
+    B, L, D = _x_shape(x, torch.bfloat16)
+    dev = x.device
+    _gate(x, u, g, GATE_BCAST, torch.bfloat16, dev)
+    out = _output(out, "out", x, dev)
+    st = library().rga_gate_add_variant(x.data_ptr(), u.data_ptr(), g.data_ptr(),
+                                        out.data_ptr(), B, L, D, int(rows_per_wave),
+                                        int(store_policy), _stream_handle(dev))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_gate_add_variant")
+    return out

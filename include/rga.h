@@ -63,15 +63,19 @@ enum {
     RGA_OK = 0,
     RGA_ERR_INVALID_ARG = 1, /* negative dim, size overflow, bad gate_mode,
                                 bad eps, NULL pointer with B*L*D > 0 */
-    RGA_ERR_UNSUPPORTED = 2, /* D % 8 != 0, misaligned pointer, D above the
-                                modulation's limit, grid too large */
+    RGA_ERR_UNSUPPORTED = 2, /* D % 8 != 0 or a pointer not 16-byte aligned
+                                (calls without a dtype), a pointer not
+                                aligned to the element size (_ex calls),
+                                grid too large */
     RGA_ERR_ALIAS = 3,       /* out overlaps an input other than as allowed */
     RGA_ERR_HIP = 4,         /* the HIP runtime rejected the launch */
 };
 
-/* Largest D that rms_modulate and rga_gate_add_rms_modulate accept (one
- * row is held in registers). The _ex calls accept any D (larger rows, and
- * D % 8 != 0, run the element-wise kernels). */
+/* Largest D whose modulation rows the 16-byte-pack kernels hold in
+ * registers. Longer rows are not rejected: rms_modulate,
+ * rga_gate_add_rms_modulate and the _ex calls run them with kernels that
+ * stage each row in LDS (or, past 64 KB per row, read it twice), in the same
+ * summation order, so the results do not depend on which kernel ran. */
 #define RGA_RMS_MAX_D 8192
 
 /* Storage types of the _ex calls (all tensors of a call share one type).
@@ -120,7 +124,8 @@ int rga_residual_gate_add(const void* x, const void* u, const void* g,
  *   x, out        : [B, L, D]
  *   scale, shift  : [B, 1, D]; row b is used for every l
  *   eps           : finite, >= 0 (else RGA_ERR_INVALID_ARG)
- *   D             : multiple of 8, at most RGA_RMS_MAX_D
+ *   D             : multiple of 8 (rows above RGA_RMS_MAX_D are staged in
+ *                   LDS; same result)
  * Per row (b, l): ss = sum of x_d^2, r = 1 / sqrt(ss / D + eps); per element
  * y = ((x_d * r) * (1 + scale_d)) + shift_d, each step binary32, then bf16.
  * The sum of squares has one fixed order: the row is cut into groups of 8
@@ -150,7 +155,7 @@ int rms_modulate(const void* x, const void* scale, const void* shift,
  *   x, u, x_out, y : [B, L, D]
  *   g              : [B, L, D] (RGA_GATE_FULL) or [B, 1, D] (RGA_GATE_BCAST)
  *   scale, shift   : [B, 1, D]
- *   eps            : finite, >= 0;  D: multiple of 8, at most RGA_RMS_MAX_D
+ *   eps            : finite, >= 0;  D: multiple of 8 (any size)
  * Results are bit-identical to rga_residual_gate_add(x, u, g, x_out) followed
  * by rms_modulate(x_out, scale, shift, eps, y): the modulation reads the
  * bf16-rounded x_out, with the same fixed reduction order.

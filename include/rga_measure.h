@@ -43,6 +43,66 @@ int rga_fill(void* dst, int64_t nbytes, uint32_t value, hipStream_t stream);
  */
 int rga_read(const void* src, int64_t nbytes, void* sink, hipStream_t stream);
 
+/*
+ * Stream ceiling of one read:write mix: nsrc source streams (0 to 3) of
+ * nbytes each, read in full, and, when dst is not NULL, one destination
+ * stream of nbytes written in full with dst[i] = XOR of the sources' word i
+ * (a fixed pattern when nsrc == 0). The access shape is the gate-add
+ * kernels': 64-lane workgroups, nontemporal 128-bit loads and stores, lane t
+ * of a workgroup on consecutive words, words_per_lane (1, 2 or 4) words per
+ * lane strided by 64 words. It times what a mix of nsrc reads and one write
+ * of the same size can reach on the device, apart from any arithmetic.
+ *   - src: array of nsrc device pointers (may be NULL when nsrc == 0).
+ *   - dst == NULL makes a read-only stream (nsrc >= 1): the XOR of all words
+ *     is then folded per lane and written to the 16 bytes at sink only if it
+ *     equals a fixed 128-bit pattern (so no load can be dropped); sink is a
+ *     16-byte aligned device word the caller owns, otherwise unused.
+ *   - dst == src[0] is the in-place form (each word is read, then written,
+ *     by one lane); any other overlap of dst with a source, or of sink with
+ *     any stream, is RGA_ERR_ALIAS.
+ * Errors: nsrc outside 0..3, words_per_lane not 1, 2 or 4, nbytes < 0, a
+ * NULL source, no destination with nsrc == 0, no sink for a read-only stream:
+ * RGA_ERR_INVALID_ARG; nbytes % 16 != 0 or a pointer not 16-byte aligned:
+ * RGA_ERR_UNSUPPORTED. nbytes == 0 is a no-op.
+ */
+int rga_stream(const void* const* src, int nsrc, void* dst, int64_t nbytes,
+               int words_per_lane, void* sink, hipStream_t stream);
+
+/* rga_stream's validation alone, on the host: the status rga_stream would
+ * return before enqueueing anything (RGA_OK when it would launch). */
+int rga_check_stream(const void* const* src, int nsrc, const void* dst, int64_t nbytes,
+                     int words_per_lane, const void* sink);
+
+/* Cache policy of the stores of rga_gate_add_variant. */
+enum {
+    RGA_STORE_NT = 0,     /* nontemporal (what every library kernel uses) */
+    RGA_STORE_PLAIN = 1,  /* default policy: the lines stay dirty in the L2 */
+    RGA_STORE_DEVICE = 2, /* device scope (SC1): written through the L2 into
+                             the memory-side cache, which may hold them */
+};
+
+/*
+ * The bf16 broadcast-gate add out = x + u * g of rga_residual_gate_add
+ * (RGA_GATE_BCAST; same arithmetic, same result bit for bit) in a chosen
+ * kernel shape, to measure the shapes the library does not use:
+ *   - rows_per_wave (1, 2, 4 or 8): one wave takes a 64-pack column chunk
+ *     of that many consecutive rows and loads its gate pack once for all of
+ *     them (the row-tiled form of the residual-gate page's "B200 Nsight
+ *     Compute check"); 1 is the library's shape;
+ *   - store_policy: RGA_STORE_*.
+ * Arguments, layout, aliasing and errors as rga_residual_gate_add with
+ * gate_mode = RGA_GATE_BCAST (D % 8 == 0, 16-byte aligned pointers); a bad
+ * rows_per_wave or store_policy is RGA_ERR_INVALID_ARG.
+ */
+int rga_gate_add_variant(const void* x, const void* u, const void* g, void* out,
+                         int64_t B, int64_t L, int64_t D, int rows_per_wave,
+                         int store_policy, hipStream_t stream);
+
+/* rga_gate_add_variant's validation alone, on the host. */
+int rga_check_gate_add_variant(const void* x, const void* u, const void* g, const void* out,
+                               int64_t B, int64_t L, int64_t D, int rows_per_wave,
+                               int store_policy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,7 +124,10 @@ def test_rms_validation_rules(dte):
     assert ck(0, 0, 0, 1e-6, 0, 0, 1, 8) == ok
     assert ck(x, s, t, 1e-6, o, 1, 1, 20) == uns
     assert ck(x, s, t, 1e-6, o, 1, 1, dte.RGA_RMS_MAX_D) == ok
-    assert ck(x, s, t, 1e-6, o, 1, 1, dte.RGA_RMS_MAX_D + 8) == uns
+    # longer rows are not an unsupported layout: they run the LDS-staged kernels
+    assert ck(x, s, t, 1e-6, o, 1, 1, dte.RGA_RMS_MAX_D + 8) == ok
+    assert ck(x, s, t, 1e-6, o, 1, 1, 16384) == ok
+    assert ck(x, s, t, 1e-6, o, 1, 1, 16388) == uns
     assert ck(x, s + 4, t, 1e-6, o, 1, 1, 8) == uns
     assert ck(x, s, t, 1e-6, x, 1, 4, 8) == ok  # in place
     assert ck(x, s, t, 1e-6, x + 16, 1, 4, 8) == ali
@@ -169,7 +172,24 @@ def test_gate_add_isa_has_no_fused_multiply_add():
     # The product of two 2-byte values is exact in binary32, so a fused
     # multiply-add would change results only for subnormal products (and for
     # binary32 storage it would change many); the build must never contract.
-    bodies = _kernel_bodies(_device_asm("gate_add.hip"))
+    every = _kernel_bodies(_device_asm("gate_add.hip"))
+    # measurement variants (rga_gate_add_variant): bf16 broadcast gate,
+    # {1, 2, 4, 8} rows per wave x {nontemporal, plain, device-scope} stores
+    variants = {n: b for n, b in every.items() if "rows_kernel" in n}
+    bodies = {n: b for n, b in every.items() if "rows_kernel" not in n}
+    assert len(variants) == 12, sorted(variants)
+    for name, body in variants.items():
+        assert not re.search(r"\bv_(pk_)?(fma|fmac|fmamk|fmaak|mad|mac)(_mix\w*)?_f(16|32|64)", body), name
+        T = int(re.search(r"rows_kernelILi(\d)E", name).group(1))
+        SP = int(re.search(r"rows_kernelILi\dELi(\d)E", name).group(1))
+        # one gate load for the whole tile, x and u per row
+        assert len(re.findall(r"global_load_dwordx4", body)) == 1 + 2 * T, name
+        if SP == 2:   # device scope: buffer stores with the SC1 bit, no nt
+            stores = re.findall(r"buffer_store_dwordx4[^\n]*", body)
+            assert len(stores) == T and all("sc1" in s and "nt" not in s for s in stores), name
+        else:
+            stores = re.findall(r"global_store_dwordx4[^\n]*", body)
+            assert len(stores) == T and all((" nt" in s) == (SP == 0) for s in stores), name
     # {full, bcast, generic full, generic bcast} x {bf16, f16, f32}
     assert len(bodies) == 12, sorted(bodies)
     fast = {n: b for n, b in bodies.items() if "generic" not in n}
@@ -240,7 +260,8 @@ def test_fused_validation_rules(dte):
     assert call(y=0) == bad
     assert call(x=0, u=0, g=0, scale=0, shift=0, x_out=0, y=0, L=0) == ok
     assert call(D=4100) == uns
-    assert call(D=8200) == uns
+    assert call(D=8200) == ok      # above the register rows: staged in LDS
+    assert call(D=8204) == uns
     assert call(shift=t + 8) == uns
     # in place: each output may be x or u (or g in full mode)
     assert call(x_out=x) == ok
@@ -286,7 +307,7 @@ def test_ex_validation_rules(dte):
     rm = dte.check_rms_modulate_ex
     s, t = A + 64 * MB, A + 96 * MB
     assert rm(x, s, t, 1e-6, o, 1, 3, dte.RGA_RMS_MAX_D + 8, ROW, BF) == ok
-    assert dte.check_rms_modulate(x, s, t, 1e-6, o, 1, 3, dte.RGA_RMS_MAX_D + 8) == uns
+    assert dte.check_rms_modulate(x, s, t, 1e-6, o, 1, 3, dte.RGA_RMS_MAX_D + 8) == ok
     assert rm(x, s, t, 1e-6, o, 1, 3, 4097, TOK, F16) == ok
     assert rm(x, s, t, 1e-6, o, 1, 3, 8, 2, BF) == bad
     assert rm(x, s, t, -1.0, o, 1, 3, 8, ROW, BF) == bad
@@ -439,3 +460,38 @@ def test_package_fails_loudly_without_the_library(tmp_path):
                        env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "no CPU fallback" in r.stderr, r.stderr[-2000:]
+
+
+def test_measurement_validation_rules(dte):
+    ok, bad, uns, ali = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED, dte.RGA_ERR_ALIAS
+    st = dte.check_stream
+    a, b, c, d, k = (A + i * 64 * MB for i in range(5))
+    n = 16 * MB
+    assert st([a, b, c], d, n, 1, 0) == ok          # 3 reads, 1 write
+    assert st([a, b], a, n, 1, 0) == ok             # in place on the first source
+    assert st([a, b], b, n, 1, 0) == ali            # only the first source may be dst
+    assert st([a, b], a + 16, n, 1, 0) == ali
+    assert st([a], None, n, 2, k) == ok             # read-only needs a sink
+    assert st([a], None, n, 2, 0) == bad
+    assert st([a], None, n, 2, a + 32) == ali       # sink inside a source
+    assert st([], d, n, 4, 0) == ok                 # write-only
+    assert st([], None, n, 1, k) == bad
+    assert st([a, b, c, a], d, n, 1, 0) == bad      # at most 3 sources
+    assert st([a], d, n, 3, 0) == bad               # 1, 2 or 4 words per lane
+    assert st([a], d, -16, 1, 0) == bad
+    assert st([a], d, 0, 1, 0) == ok                # empty: no-op
+    assert st([a], d, n + 8, 1, 0) == uns
+    assert st([a + 8], d, n, 1, 0) == uns
+    assert st([0], d, n, 1, 0) == bad
+
+    gv = dte.check_gate_add_variant
+    x, u, g, o = (A + i * 512 * MB for i in range(4))
+    for T in (1, 2, 4, 8):
+        for sp in (dte.STORE_NT, dte.STORE_PLAIN, dte.STORE_DEVICE):
+            assert gv(x, u, g, x, 1, 32640, 4096, T, sp) == ok
+    assert gv(x, u, g, o, 2, 32640, 4096, 3, 0) == bad
+    assert gv(x, u, g, o, 2, 32640, 4096, 1, 3) == bad
+    assert gv(x, u, g, o, 2, 33, 4100, 1, 0) == uns   # D % 8 != 0
+    assert gv(x, u, g + 2, o, 2, 33, 4096, 1, 0) == uns
+    assert gv(x, u, g, g, 2, 33, 4096, 1, 0) == ali   # out over the broadcast row
+    assert gv(0, 0, 0, 0, 0, 33, 4096, 1, 0) == ok
