@@ -386,7 +386,7 @@ def main():
         # and rms_modulate launches (same kernels, shapes and bytes)
         pair = per_launch["c5_bcast_gate_add_inplace"]["us"] + per_launch["c5_rms_modulate"]["us"]
         fused = {"shape": "[2,32640,4096] bcast gate, x_out in place",
-                 "kernel": "gate_add_rms_modulate_regs_kernel",
+                 "kernel": "gate_add_rms_modulate_staged_kernel",
                  "bytes": fused_bytes, "us": round(fus, 2),
                  "GBps": round(fused_bytes / (fus * 1e-6) / 1e9, 1),
                  "frac_of_hbm_peak": round(fused_bytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -648,9 +648,19 @@ def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
         out[name] = cold_and_warm(
             lambda: dte.rga_gate_add_rms_modulate_ex(x, u, g, sc, sh, 1e-6, x_out=xo, y=y,
                                                      gate_mode=mode, mod_mode=mod),
-            nbytes, "gate_add_rms_modulate_kernel"
-            if D % 8 == 0 and D <= 8192 and (mod == dte.MOD_TOKEN or dt == "f32")
-            else element_fused_kernel(D, dt))
+            nbytes, fused_kernel(D, dt, mode, mod))
+
+    def fused_kernel(D, dt, mode, mod):
+        # which kernel the call runs on 16-byte aligned tensors (csrc
+        # gate_add_rms_modulate.hip, launch_typed)
+        es = 4 if dt == "f32" else 2
+        if D % 8 == 0 and D <= 8192:
+            stage = (2 if mode == dte.GATE_FULL else 3) * D * es
+            if mod == dte.MOD_ROW and stage <= 65536:
+                return "gate_add_rms_modulate_staged_kernel"
+            if mod == dte.MOD_TOKEN or dt == "f32":
+                return "gate_add_rms_modulate_kernel"
+        return element_fused_kernel(D, dt)
 
     def element_fused_kernel(D, dt):
         # as element_norm_kernel; the fused call's LDS buffer has one more word

@@ -259,6 +259,14 @@ struct Grouped {
     {
         return load_stream_raw(b, c0, t, h);
     }
+    // load_raw from a row staged in LDS as 16-byte words in memory order
+    __device__ __forceinline__ static Pack<DT> lds_raw(const u32x4* w, int c0, int t, int h)
+    {
+        Pack<DT> p = Pack<DT>::zero();
+        if (t < h)
+            p.v = w[c0 + t];
+        return p;
+    }
 };
 
 template <>
@@ -330,6 +338,17 @@ struct Grouped<kF32> {
     }
     __device__ __forceinline__ static Pack<kF32> to_groups(const Pack<kF32>& p) { return swapped(p); }
     __device__ __forceinline__ static Pack<kF32> to_raw(const Pack<kF32>& p) { return swapped(p); }
+    // load_raw from a row staged in LDS as 16-byte words in memory order
+    __device__ __forceinline__ static Pack<kF32> lds_raw(const u32x4* w, int c0, int t, int h)
+    {
+        const u32x4* q = w + 2 * c0;
+        const int a = wa(t);
+        const u32x4 z = {0, 0, 0, 0};
+        Pack<kF32> p;
+        p.a = a < 2 * h ? q[a] : z;
+        p.b = 64 + a < 2 * h ? q[64 + a] : z;
+        return p;
+    }
     __device__ __forceinline__ static Pack<kF32> load_stream(const void* b, int64_t c0, int t,
                                                              int h)
     {

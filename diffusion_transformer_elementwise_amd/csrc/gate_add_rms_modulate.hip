@@ -16,12 +16,20 @@
 // outputs are bit-identical to rga_residual_gate_add followed by
 // rms_modulate.
 //
-// Pack path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers, with
-// per-token modulation or binary32 storage; 2-byte rows with row modulation
-// take the register-row kernel of the element path at any alignment, which
-// measured faster there), launch shape measured on MI355X: one wave per
-// workgroup and one row per
-// wave, nontemporal loads and stores. Every pack's x, u and g loads are
+// Pack path with row modulation (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte
+// aligned pointers, staged rows within one workgroup's 64 KB of LDS): two
+// waves per workgroup, one row each. The workgroup first stages its batch's
+// scale and shift rows, and a broadcast gate row, in LDS; then each wave
+// loads x and u (and a full gate), forms x', stores it, reduces it and
+// applies the modulation from LDS; the launch caps the workgroups per CU
+// through the LDS it asks for (row_wg_lds in launch.hpp). Measured on MI355X
+// at [2,32640,4096] inside a chain of the step's kernels: 349-350 us against
+// 356 us for the register-row kernel of the element path, which 2-byte rows
+// with row modulation took at any alignment before.
+//
+// Pack path with per-token modulation (and row modulation whose staging
+// would not fit), launch shape measured on MI355X: one wave per workgroup
+// and one row per wave, nontemporal loads and stores. Every pack's x, u and g loads are
 // issued before the first add, with no branch around a load (a branch per
 // bounded load made the wave wait for each pack before issuing the next);
 // each x_out pack is stored as soon as it is formed; scale and shift are read
@@ -141,6 +149,118 @@ __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_kernel(
             const float a = 1.0f + sc.get(e);
             const float m = n * a;
             o[e] = m + sh.get(e);
+        }
+        GP::store_stream_raw(Pack<DT>::make(o), y, row + 64 * i, lane, h);
+    }
+}
+
+// The same sums as a xor butterfly over __shfl_xor, bit for bit: exchanges 1
+// and 2 by DPP quad permutations, 4 and 8 by DPP half-row and row mirrors
+// (once lanes 4q..4q+3 hold equal values the mirror partner of a lane holds
+// what its xor-4 partner holds; likewise for 8 once groups of 8 agree), then
+// the exchanges at 16 and 32 from the four 16-lane sums read into scalars:
+// lane j's (s[j] + s[j^16]) + (s[j^32] + s[j^48]) is (r0 + r1) + (r2 + r3) on
+// every lane, as addition commutes. The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float a)
+{
+    a = a + dpp_from<0xB1>(a);   // quad_perm [1,0,3,2]: lane ^ 1
+    a = a + dpp_from<0x4E>(a);   // quad_perm [2,3,0,1]: lane ^ 2
+    a = a + dpp_from<0x141>(a);  // row_half_mirror: the other quad of its 8
+    a = a + dpp_from<0x140>(a);  // row_mirror: the other 8 of its 16
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Row modulation, kRowWaves waves per workgroup, one row each: rows
+// kRowWaves * blockIdx.x + wave of batch blockIdx.y. The dynamic LDS holds
+// the batch's scale row at [0, words), its shift row at [words, 2 words)
+// and, with a broadcast gate, its gate row at [2 words, 3 words), as 16-byte
+// words in memory order. Lanes past the row end hold zeros (x' = +0 there,
+// which adds +0 to the partial) and store nothing.
+template <int G, bool FULL, int DT>
+__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_staged_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int vpr)
+{
+    extern __shared__ u32x4 staged[];
+    const int lane = threadIdx.x & (kBlock - 1);
+    const int64_t b = blockIdx.y;
+    const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x / kBlock);
+    constexpr int kWords = DT == kF32 ? 2 : 1;  // 16-byte words per pack
+    const int words = vpr * kWords;
+    u32x4* s_st = staged;
+    u32x4* h_st = staged + words;
+    u32x4* g_st = staged + 2 * words;
+    const u32x4* sc = static_cast<const u32x4*>(scale) + b * words;
+    const u32x4* sh = static_cast<const u32x4*>(shift) + b * words;
+    const u32x4* gr = static_cast<const u32x4*>(g) + b * words;
+    for (int w = threadIdx.x; w < words; w += kBlock * kRowWaves) {
+        s_st[w] = load16(sc + w);
+        h_st[w] = load16(sh + w);
+        if constexpr (!FULL)
+            g_st[w] = load16(gr + w);
+    }
+    __syncthreads();
+    if (r >= L)
+        return;
+
+    using GP = Grouped<DT>;
+    const int64_t row = (b * L + r) * vpr;
+    Pack<DT> xv[G], uv[G], gv[FULL ? G : 1];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
+        uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
+        if constexpr (FULL)
+            gv[i] = GP::template load_clamped<true>(g, row + 64 * i, lane, h);
+    }
+    Pack<DT> xn[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        const Pack<DT> gi = FULL ? gv[FULL ? i : 0] : GP::lds_raw(g_st, 64 * i, lane, h);
+        const Pack<DT> xr = gate_add8<DT>(xv[i], uv[i], gi);
+        GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
+        xn[i] = GP::to_groups(xr);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float a = xn[i].get(e);
+            const float sa = a * a;
+            acc = acc + sa;
+        }
+    }
+    const float ms = wave_sum_dpp(acc) / d_float;
+    const float t = ms + eps;
+    const float q = sqrtf(t);
+    const float rr = 1.0f / q;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        const Pack<DT> xr = GP::to_raw(xn[i]);
+        const Pack<DT> s_ = GP::lds_raw(s_st, 64 * i, lane, h);
+        const Pack<DT> h_ = GP::lds_raw(h_st, 64 * i, lane, h);
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float n = xr.get(e) * rr;
+            const float a = 1.0f + s_.get(e);
+            const float m = n * a;
+            o[e] = m + h_.get(e);
         }
         GP::store_stream_raw(Pack<DT>::make(o), y, row + 64 * i, lane, h);
     }
@@ -523,6 +643,22 @@ fused_kernel_t pick(int groups)
     return nullptr;
 }
 
+template <bool FULL, int DT>
+const void* pick_staged(int groups)
+{
+    const void* t[] = {reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<1, FULL, DT>),
+                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<2, FULL, DT>),
+                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<4, FULL, DT>),
+                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<6, FULL, DT>),
+                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<8, FULL, DT>),
+                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<12, FULL, DT>),
+                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<16, FULL, DT>)};
+    for (int i = 0; i < 7; ++i)
+        if (groups <= kLadder[i])
+            return t[i];
+    return nullptr;
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <bool FULL, int DT, int MOD>
@@ -570,10 +706,23 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
                         void* x_out, void* y, int64_t B, int64_t L, int64_t D,
                         bool fast, hipStream_t stream)
 {
-    // 2-byte rows with row modulation take the register-row kernel also when
-    // aligned (its realignment is then a no-op): on MI355X it ran 1-3 %
-    // faster than the pack kernel there, and 1-3 % slower with per-token
-    // modulation, which keeps the pack kernel, as binary32 does
+    constexpr int64_t es = DT == kF32 ? 4 : 2;
+    const int64_t stage = (FULL ? 2 : 3) * D * es;
+    if (MOD == kModRow && fast && stage <= kMaxStagedLds) {
+        float d_float = (float)D;
+        int vpr = (int)(D / 8);
+        const void* k = pick_staged<FULL, DT>((int)ceil_div(vpr, 64));
+        if (k == nullptr)
+            return hipErrorInvalidValue;
+        void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
+        return hipLaunchKernel(k, dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
+                               dim3(kBlock * kRowWaves), args,
+                               (size_t)row_wg_lds(D * es, stage, kFusedRowBudget), stream);
+    }
+    // otherwise 2-byte rows with row modulation take the register-row kernel
+    // (aligned or not: on MI355X it ran 1-3 % faster than the one-wave pack
+    // kernel there, and 1-3 % slower with per-token modulation, which keeps
+    // the pack kernel, as binary32 does)
     if constexpr (DT != kF32 && MOD == kModRow) {
         return launch_element<FULL, DT, MOD>(x, u, g, scale, shift, eps, x_out, y, B, L, D,
                                              stream);

@@ -47,6 +47,34 @@ inline int lds_row_waves(int64_t row_bytes)
     return w;
 }
 
+// Row-modulation fast paths of the modulation and the fused call: waves (one
+// row each) per workgroup, and the dynamic LDS a workgroup asks for. It
+// holds the staged rows (stage_bytes: the batch's scale and shift rows, and
+// a broadcast gate row for the fused call) and is raised so that about
+// row_budget bytes of rows (kRowWaves per workgroup) stay on a CU: 4 to 12
+// workgroups of gfx950's 160 KB of LDS per CU, each asking for a whole
+// number of KB that leaves at least 1 KB of the CU unused (a request that
+// fills the CU exactly could leave room for one workgroup fewer). Measured
+// on MI355X: a kernel that holds a row per wave streams best with few rows
+// in flight per CU (a copy of 8 KB rows ran 175 us at full occupancy and
+// 165 us at 4-5 waves per CU, for 1.07 GB); the modulation of 8 KB rows ran
+// best at 5-6 workgroups per CU (4 slowed it on some boxes by 10-20 %), the
+// fused call at 4 (6 was 3 % slower, 3 4 % slower).
+constexpr int kRowWaves = 2;
+constexpr int64_t kModRowBudget = 48 * 1024;    // rms/LayerNorm modulation
+constexpr int64_t kFusedRowBudget = 32 * 1024;  // residual update + modulation
+inline int64_t row_wg_lds(int64_t row_bytes, int64_t stage_bytes, int64_t row_budget)
+{
+    constexpr int64_t kLdsPerCu = 160 * 1024;
+    int64_t wg = (row_budget + row_bytes / 2) / row_bytes;
+    wg = wg < 4 ? 4 : (wg > 12 ? 12 : wg);
+    const int64_t cap = ((kLdsPerCu - 1024) / wg) & ~(int64_t)1023;
+    return cap > stage_bytes ? cap : stage_bytes;
+}
+// one workgroup's LDS limit without an opt-in attribute: larger stagings take
+// the other kernels
+constexpr int64_t kMaxStagedLds = 64 * 1024;
+
 // residual update then modulation, one pass (gate_add_rms_modulate.hip)
 bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast);
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,

@@ -22,16 +22,21 @@
 //
 // Fast path (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte aligned pointers): the
 // row stays in registers (G packs per lane), read once from HBM and written
-// once, with nontemporal loads and stores; one wave per workgroup, two rows
-// per wave. With row modulation the scale and shift rows stay in registers
-// across the wave's rows (the shape that measured fastest on MI355X inside a
-// chain of streaming kernels; for binary32 too, 8 % faster than re-reading
-// them from L2 per row despite the register cost); per-token rows are read in
-// the apply phase instead. The LayerNorm's second sum runs
-// over the registers, so it costs arithmetic, not memory traffic. A binary32
-// pack is two words; they are moved with contiguous wave-wide accesses and
-// one lane exchange (Grouped in dtype.hpp) rather than two adjacent words per
-// lane, which left every access instruction half a cache line per lane.
+// once, with nontemporal loads and stores, one wave per row. With row
+// modulation a workgroup holds two waves (two rows of one batch); it first
+// stages that batch's scale and shift rows in LDS (from the L2: every
+// workgroup reads the same rows), then each wave loads its row, reduces it
+// and applies the modulation with scale and shift read from LDS. The launch
+// asks for more LDS than the staging needs, to cap the workgroups per CU
+// (row_wg_lds in launch.hpp); at [2,32640,4096] this form ran 168-174 us
+// against 178-183 us for the former one (two rows per wave, scale and shift
+// held in registers, 209 VGPRs), measured on MI355X in the same runs.
+// Per-token modulation reads its scale and shift rows in the apply phase,
+// one row per one-wave workgroup. The LayerNorm's second sum runs over the
+// registers, so it costs arithmetic, not memory traffic. A binary32 pack is
+// two words; they are moved with contiguous wave-wide accesses and one lane
+// exchange (Grouped in dtype.hpp) rather than two adjacent words per lane,
+// which left every access instruction half a cache line per lane.
 //
 // Element path (any D, element-aligned pointers), the same order: 2-byte
 // rows of up to 8192 elements are read once and realigned in registers
@@ -39,7 +44,9 @@
 // as one pass over the row, then the apply pass, moving spans of elements
 // through LDS with 16-byte accesses (span.hpp).
 //
-// One wave per workgroup: nothing crosses a wave. The fast path uses no LDS.
+// Apart from the row-modulation fast path (two waves sharing their staged
+// scale and shift rows) and the LDS-staged element path, one wave per
+// workgroup: no sum crosses a wave.
 #include "dtype.hpp"
 #include "launch.hpp"
 #include "row_regs.hpp"
@@ -50,16 +57,7 @@
 namespace rga {
 namespace {
 
-constexpr int kBlock = 64;  // one wave per workgroup
-// Rows per wave of the fast path: two with row modulation (the scale and
-// shift rows held in registers serve both), one with per-token modulation
-// (nothing to share, and two rows would put 64 KB of traffic through one
-// wave).
-template <int MOD>
-constexpr int rows_per_wave()
-{
-    return MOD == kModToken ? 1 : 2;
-}
+constexpr int kBlock = 64;  // one wave
 constexpr int kStage = 1024;  // element path: elements staged in LDS per sum step
 constexpr int kApply = 512;   // element path: elements per apply step
 
@@ -75,6 +73,32 @@ __device__ __forceinline__ float wave_sum(float acc)
     return acc;
 }
 
+// The same sums as wave_sum, bit for bit, with fewer round trips: exchanges
+// 1 and 2 by DPP quad permutations, 4 and 8 by DPP half-row and row mirrors
+// (once lanes 4q..4q+3 hold equal values, the mirror partner of a lane holds
+// what its xor-4 partner holds; likewise for 8 once groups of 8 agree), and
+// the exchanges at 16 and 32 from the four 16-lane sums read into scalars:
+// lane j's (s[j] + s[j^16]) + (s[j^32] + s[j^48]) is (r0 + r1) + (r2 + r3) on
+// every lane, as addition commutes. The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float a)
+{
+    a = a + dpp_from<0xB1>(a);   // quad_perm [1,0,3,2]: lane ^ 1
+    a = a + dpp_from<0x4E>(a);   // quad_perm [2,3,0,1]: lane ^ 2
+    a = a + dpp_from<0x141>(a);  // row_half_mirror: the other quad of its 8
+    a = a + dpp_from<0x140>(a);  // row_mirror: the other 8 of its 16
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 __device__ __forceinline__ float inv_std(float ss, float d_float, float eps)
 {
     const float ms = ss / d_float;
@@ -83,104 +107,147 @@ __device__ __forceinline__ float inv_std(float ss, float d_float, float eps)
     return 1.0f / q;
 }
 
-// One wave modulates rows r0 .. r1-1 of batch b. G = packs per lane (at
-// least ceil(D / 512)); lanes whose pack index is past the row end hold
-// zeros, which add +0 to a partial that is never -0 (the RMS sum of squares
-// and the LayerNorm sum of x) and are left out of the LayerNorm sum of
-// squared deviations.
+// The normalisation factor of one row held as G packs per lane (lane t,
+// pack i holds group t + 64i; lanes past the row end hold zeros, which add
+// +0 to a partial that is never -0 and are left out of the LayerNorm's sum of
+// squared deviations). Returns r; *mu is the LayerNorm mean (0 for RMS).
+template <int G, int DT, int NORM, bool DPP>
+__device__ __forceinline__ float row_factor(const Pack<DT> (&xv)[G], int lane, int vpr,
+                                            float eps, float d_float, float* mu_out)
+{
+    float mu = 0.0f;
+    if constexpr (NORM == kNormLn) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc = acc + xv[i].get(e);
+        }
+        mu = (DPP ? wave_sum_dpp(acc) : wave_sum(acc)) / d_float;
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        if (NORM == kNormLn && lane + 64 * i >= vpr)
+            continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a = xv[i].get(e);
+            if constexpr (NORM == kNormLn)
+                a = a - mu;
+            const float sa = a * a;
+            acc = acc + sa;
+        }
+    }
+    *mu_out = mu;
+    return inv_std(DPP ? wave_sum_dpp(acc) : wave_sum(acc), d_float, eps);
+}
+
+template <int DT, int NORM>
+__device__ __forceinline__ Pack<DT> modulate_pack(const Pack<DT>& xr, float mu, float rr,
+                                                  const Pack<DT>& s_, const Pack<DT>& h_)
+{
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v = xr.get(e);
+        if constexpr (NORM == kNormLn)
+            v = v - mu;
+        const float n = v * rr;
+        const float a = 1.0f + s_.get(e);
+        const float m = n * a;
+        o[e] = m + h_.get(e);
+    }
+    return Pack<DT>::make(o);
+}
+
+// Row modulation, kRowWaves waves per workgroup, one row each: rows
+// kRowWaves * blockIdx.x + wave of batch blockIdx.y. The batch's scale and
+// shift rows are staged in the dynamic LDS as 16-byte words in memory order
+// (scale at [0, words), shift at [words, 2 words)) before any row is loaded.
+template <int G, int DT, int NORM>
+__device__ __forceinline__ void modulate_staged_row(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
+{
+    extern __shared__ u32x4 staged[];
+    const int lane = threadIdx.x & (kBlock - 1);
+    const int64_t b = blockIdx.y;
+    const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x / kBlock);
+    constexpr int kWords = DT == kF32 ? 2 : 1;  // 16-byte words per pack
+    const int words = vpr * kWords;
+    const u32x4* sc = static_cast<const u32x4*>(scale) + b * words;
+    const u32x4* sh = static_cast<const u32x4*>(shift) + b * words;
+    for (int w = threadIdx.x; w < words; w += kBlock * kRowWaves) {
+        staged[w] = load16(sc + w);
+        staged[words + w] = load16(sh + w);
+    }
+    __syncthreads();
+    if (r >= L)
+        return;
+
+    const int64_t row = (b * L + r) * vpr;
+    Pack<DT> xv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        xv[i] = Grouped<DT>::load_stream(x, row + 64 * i, lane, vpr - 64 * i);
+    float mu;
+    const float rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
+    // element-wise, so in raw order (binary32 rows are turned back from group
+    // order, which needs every lane); packs past the row end are not stored
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        const Pack<DT> s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
+        const Pack<DT> h_ = Grouped<DT>::lds_raw(staged + words, 64 * i, lane, h);
+        Grouped<DT>::store_stream_raw(
+            modulate_pack<DT, NORM>(Grouped<DT>::to_raw(xv[i]), mu, rr, s_, h_), out,
+            row + 64 * i, lane, h);
+    }
+}
+
+// Per-token modulation, one wave per workgroup and per row (nothing to share
+// between rows): row blockIdx.x of batch blockIdx.y, its scale and shift rows
+// read in the apply phase.
+template <int G, int DT, int NORM>
+__device__ __forceinline__ void modulate_token_row(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
+{
+    const int lane = threadIdx.x;
+    const int64_t row = ((int64_t)blockIdx.y * L + blockIdx.x) * vpr;
+    Pack<DT> xv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        xv[i] = Grouped<DT>::load_stream(x, row + 64 * i, lane, vpr - 64 * i);
+    float mu;
+    const float rr = row_factor<G, DT, NORM, false>(xv, lane, vpr, eps, d_float, &mu);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int h = vpr - 64 * i;
+        const Pack<DT> s_ = Grouped<DT>::load_stream_raw(scale, row + 64 * i, lane, h);
+        const Pack<DT> h_ = Grouped<DT>::load_stream_raw(shift, row + 64 * i, lane, h);
+        Grouped<DT>::store_stream_raw(
+            modulate_pack<DT, NORM>(Grouped<DT>::to_raw(xv[i]), mu, rr, s_, h_), out,
+            row + 64 * i, lane, h);
+    }
+}
+
 template <int G, int DT, int MOD, int NORM>
 __device__ __forceinline__ void modulate_rows(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
-    constexpr bool kHold = (MOD == kModRow);
-    const int lane = threadIdx.x;
-    const int64_t b = blockIdx.y;
-    constexpr int kRows = rows_per_wave<MOD>();
-    const int64_t r0 = (int64_t)blockIdx.x * kRows;
-    const int64_t r1 = (r0 + kRows < L) ? r0 + kRows : L;
-
-    Pack<DT> sc[kHold ? G : 1], sh[kHold ? G : 1];
-    if constexpr (kHold) {
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            sc[i] = Grouped<DT>::load_raw(scale, b * vpr + 64 * i, lane, vpr - 64 * i);
-            sh[i] = Grouped<DT>::load_raw(shift, b * vpr + 64 * i, lane, vpr - 64 * i);
-        }
-    }
-
-    for (int64_t r = r0; r < r1; ++r) {
-        const int64_t row = (b * L + r) * vpr;
-        Pack<DT> xv[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i)
-            xv[i] = Grouped<DT>::load_stream(x, row + 64 * i, lane, vpr - 64 * i);
-
-        float mu = 0.0f;
-        if constexpr (NORM == kNormLn) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc = acc + xv[i].get(e);
-            }
-            mu = wave_sum(acc) / d_float;
-        }
-
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            if (NORM == kNormLn && lane + 64 * i >= vpr)
-                continue;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = xv[i].get(e);
-                if constexpr (NORM == kNormLn)
-                    a = a - mu;
-                const float sa = a * a;
-                acc = acc + sa;
-            }
-        }
-        const float rr = inv_std(wave_sum(acc), d_float, eps);
-
-        // element-wise, so in raw order (binary32 rows are turned back from
-        // group order, which needs every lane: no lane skips a pack); packs
-        // past the row end are not stored
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int h = vpr - 64 * i;
-            const Pack<DT> xr = Grouped<DT>::to_raw(xv[i]);
-            Pack<DT> s_, h_;
-            if constexpr (kHold) {
-                s_ = sc[i];
-                h_ = sh[i];
-            } else if constexpr (MOD == kModToken) {
-                s_ = Grouped<DT>::load_stream_raw(scale, row + 64 * i, lane, h);
-                h_ = Grouped<DT>::load_stream_raw(shift, row + 64 * i, lane, h);
-            } else {
-                s_ = Grouped<DT>::load_raw(scale, b * vpr + 64 * i, lane, h);
-                h_ = Grouped<DT>::load_raw(shift, b * vpr + 64 * i, lane, h);
-            }
-            float o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = xr.get(e);
-                if constexpr (NORM == kNormLn)
-                    v = v - mu;
-                const float n = v * rr;
-                const float a = 1.0f + s_.get(e);
-                const float m = n * a;
-                o[e] = m + h_.get(e);
-            }
-            Grouped<DT>::store_stream_raw(Pack<DT>::make(o), out, row + 64 * i, lane, h);
-        }
-    }
+    if constexpr (MOD == kModRow)
+        modulate_staged_row<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
+    else
+        modulate_token_row<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
 }
 
-// Grid: x = tile of rows_per_wave<MOD>() rows, y = batch.
+// Grid: x = pair of rows (row modulation) or row (per token), y = batch.
 template <int G, int DT, int MOD>
-__global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
+__global__ __launch_bounds__(MOD == kModRow ? kBlock * kRowWaves : kBlock) void rms_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
@@ -188,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void rms_modulate_kernel(
 }
 
 template <int G, int DT, int MOD>
-__global__ __launch_bounds__(kBlock) void ln_modulate_kernel(
+__global__ __launch_bounds__(MOD == kModRow ? kBlock * kRowWaves : kBlock) void ln_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
@@ -569,6 +636,14 @@ rms_kernel_t pick(int groups)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Dynamic LDS of a row-modulation fast-path workgroup (row_wg_lds in
+// launch.hpp): the staged scale and shift rows; a row of at most
+// RGA_RMS_MAX_D binary32 elements stages 64 KB, one workgroup's limit.
+int64_t staged_row_lds(int64_t row_bytes)
+{
+    return row_wg_lds(row_bytes, 2 * row_bytes, kModRowBudget);
+}
+
 // Element-path slots per lane for 2-byte rows held in registers: the
 // smallest entry >= ceil(ceil(D / 8) / 64); rows past the last entry (and
 // binary32 rows) take the LDS-staged kernels.
@@ -634,9 +709,13 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
     if (k == nullptr)
         return hipErrorInvalidValue;
     void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &vpr};
+    if constexpr (MOD == kModToken)
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((uint32_t)L, (uint32_t)B),
+                               dim3(kBlock), args, 0, stream);
     return hipLaunchKernel(reinterpret_cast<const void*>(k),
-                           dim3((uint32_t)ceil_div(L, rows_per_wave<MOD>()), (uint32_t)B),
-                           dim3(kBlock), args, 0, stream);
+                           dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
+                           dim3(kBlock * kRowWaves), args,
+                           (size_t)staged_row_lds(D * (DT == kF32 ? 4 : 2)), stream);
 }
 
 template <int NORM, int DT>

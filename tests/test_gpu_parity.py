@@ -225,11 +225,18 @@ def test_rejections_through_the_binding(dte):
     with pytest.raises(dte.RGAError) as e:
         dte.rga_residual_gate_add(a, a, a, out=b)
     assert e.value.status == dte.RGA_ERR_ALIAS
+    # the modulation rejects only the layout (D % 8, alignment); rows longer
+    # than the register-held ones run (their parity: tests/test_gpu_measure.py)
+    ragged = torch.zeros(1, 2, 8204, dtype=torch.bfloat16, device=x.device)
+    rrow = torch.zeros(1, 1, 8204, dtype=torch.bfloat16, device=x.device)
+    with pytest.raises(dte.RGAError) as e:
+        dte.rms_modulate(ragged, rrow, rrow)
+    assert e.value.status == dte.RGA_ERR_UNSUPPORTED
     wide = torch.zeros(1, 2, 8200, dtype=torch.bfloat16, device=x.device)
     row = torch.zeros(1, 1, 8200, dtype=torch.bfloat16, device=x.device)
-    with pytest.raises(dte.RGAError) as e:
-        dte.rms_modulate(wide, row, row)
-    assert e.value.status == dte.RGA_ERR_UNSUPPORTED
+    y = dte.rms_modulate(wide, row, row)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0   # zero rows: y = shift = 0
 
 
 def test_empty_inputs_are_no_ops(dte):
