@@ -144,11 +144,20 @@ def parse_args():
                    help="repetitions of the fused-vs-separate comparison (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="repeat the CPU oracle sample until this much time has passed")
+    p.add_argument("--summarize", nargs="+", metavar="ARG",
+                   help="no GPU run: summarize rocprofv3 csv output of this bench. "
+                        "'trace KERNEL_TRACE.csv [BENCH.json]' prints per-launch-shape "
+                        "device durations; 'counters OUT.json CSV...' prints HBM bytes "
+                        "(FETCH_SIZE, WRITE_SIZE scaled by the 1 GiB copy) and instruction "
+                        "counts per launch shape and writes the traffic summary OUT.json")
     return p.parse_args()
 
 
 def main():
     args = parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this path runs on one GPU only (asked for {max(args.gpus, world)}); "
@@ -927,6 +936,238 @@ def cpu_baseline(host, fraction, min_seconds, log):
                               "sample": f"{reps1} passes, {sample * reps1} algorithmic "
                                         f"bytes in {dt1:.1f} s"},
             "host_cpus": os.cpu_count()}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (no GPU): per launch shape, from the csv files of
+#   rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py
+#   rocprofv3 --pmc <counters> --output-format csv -- python3 bench.py ...
+
+def _short_kernel(name: str) -> str:
+    """Kernel name without 'void', the namespaces and the argument list."""
+    n = name.replace("void ", "").replace("rga::(anonymous namespace)::", "")
+    depth = 0
+    for i, c in enumerate(n):
+        if c == "<":
+            depth += 1
+        elif c == ">":
+            depth -= 1
+        elif c == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def known_launches():
+    """(label, kernel, grid x in work-items, grid y, algorithmic bytes,
+    elements) of the fixed-shape launches of the default bench and of
+    --ablations 1. Grid sizes follow the launchers in csrc."""
+    cdiv = lambda a, b: -(-a // b)
+    out = []
+
+    def bcast(label, B, L, D, es=2, kernel="gate_add_bcast_kernel<0>"):
+        out.append((label, kernel, L * cdiv(D // 8, 64) * 64, B, (3 * B * L * D + B * D) * es,
+                    B * L * D))
+
+    def full(label, B, L, D, es=2, kernel="gate_add_full_kernel<0>"):
+        n = B * L * D
+        out.append((label, kernel, cdiv(n // 8 + (1 if n % 8 else 0), 64) * 64, 1, 4 * n * es, n))
+
+    def mod(label, B, L, D, kernel, es=2):
+        out.append((label, kernel, cdiv(L, 2) * 128, B, (2 * B * L * D + 2 * B * D) * es,
+                    B * L * D))
+
+    full("c3 full [1,8160,4096]", 1, 8160, 4096)
+    bcast("c4 bcast in place [1,32640,4096]", 1, 32640, 4096)
+    bcast("c5 bcast in place [2,32640,4096]", 2, 32640, 4096)
+    mod("c5 rms_modulate [2,32640,4096]", 2, 32640, 4096, "rms_modulate_kernel<8, 0, 0>")
+    out.append(("fused gate+rms [2,32640,4096]", "gate_add_rms_modulate_staged_kernel<8, false, 0>",
+                16320 * 128, 2, (4 * 2 * 32640 * 4096 + 3 * 2 * 4096) * 2, 2 * 32640 * 4096))
+    full("c1 full [1,126,2048]", 1, 126, 2048)
+    mod("c1 rms_modulate [1,126,2048]", 1, 126, 2048, "rms_modulate_kernel<4, 0, 0>")
+    for L in (512, 4096, 4608):
+        bcast(f"c2 bcast [1,{L},3072]", 1, L, 3072)
+    bcast("ideogram4 bcast [1,4096,4608]", 1, 4096, 4608)
+    mod("f16 rms_modulate [2,32640,4096]", 2, 32640, 4096, "rms_modulate_kernel<8, 1, 0>")
+    mod("bf16 LayerNorm modulation [2,32640,4096]", 2, 32640, 4096, "ln_modulate_kernel<8, 0, 0>")
+    n = 32640 * 16384
+    out.append(("bf16 tanh-GELU [1,32640,16384]", "gelu_tanh_flat_kernel<0>", n // 8, 1, 4 * n, n))
+    e3, e4 = 8160 * 4096 * 2, 32640 * 4096 * 2
+    for label, k, n16, nbytes in (
+            ("mix 3R:1W [1,8160,4096]", "stream_kernel<3, true, 1>", e3 // 16, 4 * e3),
+            ("mix 2R:1W in place [1,32640,4096]", "stream_kernel<2, true, 1>", e4 // 16, 3 * e4),
+            ("mix 2R:1W in place [2,32640,4096]", "stream_kernel<2, true, 1>", 2 * e4 // 16, 6 * e4),
+            ("mix 1R:1W [2,32640,4096]", "stream_kernel<1, true, 1>", 2 * e4 // 16, 4 * e4),
+            ("mix R [2,32640,4096], 1 word/lane", "stream_kernel<1, false, 1>", 2 * e4 // 16, 2 * e4),
+            ("mix R [2,32640,4096], 2 words/lane", "stream_kernel<1, false, 2>", e4 // 16, 2 * e4),
+            ("copy 1 GiB", "copy_kernel", FLUSH_BYTES // 16, 2 * FLUSH_BYTES),
+            ("flush read 1 GiB", "read_kernel", 256 * 1024, FLUSH_BYTES)):
+        out.append((label, k, n16 if k != "read_kernel" else n16, 1, nbytes, 0))
+    for T in (1, 2, 4, 8):
+        for sp, pname in ((0, "nt"), (1, "plain"), (2, "device")):
+            out.append((f"ablation c4 bcast, {T} rows/wave, store {pname}",
+                        f"gate_add_bcast_rows_kernel<{T}, {sp}>", cdiv(32640, T) * 8 * 64, 1,
+                        (3 * 32640 * 4096 + 4096) * 2, 32640 * 4096))
+    return out
+
+
+def _dispatch_groups(rows, grid_of):
+    """{(kernel, grid_x, grid_y): [row, ...]} with kernel = short name."""
+    groups = {}
+    for r in rows:
+        groups.setdefault((_short_kernel(r["Kernel_Name"]),) + grid_of(r), []).append(r)
+    return groups
+
+
+def summarize(argv):
+    import csv
+    what = argv[0]
+    if what == "trace":
+        rows = list(csv.DictReader(open(argv[1])))
+        bench_line = None
+        if len(argv) > 2:
+            with open(argv[2]) as f:
+                for line in f:
+                    if line.startswith("{"):
+                        bench_line = json.loads(line)
+        g = _dispatch_groups(rows, lambda r: (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"])))
+        dur = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        print("--stats view (every launch of the run; one kernel name spans several shapes)")
+        by_name = {}
+        for (k, gx, gy), rs in g.items():
+            by_name.setdefault(k, []).extend(dur(rs))
+        print(f"{'kernel':52s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
+        for k, ds in sorted(by_name.items(), key=lambda kv: -sum(kv[1])):
+            if not k.startswith(("gate_", "rms_", "ln_", "gelu_", "modulate_", "stream_",
+                                 "copy_", "read_", "fill_")):
+                continue
+            print(f"{k[:52]:52s} {len(ds):6d} {statistics.mean(ds):9.2f} {min(ds):9.2f} "
+                  f"{max(ds):9.2f}")
+        print()
+        print("per launch shape (device durations from the kernel trace; algorithmic bytes / "
+              "average duration)")
+        print(f"{'launch':44s} {'kernel':44s} {'grid':>14s} {'wg':>4s} {'vgpr*':>5s} "
+              f"{'calls':>5s} {'avg us':>8s} {'GB/s':>7s} {'of 8TB/s':>8s}")
+        step = {}
+        for label, k, gx, gy, nbytes, _ in known_launches():
+            rs = g.get((k, gx, gy))
+            if not rs:
+                continue
+            ds = dur(rs)
+            avg = statistics.mean(ds)
+            gbps = nbytes / (avg * 1e-6) / 1e9
+            print(f"{label[:44]:44s} {k[:44]:44s} {f'{gx}x{gy}':>14s} "
+                  f"{rs[0]['Workgroup_Size_X']:>4s} {rs[0]['VGPR_Count']:>5s} {len(ds):5d} "
+                  f"{avg:8.2f} {gbps:7.0f} {gbps / HBM_PEAK_GBPS:8.3f}")
+            step[label] = (k, ds, nbytes)
+        print("* VGPR_Count as rocprofv3 reports it")
+        dom = [step[l] for l in ("c4 bcast in place [1,32640,4096]",
+                                 "c5 bcast in place [2,32640,4096]") if l in step]
+        if dom:
+            # the bench's roofline: mean bytes per launch / mean duration per
+            # launch over the step's launches of the kernel (equal counts)
+            n4, n5 = len(dom[0][1]), len(dom[-1][1])
+            avg = (statistics.mean(dom[0][1]) + statistics.mean(dom[-1][1])) / 2
+            mb = (dom[0][2] + dom[-1][2]) / 2
+            print()
+            print(f"gate_add_bcast_kernel<0> over the step's shapes (c4 and c5, {n4} + {n5} "
+                  f"launches): avg {avg:.2f} us per launch, {mb / (avg * 1e-6) / 1e9:.1f} GB/s, "
+                  f"frac {mb / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.4f}")
+        if bench_line:
+            r = bench_line["roofline"]
+            print(f"the same run's bench line: roofline.avg_launch_us {r['avg_launch_us']} "
+                  f"(HIP events on the launch stream), achieved {r['achieved']} GB/s, frac "
+                  f"{r['frac']}; value {bench_line['value']} GB/s, ms_per_step "
+                  f"{bench_line['ms_per_step']}")
+        return
+    if what == "counters":
+        out_json = argv[1]
+        vals = {}   # (kernel, grid) -> counter -> [values]
+        valu_us = {}  # (kernel, grid) -> durations of the dispatches that counted VALU
+        for path in argv[2:]:
+            for r in csv.DictReader(open(path)):
+                key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]))
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+                if r["Counter_Name"] == "SQ_INSTS_VALU":
+                    valu_us.setdefault(key, []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        mean = lambda v: sum(v) / len(v)
+        copy = vals.get(("copy_kernel", FLUSH_BYTES // 16), {})
+        fs = ws = None
+        if "FETCH_SIZE" in copy:
+            fs = FLUSH_BYTES / (mean(copy["FETCH_SIZE"]) * 1024)
+        if "WRITE_SIZE" in copy:
+            ws = FLUSH_BYTES / (mean(copy["WRITE_SIZE"]) * 1024)
+        print("calibration on the 1 GiB copy (1 GiB read, 1 GiB written): "
+              f"FETCH_SIZE scale {fs if fs is None else round(fs, 5)}, "
+              f"WRITE_SIZE scale {ws if ws is None else round(ws, 5)}")
+        names = sorted({c for v in vals.values() for c in v})
+        print(f"counters: {', '.join(names)} (mean per dispatch; instruction counts per "
+              "element are wave instructions x 64 / elements)")
+        hdr = f"{'launch':44s} {'n':>3s} {'read B':>12s} {'write B':>12s} {'traffic/alg':>11s}"
+        extra = [c for c in names if c not in ("FETCH_SIZE", "WRITE_SIZE")]
+        for c in extra:
+            hdr += f" {c[:16]:>16s}"
+        if "SQ_INSTS_VALU" in names:
+            hdr += f" {'VALU use':>9s}"
+        print(hdr)
+        traffic = {}
+        for label, k, gx, gy, nbytes, elems in known_launches():
+            v = vals.get((k, gx * gy))
+            if not v:
+                continue
+            rd = mean(v["FETCH_SIZE"]) * 1024 * fs if ("FETCH_SIZE" in v and fs) else None
+            wr = mean(v["WRITE_SIZE"]) * 1024 * ws if ("WRITE_SIZE" in v and ws) else None
+            n = max(len(x) for x in v.values())
+            line = f"{label[:44]:44s} {n:3d} "
+            line += f"{rd:12.0f} " if rd is not None else f"{'-':>12s} "
+            line += f"{wr:12.0f} " if wr is not None else f"{'-':>12s} "
+            line += f"{(rd + wr) / nbytes:11.4f}" if rd is not None and wr is not None else f"{'-':>11s}"
+            for c in extra:
+                if c in v and elems:
+                    per = mean(v[c]) * (64 if c.startswith("SQ_INSTS") else 1) / elems
+                    line += f" {per:16.4f}"
+                elif c in v:
+                    line += f" {mean(v[c]):16.0f}"
+                else:
+                    line += f" {'-':>16s}"
+            if "SQ_INSTS_VALU" in names:
+                d = valu_us.get((k, gx * gy))
+                if d and "SQ_INSTS_VALU" in v:
+                    # lane-ops over the non-packed issue rate: 256 CUs x 64 lanes x 2.4 GHz
+                    use = mean(v["SQ_INSTS_VALU"]) * 64 / (mean(d) * 1e-6 * 256 * 64 * 2.4e9)
+                    line += f" {use:9.3f}"
+                else:
+                    line += f" {'-':>9s}"
+            print(line)
+            if rd is not None and wr is not None:
+                traffic[label] = {"kernel": k, "bytes_per_launch": round(rd + wr),
+                                  "algorithmic_bytes": nbytes}
+        if out_json and traffic:
+            step = {}
+            for label, kk in (("c3 full [1,8160,4096]", "gate_add_full_kernel"),
+                              ("c5 rms_modulate [2,32640,4096]", "rms_modulate_kernel"),
+                              ("fused gate+rms [2,32640,4096]",
+                               "gate_add_rms_modulate_staged_kernel")):
+                if label in traffic:
+                    step[kk] = {"bytes_per_launch": traffic[label]["bytes_per_launch"],
+                                "launches_averaged": 1}
+            b = [traffic[l]["bytes_per_launch"] for l in ("c4 bcast in place [1,32640,4096]",
+                                                          "c5 bcast in place [2,32640,4096]")
+                 if l in traffic]
+            if len(b) == 2:
+                step["gate_add_bcast_kernel"] = {"bytes_per_launch": round(sum(b) / 2),
+                                                 "launches_averaged": 2}
+            with open(out_json, "w") as f:
+                json.dump({"source_digest": kernel_source_digest(),
+                           "about": "HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, scaled by "
+                                    "the copy-kernel calibration) for the bench's launches; used "
+                                    "only while the kernel sources match the digest",
+                           "calibration": {"fetch_scale": fs, "write_scale": ws},
+                           "kernels": step, "launches": traffic}, f, indent=1)
+                f.write("\n")
+        return
+    raise SystemExit(f"--summarize: unknown kind {what!r}")
 
 
 if __name__ == "__main__":
