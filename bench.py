@@ -641,7 +641,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
         log(f"variant {name}")
         out[name] = cold_and_warm(
             lambda: dte.rga_rms_modulate_ex(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
-            "rms_modulate_kernel" if fast else element_norm_kernel("rms", D, dt))
+            "rms_modulate_kernel" if fast else element_norm_kernel("rms", D, dt, mod))
 
     def fused(name, B, L, D, dt, mode, mod):
         mshape = (B, L, D) if mod == dte.MOD_TOKEN else (B, 1, D)
@@ -669,23 +669,24 @@ def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
                 return "gate_add_rms_modulate_staged_kernel"
             if mod == dte.MOD_TOKEN or dt == "f32":
                 return "gate_add_rms_modulate_kernel"
-        return element_fused_kernel(D, dt)
+        return element_fused_kernel(D, dt, mod)
 
-    def element_fused_kernel(D, dt):
+    def element_fused_kernel(D, dt, mod=dte.MOD_ROW):
         # as element_norm_kernel; the fused call's LDS buffer has one more word
         if dt != "f32" and -(-(-(-D // 8)) // 64) <= 16:
-            return "gate_add_rms_modulate_regs_kernel"
+            return ("gate_add_rms_modulate_regs_staged_kernel" if mod == dte.MOD_ROW
+                    else "gate_add_rms_modulate_regs_kernel")
         es = 4 if dt == "f32" else 2
         if (-(-D * es // 16) + 3) * 16 <= 65536 - 256:
             return "gate_add_rms_modulate_lds_kernel"
         return "gate_add_rms_modulate_generic_kernel"
 
-    def element_norm_kernel(norm, D, dt):
-        # 2-byte rows of up to 16 slots of 64 groups sit in registers; other
-        # rows up to 64 KB (with two spare words, less 256 B of static LDS)
-        # are staged in LDS once
+    def element_norm_kernel(norm, D, dt, mod=dte.MOD_ROW):
+        # 2-byte rows of up to 16 slots of 64 groups sit in registers (two
+        # rows per workgroup with row modulation); other rows up to 64 KB
+        # (with two spare words, less 256 B of static LDS) are staged in LDS
         if dt != "f32" and -(-(-(-D // 8)) // 64) <= 16:
-            return "modulate_regs_kernel"
+            return "modulate_regs_staged_kernel" if mod == dte.MOD_ROW else "modulate_regs_kernel"
         es = 4 if dt == "f32" else 2
         if (-(-D * es // 16) + 2) * 16 <= 65536 - 256:
             return "modulate_lds_kernel"
@@ -714,7 +715,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
         log(f"variant {name}")
         out[name] = cold_and_warm(
             lambda: dte.rga_ln_modulate(x, sc, sh, 1e-6, out=o, mod_mode=mod), nbytes,
-            "ln_modulate_kernel" if D % 8 == 0 else element_norm_kernel("ln", D, dt))
+            "ln_modulate_kernel" if D % 8 == 0 else element_norm_kernel("ln", D, dt, mod))
 
     # tanh-GELU on the FFN intermediate (video tokens x 4 hidden)
     def gelu(name, rows, F, dt, with_bias=False):

@@ -16,8 +16,9 @@
 // outputs are bit-identical to rga_residual_gate_add followed by
 // rms_modulate.
 //
-// Pack path with row modulation (D % 8 == 0, D <= RGA_RMS_MAX_D, 16-byte
-// aligned pointers, staged rows within one workgroup's 64 KB of LDS): two
+// Pack path with row modulation of 2-byte rows (D % 8 == 0,
+// D <= RGA_RMS_MAX_D, 16-byte aligned pointers, staged rows within one
+// workgroup's 64 KB of LDS): two
 // waves per workgroup, one row each. The workgroup first stages its batch's
 // scale and shift rows, and a broadcast gate row, in LDS; then each wave
 // loads x and u (and a full gate), forms x', stores it, reduces it and
@@ -27,9 +28,9 @@
 // 356 us for the register-row kernel of the element path, which 2-byte rows
 // with row modulation took at any alignment before.
 //
-// Pack path with per-token modulation (and row modulation whose staging
-// would not fit), launch shape measured on MI355X: one wave per workgroup
-// and one row per wave, nontemporal loads and stores. Every pack's x, u and g loads are
+// Pack path with per-token modulation and for binary32 rows (kept as they
+// were measured fastest), launch shape measured on MI355X: one wave per
+// workgroup and one row per wave, nontemporal loads and stores. Every pack's x, u and g loads are
 // issued before the first add, with no branch around a load (a branch per
 // bounded load made the wave wait for each pack before issuing the next);
 // each x_out pack is stored as soon as it is formed; scale and shift are read
@@ -554,6 +555,68 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
 // x' is formed there, written to x_out realigned to its offset, and the
 // rounded x' groups stay in registers for the modulation (row_regs.hpp), so
 // x_out is never read back.
+// Row modulation of 2-byte rows held in registers: kRowWaves waves per
+// workgroup, one row each. The workgroup realigns its batch's scale and
+// shift rows (and a broadcast gate row) into the dynamic LDS once (groups,
+// 64 K words per row: scale, shift, gate), wave 0 the scale and gate rows,
+// wave 1 the shift row, before any row is loaded.
+template <int K, bool FULL, int DT>
+__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs_staged_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int64_t D)
+{
+    extern __shared__ u32x4 staged[];
+    const int wave = threadIdx.x / kBlock;
+    const int64_t b = blockIdx.y;
+    const int64_t r = (int64_t)blockIdx.x * kRowWaves + wave;
+    const int n = (int)D;
+    static_assert(kRowWaves == 2, "staged rows split over two waves");
+    u32x4* s_st = staged;
+    u32x4* h_st = staged + 64 * K;
+    u32x4* g_st = staged + 2 * 64 * K;
+    if (wave == 0) {
+        regs::stage_row<K>(s_st, elem_ptr<DT>(scale, b * D), n);
+        if constexpr (!FULL)
+            regs::stage_row<K>(g_st, elem_ptr<DT>(g, b * D), n);
+    } else {
+        regs::stage_row<K>(h_st, elem_ptr<DT>(shift, b * D), n);
+    }
+    __syncthreads();
+    if (r >= L)
+        return;
+    const int64_t row = (b * L + r) * D;
+    const int lane = threadIdx.x & (kBlock - 1);
+
+    u32x4 xv[K];
+    {
+        // every input's loads issued before any is realigned
+        u32x4 uv[K], gv[FULL ? K : 1], xe, ue, ge;
+        const void* px = elem_ptr<DT>(x, row);
+        const void* pu = elem_ptr<DT>(u, row);
+        load_run<K, true>(px, n, xv, xe);
+        load_run<K, true>(pu, n, uv, ue);
+        if constexpr (FULL)
+            load_run<K, true>(elem_ptr<DT>(g, row), n, gv, ge);
+        realign_in<K>(xv, xe, start_offset(px));
+        realign_in<K>(uv, ue, start_offset(pu));
+        if constexpr (FULL)
+            realign_in<K>(gv, ge, start_offset(elem_ptr<DT>(g, row)));
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            Pack<DT> a, c, e;
+            a.v = xv[k];
+            c.v = uv[k];
+            e.v = FULL ? gv[FULL ? k : 0] : g_st[64 * k + lane];
+            xv[k] = gate_add8<DT>(a, c, e).v;
+        }
+    }
+    store_run<K, true>(elem_ptr<DT>(x_out, row), n, xv);
+    float mu, rr;
+    regs::row_factors<K, DT, regs::kRms>(xv, n, d_float, eps, &mu, &rr);
+    regs::apply_store_staged<K, DT, regs::kRms>(xv, s_st, h_st, n, mu, rr, elem_ptr<DT>(y, row));
+}
+
 template <int K, bool FULL, int DT, int MOD>
 __global__ __launch_bounds__(kBlock) void gate_add_rms_modulate_regs_kernel(
     const void* x, const void* u, const void* g, const void* scale,
@@ -602,6 +665,29 @@ typedef void (*regs_kernel_t)(const void*, const void*, const void*, const void*
 // Slots per lane for the register-resident element path: the smallest entry
 // >= ceil(ceil(D / 8) / 64); longer rows (and binary32) take the LDS path.
 using regs::kRegsLadder;
+
+int pick_regs_slots(int64_t slots)
+{
+    for (int i = 0; i < 8; ++i)
+        if (slots <= kRegsLadder[i])
+            return kRegsLadder[i];
+    return 0;
+}
+
+template <bool FULL, int DT>
+const void* pick_regs_staged(int K)
+{
+    switch (K) {
+    case 1: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<1, FULL, DT>);
+    case 2: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<2, FULL, DT>);
+    case 4: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<4, FULL, DT>);
+    case 6: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<6, FULL, DT>);
+    case 8: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<8, FULL, DT>);
+    case 9: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<9, FULL, DT>);
+    case 12: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<12, FULL, DT>);
+    default: return reinterpret_cast<const void*>(&gate_add_rms_modulate_regs_staged_kernel<16, FULL, DT>);
+    }
+}
 
 template <bool FULL, int DT, int MOD>
 regs_kernel_t pick_regs(int64_t slots)
@@ -681,6 +767,18 @@ hipError_t launch_element(const void* x, const void* u, const void* g,
 {
     float d_float = (float)D;
     void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &D};
+    if constexpr (DT != kF32 && MOD == kModRow) {
+        const int K = pick_regs_slots(ceil_div(ceil_div(D, 8), 64));
+        if (K > 0) {
+            // two rows per workgroup with the realigned scale, shift (and
+            // broadcast gate) rows staged once, occupancy capped
+            const int64_t stage = (FULL ? 2 : 3) * 1024 * (int64_t)K;
+            return hipLaunchKernel(pick_regs_staged<FULL, DT>(K),
+                                   dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
+                                   dim3(kBlock * kRowWaves), args,
+                                   (size_t)row_wg_lds(2 * D, stage, kFusedRowBudget), stream);
+        }
+    }
     if constexpr (DT != kF32) {
         regs_kernel_t rk = pick_regs<FULL, DT, MOD>(ceil_div(ceil_div(D, 8), 64));
         if (rk != nullptr)
@@ -708,7 +806,7 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
 {
     constexpr int64_t es = DT == kF32 ? 4 : 2;
     const int64_t stage = (FULL ? 2 : 3) * D * es;
-    if (MOD == kModRow && fast && stage <= kMaxStagedLds) {
+    if (DT != kF32 && MOD == kModRow && fast && stage <= kMaxStagedLds) {
         float d_float = (float)D;
         int vpr = (int)(D / 8);
         const void* k = pick_staged<FULL, DT>((int)ceil_div(vpr, 64));

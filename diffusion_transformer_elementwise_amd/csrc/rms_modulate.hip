@@ -31,8 +31,10 @@
 // (row_wg_lds in launch.hpp); at [2,32640,4096] this form ran 168-174 us
 // against 178-183 us for the former one (two rows per wave, scale and shift
 // held in registers, 209 VGPRs), measured on MI355X in the same runs.
-// Per-token modulation reads its scale and shift rows in the apply phase,
-// one row per one-wave workgroup. The LayerNorm's second sum runs over the
+// Binary32 rows with row modulation keep the former form (one wave, two
+// rows per wave, scale and shift held in registers), which measured faster
+// there. Per-token modulation reads its scale and shift rows in the apply
+// phase, one row per one-wave workgroup. The LayerNorm's second sum runs over the
 // registers, so it costs arithmetic, not memory traffic. A binary32 pack is
 // two words; they are moved with contiguous wave-wide accesses and one lane
 // exchange (Grouped in dtype.hpp) rather than two adjacent words per lane,
@@ -234,20 +236,66 @@ __device__ __forceinline__ void modulate_token_row(
     }
 }
 
+// Row modulation of binary32 rows: one wave per workgroup, two rows per
+// wave (rows 2 blockIdx.x, 2 blockIdx.x + 1 of batch blockIdx.y), the scale
+// and shift rows held in registers across both. For these 16-byte-per-pair
+// rows this form measured faster than the staged one (377 against 442 us
+// at [2,32640,4096], MI355X, same run as the 2-byte gains).
+template <int G, int DT, int NORM>
+__device__ __forceinline__ void modulate_held_rows(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
+{
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * 2;
+    const int64_t r1 = (r0 + 2 < L) ? r0 + 2 : L;
+    Pack<DT> sc[G], sh[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        sc[i] = Grouped<DT>::load_raw(scale, b * vpr + 64 * i, lane, vpr - 64 * i);
+        sh[i] = Grouped<DT>::load_raw(shift, b * vpr + 64 * i, lane, vpr - 64 * i);
+    }
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t row = (b * L + r) * vpr;
+        Pack<DT> xv[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            xv[i] = Grouped<DT>::load_stream(x, row + 64 * i, lane, vpr - 64 * i);
+        float mu;
+        const float rr = row_factor<G, DT, NORM, false>(xv, lane, vpr, eps, d_float, &mu);
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            Grouped<DT>::store_stream_raw(
+                modulate_pack<DT, NORM>(Grouped<DT>::to_raw(xv[i]), mu, rr, sc[i], sh[i]), out,
+                row + 64 * i, lane, vpr - 64 * i);
+    }
+}
+
+// Launch shape of the fast path: workgroups of kRowWaves waves with staged
+// rows for 2-byte row modulation, else one wave.
+template <int DT, int MOD>
+constexpr bool staged_rows()
+{
+    return MOD == kModRow && DT != kF32;
+}
+
 template <int G, int DT, int MOD, int NORM>
 __device__ __forceinline__ void modulate_rows(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
-    if constexpr (MOD == kModRow)
+    if constexpr (staged_rows<DT, MOD>())
         modulate_staged_row<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
+    else if constexpr (MOD == kModRow)
+        modulate_held_rows<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
     else
         modulate_token_row<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
 }
 
 // Grid: x = pair of rows (row modulation) or row (per token), y = batch.
 template <int G, int DT, int MOD>
-__global__ __launch_bounds__(MOD == kModRow ? kBlock * kRowWaves : kBlock) void rms_modulate_kernel(
+__global__ __launch_bounds__((staged_rows<DT, MOD>() ? kBlock * kRowWaves : kBlock)) void rms_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
@@ -255,7 +303,7 @@ __global__ __launch_bounds__(MOD == kModRow ? kBlock * kRowWaves : kBlock) void 
 }
 
 template <int G, int DT, int MOD>
-__global__ __launch_bounds__(MOD == kModRow ? kBlock * kRowWaves : kBlock) void ln_modulate_kernel(
+__global__ __launch_bounds__((staged_rows<DT, MOD>() ? kBlock * kRowWaves : kBlock)) void ln_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
@@ -588,6 +636,36 @@ __global__ __launch_bounds__(kBlock * NW) void modulate_lds_kernel(
 // holds group t + 64k, which is the fixed order's assignment (row_regs.hpp).
 // Scale and shift are realigned the same way and the result is realigned
 // to the output's offset.
+// Row modulation of 2-byte rows held in registers: kRowWaves waves per
+// workgroup, one row each (rows kRowWaves * blockIdx.x + wave of batch
+// blockIdx.y). Wave 0 realigns the batch's scale row and wave 1 its shift
+// row into the dynamic LDS (groups, 64 K words each) before any row is
+// loaded.
+template <int K, int DT, int NORM>
+__global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kernel(
+    const void* x, const void* scale, const void* shift, float eps, float d_float,
+    void* out, int64_t L, int64_t D)
+{
+    extern __shared__ u32x4 staged[];
+    const int wave = threadIdx.x / kBlock;
+    const int64_t b = blockIdx.y;
+    const int64_t r = (int64_t)blockIdx.x * kRowWaves + wave;
+    const int n = (int)D;
+    constexpr int kNorm = NORM == kNormLn ? regs::kLn : regs::kRms;
+    static_assert(kRowWaves == 2, "one staged row per wave");
+    regs::stage_row<K>(staged + 64 * K * wave, elem_ptr<DT>(wave == 0 ? scale : shift, b * D), n);
+    __syncthreads();
+    if (r >= L)
+        return;
+    const int64_t row = (b * L + r) * D;
+    u32x4 xv[K];
+    load_groups<K, true>(elem_ptr<DT>(x, row), n, xv);
+    float mu, rr;
+    regs::row_factors<K, DT, kNorm>(xv, n, d_float, eps, &mu, &rr);
+    regs::apply_store_staged<K, DT, kNorm>(xv, staged, staged + 64 * K, n, mu, rr,
+                                           elem_ptr<DT>(out, row));
+}
+
 template <int K, int DT, int MOD, int NORM>
 __global__ __launch_bounds__(kBlock) void modulate_regs_kernel(
     const void* x, const void* scale, const void* shift, float eps, float d_float,
@@ -655,6 +733,36 @@ const void* regs_kernel()
     return reinterpret_cast<const void*>(&modulate_regs_kernel<K, DT, MOD, NORM>);
 }
 
+template <int NORM, int K, int DT>
+const void* regs_staged_kernel()
+{
+    return reinterpret_cast<const void*>(&modulate_regs_staged_kernel<K, DT, NORM>);
+}
+
+// the register-row kernel of a row of `slots` slots: K from the ladder
+int pick_regs_slots(int64_t slots)
+{
+    for (int i = 0; i < 8; ++i)
+        if (slots <= kRegsLadder[i])
+            return kRegsLadder[i];
+    return 0;
+}
+
+template <int NORM, int DT>
+const void* pick_regs_staged(int K)
+{
+    switch (K) {
+    case 1: return regs_staged_kernel<NORM, 1, DT>();
+    case 2: return regs_staged_kernel<NORM, 2, DT>();
+    case 4: return regs_staged_kernel<NORM, 4, DT>();
+    case 6: return regs_staged_kernel<NORM, 6, DT>();
+    case 8: return regs_staged_kernel<NORM, 8, DT>();
+    case 9: return regs_staged_kernel<NORM, 9, DT>();
+    case 12: return regs_staged_kernel<NORM, 12, DT>();
+    default: return regs_staged_kernel<NORM, 16, DT>();
+    }
+}
+
 template <int NORM, int DT, int MOD>
 const void* pick_regs(int64_t slots)
 {
@@ -687,7 +795,19 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
     if (!fast) {
         void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &D};
         if constexpr (DT != kF32) {
-            const void* rk = pick_regs<NORM, DT, MOD>((int)ceil_div(ceil_div(D, 8), 64));
+            const int64_t slots = ceil_div(ceil_div(D, 8), 64);
+            const int K = pick_regs_slots(slots);
+            if (K > 0 && MOD == kModRow) {
+                // two rows per workgroup with the realigned scale and shift
+                // rows staged once (2 * 1 KB per slot), occupancy capped
+                return hipLaunchKernel(pick_regs_staged<NORM, DT>(K),
+                                       dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
+                                       dim3(kBlock * kRowWaves), args,
+                                       (size_t)row_wg_lds(2 * D, 2 * 1024 * (int64_t)K,
+                                                          kModRowBudget),
+                                       stream);
+            }
+            const void* rk = pick_regs<NORM, DT, MOD>(slots);
             if (rk != nullptr)
                 return hipLaunchKernel(rk, dim3((uint32_t)L, (uint32_t)B), dim3(kBlock), args, 0,
                                        stream);
@@ -712,6 +832,10 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
     if constexpr (MOD == kModToken)
         return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((uint32_t)L, (uint32_t)B),
                                dim3(kBlock), args, 0, stream);
+    if constexpr (!staged_rows<DT, MOD>())
+        return hipLaunchKernel(reinterpret_cast<const void*>(k),
+                               dim3((uint32_t)ceil_div(L, 2), (uint32_t)B), dim3(kBlock), args, 0,
+                               stream);
     return hipLaunchKernel(reinterpret_cast<const void*>(k),
                            dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                            dim3(kBlock * kRowWaves), args,

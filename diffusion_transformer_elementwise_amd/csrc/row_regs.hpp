@@ -144,5 +144,53 @@ __device__ __forceinline__ void apply_store(u32x4 (&xv)[K], const void* scale, c
     store_run<K, true>(out, n, xv);
 }
 
+// One row of n elements at p realigned to groups into LDS (group g of the
+// row at dst[g], K slots: 64 K words). Rows a workgroup shares (scale, shift,
+// a broadcast gate) are staged once this way instead of realigned by every
+// wave for every row.
+template <int K>
+__device__ __forceinline__ void stage_row(u32x4* dst, const void* p, int n)
+{
+    const int lane = threadIdx.x & 63;
+    u32x4 g[K];
+    load_groups<K, false>(p, n, g);
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        dst[64 * k + lane] = g[k];
+}
+
+// apply_store with the scale and shift rows staged in LDS as groups
+// (stage_row): no per-row loads or realignment of them.
+template <int K, int DT, int NORM>
+__device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* s_lds,
+                                                   const u32x4* h_lds, int n, float mu,
+                                                   float rr, void* out)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        __asm__ volatile("" : "+v"(xv[k]));
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        Pack<DT> xp, sp, hp;
+        xp.v = xv[k];
+        sp.v = s_lds[64 * k + lane];
+        hp.v = h_lds[64 * k + lane];
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = xp.get(e);
+            if constexpr (NORM == kLn)
+                v = v - mu;
+            const float nv = v * rr;
+            const float a = 1.0f + sp.get(e);
+            const float m = nv * a;
+            o[e] = m + hp.get(e);
+        }
+        xv[k] = Pack<DT>::make(o).v;
+    }
+    store_run<K, true>(out, n, xv);
+}
+
 }  // namespace regs
 }  // namespace rga
