@@ -365,6 +365,8 @@ def main():
     if args.ablations and args.cold_reps > 0:
         log("ablations: broadcast-gate add shapes and store policies at c4")
         ablations = run_ablations(dte, torch, dev, d4, cold_times, hev, stream, args.cold_reps, log)
+        ablations["occupancy"] = run_occupancy(dte, torch, dev, d4, cold_times, hev, stream,
+                                               args.cold_reps, log)
         torch.cuda.empty_cache()
 
     fused = {}
@@ -523,6 +525,57 @@ def mix_ceilings(dte, torch, dev, cold_times, reps, log):
                      "compares_with": bounds}
         log(f"mix {name}: {med:.2f} us, {total / (med * 1e-6) / 1e9:.0f} GB/s")
         del srcs, dst
+    return out
+
+
+def run_occupancy(dte, torch, dev, d4, cold_times, hev, stream, reps, log):
+    """The row-modulation kernels (two rows per workgroup, scale/shift staged
+    in LDS) at a chosen number of workgroups per CU (rga_modulate_occupancy,
+    rga_fused_occupancy; -1 = no cap, 0 = the library's rule): the modulation
+    and the fused call at [2,32640,4096] (16-byte-pack kernels) and
+    [2,32640,4100] (register-row element kernels), bf16. Timed cold (median
+    after a 1 GiB cache-allocating read) and right after the c4 gate-add
+    (mean of 10 pairs, HIP events around the variant)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    out = {}
+
+    def draw(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+
+    def after_c4(fn):
+        evs = [(hev.new(), hev.new()) for _ in range(10)]
+        for a, b in evs:
+            dte.rga_residual_gate_add(d4["x"], d4["u"], d4["g"], out=d4["x"], gate_mode=1)
+            hev.record(a, stream)
+            fn()
+            hev.record(b, stream)
+        torch.cuda.synchronize()
+        return statistics.mean(hev.ms(a, b) * 1e3 for a, b in evs)
+
+    for D in (4096, 4100):
+        B, L = 2, 32640
+        x, u = draw((B, L, D), 2.0), draw((B, L, D), 1.0)
+        g, s, t = draw((B, 1, D), 0.1), draw((B, 1, D), 0.1), draw((B, 1, D), 0.1)
+        y, xo = torch.empty_like(x), torch.empty_like(x)
+        mb = (2 * B * L * D + 2 * B * D) * 2
+        fb = (4 * B * L * D + 3 * B * D) * 2
+        for w in (-1, 0, 4, 5, 6, 8, 12):
+            for name, nbytes, fn in (
+                    (f"rms_modulate [2,32640,{D}]", mb,
+                     lambda: dte.modulate_occupancy(x, s, t, 1e-6, out=y, wg_per_cu=w)),
+                    (f"fused bcast [2,32640,{D}]", fb,
+                     lambda: dte.fused_occupancy(x, u, g, s, t, 1e-6, x_out=xo, y=y,
+                                                 wg_per_cu=w))):
+                fn()
+                med = statistics.median(cold_times(fn, reps))
+                pair = after_c4(fn)
+                key = f"{name} wg_per_cu={w}"
+                out[key] = {"bytes": nbytes, "cold_us_median": round(med, 2),
+                            "cold_frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "after_c4_us": round(pair, 2)}
+                log(f"occupancy {key}: cold {med:.2f} us, after c4 {pair:.2f} us")
+        del x, u, g, s, t, y, xo
     return out
 
 

@@ -32,8 +32,10 @@ The FFN's tanh-GELU, any storage type, over the last dimension F:
     gelu_tanh(x, bias=None, out=None)   out = gelu(x + bias)
 
 Measurement helpers (include/rga_measure.h): copy_, fill_, read_ (cache
-flush), stream_ (read:write mix ceilings) and gate_add_variant (the
-broadcast-gate add in the shapes the library does not use).
+flush), stream_ (read:write mix ceilings), gate_add_variant (the
+broadcast-gate add in the shapes the library does not use), and
+modulate_occupancy / fused_occupancy (the row-modulation kernels at a chosen
+number of workgroups per CU).
 """
 from __future__ import annotations
 
@@ -60,8 +62,10 @@ from ._lib import (  # noqa: F401
     check_residual_gate_add,
     check_residual_gate_add_ex,
     check_rms_modulate,
+    check_fused_occupancy,
     check_gate_add_variant,
     check_gelu_tanh,
+    check_modulate_occupancy,
     check_stream,
     check_ln_modulate,
     check_rms_modulate_ex,
@@ -72,7 +76,9 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     copy_,
     fill_,
+    fused_occupancy,
     gate_add_variant,
+    modulate_occupancy,
     stream_,
     gelu_tanh,
     read_,

@@ -115,6 +115,15 @@ def _load():
     lib.rga_gate_add_variant.restype = i32
     lib.rga_check_gate_add_variant.argtypes = [p, p, p, p, i64, i64, i64, i32, i32]
     lib.rga_check_gate_add_variant.restype = i32
+    lib.rga_modulate_occupancy.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, i32, p]
+    lib.rga_modulate_occupancy.restype = i32
+    lib.rga_check_modulate_occupancy.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, i32]
+    lib.rga_check_modulate_occupancy.restype = i32
+    lib.rga_fused_occupancy.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32, i32, i32, p]
+    lib.rga_fused_occupancy.restype = i32
+    lib.rga_check_fused_occupancy.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32, i32,
+                                              i32]
+    lib.rga_check_fused_occupancy.restype = i32
     return lib
 
 
@@ -184,3 +193,14 @@ def check_stream(srcs, dst, nbytes, words_per_lane, sink) -> int:
 def check_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave, store_policy) -> int:
     return _LIB.rga_check_gate_add_variant(x, u, g, out, B, L, D, rows_per_wave,
                                            store_policy)
+
+
+def check_modulate_occupancy(x, scale, shift, eps, out, B, L, D, dtype, wg_per_cu) -> int:
+    return _LIB.rga_check_modulate_occupancy(x, scale, shift, eps, out, B, L, D, dtype,
+                                             wg_per_cu)
+
+
+def check_fused_occupancy(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, dtype,
+                          wg_per_cu) -> int:
+    return _LIB.rga_check_fused_occupancy(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                                          gate_mode, dtype, wg_per_cu)

@@ -599,6 +599,59 @@ int rga_gate_add_variant(const void* x, const void* u, const void* g, void* out,
                                                  store_policy, stream));
 }
 
+int rga_check_modulate_occupancy(const void* x, const void* scale, const void* shift, float eps,
+                                 const void* out, int64_t B, int64_t L, int64_t D, int dtype,
+                                 int wg_per_cu)
+{
+    if (wg_per_cu < -1 || wg_per_cu > 16)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    return check_rms(x, scale, shift, eps, out, B, L, D, RGA_MOD_ROW, dtype, false, &fast);
+}
+
+int rga_modulate_occupancy(const void* x, const void* scale, const void* shift, float eps,
+                           void* out, int64_t B, int64_t L, int64_t D, int dtype, int wg_per_cu,
+                           hipStream_t stream)
+{
+    if (wg_per_cu < -1 || wg_per_cu > 16)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    const int st = check_rms(x, scale, shift, eps, out, B, L, D, RGA_MOD_ROW, dtype, false, &fast);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return launched(rga::launch_rms_modulate(x, scale, shift, eps, out, B, L, D, RGA_MOD_ROW,
+                                             dtype, fast, stream, wg_per_cu));
+}
+
+int rga_check_fused_occupancy(const void* x, const void* u, const void* g, const void* scale,
+                              const void* shift, float eps, const void* x_out, const void* y,
+                              int64_t B, int64_t L, int64_t D, int gate_mode, int dtype,
+                              int wg_per_cu)
+{
+    if (wg_per_cu < -1 || wg_per_cu > 16)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    return check_fused(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, RGA_MOD_ROW,
+                       dtype, false, &fast);
+}
+
+int rga_fused_occupancy(const void* x, const void* u, const void* g, const void* scale,
+                        const void* shift, float eps, void* x_out, void* y, int64_t B,
+                        int64_t L, int64_t D, int gate_mode, int dtype, int wg_per_cu,
+                        hipStream_t stream)
+{
+    if (wg_per_cu < -1 || wg_per_cu > 16)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    const int st = check_fused(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode,
+                               RGA_MOD_ROW, dtype, false, &fast);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return launched(rga::launch_gate_add_rms_modulate(x, u, g, scale, shift, eps, x_out, y, B,
+                                                      L, D, gate_mode, RGA_MOD_ROW, dtype, fast,
+                                                      stream, wg_per_cu));
+}
+
 const char* rga_status_string(int status)
 {
     switch (status) {

@@ -763,7 +763,7 @@ template <bool FULL, int DT, int MOD>
 hipError_t launch_element(const void* x, const void* u, const void* g,
                           const void* scale, const void* shift, float eps,
                           void* x_out, void* y, int64_t B, int64_t L, int64_t D,
-                          hipStream_t stream)
+                          hipStream_t stream, int wg_per_cu)
 {
     float d_float = (float)D;
     void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &D};
@@ -776,7 +776,8 @@ hipError_t launch_element(const void* x, const void* u, const void* g,
             return hipLaunchKernel(pick_regs_staged<FULL, DT>(K),
                                    dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                    dim3(kBlock * kRowWaves), args,
-                                   (size_t)row_wg_lds(2 * D, stage, kFusedRowBudget), stream);
+                                   (size_t)row_wg_lds(2 * D, stage, kFusedRowBudget, wg_per_cu),
+                                   stream);
         }
     }
     if constexpr (DT != kF32) {
@@ -802,7 +803,7 @@ template <bool FULL, int DT, int MOD>
 hipError_t launch_typed(const void* x, const void* u, const void* g,
                         const void* scale, const void* shift, float eps,
                         void* x_out, void* y, int64_t B, int64_t L, int64_t D,
-                        bool fast, hipStream_t stream)
+                        bool fast, hipStream_t stream, int wg_per_cu)
 {
     constexpr int64_t es = DT == kF32 ? 4 : 2;
     const int64_t stage = (FULL ? 2 : 3) * D * es;
@@ -815,7 +816,8 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
         void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
         return hipLaunchKernel(k, dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                dim3(kBlock * kRowWaves), args,
-                               (size_t)row_wg_lds(D * es, stage, kFusedRowBudget), stream);
+                               (size_t)row_wg_lds(D * es, stage, kFusedRowBudget, wg_per_cu),
+                               stream);
     }
     // otherwise 2-byte rows with row modulation take the register-row kernel
     // (aligned or not: on MI355X it ran 1-3 % faster than the one-wave pack
@@ -823,11 +825,11 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
     // the pack kernel, as binary32 does)
     if constexpr (DT != kF32 && MOD == kModRow) {
         return launch_element<FULL, DT, MOD>(x, u, g, scale, shift, eps, x_out, y, B, L, D,
-                                             stream);
+                                             stream, wg_per_cu);
     } else {
         if (!fast)
             return launch_element<FULL, DT, MOD>(x, u, g, scale, shift, eps, x_out, y, B, L, D,
-                                                 stream);
+                                                 stream, wg_per_cu);
         float d_float = (float)D;
         int vpr = (int)(D / 8);
         fused_kernel_t k = pick<FULL, DT, MOD>((int)ceil_div(vpr, 64));
@@ -844,17 +846,17 @@ template <int DT>
 hipError_t launch_dt(const void* x, const void* u, const void* g,
                      const void* scale, const void* shift, float eps,
                      void* x_out, void* y, int64_t B, int64_t L, int64_t D,
-                     int gate_mode, int mod_mode, bool fast, hipStream_t stream)
+                     int gate_mode, int mod_mode, bool fast, hipStream_t stream, int w)
 {
     const bool full = gate_mode == RGA_GATE_FULL;
     const bool token = mod_mode == RGA_MOD_TOKEN;
     if (full && token)
-        return launch_typed<true, DT, kModToken>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+        return launch_typed<true, DT, kModToken>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream, w);
     if (full)
-        return launch_typed<true, DT, kModRow>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+        return launch_typed<true, DT, kModRow>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream, w);
     if (token)
-        return launch_typed<false, DT, kModToken>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
-    return launch_typed<false, DT, kModRow>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream);
+        return launch_typed<false, DT, kModToken>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream, w);
+    return launch_typed<false, DT, kModRow>(x, u, g, scale, shift, eps, x_out, y, B, L, D, fast, stream, w);
 }
 
 }  // namespace
@@ -877,15 +879,15 @@ hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
                                         void* x_out, void* y, int64_t B,
                                         int64_t L, int64_t D, int gate_mode,
                                         int mod_mode, int dtype, bool fast,
-                                        hipStream_t stream)
+                                        hipStream_t stream, int wg_per_cu)
 {
     switch (dtype) {
     case RGA_DTYPE_F16:
-        return launch_dt<kF16>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream);
+        return launch_dt<kF16>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream, wg_per_cu);
     case RGA_DTYPE_F32:
-        return launch_dt<kF32>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream);
+        return launch_dt<kF32>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream, wg_per_cu);
     default:
-        return launch_dt<kBF16>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream);
+        return launch_dt<kBF16>(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mode, mod_mode, fast, stream, wg_per_cu);
     }
 }
 

@@ -21,10 +21,12 @@ hipError_t launch_gate_add(const void* x, const void* u, const void* g,
 
 // modulation (rms_modulate.hip)
 bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast);
+// wg_per_cu: see row_wg_lds (0: the library's rule)
 hipError_t launch_rms_modulate(const void* x, const void* scale,
                                const void* shift, float eps, void* out,
                                int64_t B, int64_t L, int64_t D, int mod_mode,
-                               int dtype, bool fast, hipStream_t stream);
+                               int dtype, bool fast, hipStream_t stream,
+                               int wg_per_cu = 0);
 
 // modulation after a weightless LayerNorm (rms_modulate.hip); same grid
 // limits as rms_modulate_grid_fits
@@ -63,11 +65,19 @@ inline int lds_row_waves(int64_t row_bytes)
 constexpr int kRowWaves = 2;
 constexpr int64_t kModRowBudget = 48 * 1024;    // rms/LayerNorm modulation
 constexpr int64_t kFusedRowBudget = 32 * 1024;  // residual update + modulation
-inline int64_t row_wg_lds(int64_t row_bytes, int64_t stage_bytes, int64_t row_budget)
+// wg_per_cu overrides the rule for measurement (rga_measure.h): > 0 asks
+// for that many workgroups per CU, -1 for no cap (the staging alone).
+inline int64_t row_wg_lds(int64_t row_bytes, int64_t stage_bytes, int64_t row_budget,
+                          int wg_per_cu = 0)
 {
     constexpr int64_t kLdsPerCu = 160 * 1024;
-    int64_t wg = (row_budget + row_bytes / 2) / row_bytes;
-    wg = wg < 4 ? 4 : (wg > 12 ? 12 : wg);
+    if (wg_per_cu < 0)
+        return stage_bytes;
+    int64_t wg = wg_per_cu;
+    if (wg == 0) {
+        wg = (row_budget + row_bytes / 2) / row_bytes;
+        wg = wg < 4 ? 4 : (wg > 12 ? 12 : wg);
+    }
     const int64_t cap = ((kLdsPerCu - 1024) / wg) & ~(int64_t)1023;
     return cap > stage_bytes ? cap : stage_bytes;
 }
@@ -83,7 +93,7 @@ hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,
                                         void* x_out, void* y, int64_t B,
                                         int64_t L, int64_t D, int gate_mode,
                                         int mod_mode, int dtype, bool fast,
-                                        hipStream_t stream);
+                                        hipStream_t stream, int wg_per_cu = 0);
 
 // tanh-GELU over [rows, F] with an optional bias row (gelu_tanh.hip); fast:
 // every pointer 16-byte aligned and, with a bias, F % 8 == 0

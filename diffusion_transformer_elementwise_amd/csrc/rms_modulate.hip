@@ -717,9 +717,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Dynamic LDS of a row-modulation fast-path workgroup (row_wg_lds in
 // launch.hpp): the staged scale and shift rows; a row of at most
 // RGA_RMS_MAX_D binary32 elements stages 64 KB, one workgroup's limit.
-int64_t staged_row_lds(int64_t row_bytes)
+int64_t staged_row_lds(int64_t row_bytes, int wg_per_cu)
 {
-    return row_wg_lds(row_bytes, 2 * row_bytes, kModRowBudget);
+    return row_wg_lds(row_bytes, 2 * row_bytes, kModRowBudget, wg_per_cu);
 }
 
 // Element-path slots per lane for 2-byte rows held in registers: the
@@ -789,7 +789,7 @@ const void* lds_kernel(int w)
 template <int NORM, int DT, int MOD>
 hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                         float eps, void* out, int64_t B, int64_t L, int64_t D,
-                        bool fast, hipStream_t stream)
+                        bool fast, hipStream_t stream, int wg_per_cu)
 {
     float d_float = (float)D;
     if (!fast) {
@@ -804,7 +804,7 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                                        dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                        dim3(kBlock * kRowWaves), args,
                                        (size_t)row_wg_lds(2 * D, 2 * 1024 * (int64_t)K,
-                                                          kModRowBudget),
+                                                          kModRowBudget, wg_per_cu),
                                        stream);
             }
             const void* rk = pick_regs<NORM, DT, MOD>(slots);
@@ -839,31 +839,36 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
     return hipLaunchKernel(reinterpret_cast<const void*>(k),
                            dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                            dim3(kBlock * kRowWaves), args,
-                           (size_t)staged_row_lds(D * (DT == kF32 ? 4 : 2)), stream);
+                           (size_t)staged_row_lds(D * (DT == kF32 ? 4 : 2), wg_per_cu), stream);
 }
 
 template <int NORM, int DT>
 hipError_t launch_mod(const void* x, const void* scale, const void* shift,
                       float eps, void* out, int64_t B, int64_t L, int64_t D,
-                      int mod_mode, bool fast, hipStream_t stream)
+                      int mod_mode, bool fast, hipStream_t stream, int wg_per_cu)
 {
     return mod_mode == RGA_MOD_TOKEN
-               ? launch_typed<NORM, DT, kModToken>(x, scale, shift, eps, out, B, L, D, fast, stream)
-               : launch_typed<NORM, DT, kModRow>(x, scale, shift, eps, out, B, L, D, fast, stream);
+               ? launch_typed<NORM, DT, kModToken>(x, scale, shift, eps, out, B, L, D, fast,
+                                                   stream, wg_per_cu)
+               : launch_typed<NORM, DT, kModRow>(x, scale, shift, eps, out, B, L, D, fast,
+                                                 stream, wg_per_cu);
 }
 
 template <int NORM>
 hipError_t launch_norm(const void* x, const void* scale, const void* shift, float eps,
                        void* out, int64_t B, int64_t L, int64_t D, int mod_mode,
-                       int dtype, bool fast, hipStream_t stream)
+                       int dtype, bool fast, hipStream_t stream, int wg_per_cu)
 {
     switch (dtype) {
     case RGA_DTYPE_F16:
-        return launch_mod<NORM, kF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+        return launch_mod<NORM, kF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast,
+                                      stream, wg_per_cu);
     case RGA_DTYPE_F32:
-        return launch_mod<NORM, kF32>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+        return launch_mod<NORM, kF32>(x, scale, shift, eps, out, B, L, D, mod_mode, fast,
+                                      stream, wg_per_cu);
     default:
-        return launch_mod<NORM, kBF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast, stream);
+        return launch_mod<NORM, kBF16>(x, scale, shift, eps, out, B, L, D, mod_mode, fast,
+                                       stream, wg_per_cu);
     }
 }
 
@@ -887,10 +892,10 @@ bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast)
 hipError_t launch_rms_modulate(const void* x, const void* scale,
                                const void* shift, float eps, void* out,
                                int64_t B, int64_t L, int64_t D, int mod_mode,
-                               int dtype, bool fast, hipStream_t stream)
+                               int dtype, bool fast, hipStream_t stream, int wg_per_cu)
 {
     return launch_norm<kNormRms>(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, fast,
-                                 stream);
+                                 stream, wg_per_cu);
 }
 
 hipError_t launch_ln_modulate(const void* x, const void* scale,
@@ -899,7 +904,7 @@ hipError_t launch_ln_modulate(const void* x, const void* scale,
                               int dtype, bool fast, hipStream_t stream)
 {
     return launch_norm<kNormLn>(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, fast,
-                                stream);
+                                stream, 0);
 }
 
 }  // namespace rga

@@ -341,3 +341,44 @@ def gate_add_variant(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor,
     if st != RGA_OK:
         raise RGAError(st, "rga_gate_add_variant")
     return out
+
+
+def modulate_occupancy(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                       eps: float = 1e-6, out: torch.Tensor | None = None,
+                       wg_per_cu: int = 0) -> torch.Tensor:
+    """Measurement helper (rga_modulate_occupancy): rga_rms_modulate_ex with
+    row modulation and a chosen number of workgroups per CU for the kernels
+    that stage scale and shift in LDS (-1: no cap, 0: the library's rule)."""
+    dt = _storage(x)
+    B, L, D = _x_shape(x, dt)
+    dev = x.device
+    _modulation(x, scale, shift, MOD_ROW, dt, dev)
+    out = _output(out, "out", x, dev)
+    st = library().rga_modulate_occupancy(x.data_ptr(), scale.data_ptr(), shift.data_ptr(),
+                                          float(eps), out.data_ptr(), B, L, D, _DTYPES[dt],
+                                          int(wg_per_cu), _stream_handle(dev))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_modulate_occupancy")
+    return out
+
+
+def fused_occupancy(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor, scale: torch.Tensor,
+                    shift: torch.Tensor, eps: float = 1e-6, x_out: torch.Tensor | None = None,
+                    y: torch.Tensor | None = None, gate_mode: int | None = None,
+                    wg_per_cu: int = 0):
+    """Measurement helper (rga_fused_occupancy): rga_gate_add_rms_modulate_ex
+    with row modulation and a chosen number of workgroups per CU."""
+    dt = _storage(x)
+    B, L, D = _x_shape(x, dt)
+    dev = x.device
+    gate_mode = _gate(x, u, g, gate_mode, dt, dev)
+    _modulation(x, scale, shift, MOD_ROW, dt, dev)
+    x_out = _output(x_out, "x_out", x, dev)
+    y = _output(y, "y", x, dev)
+    st = library().rga_fused_occupancy(x.data_ptr(), u.data_ptr(), g.data_ptr(),
+                                       scale.data_ptr(), shift.data_ptr(), float(eps),
+                                       x_out.data_ptr(), y.data_ptr(), B, L, D, gate_mode,
+                                       _DTYPES[dt], int(wg_per_cu), _stream_handle(dev))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_fused_occupancy")
+    return x_out, y

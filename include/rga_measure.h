@@ -103,6 +103,36 @@ int rga_check_gate_add_variant(const void* x, const void* u, const void* g, cons
                                int64_t B, int64_t L, int64_t D, int rows_per_wave,
                                int store_policy);
 
+/*
+ * rga_rms_modulate_ex with row modulation (RGA_MOD_ROW) and
+ * rga_gate_add_rms_modulate_ex with row modulation, with the number of
+ * workgroups each CU may hold set by the caller: same kernels, arithmetic,
+ * results and argument rules as those calls (plus wg_per_cu), to measure
+ * the occupancy rule of the kernels that stage scale and shift rows in LDS
+ * (two rows per workgroup; 2-byte storage). Those kernels ask for more LDS
+ * than the staging needs so that only about a chosen amount of rows stays
+ * on a CU: wg_per_cu > 0 asks for that many workgroups per CU, -1 for no cap
+ * (the staging alone decides), 0 for the library's rule. Kernels that stage
+ * nothing (binary32 rows, per-token modulation) ignore it.
+ * wg_per_cu outside -1..16 is RGA_ERR_INVALID_ARG.
+ */
+int rga_modulate_occupancy(const void* x, const void* scale, const void* shift, float eps,
+                           void* out, int64_t B, int64_t L, int64_t D, int dtype, int wg_per_cu,
+                           hipStream_t stream);
+int rga_fused_occupancy(const void* x, const void* u, const void* g, const void* scale,
+                        const void* shift, float eps, void* x_out, void* y, int64_t B,
+                        int64_t L, int64_t D, int gate_mode, int dtype, int wg_per_cu,
+                        hipStream_t stream);
+
+/* Their validation alone, on the host. */
+int rga_check_modulate_occupancy(const void* x, const void* scale, const void* shift, float eps,
+                                 const void* out, int64_t B, int64_t L, int64_t D, int dtype,
+                                 int wg_per_cu);
+int rga_check_fused_occupancy(const void* x, const void* u, const void* g, const void* scale,
+                              const void* shift, float eps, const void* x_out, const void* y,
+                              int64_t B, int64_t L, int64_t D, int gate_mode, int dtype,
+                              int wg_per_cu);
+
 #ifdef __cplusplus
 }
 #endif

@@ -495,3 +495,22 @@ def test_measurement_validation_rules(dte):
     assert gv(x, u, g + 2, o, 2, 33, 4096, 1, 0) == uns
     assert gv(x, u, g, g, 2, 33, 4096, 1, 0) == ali   # out over the broadcast row
     assert gv(0, 0, 0, 0, 0, 33, 4096, 1, 0) == ok
+
+
+def test_occupancy_helpers_follow_the_ex_rules(dte):
+    ok, bad, uns = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED
+    x, s, t, o, u, g, y = (A + i * 512 * MB for i in range(7))
+    mo, ref = dte.check_modulate_occupancy, dte.check_rms_modulate_ex
+    for D, dt in ((4096, 0), (4100, 0), (4096, 2), (8200, 1)):
+        for w in (-1, 0, 4, 16):
+            assert mo(x, s, t, 1e-6, o, 2, 32640, D, dt, w) == ok == ref(
+                x, s, t, 1e-6, o, 2, 32640, D, dte.MOD_ROW, dt)
+    assert mo(x, s, t, 1e-6, o, 2, 32640, 4096, 0, 17) == bad
+    assert mo(x, s, t, 1e-6, o, 2, 32640, 4096, 0, -2) == bad
+    assert mo(x + 1, s, t, 1e-6, o, 2, 3, 4096, 0, 4) == uns
+    assert mo(x, s, t, -1.0, o, 2, 3, 4096, 0, 4) == bad
+    fo = dte.check_fused_occupancy
+    for gm in (dte.GATE_BCAST, dte.GATE_FULL):
+        assert fo(x, u, g, s, t, 1e-6, x, y, 2, 32640, 4096, gm, 0, 4) == ok
+    assert fo(x, u, g, s, t, 1e-6, x, y, 2, 32640, 4096, 1, 0, 99) == bad
+    assert fo(x, u, g, s, t, 1e-6, x, x, 2, 32640, 4096, 1, 0, 4) == dte.RGA_ERR_ALIAS

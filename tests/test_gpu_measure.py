@@ -109,3 +109,25 @@ def test_stream_writes_the_xor_of_its_sources(dte, wpl):
     dte.stream_([], w, words_per_lane=wpl)                   # write-only: a pattern
     torch.cuda.synchronize()
     assert torch.count_nonzero(w).item() > 0
+
+
+@pytest.mark.parametrize("D,dt", [(4096, 0), (2048, 1), (4100, 0), (520, 1)])
+def test_occupancy_helpers_equal_the_library(dte, D, dt):
+    from tests.gpu_util import to_dev_typed, to_host_typed
+    from synth_inputs import random_typed
+    B, L = 2, 37
+    seed = D + dt
+    x = to_dev_typed(random_typed(seed, (B, L, D), N02, dt), dt)
+    u = to_dev_typed(random_typed(seed + 1, (B, L, D), dtype=dt), dt)
+    g = to_dev_typed(random_typed(seed + 2, (B, 1, D), U11, dt), dt)
+    s = to_dev_typed(random_typed(seed + 3, (B, 1, D), N001, dt), dt)
+    t = to_dev_typed(random_typed(seed + 4, (B, 1, D), N001, dt), dt)
+    want_y = to_host_typed(dte.rga_rms_modulate_ex(x, s, t, 1e-6))
+    want_xo, want_fy = (to_host_typed(a) for a in dte.rga_gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6))
+    for w in (-1, 0, 3, 5, 12):
+        say(f"[occupancy] D={D} dtype={dt} wg_per_cu={w}")
+        got = to_host_typed(dte.modulate_occupancy(x, s, t, 1e-6, wg_per_cu=w))
+        assert np.array_equal(got, want_y)
+        xo, fy = dte.fused_occupancy(x, u, g, s, t, 1e-6, wg_per_cu=w)
+        assert np.array_equal(to_host_typed(xo), want_xo)
+        assert np.array_equal(to_host_typed(fy), want_fy)
