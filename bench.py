@@ -1033,16 +1033,16 @@ def known_launches():
     full("c3 full [1,8160,4096]", 1, 8160, 4096)
     bcast("c4 bcast in place [1,32640,4096]", 1, 32640, 4096)
     bcast("c5 bcast in place [2,32640,4096]", 2, 32640, 4096)
-    mod("c5 rms_modulate [2,32640,4096]", 2, 32640, 4096, "rms_modulate_kernel<8, 0, 0>")
-    out.append(("fused gate+rms [2,32640,4096]", "gate_add_rms_modulate_staged_kernel<8, false, 0>",
+    mod("c5 rms_modulate [2,32640,4096]", 2, 32640, 4096, "rms_modulate_kernel<8, 0, 0, true>")
+    out.append(("fused gate+rms [2,32640,4096]", "gate_add_rms_modulate_staged_kernel<8, false, 0, true>",
                 16320 * 128, 2, (4 * 2 * 32640 * 4096 + 3 * 2 * 4096) * 2, 2 * 32640 * 4096))
     full("c1 full [1,126,2048]", 1, 126, 2048)
-    mod("c1 rms_modulate [1,126,2048]", 1, 126, 2048, "rms_modulate_kernel<4, 0, 0>")
+    mod("c1 rms_modulate [1,126,2048]", 1, 126, 2048, "rms_modulate_kernel<4, 0, 0, true>")
     for L in (512, 4096, 4608):
         bcast(f"c2 bcast [1,{L},3072]", 1, L, 3072)
     bcast("ideogram4 bcast [1,4096,4608]", 1, 4096, 4608)
-    mod("f16 rms_modulate [2,32640,4096]", 2, 32640, 4096, "rms_modulate_kernel<8, 1, 0>")
-    mod("bf16 LayerNorm modulation [2,32640,4096]", 2, 32640, 4096, "ln_modulate_kernel<8, 0, 0>")
+    mod("f16 rms_modulate [2,32640,4096]", 2, 32640, 4096, "rms_modulate_kernel<8, 1, 0, true>")
+    mod("bf16 LayerNorm modulation [2,32640,4096]", 2, 32640, 4096, "ln_modulate_kernel<8, 0, 0, true>")
     n = 32640 * 16384
     out.append(("bf16 tanh-GELU [1,32640,16384]", "gelu_tanh_flat_kernel<0>", n // 8, 1, 4 * n, n))
     e3, e4 = 8160 * 4096 * 2, 32640 * 4096 * 2

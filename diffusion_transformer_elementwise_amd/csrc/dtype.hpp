@@ -259,12 +259,17 @@ struct Grouped {
     {
         return load_stream_raw(b, c0, t, h);
     }
-    // load_raw from a row staged in LDS as 16-byte words in memory order
+    // load_raw from a row staged in LDS as 16-byte words in memory order;
+    // the index is clamped into the row and zeros selected past its end (no
+    // branch, so a wave's reads can all be issued before the first use)
     __device__ __forceinline__ static Pack<DT> lds_raw(const u32x4* w, int c0, int t, int h)
     {
-        Pack<DT> p = Pack<DT>::zero();
-        if (t < h)
-            p.v = w[c0 + t];
+        Pack<DT> p;
+        p.v = w[c0 + (t < h ? t : h - 1)];
+        const bool in = t < h;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            p.v[d] = in ? p.v[d] : 0u;
         return p;
     }
 };

@@ -187,7 +187,8 @@ __device__ __forceinline__ float wave_sum_dpp(float a)
 // and, with a broadcast gate, its gate row at [2 words, 3 words), as 16-byte
 // words in memory order. Lanes past the row end hold zeros (x' = +0 there,
 // which adds +0 to the partial) and store nothing.
-template <int G, bool FULL, int DT>
+// WHOLE: D = 512 G (every lane's packs lie in the row): no bounds at all.
+template <int G, bool FULL, int DT, bool WHOLE>
 __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_staged_kernel(
     const void* x, const void* u, const void* g, const void* scale,
     const void* shift, float eps, float d_float, void* x_out, void* y,
@@ -217,23 +218,40 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_stag
 
     using GP = Grouped<DT>;
     const int64_t row = (b * L + r) * vpr;
+    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
     Pack<DT> xv[G], uv[G], gv[FULL ? G : 1];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int h = vpr - 64 * i;
-        xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
-        uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
-        if constexpr (FULL)
-            gv[i] = GP::template load_clamped<true>(g, row + 64 * i, lane, h);
+        if constexpr (WHOLE) {
+            xv[i] = Pack<DT>::load_stream(x, row + 64 * i + lane);
+            uv[i] = Pack<DT>::load_stream(u, row + 64 * i + lane);
+            if constexpr (FULL)
+                gv[i] = Pack<DT>::load_stream(g, row + 64 * i + lane);
+        } else {
+            xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
+            uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
+            if constexpr (FULL)
+                gv[i] = GP::template load_clamped<true>(g, row + 64 * i, lane, h);
+        }
     }
     Pack<DT> xn[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int h = vpr - 64 * i;
-        const Pack<DT> gi = FULL ? gv[FULL ? i : 0] : GP::lds_raw(g_st, 64 * i, lane, h);
+        Pack<DT> gi;
+        if constexpr (FULL)
+            gi = gv[FULL ? i : 0];
+        else if constexpr (WHOLE)
+            gi.v = g_st[64 * i + lane];
+        else
+            gi = GP::lds_raw(g_st, 64 * i, lane, h);
         const Pack<DT> xr = gate_add8<DT>(xv[i], uv[i], gi);
-        GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
-        xn[i] = GP::to_groups(xr);
+        if constexpr (WHOLE)
+            xr.store_stream(x_out, row + 64 * i + lane);
+        else
+            GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
+        xn[i] = xr;
     }
     float acc = 0.0f;
 #pragma unroll
@@ -252,9 +270,15 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_stag
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int h = vpr - 64 * i;
-        const Pack<DT> xr = GP::to_raw(xn[i]);
-        const Pack<DT> s_ = GP::lds_raw(s_st, 64 * i, lane, h);
-        const Pack<DT> h_ = GP::lds_raw(h_st, 64 * i, lane, h);
+        const Pack<DT>& xr = xn[i];
+        Pack<DT> s_, h_;
+        if constexpr (WHOLE) {
+            s_.v = s_st[64 * i + lane];
+            h_.v = h_st[64 * i + lane];
+        } else {
+            s_ = GP::lds_raw(s_st, 64 * i, lane, h);
+            h_ = GP::lds_raw(h_st, 64 * i, lane, h);
+        }
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -263,7 +287,10 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_stag
             const float m = n * a;
             o[e] = m + h_.get(e);
         }
-        GP::store_stream_raw(Pack<DT>::make(o), y, row + 64 * i, lane, h);
+        if constexpr (WHOLE)
+            Pack<DT>::make(o).store_stream(y, row + 64 * i + lane);
+        else
+            GP::store_stream_raw(Pack<DT>::make(o), y, row + 64 * i, lane, h);
     }
 }
 
@@ -729,19 +756,29 @@ fused_kernel_t pick(int groups)
     return nullptr;
 }
 
-template <bool FULL, int DT>
-const void* pick_staged(int groups)
+template <int G, bool FULL, int DT>
+const void* staged_kernel(bool whole)
 {
-    const void* t[] = {reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<1, FULL, DT>),
-                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<2, FULL, DT>),
-                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<4, FULL, DT>),
-                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<6, FULL, DT>),
-                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<8, FULL, DT>),
-                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<12, FULL, DT>),
-                       reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<16, FULL, DT>)};
+    return whole ? reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<G, FULL, DT, true>)
+                 : reinterpret_cast<const void*>(&gate_add_rms_modulate_staged_kernel<G, FULL, DT, false>);
+}
+
+// the staged kernel for rows of `groups` packs per lane; `whole`: the row is
+// exactly 64 * groups packs (D = 512 G)
+template <bool FULL, int DT>
+const void* pick_staged(int groups, bool whole)
+{
+    const void* t[] = {staged_kernel<1, FULL, DT>(false), staged_kernel<2, FULL, DT>(false),
+                       staged_kernel<4, FULL, DT>(false), staged_kernel<6, FULL, DT>(false),
+                       staged_kernel<8, FULL, DT>(false), staged_kernel<12, FULL, DT>(false),
+                       staged_kernel<16, FULL, DT>(false)};
+    const void* w[] = {staged_kernel<1, FULL, DT>(true), staged_kernel<2, FULL, DT>(true),
+                       staged_kernel<4, FULL, DT>(true), staged_kernel<6, FULL, DT>(true),
+                       staged_kernel<8, FULL, DT>(true), staged_kernel<12, FULL, DT>(true),
+                       staged_kernel<16, FULL, DT>(true)};
     for (int i = 0; i < 7; ++i)
         if (groups <= kLadder[i])
-            return t[i];
+            return (whole && groups == kLadder[i]) ? w[i] : t[i];
     return nullptr;
 }
 
@@ -807,17 +844,19 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
 {
     constexpr int64_t es = DT == kF32 ? 4 : 2;
     const int64_t stage = (FULL ? 2 : 3) * D * es;
-    if (DT != kF32 && MOD == kModRow && fast && stage <= kMaxStagedLds) {
-        float d_float = (float)D;
-        int vpr = (int)(D / 8);
-        const void* k = pick_staged<FULL, DT>((int)ceil_div(vpr, 64));
-        if (k == nullptr)
-            return hipErrorInvalidValue;
-        void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
-        return hipLaunchKernel(k, dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
-                               dim3(kBlock * kRowWaves), args,
-                               (size_t)row_wg_lds(D * es, stage, kFusedRowBudget, wg_per_cu),
-                               stream);
+    if constexpr (DT != kF32 && MOD == kModRow) {
+        if (fast && stage <= kMaxStagedLds) {
+            float d_float = (float)D;
+            int vpr = (int)(D / 8);
+            const void* k = pick_staged<FULL, DT>((int)ceil_div(vpr, 64), vpr % 64 == 0);
+            if (k == nullptr)
+                return hipErrorInvalidValue;
+            void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
+            return hipLaunchKernel(k, dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
+                                   dim3(kBlock * kRowWaves), args,
+                                   (size_t)row_wg_lds(D * es, stage, kFusedRowBudget, wg_per_cu),
+                                   stream);
+        }
     }
     // otherwise 2-byte rows with row modulation take the register-row kernel
     // (aligned or not: on MI355X it ran 1-3 % faster than the one-wave pack

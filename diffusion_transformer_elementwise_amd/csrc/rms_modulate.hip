@@ -168,7 +168,7 @@ __device__ __forceinline__ Pack<DT> modulate_pack(const Pack<DT>& xr, float mu, 
 // kRowWaves * blockIdx.x + wave of batch blockIdx.y. The batch's scale and
 // shift rows are staged in the dynamic LDS as 16-byte words in memory order
 // (scale at [0, words), shift at [words, 2 words)) before any row is loaded.
-template <int G, int DT, int NORM>
+template <int G, int DT, int NORM, bool WHOLE>
 __device__ __forceinline__ void modulate_staged_row(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
@@ -189,23 +189,37 @@ __device__ __forceinline__ void modulate_staged_row(
     if (r >= L)
         return;
 
+    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
     const int64_t row = (b * L + r) * vpr;
+    // WHOLE (D = 512 G): every lane's G packs lie in the row, no bounds at
+    // all. Otherwise no branch around a load: the index is clamped into the
+    // row and zeros are selected past its end (a branch per load made the
+    // compiler wait for each load before issuing the next).
     Pack<DT> xv[G];
 #pragma unroll
     for (int i = 0; i < G; ++i)
-        xv[i] = Grouped<DT>::load_stream(x, row + 64 * i, lane, vpr - 64 * i);
+        xv[i] = WHOLE ? Pack<DT>::load_stream(x, row + 64 * i + lane)
+                      : Grouped<DT>::template load_clamped<true>(x, row + 64 * i, lane,
+                                                                 vpr - 64 * i);
     float mu;
     const float rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
-    // element-wise, so in raw order (binary32 rows are turned back from group
-    // order, which needs every lane); packs past the row end are not stored
+    // element-wise; packs past the row end are not stored
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         const int h = vpr - 64 * i;
-        const Pack<DT> s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
-        const Pack<DT> h_ = Grouped<DT>::lds_raw(staged + words, 64 * i, lane, h);
-        Grouped<DT>::store_stream_raw(
-            modulate_pack<DT, NORM>(Grouped<DT>::to_raw(xv[i]), mu, rr, s_, h_), out,
-            row + 64 * i, lane, h);
+        Pack<DT> s_, h_;
+        if constexpr (WHOLE) {
+            s_.v = staged[64 * i + lane];
+            h_.v = staged[words + 64 * i + lane];
+        } else {
+            s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
+            h_ = Grouped<DT>::lds_raw(staged + words, 64 * i, lane, h);
+        }
+        const Pack<DT> o = modulate_pack<DT, NORM>(xv[i], mu, rr, s_, h_);
+        if constexpr (WHOLE)
+            o.store_stream(out, row + 64 * i + lane);
+        else
+            Grouped<DT>::store_stream_raw(o, out, row + 64 * i, lane, h);
     }
 }
 
@@ -280,13 +294,13 @@ constexpr bool staged_rows()
     return MOD == kModRow && DT != kF32;
 }
 
-template <int G, int DT, int MOD, int NORM>
+template <int G, int DT, int MOD, int NORM, bool WHOLE>
 __device__ __forceinline__ void modulate_rows(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
     if constexpr (staged_rows<DT, MOD>())
-        modulate_staged_row<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
+        modulate_staged_row<G, DT, NORM, WHOLE>(x, scale, shift, eps, d_float, out, L, vpr);
     else if constexpr (MOD == kModRow)
         modulate_held_rows<G, DT, NORM>(x, scale, shift, eps, d_float, out, L, vpr);
     else
@@ -294,20 +308,21 @@ __device__ __forceinline__ void modulate_rows(
 }
 
 // Grid: x = pair of rows (row modulation) or row (per token), y = batch.
-template <int G, int DT, int MOD>
+// WHOLE: D = 512 G (every lane's packs lie in the row; 2-byte row modulation)
+template <int G, int DT, int MOD, bool WHOLE = false>
 __global__ __launch_bounds__((staged_rows<DT, MOD>() ? kBlock * kRowWaves : kBlock)) void rms_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
-    modulate_rows<G, DT, MOD, kNormRms>(x, scale, shift, eps, d_float, out, L, vpr);
+    modulate_rows<G, DT, MOD, kNormRms, WHOLE>(x, scale, shift, eps, d_float, out, L, vpr);
 }
 
-template <int G, int DT, int MOD>
+template <int G, int DT, int MOD, bool WHOLE = false>
 __global__ __launch_bounds__((staged_rows<DT, MOD>() ? kBlock * kRowWaves : kBlock)) void ln_modulate_kernel(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
-    modulate_rows<G, DT, MOD, kNormLn>(x, scale, shift, eps, d_float, out, L, vpr);
+    modulate_rows<G, DT, MOD, kNormLn, WHOLE>(x, scale, shift, eps, d_float, out, L, vpr);
 }
 
 template <int DT>
@@ -693,22 +708,30 @@ typedef void (*rms_kernel_t)(const void*, const void*, const void*, float,
 constexpr int kLadder[] = {1, 2, 4, 6, 8, 12, 16};
 static_assert(RGA_RMS_MAX_D / 512 == 16, "ladder tops out at RGA_RMS_MAX_D");
 
-template <int NORM, int G, int DT, int MOD>
+template <int NORM, int G, int DT, int MOD, bool WHOLE>
 constexpr rms_kernel_t fast_kernel()
 {
-    return NORM == kNormLn ? &ln_modulate_kernel<G, DT, MOD> : &rms_modulate_kernel<G, DT, MOD>;
+    return NORM == kNormLn ? &ln_modulate_kernel<G, DT, MOD, WHOLE>
+                           : &rms_modulate_kernel<G, DT, MOD, WHOLE>;
 }
 
+// the kernel for rows of `groups` packs per lane; `whole`: the row is
+// exactly 64 * groups packs (D = 512 G), every lane's packs in the row
 template <int NORM, int DT, int MOD>
-rms_kernel_t pick(int groups)
+rms_kernel_t pick(int groups, bool whole)
 {
-    rms_kernel_t t[] = {fast_kernel<NORM, 1, DT, MOD>(), fast_kernel<NORM, 2, DT, MOD>(),
-                        fast_kernel<NORM, 4, DT, MOD>(), fast_kernel<NORM, 6, DT, MOD>(),
-                        fast_kernel<NORM, 8, DT, MOD>(), fast_kernel<NORM, 12, DT, MOD>(),
-                        fast_kernel<NORM, 16, DT, MOD>()};
+    constexpr bool kW = staged_rows<DT, MOD>();  // only the staged rows have a WHOLE form
+    rms_kernel_t t[] = {fast_kernel<NORM, 1, DT, MOD, false>(), fast_kernel<NORM, 2, DT, MOD, false>(),
+                        fast_kernel<NORM, 4, DT, MOD, false>(), fast_kernel<NORM, 6, DT, MOD, false>(),
+                        fast_kernel<NORM, 8, DT, MOD, false>(), fast_kernel<NORM, 12, DT, MOD, false>(),
+                        fast_kernel<NORM, 16, DT, MOD, false>()};
+    rms_kernel_t w[] = {fast_kernel<NORM, 1, DT, MOD, kW>(), fast_kernel<NORM, 2, DT, MOD, kW>(),
+                        fast_kernel<NORM, 4, DT, MOD, kW>(), fast_kernel<NORM, 6, DT, MOD, kW>(),
+                        fast_kernel<NORM, 8, DT, MOD, kW>(), fast_kernel<NORM, 12, DT, MOD, kW>(),
+                        fast_kernel<NORM, 16, DT, MOD, kW>()};
     for (int i = 0; i < 7; ++i)
         if (groups <= kLadder[i])
-            return t[i];
+            return (whole && groups == kLadder[i]) ? w[i] : t[i];
     return nullptr;
 }
 
@@ -825,7 +848,7 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                                (size_t)generic_lds_bytes<DT>(), stream);
     }
     int vpr = (int)(D / 8);
-    rms_kernel_t k = pick<NORM, DT, MOD>((int)ceil_div(vpr, 64));
+    rms_kernel_t k = pick<NORM, DT, MOD>((int)ceil_div(vpr, 64), vpr % 64 == 0);
     if (k == nullptr)
         return hipErrorInvalidValue;
     void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &vpr};
