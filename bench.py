@@ -149,7 +149,10 @@ def parse_args():
                         "'trace KERNEL_TRACE.csv [BENCH.json]' prints per-launch-shape "
                         "device durations; 'counters OUT.json CSV...' prints HBM bytes "
                         "(FETCH_SIZE, WRITE_SIZE scaled by the 1 GiB copy) and instruction "
-                        "counts per launch shape and writes the traffic summary OUT.json")
+                        "counts per launch shape and writes the traffic summary OUT.json; "
+                        "'variants BENCH.json CSV...' prints per-variant kernels and device "
+                        "times (kernel trace) or HBM bytes and instruction counts (counter "
+                        "files) for a run with --variants 1 --fused-reps 0 --ablations 0")
     return p.parse_args()
 
 
@@ -328,7 +331,8 @@ def main():
         med = statistics.median(ts)
         # the cold median is the measurement; back to back, inputs that fit
         # the 256 MB memory-side cache are served from it (context only)
-        return {"kernel": kernel, "bytes": nbytes, "cold_us_median": round(med, 2),
+        return {"kernel": kernel, "bytes": nbytes, "cold_reps": len(ts), "warm_reps": 100,
+                "cold_us_median": round(med, 2),
                 "cold_us_p10": round(float(np.percentile(ts, 10)), 2),
                 "cold_us_p90": round(float(np.percentile(ts, 90)), 2),
                 "cold_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
@@ -755,6 +759,7 @@ def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
     out[c.name + "_gate_add"] = cold_and_warm(
         lambda: dte.rga_residual_gate_add(dx, du, dg, out=do, gate_mode=c.gate),
         (3 * c.elems + c.B * c.D) * 2, "gate_add_bcast_kernel")
+    out[c.name + "_gate_add"]["shape"] = [c.B, c.L, c.D]
     del dx, du, dg, do
 
     # LayerNorm modulation at the modulation shape
@@ -1221,7 +1226,124 @@ def summarize(argv):
                            "kernels": step, "launches": traffic}, f, indent=1)
                 f.write("\n")
         return
+    if what == "variants":
+        summarize_variants(argv[1], argv[2:])
+        return
     raise SystemExit(f"--summarize: unknown kind {what!r}")
+
+
+def _library_dispatches(paths):
+    """[(dispatch id, short kernel name, grid work-items, {column: value}),
+    ...] in dispatch order for the library's compute kernels (the cache
+    flush excluded), from kernel-trace or counter csv files; a counter file
+    has one row per counter per dispatch, merged here."""
+    import csv
+    by_id = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if "rga::" not in r["Kernel_Name"]:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            if k == "read_kernel":
+                continue
+            if "Grid_Size" in r:
+                grid = int(r["Grid_Size"])
+            else:
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            d = by_id.setdefault(int(r["Dispatch_Id"]), (k, grid, {}))[2]
+            d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            d["vgpr"] = r.get("VGPR_Count")
+            if "Counter_Name" in r:
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+    return [(i,) + by_id[i] for i in sorted(by_id)]
+
+
+def summarize_variants(bench_json, paths):
+    """Per-variant kernel, grid and device time (kernel trace) or HBM bytes
+    and instruction counts (counter csv files) for a run with
+    '--variants 1 --fused-reps 0 --ablations 0', where the variants' calls
+    are the run's last library dispatches: each variant is cold_reps calls
+    after a flush, then 100 back to back, all one kernel and grid. Matching
+    runs backwards from the last dispatch and checks that every call of a
+    variant is the same launch of the kernel the bench names."""
+    line = None
+    with open(bench_json) as f:
+        for s in f:
+            if s.startswith("{"):
+                line = json.loads(s)
+    variants = line["variants"]
+    disp = _library_dispatches(paths)
+    counters = sorted({c for _, _, _, d in disp for c in d if c.isupper()})
+    calib = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = [d[c] for _, k, g, d in disp if k == "copy_kernel" and g == FLUSH_BYTES // 16
+              and c in d]
+        if cp:
+            calib[c] = FLUSH_BYTES / (sum(cp) / len(cp) * 1024)
+    if calib:
+        print("calibration on the 1 GiB copy: " + ", ".join(
+            f"{c} scale {v:.5f}" for c, v in calib.items()))
+    rows = []
+    end = len(disp)
+    for name in reversed(list(variants)):
+        v = variants[name]
+        n = v["cold_reps"] + v["warm_reps"]
+        k, g = disp[end - 1][1], disp[end - 1][2]
+        start = end - n
+        if start < 0 or any((x[1], x[2]) != (k, g) for x in disp[start:end]):
+            raise SystemExit(f"variants: dispatches before the end do not match {name}")
+        if not k.startswith(v["kernel"]):
+            raise SystemExit(f"variants: {name} ran {k}, the bench names {v['kernel']}")
+        rows.append((name, v, k, g, [x[3] for x in disp[start:end]]))
+        end = start
+    rows.reverse()
+    mean = lambda a: sum(a) / len(a)
+
+    def elements(name, v):
+        m = re.search(r"\[([\d,]+)\]", name)
+        s = v.get("shape") or ([int(t) for t in m.group(1).split(",")] if m else None)
+        return s[0] * s[1] * s[2] if s else None
+    if "FETCH_SIZE" in counters or "WRITE_SIZE" in counters:
+        hdr = f"{'variant':44s} {'kernel':46s} {'read B':>11s} {'write B':>11s} {'traffic/alg':>11s}"
+        for c in counters:
+            if c.startswith("SQ_"):
+                hdr += f" {c[3:17]:>14s}"
+        print(hdr)
+        print("(SQ_ columns: wave instructions x 64 per element)")
+        for name, v, k, g, ds in rows:
+            elems = elements(name, v)
+            out = f"{name[:44]:44s} {k[:46]:46s}"
+            tot = 0
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                vals = [d[c] for d in ds if c in d]
+                if vals and c in calib:
+                    b = mean(vals) * 1024 * calib[c]
+                    tot += b
+                    out += f" {b:11.0f}"
+                else:
+                    tot = None if vals else tot
+                    out += f" {'-':>11s}"
+            have = all(any(c in d for d in ds) for c in ("FETCH_SIZE", "WRITE_SIZE"))
+            out += f" {tot / v['bytes']:11.4f}" if have and tot else f" {'-':>11s}"
+            for c in counters:
+                if c.startswith("SQ_"):
+                    vals = [d[c] for d in ds if c in d]
+                    out += f" {mean(vals) * 64 / elems:14.4f}" if vals and elems else f" {'-':>14s}"
+            print(out)
+        return
+    print(f"{'variant':44s} {'kernel':50s} {'grid':>9s} {'vgpr*':>5s} {'cold us':>8s} "
+          f"{'b2b us':>8s} {'trace cold':>10s} {'trace b2b':>9s} {'of 8TB/s':>8s}")
+    for name, v, k, g, ds in rows:
+        nc = v["cold_reps"]
+        tc = statistics.median([d["us"] for d in ds[:nc]]) if nc > 0 else float("nan")
+        tw = mean([d["us"] for d in ds[nc:]])
+        print(f"{name[:44]:44s} {k[:50]:50s} {g:9d} {str(ds[0]['vgpr']):>5s} "
+              f"{v['cold_us_median']:8.2f} {v['back_to_back_us']:8.2f} {tc:10.2f} {tw:9.2f} "
+              f"{v['frac_of_hbm_peak']:8.4f}")
+    print("cold us, b2b us: the bench's HIP events (cold = median after a 1 GiB flush; b2b = mean "
+          "of 100 consecutive calls); trace cold / b2b: the same calls' device durations from the "
+          "kernel trace (median / mean); of 8TB/s: algorithmic bytes / cold median; "
+          "* VGPR_Count as rocprofv3 reports it")
 
 
 if __name__ == "__main__":
