@@ -397,4 +397,46 @@ __device__ __forceinline__ void store_elem(void* base, int64_t i, float v)
         static_cast<uint16_t*>(base)[i] = (uint16_t)narrow_elem<DT>(v);
 }
 
+// ---- Modulation factors staged for many rows ---------------------------------
+//
+// The element path's staged rows (row_regs.hpp) hold 1 + scale already
+// widened to binary32: two words per group of eight 2-byte elements
+// (elements 0-3, then 4-7). It is the same binary32 sum that would
+// otherwise be taken per element of every row, so results do not change;
+// each row's apply then skips a widening and an add per element, which
+// counts on that path's realigning, instruction-heavy rows.
+template <int DT>
+__device__ __forceinline__ void one_plus(const u32x4& s, u32x4& lo, u32x4& hi)
+{
+    static_assert(DT != kF32, "groups of eight 2-byte elements");
+    Pack<DT> p;
+    p.v = s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = __float_as_uint(1.0f + p.get(e));
+        hi[e] = __float_as_uint(1.0f + p.get(4 + e));
+    }
+}
+
+// (((x - mu) or x) * rr) * a + shift per element of a group, rounded once to
+// the storage type; a = 1 + scale as one_plus stores it.
+template <int DT, bool CENTER>
+__device__ __forceinline__ Pack<DT> modulate_group(const Pack<DT>& x, float mu, float rr,
+                                                   const u32x4& a_lo, const u32x4& a_hi,
+                                                   const Pack<DT>& shift)
+{
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v = x.get(e);
+        if constexpr (CENTER)
+            v = v - mu;
+        const float n = v * rr;
+        const float a = __uint_as_float(e < 4 ? a_lo[e] : a_hi[e - 4]);
+        const float m = n * a;
+        o[e] = m + shift.get(e);
+    }
+    return Pack<DT>::make(o);
+}
+
 }  // namespace rga

@@ -183,10 +183,10 @@ __device__ __forceinline__ float wave_sum_dpp(float a)
 
 // Row modulation, kRowWaves waves per workgroup, one row each: rows
 // kRowWaves * blockIdx.x + wave of batch blockIdx.y. The dynamic LDS holds
-// the batch's scale row at [0, words), its shift row at [words, 2 words)
-// and, with a broadcast gate, its gate row at [2 words, 3 words), as 16-byte
-// words in memory order. Lanes past the row end hold zeros (x' = +0 there,
-// which adds +0 to the partial) and store nothing.
+// the batch's scale row at [0, vpr), its shift row at [vpr, 2 vpr) and,
+// with a broadcast gate, its gate row at [2 vpr, 3 vpr), as 16-byte words
+// in memory order. Lanes past the row end hold zeros (x' = +0 there, which
+// adds +0 to the partial) and store nothing.
 // WHOLE: D = 512 G (every lane's packs lie in the row): no bounds at all.
 template <int G, bool FULL, int DT, bool WHOLE>
 __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_staged_kernel(
@@ -194,31 +194,50 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_stag
     const void* shift, float eps, float d_float, void* x_out, void* y,
     int64_t L, int vpr)
 {
+    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
     extern __shared__ u32x4 staged[];
     const int lane = threadIdx.x & (kBlock - 1);
     const int64_t b = blockIdx.y;
     const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x / kBlock);
-    constexpr int kWords = DT == kF32 ? 2 : 1;  // 16-byte words per pack
-    const int words = vpr * kWords;
+    using GP = Grouped<DT>;
+    // the batch's rows, vpr <= 64 G words each: every load issued before any
+    // LDS write (one round trip to the L2, not one per word a thread
+    // stages), at most kS words of each per thread, indexes clamped and
+    // writes guarded
     u32x4* s_st = staged;
-    u32x4* h_st = staged + words;
-    u32x4* g_st = staged + 2 * words;
-    const u32x4* sc = static_cast<const u32x4*>(scale) + b * words;
-    const u32x4* sh = static_cast<const u32x4*>(shift) + b * words;
-    const u32x4* gr = static_cast<const u32x4*>(g) + b * words;
-    for (int w = threadIdx.x; w < words; w += kBlock * kRowWaves) {
-        s_st[w] = load16(sc + w);
-        h_st[w] = load16(sh + w);
-        if constexpr (!FULL)
-            g_st[w] = load16(gr + w);
+    u32x4* h_st = staged + vpr;
+    u32x4* g_st = staged + 2 * vpr;
+    constexpr int kS = (64 * G + kBlock * kRowWaves - 1) / (kBlock * kRowWaves);
+    const u32x4* sc = static_cast<const u32x4*>(scale) + b * vpr;
+    const u32x4* sh = static_cast<const u32x4*>(shift) + b * vpr;
+    const u32x4* gr = static_cast<const u32x4*>(g) + b * vpr;
+    {
+        u32x4 sv[kS], hv[kS], bv[FULL ? 1 : kS];
+#pragma unroll
+        for (int j = 0; j < kS; ++j) {
+            const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
+            const int wc = w < vpr ? w : vpr - 1;
+            sv[j] = load16(sc + wc);
+            hv[j] = load16(sh + wc);
+            if constexpr (!FULL)
+                bv[FULL ? 0 : j] = load16(gr + wc);
+        }
+#pragma unroll
+        for (int j = 0; j < kS; ++j) {
+            const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
+            if (w < vpr) {
+                s_st[w] = sv[j];
+                h_st[w] = hv[j];
+                if constexpr (!FULL)
+                    g_st[w] = bv[FULL ? 0 : j];
+            }
+        }
     }
     __syncthreads();
     if (r >= L)
         return;
 
-    using GP = Grouped<DT>;
     const int64_t row = (b * L + r) * vpr;
-    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
     Pack<DT> xv[G], uv[G], gv[FULL ? G : 1];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -583,10 +602,11 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
 // rounded x' groups stay in registers for the modulation (row_regs.hpp), so
 // x_out is never read back.
 // Row modulation of 2-byte rows held in registers: kRowWaves waves per
-// workgroup, one row each. The workgroup realigns its batch's scale and
-// shift rows (and a broadcast gate row) into the dynamic LDS once (groups,
-// 64 K words per row: scale, shift, gate), wave 0 the scale and gate rows,
-// wave 1 the shift row, before any row is loaded.
+// workgroup, one row each. Before any row is loaded the workgroup stages
+// its batch's rows in the dynamic LDS once, as groups in planes of
+// P = ceil(D / 8) words (row_regs.hpp): wave 0 1 + scale in binary32
+// (elements 0-3 at [0, P), 4-7 at [P, 2P)) and a broadcast gate row (at
+// [3P, 4P)), wave 1 the shift row (at [2P, 3P)).
 template <int K, bool FULL, int DT>
 __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs_staged_kernel(
     const void* x, const void* u, const void* g, const void* scale,
@@ -599,11 +619,11 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
     const int64_t r = (int64_t)blockIdx.x * kRowWaves + wave;
     const int n = (int)D;
     static_assert(kRowWaves == 2, "staged rows split over two waves");
-    u32x4* s_st = staged;
-    u32x4* h_st = staged + 64 * K;
-    u32x4* g_st = staged + 2 * 64 * K;
+    const int planes = (n + 7) >> 3;
+    u32x4* h_st = staged + 2 * planes;
+    u32x4* g_st = staged + 3 * planes;
     if (wave == 0) {
-        regs::stage_row<K>(s_st, elem_ptr<DT>(scale, b * D), n);
+        regs::stage_one_plus<K, DT>(staged, staged + planes, elem_ptr<DT>(scale, b * D), n);
         if constexpr (!FULL)
             regs::stage_row<K>(g_st, elem_ptr<DT>(g, b * D), n);
     } else {
@@ -634,14 +654,15 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
             Pack<DT> a, c, e;
             a.v = xv[k];
             c.v = uv[k];
-            e.v = FULL ? gv[FULL ? k : 0] : g_st[64 * k + lane];
+            e.v = FULL ? gv[FULL ? k : 0] : g_st[regs::staged_index<K>(k, lane, planes)];
             xv[k] = gate_add8<DT>(a, c, e).v;
         }
     }
     store_run<K, true>(elem_ptr<DT>(x_out, row), n, xv);
     float mu, rr;
     regs::row_factors<K, DT, regs::kRms>(xv, n, d_float, eps, &mu, &rr);
-    regs::apply_store_staged<K, DT, regs::kRms>(xv, s_st, h_st, n, mu, rr, elem_ptr<DT>(y, row));
+    regs::apply_store_staged<K, DT, regs::kRms>(xv, staged, staged + planes, h_st, n, mu, rr,
+                                                elem_ptr<DT>(y, row));
 }
 
 template <int K, bool FULL, int DT, int MOD>
@@ -807,9 +828,10 @@ hipError_t launch_element(const void* x, const void* u, const void* g,
     if constexpr (DT != kF32 && MOD == kModRow) {
         const int K = pick_regs_slots(ceil_div(ceil_div(D, 8), 64));
         if (K > 0) {
-            // two rows per workgroup with the realigned scale, shift (and
-            // broadcast gate) rows staged once, occupancy capped
-            const int64_t stage = (FULL ? 2 : 3) * 1024 * (int64_t)K;
+            // two rows per workgroup with 1 + scale, the shift (and a
+            // broadcast gate) row staged once (planes of ceil(D / 8)
+            // words), occupancy capped
+            const int64_t stage = (FULL ? 3 : 4) * 16 * ceil_div(D, 8);
             return hipLaunchKernel(pick_regs_staged<FULL, DT>(K),
                                    dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                    dim3(kBlock * kRowWaves), args,

@@ -167,29 +167,46 @@ __device__ __forceinline__ Pack<DT> modulate_pack(const Pack<DT>& xr, float mu, 
 // Row modulation, kRowWaves waves per workgroup, one row each: rows
 // kRowWaves * blockIdx.x + wave of batch blockIdx.y. The batch's scale and
 // shift rows are staged in the dynamic LDS as 16-byte words in memory order
-// (scale at [0, words), shift at [words, 2 words)) before any row is loaded.
+// (scale at [0, vpr), shift at [vpr, 2 vpr)) before any row is loaded.
 template <int G, int DT, int NORM, bool WHOLE>
 __device__ __forceinline__ void modulate_staged_row(
     const void* x, const void* scale, const void* shift, float eps,
     float d_float, void* out, int64_t L, int vpr)
 {
+    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
     extern __shared__ u32x4 staged[];
     const int lane = threadIdx.x & (kBlock - 1);
     const int64_t b = blockIdx.y;
     const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x / kBlock);
-    constexpr int kWords = DT == kF32 ? 2 : 1;  // 16-byte words per pack
-    const int words = vpr * kWords;
-    const u32x4* sc = static_cast<const u32x4*>(scale) + b * words;
-    const u32x4* sh = static_cast<const u32x4*>(shift) + b * words;
-    for (int w = threadIdx.x; w < words; w += kBlock * kRowWaves) {
-        staged[w] = load16(sc + w);
-        staged[words + w] = load16(sh + w);
+    // the batch's scale and shift rows, vpr <= 64 G words each: every load
+    // issued before any LDS write (one round trip to the L2, not one per
+    // word a thread stages), at most kS words of each per thread, indexes
+    // clamped and writes guarded
+    constexpr int kS = (64 * G + kBlock * kRowWaves - 1) / (kBlock * kRowWaves);
+    const u32x4* sc = static_cast<const u32x4*>(scale) + b * vpr;
+    const u32x4* sh = static_cast<const u32x4*>(shift) + b * vpr;
+    {
+        u32x4 sv[kS], hv[kS];
+#pragma unroll
+        for (int j = 0; j < kS; ++j) {
+            const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
+            const int wc = w < vpr ? w : vpr - 1;
+            sv[j] = load16(sc + wc);
+            hv[j] = load16(sh + wc);
+        }
+#pragma unroll
+        for (int j = 0; j < kS; ++j) {
+            const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
+            if (w < vpr) {
+                staged[w] = sv[j];
+                staged[vpr + w] = hv[j];
+            }
+        }
     }
     __syncthreads();
     if (r >= L)
         return;
 
-    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
     const int64_t row = (b * L + r) * vpr;
     // WHOLE (D = 512 G): every lane's G packs lie in the row, no bounds at
     // all. Otherwise no branch around a load: the index is clamped into the
@@ -210,10 +227,10 @@ __device__ __forceinline__ void modulate_staged_row(
         Pack<DT> s_, h_;
         if constexpr (WHOLE) {
             s_.v = staged[64 * i + lane];
-            h_.v = staged[words + 64 * i + lane];
+            h_.v = staged[vpr + 64 * i + lane];
         } else {
             s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
-            h_ = Grouped<DT>::lds_raw(staged + words, 64 * i, lane, h);
+            h_ = Grouped<DT>::lds_raw(staged + vpr, 64 * i, lane, h);
         }
         const Pack<DT> o = modulate_pack<DT, NORM>(xv[i], mu, rr, s_, h_);
         if constexpr (WHOLE)
@@ -653,9 +670,10 @@ __global__ __launch_bounds__(kBlock * NW) void modulate_lds_kernel(
 // to the output's offset.
 // Row modulation of 2-byte rows held in registers: kRowWaves waves per
 // workgroup, one row each (rows kRowWaves * blockIdx.x + wave of batch
-// blockIdx.y). Wave 0 realigns the batch's scale row and wave 1 its shift
-// row into the dynamic LDS (groups, 64 K words each) before any row is
-// loaded.
+// blockIdx.y). Before any row is loaded, wave 0 stages the batch's 1 + scale
+// in binary32 and wave 1 its shift row in the dynamic LDS, as groups in
+// planes of P = ceil(D / 8) words (row_regs.hpp): 1 + scale elements 0-3 at
+// [0, P), 4-7 at [P, 2P), shift at [2P, 3P).
 template <int K, int DT, int NORM>
 __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kernel(
     const void* x, const void* scale, const void* shift, float eps, float d_float,
@@ -666,9 +684,13 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kerne
     const int64_t b = blockIdx.y;
     const int64_t r = (int64_t)blockIdx.x * kRowWaves + wave;
     const int n = (int)D;
+    const int planes = (n + 7) >> 3;
     constexpr int kNorm = NORM == kNormLn ? regs::kLn : regs::kRms;
     static_assert(kRowWaves == 2, "one staged row per wave");
-    regs::stage_row<K>(staged + 64 * K * wave, elem_ptr<DT>(wave == 0 ? scale : shift, b * D), n);
+    if (wave == 0)
+        regs::stage_one_plus<K, DT>(staged, staged + planes, elem_ptr<DT>(scale, b * D), n);
+    else
+        regs::stage_row<K>(staged + 2 * planes, elem_ptr<DT>(shift, b * D), n);
     __syncthreads();
     if (r >= L)
         return;
@@ -677,8 +699,8 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kerne
     load_groups<K, true>(elem_ptr<DT>(x, row), n, xv);
     float mu, rr;
     regs::row_factors<K, DT, kNorm>(xv, n, d_float, eps, &mu, &rr);
-    regs::apply_store_staged<K, DT, kNorm>(xv, staged, staged + 64 * K, n, mu, rr,
-                                           elem_ptr<DT>(out, row));
+    regs::apply_store_staged<K, DT, kNorm>(xv, staged, staged + planes, staged + 2 * planes, n,
+                                           mu, rr, elem_ptr<DT>(out, row));
 }
 
 template <int K, int DT, int MOD, int NORM>
@@ -821,12 +843,13 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
             const int64_t slots = ceil_div(ceil_div(D, 8), 64);
             const int K = pick_regs_slots(slots);
             if (K > 0 && MOD == kModRow) {
-                // two rows per workgroup with the realigned scale and shift
-                // rows staged once (2 * 1 KB per slot), occupancy capped
+                // two rows per workgroup with 1 + scale and the shift row
+                // staged once (three planes of ceil(D / 8) words),
+                // occupancy capped
                 return hipLaunchKernel(pick_regs_staged<NORM, DT>(K),
                                        dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                        dim3(kBlock * kRowWaves), args,
-                                       (size_t)row_wg_lds(2 * D, 2 * 1024 * (int64_t)K,
+                                       (size_t)row_wg_lds(2 * D, 3 * 16 * ceil_div(D, 8),
                                                           kModRowBudget, wg_per_cu),
                                        stream);
             }

@@ -144,50 +144,80 @@ __device__ __forceinline__ void apply_store(u32x4 (&xv)[K], const void* scale, c
     store_run<K, true>(out, n, xv);
 }
 
-// One row of n elements at p realigned to groups into LDS (group g of the
-// row at dst[g], K slots: 64 K words). Rows a workgroup shares (scale, shift,
-// a broadcast gate) are staged once this way instead of realigned by every
-// wave for every row.
+// Rows a workgroup shares (scale, shift, a broadcast gate) are staged once
+// in LDS as groups instead of realigned by every wave for every row: the
+// P = ceil(n / 8) groups of a row of n elements, group g at word g of a
+// plane of P words. Slots from whole_slots<K>() on can reach past P; their
+// indexes are clamped into the plane (the groups they stand for are
+// neither summed nor stored).
+template <int K>
+__device__ __forceinline__ int staged_index(int k, int lane, int planes)
+{
+    const int i = 64 * k + lane;
+    return (k < whole_slots<K>() || i < planes) ? i : planes - 1;
+}
+
+// The groups of the row of n elements at p into the plane at dst.
 template <int K>
 __device__ __forceinline__ void stage_row(u32x4* dst, const void* p, int n)
 {
     const int lane = threadIdx.x & 63;
+    const int planes = (n + 7) >> 3;
     u32x4 g[K];
     load_groups<K, false>(p, n, g);
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        dst[64 * k + lane] = g[k];
+    for (int k = 0; k < K; ++k) {
+        const int i = 64 * k + lane;
+        if (k < whole_slots<K>() || i < planes)
+            dst[i] = g[k];
+    }
 }
 
-// apply_store with the scale and shift rows staged in LDS as groups
-// (stage_row): no per-row loads or realignment of them.
-template <int K, int DT, int NORM>
-__device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* s_lds,
-                                                   const u32x4* h_lds, int n, float mu,
-                                                   float rr, void* out)
+// 1 + scale of the row of n elements at p, in binary32 (one_plus), into
+// the planes a_lo (elements 0-3 of each group) and a_hi (4-7).
+template <int K, int DT>
+__device__ __forceinline__ void stage_one_plus(u32x4* a_lo, u32x4* a_hi, const void* p, int n)
 {
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        __asm__ volatile("" : "+v"(xv[k]));
+    const int planes = (n + 7) >> 3;
+    u32x4 g[K];
+    load_groups<K, false>(p, n, g);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        Pack<DT> xp, sp, hp;
-        xp.v = xv[k];
-        sp.v = s_lds[64 * k + lane];
-        hp.v = h_lds[64 * k + lane];
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = xp.get(e);
-            if constexpr (NORM == kLn)
-                v = v - mu;
-            const float nv = v * rr;
-            const float a = 1.0f + sp.get(e);
-            const float m = nv * a;
-            o[e] = m + hp.get(e);
+        const int i = 64 * k + lane;
+        u32x4 lo, hi;
+        one_plus<DT>(g[k], lo, hi);
+        if (k < whole_slots<K>() || i < planes) {
+            a_lo[i] = lo;
+            a_hi[i] = hi;
         }
-        xv[k] = Pack<DT>::make(o).v;
+    }
+}
+
+// apply_store with 1 + scale and the shift row staged in LDS
+// (stage_one_plus, stage_row): no per-row loads or realignment of them.
+template <int K, int DT, int NORM>
+__device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* a_lo,
+                                                   const u32x4* a_hi, const u32x4* h_lds, int n,
+                                                   float mu, float rr, void* out)
+{
+    const int lane = threadIdx.x & 63;
+    const int planes = (n + 7) >> 3;
+    // up to 9 slots the widened row fits beside the rest (one widening for
+    // the sum and the apply: 1-2 % faster at D = 4100 on MI355X); longer
+    // rows stay packed across the reduction, as in apply_store
+    if constexpr (K > 9) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            __asm__ volatile("" : "+v"(xv[k]));
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = staged_index<K>(k, lane, planes);
+        Pack<DT> xp, hp;
+        xp.v = xv[k];
+        hp.v = h_lds[i];
+        xv[k] = modulate_group<DT, NORM == kLn>(xp, mu, rr, a_lo[i], a_hi[i], hp).v;
     }
     store_run<K, true>(out, n, xv);
 }
