@@ -56,15 +56,15 @@ inline int lds_row_waves(int64_t row_bytes)
 // row_budget bytes of rows (kRowWaves per workgroup) stay on a CU: 4 to 12
 // workgroups of gfx950's 160 KB of LDS per CU, each asking for a whole
 // number of KB that leaves at least 1 KB of the CU unused (a request that
-// fills the CU exactly could leave room for one workgroup fewer). Measured
-// on MI355X: a kernel that holds a row per wave streams best with few rows
-// in flight per CU (a copy of 8 KB rows ran 175 us at full occupancy and
-// 165 us at 4-5 waves per CU, for 1.07 GB); the modulation of 8 KB rows ran
-// best at 5-6 workgroups per CU (4 slowed it on some boxes by 10-20 %), the
-// fused call at 4 (6 was 3 % slower, 3 4 % slower).
+// fills the CU exactly could leave room for one workgroup fewer). A kernel
+// that holds a row per wave streams best with few rows in flight per CU; the
+// sweeps over workgroups per CU on MI355X (the bench's occupancy ablation)
+// put the fast path's 8 KB modulation rows best at 5, the element path's
+// realigned rows at 6-8, and the fused call at 4.
 constexpr int kRowWaves = 2;
-constexpr int64_t kModRowBudget = 48 * 1024;    // rms/LayerNorm modulation
-constexpr int64_t kFusedRowBudget = 32 * 1024;  // residual update + modulation
+constexpr int64_t kModRowBudget = 40 * 1024;      // rms/LayerNorm modulation, fast path
+constexpr int64_t kModElemRowBudget = 48 * 1024;  // the same, element path
+constexpr int64_t kFusedRowBudget = 32 * 1024;    // residual update + modulation
 // wg_per_cu overrides the rule for measurement (rga_measure.h): > 0 asks
 // for that many workgroups per CU, -1 for no cap (the staging alone).
 inline int64_t row_wg_lds(int64_t row_bytes, int64_t stage_bytes, int64_t row_budget,

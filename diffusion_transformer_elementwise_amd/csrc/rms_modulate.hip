@@ -850,7 +850,7 @@ hipError_t launch_typed(const void* x, const void* scale, const void* shift,
                                        dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                        dim3(kBlock * kRowWaves), args,
                                        (size_t)row_wg_lds(2 * D, 3 * 16 * ceil_div(D, 8),
-                                                          kModRowBudget, wg_per_cu),
+                                                          kModElemRowBudget, wg_per_cu),
                                        stream);
             }
             const void* rk = pick_regs<NORM, DT, MOD>(slots);
