@@ -372,6 +372,9 @@ def main():
         ablations["occupancy"] = run_occupancy(dte, torch, dev, d4, cold_times, hev, stream,
                                                args.cold_reps, log)
         torch.cuda.empty_cache()
+        ablations["schedules"] = run_schedules(dte, torch, dev, d4, cold_times, hev, stream,
+                                               args.cold_reps, log)
+        torch.cuda.empty_cache()
 
     fused = {}
     if args.fused_reps > 0:
@@ -580,6 +583,68 @@ def run_occupancy(dte, torch, dev, d4, cold_times, hev, stream, reps, log):
                             "after_c4_us": round(pair, 2)}
                 log(f"occupancy {key}: cold {med:.2f} us, after c4 {pair:.2f} us")
         del x, u, g, s, t, y, xo
+    return out
+
+
+SCHEDULES = ("library", "loads_first", "one_plus", "two_rows", "prefetch")
+
+
+def run_schedules(dte, torch, dev, d4, cold_times, hev, stream, reps, log):
+    """The staged row-modulation kernels in each schedule (rga_modulate_variant,
+    rga_fused_variant; SCHED_* in order): the modulation and the fused call
+    (broadcast gate, out of place) at [2,32640,4096] bf16. Cold calls (after
+    a 1 GiB cache-allocating read) taken in rounds that visit every schedule
+    once, so drift over the run touches all alike; the median per schedule.
+    Then right after the c4 gate-add (mean of 10 pairs, HIP events)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4343)
+    B, L, D = 2, 32640, 4096
+
+    def draw(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+
+    x, u = draw((B, L, D), 2.0), draw((B, L, D), 1.0)
+    g, sc, sh = draw((B, 1, D), 0.1), draw((B, 1, D), 0.1), draw((B, 1, D), 0.1)
+    y, xo = torch.empty_like(x), torch.empty_like(x)
+    mb = (2 * B * L * D + 2 * B * D) * 2
+    fb = (4 * B * L * D + 3 * B * D) * 2
+
+    def modulation(k):
+        return lambda: dte.modulate_variant(x, sc, sh, 1e-6, out=y, schedule=k)
+
+    def fused(k):
+        return lambda: dte.fused_variant(x, u, g, sc, sh, 1e-6, x_out=xo, y=y, schedule=k)
+
+    calls = []
+    for k, name in enumerate(SCHEDULES):
+        calls.append((f"rms_modulate [2,32640,4096] schedule={name}", mb, modulation(k)))
+        calls.append((f"fused bcast [2,32640,4096] schedule={name}", fb, fused(k)))
+    times = {n: [] for n, _, _ in calls}
+    for _, _, fn in calls:
+        fn()
+    for _ in range(reps):
+        for n, _, fn in calls:
+            times[n] += cold_times(fn, 1)
+
+    def after_c4(fn):
+        evs = [(hev.new(), hev.new()) for _ in range(10)]
+        for a, b in evs:
+            dte.rga_residual_gate_add(d4["x"], d4["u"], d4["g"], out=d4["x"], gate_mode=1)
+            hev.record(a, stream)
+            fn()
+            hev.record(b, stream)
+        torch.cuda.synchronize()
+        return statistics.mean(hev.ms(a, b) * 1e3 for a, b in evs)
+
+    out = {}
+    for n, nbytes, fn in calls:
+        med = statistics.median(times[n])
+        pair = after_c4(fn)
+        out[n] = {"bytes": nbytes, "cold_us_median": round(med, 2),
+                  "cold_frac_of_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "after_c4_us": round(pair, 2)}
+        log(f"schedule {n}: cold {med:.2f} us, after c4 {pair:.2f} us")
+    del x, u, y, xo
     return out
 
 
@@ -1061,6 +1126,15 @@ def known_launches():
             ("copy 1 GiB", "copy_kernel", FLUSH_BYTES // 16, 2 * FLUSH_BYTES),
             ("flush read 1 GiB", "read_kernel", 256 * 1024, FLUSH_BYTES)):
         out.append((label, k, n16 if k != "read_kernel" else n16, 1, nbytes, 0))
+    for k, name in enumerate(SCHEDULES):
+        rows = 2 * (2 if k >= 3 else 1)  # rows per workgroup
+        gx = cdiv(32640, rows) * 128
+        out.append((f"schedule {name}: rms_modulate [2,32640,4096]",
+                    f"rms_modulate_variant_kernel<{k}>", gx, 2,
+                    (2 * 2 * 32640 * 4096 + 2 * 2 * 4096) * 2, 2 * 32640 * 4096))
+        out.append((f"schedule {name}: fused bcast [2,32640,4096]",
+                    f"gate_add_rms_modulate_variant_kernel<{k}>", gx, 2,
+                    (4 * 2 * 32640 * 4096 + 3 * 2 * 4096) * 2, 2 * 32640 * 4096))
     for T in (1, 2, 4, 8):
         for sp, pname in ((0, "nt"), (1, "plain"), (2, "device")):
             out.append((f"ablation c4 bcast, {T} rows/wave, store {pname}",

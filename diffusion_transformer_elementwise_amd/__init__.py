@@ -33,9 +33,10 @@ The FFN's tanh-GELU, any storage type, over the last dimension F:
 
 Measurement helpers (include/rga_measure.h): copy_, fill_, read_ (cache
 flush), stream_ (read:write mix ceilings), gate_add_variant (the
-broadcast-gate add in the shapes the library does not use), and
+broadcast-gate add in the shapes the library does not use),
 modulate_occupancy / fused_occupancy (the row-modulation kernels at a chosen
-number of workgroups per CU).
+number of workgroups per CU) and modulate_variant / fused_variant (those
+kernels in other schedules, SCHED_*).
 """
 from __future__ import annotations
 
@@ -53,6 +54,11 @@ from ._lib import (  # noqa: F401
     RGA_ERR_UNSUPPORTED,
     RGA_OK,
     RGA_RMS_MAX_D,
+    SCHED_LIBRARY,
+    SCHED_LOADS_FIRST,
+    SCHED_ONE_PLUS,
+    SCHED_PREFETCH,
+    SCHED_TWO_ROWS,
     STORE_DEVICE,
     STORE_NT,
     STORE_PLAIN,
@@ -63,9 +69,11 @@ from ._lib import (  # noqa: F401
     check_residual_gate_add_ex,
     check_rms_modulate,
     check_fused_occupancy,
+    check_fused_variant,
     check_gate_add_variant,
     check_gelu_tanh,
     check_modulate_occupancy,
+    check_modulate_variant,
     check_stream,
     check_ln_modulate,
     check_rms_modulate_ex,
@@ -77,8 +85,10 @@ from .ops import (  # noqa: F401
     copy_,
     fill_,
     fused_occupancy,
+    fused_variant,
     gate_add_variant,
     modulate_occupancy,
+    modulate_variant,
     stream_,
     gelu_tanh,
     read_,

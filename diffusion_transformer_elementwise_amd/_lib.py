@@ -42,6 +42,12 @@ STORE_NT = 0
 STORE_PLAIN = 1
 STORE_DEVICE = 2
 
+SCHED_LIBRARY = 0
+SCHED_LOADS_FIRST = 1
+SCHED_ONE_PLUS = 2
+SCHED_TWO_ROWS = 3
+SCHED_PREFETCH = 4
+
 
 class RGAError(RuntimeError):
     def __init__(self, status: int, call: str):
@@ -124,6 +130,14 @@ def _load():
     lib.rga_check_fused_occupancy.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32, i32,
                                               i32]
     lib.rga_check_fused_occupancy.restype = i32
+    lib.rga_modulate_variant.argtypes = [p, p, p, f32, p, i64, i64, i64, i32, p]
+    lib.rga_modulate_variant.restype = i32
+    lib.rga_check_modulate_variant.argtypes = [p, p, p, f32, p, i64, i64, i64, i32]
+    lib.rga_check_modulate_variant.restype = i32
+    lib.rga_fused_variant.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32, p]
+    lib.rga_fused_variant.restype = i32
+    lib.rga_check_fused_variant.argtypes = [p, p, p, p, p, f32, p, p, i64, i64, i64, i32]
+    lib.rga_check_fused_variant.restype = i32
     return lib
 
 
@@ -204,3 +218,12 @@ def check_fused_occupancy(x, u, g, scale, shift, eps, x_out, y, B, L, D, gate_mo
                           wg_per_cu) -> int:
     return _LIB.rga_check_fused_occupancy(x, u, g, scale, shift, eps, x_out, y, B, L, D,
                                           gate_mode, dtype, wg_per_cu)
+
+
+def check_modulate_variant(x, scale, shift, eps, out, B, L, D, schedule) -> int:
+    return _LIB.rga_check_modulate_variant(x, scale, shift, eps, out, B, L, D, schedule)
+
+
+def check_fused_variant(x, u, g, scale, shift, eps, x_out, y, B, L, D, schedule) -> int:
+    return _LIB.rga_check_fused_variant(x, u, g, scale, shift, eps, x_out, y, B, L, D,
+                                        schedule)

@@ -652,6 +652,69 @@ int rga_fused_occupancy(const void* x, const void* u, const void* g, const void*
                                                       stream, wg_per_cu));
 }
 
+static int check_modulate_variant(const void* x, const void* scale, const void* shift,
+                                  float eps, const void* out, int64_t B, int64_t L, int64_t D,
+                                  int schedule)
+{
+    if (schedule < 0 || schedule >= rga::kSchedCount)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    const int st = check_rms(x, scale, shift, eps, out, B, L, D, RGA_MOD_ROW, RGA_DTYPE_BF16,
+                             true, &fast);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return D == rga::kSchedD ? RGA_OK : RGA_ERR_UNSUPPORTED;
+}
+
+int rga_check_modulate_variant(const void* x, const void* scale, const void* shift, float eps,
+                               const void* out, int64_t B, int64_t L, int64_t D, int schedule)
+{
+    return check_modulate_variant(x, scale, shift, eps, out, B, L, D, schedule);
+}
+
+int rga_modulate_variant(const void* x, const void* scale, const void* shift, float eps,
+                         void* out, int64_t B, int64_t L, int64_t D, int schedule,
+                         hipStream_t stream)
+{
+    const int st = check_modulate_variant(x, scale, shift, eps, out, B, L, D, schedule);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return launched(rga::launch_modulate_variant(x, scale, shift, eps, out, B, L, schedule,
+                                                 stream));
+}
+
+static int check_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                               const void* shift, float eps, const void* x_out, const void* y,
+                               int64_t B, int64_t L, int64_t D, int schedule)
+{
+    if (schedule < 0 || schedule >= rga::kSchedCount)
+        return RGA_ERR_INVALID_ARG;
+    bool fast = false;
+    const int st = check_fused(x, u, g, scale, shift, eps, x_out, y, B, L, D, RGA_GATE_BCAST,
+                               RGA_MOD_ROW, RGA_DTYPE_BF16, true, &fast);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return D == rga::kSchedD ? RGA_OK : RGA_ERR_UNSUPPORTED;
+}
+
+int rga_check_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                            const void* shift, float eps, const void* x_out, const void* y,
+                            int64_t B, int64_t L, int64_t D, int schedule)
+{
+    return check_fused_variant(x, u, g, scale, shift, eps, x_out, y, B, L, D, schedule);
+}
+
+int rga_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                      const void* shift, float eps, void* x_out, void* y, int64_t B, int64_t L,
+                      int64_t D, int schedule, hipStream_t stream)
+{
+    const int st = check_fused_variant(x, u, g, scale, shift, eps, x_out, y, B, L, D, schedule);
+    if (st != RGA_OK || B == 0 || L == 0 || D == 0)
+        return st;
+    return launched(rga::launch_fused_variant(x, u, g, scale, shift, eps, x_out, y, B, L,
+                                              schedule, stream));
+}
+
 const char* rga_status_string(int status)
 {
     switch (status) {

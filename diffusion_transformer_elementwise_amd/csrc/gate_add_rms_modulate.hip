@@ -181,37 +181,69 @@ __device__ __forceinline__ float wave_sum_dpp(float a)
     return (r0 + r1) + (r2 + r3);
 }
 
-// Row modulation, kRowWaves waves per workgroup, one row each: rows
-// kRowWaves * blockIdx.x + wave of batch blockIdx.y. The dynamic LDS holds
-// the batch's scale row at [0, vpr), its shift row at [vpr, 2 vpr) and,
-// with a broadcast gate, its gate row at [2 vpr, 3 vpr), as 16-byte words
-// in memory order. Lanes past the row end hold zeros (x' = +0 there, which
-// adds +0 to the partial) and store nothing.
+// Row modulation, kRowWaves waves per workgroup, sched_rows_per_wave(SCHED)
+// rows per wave (launch.hpp; the library runs kSchedLibrary, one row per
+// wave): rows kRowWaves * (R * blockIdx.x + j) + wave, j < R, of batch
+// blockIdx.y. The dynamic LDS holds the batch's scale row at [0, vpr), its
+// shift row at [vpr, 2 vpr) and, with a broadcast gate, its gate row at
+// [2 vpr, 3 vpr), as 16-byte words in memory order; with kSchedOnePlus,
+// 1 + scale in binary32 at [0, 2 vpr) (one_plus: elements 0-3, then 4-7 of
+// each pack) and the shift and gate rows one plane further on. Lanes past
+// the row end hold zeros (x' = +0 there, which adds +0 to the partial) and
+// store nothing.
 // WHOLE: D = 512 G (every lane's packs lie in the row): no bounds at all.
-template <int G, bool FULL, int DT, bool WHOLE>
-__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_staged_kernel(
+template <int G, bool FULL, int DT, bool WHOLE, int SCHED>
+__device__ __forceinline__ void fused_staged_rows(
     const void* x, const void* u, const void* g, const void* scale,
     const void* shift, float eps, float d_float, void* x_out, void* y,
     int64_t L, int vpr)
 {
     static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
+    constexpr int R = sched_rows_per_wave(SCHED);
+    constexpr bool kOnePlus = SCHED == kSchedOnePlus;
     extern __shared__ u32x4 staged[];
     const int lane = threadIdx.x & (kBlock - 1);
     const int64_t b = blockIdx.y;
-    const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x / kBlock);
+    const int64_t r0 = (int64_t)blockIdx.x * kRowWaves * R + (threadIdx.x / kBlock);
     using GP = Grouped<DT>;
+    u32x4* s_st = staged;
+    u32x4* h_st = staged + (kOnePlus ? 2 : 1) * vpr;
+    u32x4* g_st = staged + (kOnePlus ? 3 : 2) * vpr;
+
+    auto load_row = [&](Pack<DT> (&xv)[G], Pack<DT> (&uv)[G], Pack<DT> (&gv)[FULL ? G : 1],
+                        int64_t row) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int h = vpr - 64 * i;
+            if constexpr (WHOLE) {
+                xv[i] = Pack<DT>::load_stream(x, row + 64 * i + lane);
+                uv[i] = Pack<DT>::load_stream(u, row + 64 * i + lane);
+                if constexpr (FULL)
+                    gv[i] = Pack<DT>::load_stream(g, row + 64 * i + lane);
+            } else {
+                xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
+                uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
+                if constexpr (FULL)
+                    gv[i] = GP::template load_clamped<true>(g, row + 64 * i, lane, h);
+            }
+        }
+    };
+
+    Pack<DT> xv[G], uv[G], gv[FULL ? G : 1];
+    if constexpr (SCHED == kSchedLoadsFirst) {
+        // a wave past the last row (odd L) loads the last row and stores
+        // nothing
+        load_row(xv, uv, gv, (b * L + (r0 < L ? r0 : L - 1)) * vpr);
+    }
     // the batch's rows, vpr <= 64 G words each: every load issued before any
     // LDS write (one round trip to the L2, not one per word a thread
     // stages), at most kS words of each per thread, indexes clamped and
     // writes guarded
-    u32x4* s_st = staged;
-    u32x4* h_st = staged + vpr;
-    u32x4* g_st = staged + 2 * vpr;
-    constexpr int kS = (64 * G + kBlock * kRowWaves - 1) / (kBlock * kRowWaves);
-    const u32x4* sc = static_cast<const u32x4*>(scale) + b * vpr;
-    const u32x4* sh = static_cast<const u32x4*>(shift) + b * vpr;
-    const u32x4* gr = static_cast<const u32x4*>(g) + b * vpr;
     {
+        constexpr int kS = (64 * G + kBlock * kRowWaves - 1) / (kBlock * kRowWaves);
+        const u32x4* sc = static_cast<const u32x4*>(scale) + b * vpr;
+        const u32x4* sh = static_cast<const u32x4*>(shift) + b * vpr;
+        const u32x4* gr = static_cast<const u32x4*>(g) + b * vpr;
         u32x4 sv[kS], hv[kS], bv[FULL ? 1 : kS];
 #pragma unroll
         for (int j = 0; j < kS; ++j) {
@@ -226,7 +258,14 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_stag
         for (int j = 0; j < kS; ++j) {
             const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
             if (w < vpr) {
-                s_st[w] = sv[j];
+                if constexpr (kOnePlus) {
+                    u32x4 lo, hi;
+                    one_plus<DT>(sv[j], lo, hi);
+                    s_st[w] = lo;
+                    s_st[vpr + w] = hi;
+                } else {
+                    s_st[w] = sv[j];
+                }
                 h_st[w] = hv[j];
                 if constexpr (!FULL)
                     g_st[w] = bv[FULL ? 0 : j];
@@ -234,83 +273,129 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_stag
         }
     }
     __syncthreads();
-    if (r >= L)
+    if (r0 >= L)
         return;
+    if constexpr (SCHED != kSchedLoadsFirst)
+        load_row(xv, uv, gv, (b * L + r0) * vpr);
 
-    const int64_t row = (b * L + r) * vpr;
-    Pack<DT> xv[G], uv[G], gv[FULL ? G : 1];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const int h = vpr - 64 * i;
-        if constexpr (WHOLE) {
-            xv[i] = Pack<DT>::load_stream(x, row + 64 * i + lane);
-            uv[i] = Pack<DT>::load_stream(u, row + 64 * i + lane);
+    for (int j = 0; j < R; ++j) {
+        const int64_t r = r0 + (int64_t)kRowWaves * j;
+        const int64_t row = (b * L + r) * vpr;
+        const bool more = j + 1 < R && r + kRowWaves < L;
+        constexpr int kQ = SCHED == kSchedPrefetch ? G : 1;
+        Pack<DT> xq[kQ], uq[kQ], gq[FULL ? kQ : 1];
+        if constexpr (SCHED == kSchedPrefetch)
+            if (more)
+                load_row(xq, uq, gq, row + (int64_t)kRowWaves * vpr);
+
+        Pack<DT> xn[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int h = vpr - 64 * i;
+            Pack<DT> gi;
             if constexpr (FULL)
-                gv[i] = Pack<DT>::load_stream(g, row + 64 * i + lane);
-        } else {
-            xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
-            uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
-            if constexpr (FULL)
-                gv[i] = GP::template load_clamped<true>(g, row + 64 * i, lane, h);
+                gi = gv[FULL ? i : 0];
+            else if constexpr (WHOLE)
+                gi.v = g_st[64 * i + lane];
+            else
+                gi = GP::lds_raw(g_st, 64 * i, lane, h);
+            const Pack<DT> xr = gate_add8<DT>(xv[i], uv[i], gi);
+            if constexpr (WHOLE)
+                xr.store_stream(x_out, row + 64 * i + lane);
+            else
+                GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
+            xn[i] = xr;
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = xn[i].get(e);
+                const float sa = a * a;
+                acc = acc + sa;
+            }
+        }
+        const float ms = wave_sum_dpp(acc) / d_float;
+        const float t = ms + eps;
+        const float q = sqrtf(t);
+        const float rr = 1.0f / q;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int h = vpr - 64 * i;
+            Pack<DT> o;
+            if constexpr (kOnePlus) {
+                // past the row end the index is clamped into it: not stored
+                const int p = WHOLE ? 64 * i + lane
+                                    : (64 * i + lane < vpr ? 64 * i + lane : vpr - 1);
+                Pack<DT> h_;
+                h_.v = h_st[p];
+                o = modulate_group<DT, false>(xn[i], 0.0f, rr, s_st[p], s_st[vpr + p], h_);
+            } else {
+                Pack<DT> s_, h_;
+                if constexpr (WHOLE) {
+                    s_.v = s_st[64 * i + lane];
+                    h_.v = h_st[64 * i + lane];
+                } else {
+                    s_ = GP::lds_raw(s_st, 64 * i, lane, h);
+                    h_ = GP::lds_raw(h_st, 64 * i, lane, h);
+                }
+                float of[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float n = xn[i].get(e) * rr;
+                    const float a = 1.0f + s_.get(e);
+                    const float m = n * a;
+                    of[e] = m + h_.get(e);
+                }
+                o = Pack<DT>::make(of);
+            }
+            if constexpr (WHOLE)
+                o.store_stream(y, row + 64 * i + lane);
+            else
+                GP::store_stream_raw(o, y, row + 64 * i, lane, h);
+        }
+
+        if (j + 1 < R) {
+            if (!more)
+                return;
+            if constexpr (SCHED == kSchedPrefetch) {
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    xv[i] = xq[i];
+                    uv[i] = uq[i];
+                    if constexpr (FULL)
+                        gv[FULL ? i : 0] = gq[FULL ? i : 0];
+                }
+            } else {
+                load_row(xv, uv, gv, row + (int64_t)kRowWaves * vpr);
+            }
         }
     }
-    Pack<DT> xn[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const int h = vpr - 64 * i;
-        Pack<DT> gi;
-        if constexpr (FULL)
-            gi = gv[FULL ? i : 0];
-        else if constexpr (WHOLE)
-            gi.v = g_st[64 * i + lane];
-        else
-            gi = GP::lds_raw(g_st, 64 * i, lane, h);
-        const Pack<DT> xr = gate_add8<DT>(xv[i], uv[i], gi);
-        if constexpr (WHOLE)
-            xr.store_stream(x_out, row + 64 * i + lane);
-        else
-            GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
-        xn[i] = xr;
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float a = xn[i].get(e);
-            const float sa = a * a;
-            acc = acc + sa;
-        }
-    }
-    const float ms = wave_sum_dpp(acc) / d_float;
-    const float t = ms + eps;
-    const float q = sqrtf(t);
-    const float rr = 1.0f / q;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const int h = vpr - 64 * i;
-        const Pack<DT>& xr = xn[i];
-        Pack<DT> s_, h_;
-        if constexpr (WHOLE) {
-            s_.v = s_st[64 * i + lane];
-            h_.v = h_st[64 * i + lane];
-        } else {
-            s_ = GP::lds_raw(s_st, 64 * i, lane, h);
-            h_ = GP::lds_raw(h_st, 64 * i, lane, h);
-        }
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float n = xr.get(e) * rr;
-            const float a = 1.0f + s_.get(e);
-            const float m = n * a;
-            o[e] = m + h_.get(e);
-        }
-        if constexpr (WHOLE)
-            Pack<DT>::make(o).store_stream(y, row + 64 * i + lane);
-        else
-            GP::store_stream_raw(Pack<DT>::make(o), y, row + 64 * i, lane, h);
-    }
+}
+
+template <int G, bool FULL, int DT, bool WHOLE>
+__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_staged_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int vpr)
+{
+    fused_staged_rows<G, FULL, DT, WHOLE, kSchedLibrary>(x, u, g, scale, shift, eps, d_float,
+                                                         x_out, y, L, vpr);
+}
+
+// The staged fused call in schedule SCHED (kSched*, launch.hpp), for
+// measurement: bf16 rows of kSchedD = 4096 elements (G = 8, whole rows),
+// broadcast gate, row modulation.
+template <int SCHED>
+__global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_variant_kernel(
+    const void* x, const void* u, const void* g, const void* scale,
+    const void* shift, float eps, float d_float, void* x_out, void* y,
+    int64_t L, int vpr)
+{
+    fused_staged_rows<8, false, kBF16, true, SCHED>(x, u, g, scale, shift, eps, d_float, x_out,
+                                                    y, L, vpr);
 }
 
 template <int DT>
@@ -932,6 +1017,32 @@ bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bo
     const bool lds = !fast && !regs && row_lds_bytes(D, es) <= kMaxRowLds;
     const int64_t wg = lds ? kBlock * lds_row_waves(D * es) : kBlock;
     return L <= (((int64_t)1 << 32) - 1) / wg;
+}
+
+hipError_t launch_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                                const void* shift, float eps, void* x_out, void* y, int64_t B,
+                                int64_t L, int sched, hipStream_t stream)
+{
+    static_assert(kSchedD == 512 * 8, "whole rows of 8 packs per lane");
+    const void* k = nullptr;
+    switch (sched) {
+    case kSchedLibrary: k = reinterpret_cast<const void*>(&gate_add_rms_modulate_variant_kernel<kSchedLibrary>); break;
+    case kSchedLoadsFirst: k = reinterpret_cast<const void*>(&gate_add_rms_modulate_variant_kernel<kSchedLoadsFirst>); break;
+    case kSchedOnePlus: k = reinterpret_cast<const void*>(&gate_add_rms_modulate_variant_kernel<kSchedOnePlus>); break;
+    case kSchedTwoRows: k = reinterpret_cast<const void*>(&gate_add_rms_modulate_variant_kernel<kSchedTwoRows>); break;
+    case kSchedPrefetch: k = reinterpret_cast<const void*>(&gate_add_rms_modulate_variant_kernel<kSchedPrefetch>); break;
+    default: return hipErrorInvalidValue;
+    }
+    float d_float = (float)kSchedD;
+    int vpr = (int)(kSchedD / 8);
+    void* args[] = {&x, &u, &g, &scale, &shift, &eps, &d_float, &x_out, &y, &L, &vpr};
+    const int64_t row_bytes = kSchedD * 2;
+    // scale (two planes with kSchedOnePlus), shift and gate rows
+    const int64_t stage = (sched == kSchedOnePlus ? 4 : 3) * row_bytes;
+    return hipLaunchKernel(
+        k, dim3((uint32_t)ceil_div(L, kRowWaves * sched_rows_per_wave(sched)), (uint32_t)B),
+        dim3(kBlock * kRowWaves), args, (size_t)row_wg_lds(row_bytes, stage, kFusedRowBudget, 0),
+        stream);
 }
 
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,

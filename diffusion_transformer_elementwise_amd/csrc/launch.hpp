@@ -85,6 +85,38 @@ inline int64_t row_wg_lds(int64_t row_bytes, int64_t stage_bytes, int64_t row_bu
 // the other kernels
 constexpr int64_t kMaxStagedLds = 64 * 1024;
 
+// Schedules of the row-modulation kernels that stage the batch's rows in
+// LDS (the values of the RGA_SCHED_* measurement constants). The library
+// runs kSchedLibrary; the others are kept for measurement
+// (rga_modulate_variant, rga_fused_variant), each the same arithmetic and
+// the same results in another schedule:
+//   kSchedLoadsFirst  the row's loads go out before the staging loads (the
+//                     modulation also reduces before the workgroup barrier)
+//   kSchedOnePlus     1 + scale staged widened to binary32 (two planes)
+//                     beside the shift row: no widening or add per element
+//   kSchedTwoRows     two rows per wave, one after the other
+//   kSchedPrefetch    two rows per wave; the second row's loads go out
+//                     before the first row is worked on
+enum : int {
+    kSchedLibrary = 0,
+    kSchedLoadsFirst = 1,
+    kSchedOnePlus = 2,
+    kSchedTwoRows = 3,
+    kSchedPrefetch = 4,
+    kSchedCount = 5
+};
+
+constexpr int sched_rows_per_wave(int sched) { return sched >= kSchedTwoRows ? 2 : 1; }
+
+// the measurement variants run the workload's rows: bf16, D = 4096
+constexpr int64_t kSchedD = 4096;
+hipError_t launch_modulate_variant(const void* x, const void* scale, const void* shift,
+                                   float eps, void* out, int64_t B, int64_t L, int sched,
+                                   hipStream_t stream);
+hipError_t launch_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                                const void* shift, float eps, void* x_out, void* y, int64_t B,
+                                int64_t L, int sched, hipStream_t stream);
+
 // residual update then modulation, one pass (gate_add_rms_modulate.hip)
 bool gate_add_rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast);
 hipError_t launch_gate_add_rms_modulate(const void* x, const void* u,

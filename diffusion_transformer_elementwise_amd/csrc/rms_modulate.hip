@@ -164,79 +164,139 @@ __device__ __forceinline__ Pack<DT> modulate_pack(const Pack<DT>& xr, float mu, 
     return Pack<DT>::make(o);
 }
 
-// Row modulation, kRowWaves waves per workgroup, one row each: rows
-// kRowWaves * blockIdx.x + wave of batch blockIdx.y. The batch's scale and
-// shift rows are staged in the dynamic LDS as 16-byte words in memory order
-// (scale at [0, vpr), shift at [vpr, 2 vpr)) before any row is loaded.
-template <int G, int DT, int NORM, bool WHOLE>
-__device__ __forceinline__ void modulate_staged_row(
-    const void* x, const void* scale, const void* shift, float eps,
-    float d_float, void* out, int64_t L, int vpr)
+// 16-byte LDS words per pack of the row
+constexpr int staged_words_per_pack(int var) { return var == kSchedOnePlus ? 3 : 2; }
+
+// The batch's scale and shift rows (vpr <= 64 G words each) into the
+// dynamic LDS: every load issued before any LDS write (one round trip to the
+// L2, not one per word a thread stages), at most kS words of each per
+// thread, indexes clamped and writes guarded. As stored at [0, vpr) and
+// [vpr, 2 vpr); with ONE_PLUS, 1 + scale at [0, 2 vpr) (elements 0-3, then
+// 4-7 of each pack) and the shift row at [2 vpr, 3 vpr).
+template <int G, int DT, bool ONE_PLUS>
+__device__ __forceinline__ void stage_scale_shift(u32x4* staged, const u32x4* sc,
+                                                  const u32x4* sh, int vpr)
 {
-    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
-    extern __shared__ u32x4 staged[];
-    const int lane = threadIdx.x & (kBlock - 1);
-    const int64_t b = blockIdx.y;
-    const int64_t r = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x / kBlock);
-    // the batch's scale and shift rows, vpr <= 64 G words each: every load
-    // issued before any LDS write (one round trip to the L2, not one per
-    // word a thread stages), at most kS words of each per thread, indexes
-    // clamped and writes guarded
     constexpr int kS = (64 * G + kBlock * kRowWaves - 1) / (kBlock * kRowWaves);
-    const u32x4* sc = static_cast<const u32x4*>(scale) + b * vpr;
-    const u32x4* sh = static_cast<const u32x4*>(shift) + b * vpr;
-    {
-        u32x4 sv[kS], hv[kS];
+    u32x4 sv[kS], hv[kS];
 #pragma unroll
-        for (int j = 0; j < kS; ++j) {
-            const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
-            const int wc = w < vpr ? w : vpr - 1;
-            sv[j] = load16(sc + wc);
-            hv[j] = load16(sh + wc);
-        }
+    for (int j = 0; j < kS; ++j) {
+        const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
+        const int wc = w < vpr ? w : vpr - 1;
+        sv[j] = load16(sc + wc);
+        hv[j] = load16(sh + wc);
+    }
 #pragma unroll
-        for (int j = 0; j < kS; ++j) {
-            const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
-            if (w < vpr) {
+    for (int j = 0; j < kS; ++j) {
+        const int w = (int)threadIdx.x + kBlock * kRowWaves * j;
+        if (w < vpr) {
+            if constexpr (ONE_PLUS) {
+                u32x4 lo, hi;
+                one_plus<DT>(sv[j], lo, hi);
+                staged[w] = lo;
+                staged[vpr + w] = hi;
+                staged[2 * vpr + w] = hv[j];
+            } else {
                 staged[w] = sv[j];
                 staged[vpr + w] = hv[j];
             }
         }
     }
-    __syncthreads();
-    if (r >= L)
-        return;
+}
 
-    const int64_t row = (b * L + r) * vpr;
+// Row modulation, kRowWaves waves per workgroup, sched_rows_per_wave(VAR)
+// rows per wave: rows kRowWaves * (R * blockIdx.x + j) + wave, j < R, of
+// batch blockIdx.y. The batch's scale and shift rows are staged in the
+// dynamic LDS (stage_scale_shift) before any row is loaded.
+template <int G, int DT, int NORM, bool WHOLE, int VAR = kSchedLibrary>
+__device__ __forceinline__ void modulate_staged_row(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
+{
+    static_assert(DT != kF32, "2-byte rows: a pack is one word, raw order is group order");
+    constexpr int R = sched_rows_per_wave(VAR);
+    constexpr bool kOnePlus = VAR == kSchedOnePlus;
+    extern __shared__ u32x4 staged[];
+    const int lane = threadIdx.x & (kBlock - 1);
+    const int64_t b = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * kRowWaves * R + (threadIdx.x / kBlock);
     // WHOLE (D = 512 G): every lane's G packs lie in the row, no bounds at
     // all. Otherwise no branch around a load: the index is clamped into the
     // row and zeros are selected past its end (a branch per load made the
     // compiler wait for each load before issuing the next).
+    auto load_row = [&](Pack<DT> (&xv)[G], int64_t row) {
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            xv[i] = WHOLE ? Pack<DT>::load_stream(x, row + 64 * i + lane)
+                          : Grouped<DT>::template load_clamped<true>(x, row + 64 * i, lane,
+                                                                     vpr - 64 * i);
+    };
     Pack<DT> xv[G];
+    float mu = 0.0f, rr = 0.0f;
+    if constexpr (VAR == kSchedLoadsFirst) {
+        // a wave past the last row (odd L) loads the last row and stores
+        // nothing
+        load_row(xv, (b * L + (r0 < L ? r0 : L - 1)) * vpr);
+    }
+    stage_scale_shift<G, DT, kOnePlus>(staged, static_cast<const u32x4*>(scale) + b * vpr,
+                                       static_cast<const u32x4*>(shift) + b * vpr, vpr);
+    if constexpr (VAR == kSchedLoadsFirst)
+        rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
+    __syncthreads();
+    if (r0 >= L)
+        return;
+    if constexpr (VAR != kSchedLoadsFirst)
+        load_row(xv, (b * L + r0) * vpr);
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-        xv[i] = WHOLE ? Pack<DT>::load_stream(x, row + 64 * i + lane)
-                      : Grouped<DT>::template load_clamped<true>(x, row + 64 * i, lane,
-                                                                 vpr - 64 * i);
-    float mu;
-    const float rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
-    // element-wise; packs past the row end are not stored
+    for (int j = 0; j < R; ++j) {
+        const int64_t r = r0 + (int64_t)kRowWaves * j;
+        const int64_t row = (b * L + r) * vpr;
+        const bool more = j + 1 < R && r + kRowWaves < L;
+        Pack<DT> xq[VAR == kSchedPrefetch ? G : 1];
+        if constexpr (VAR == kSchedPrefetch)
+            if (more)
+                load_row(xq, row + (int64_t)kRowWaves * vpr);
+        if constexpr (VAR != kSchedLoadsFirst)
+            rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
+        // element-wise; packs past the row end are not stored
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const int h = vpr - 64 * i;
-        Pack<DT> s_, h_;
-        if constexpr (WHOLE) {
-            s_.v = staged[64 * i + lane];
-            h_.v = staged[vpr + 64 * i + lane];
-        } else {
-            s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
-            h_ = Grouped<DT>::lds_raw(staged + vpr, 64 * i, lane, h);
+        for (int i = 0; i < G; ++i) {
+            const int h = vpr - 64 * i;
+            Pack<DT> o;
+            if constexpr (kOnePlus) {
+                const int p = WHOLE ? 64 * i + lane
+                                    : (64 * i + lane < vpr ? 64 * i + lane : vpr - 1);
+                Pack<DT> h_;
+                h_.v = staged[2 * vpr + p];
+                o = modulate_group<DT, NORM == kNormLn>(xv[i], mu, rr, staged[p],
+                                                        staged[vpr + p], h_);
+            } else {
+                Pack<DT> s_, h_;
+                if constexpr (WHOLE) {
+                    s_.v = staged[64 * i + lane];
+                    h_.v = staged[vpr + 64 * i + lane];
+                } else {
+                    s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
+                    h_ = Grouped<DT>::lds_raw(staged + vpr, 64 * i, lane, h);
+                }
+                o = modulate_pack<DT, NORM>(xv[i], mu, rr, s_, h_);
+            }
+            if constexpr (WHOLE)
+                o.store_stream(out, row + 64 * i + lane);
+            else
+                Grouped<DT>::store_stream_raw(o, out, row + 64 * i, lane, h);
         }
-        const Pack<DT> o = modulate_pack<DT, NORM>(xv[i], mu, rr, s_, h_);
-        if constexpr (WHOLE)
-            o.store_stream(out, row + 64 * i + lane);
-        else
-            Grouped<DT>::store_stream_raw(o, out, row + 64 * i, lane, h);
+        if (j + 1 < R) {
+            if (!more)
+                return;
+            if constexpr (VAR == kSchedPrefetch) {
+#pragma unroll
+                for (int i = 0; i < G; ++i)
+                    xv[i] = xq[i];
+            } else {
+                load_row(xv, row + (int64_t)kRowWaves * vpr);
+            }
+        }
     }
 }
 
@@ -332,6 +392,18 @@ __global__ __launch_bounds__((staged_rows<DT, MOD>() ? kBlock * kRowWaves : kBlo
     float d_float, void* out, int64_t L, int vpr)
 {
     modulate_rows<G, DT, MOD, kNormRms, WHOLE>(x, scale, shift, eps, d_float, out, L, vpr);
+}
+
+// The staged modulation in schedule SCHED (kSched*, launch.hpp), for
+// measurement: bf16 rows of kSchedD = 4096 elements (G = 8, whole rows),
+// RMSNorm, row modulation.
+template <int SCHED>
+__global__ __launch_bounds__(kBlock * kRowWaves) void rms_modulate_variant_kernel(
+    const void* x, const void* scale, const void* shift, float eps,
+    float d_float, void* out, int64_t L, int vpr)
+{
+    modulate_staged_row<8, kBF16, kNormRms, true, SCHED>(x, scale, shift, eps, d_float, out, L,
+                                                         vpr);
 }
 
 template <int G, int DT, int MOD, bool WHOLE = false>
@@ -942,6 +1014,31 @@ hipError_t launch_rms_modulate(const void* x, const void* scale,
 {
     return launch_norm<kNormRms>(x, scale, shift, eps, out, B, L, D, mod_mode, dtype, fast,
                                  stream, wg_per_cu);
+}
+
+hipError_t launch_modulate_variant(const void* x, const void* scale, const void* shift,
+                                   float eps, void* out, int64_t B, int64_t L, int sched,
+                                   hipStream_t stream)
+{
+    static_assert(kSchedD == 512 * 8, "whole rows of 8 packs per lane");
+    const void* k = nullptr;
+    switch (sched) {
+    case kSchedLibrary: k = reinterpret_cast<const void*>(&rms_modulate_variant_kernel<kSchedLibrary>); break;
+    case kSchedLoadsFirst: k = reinterpret_cast<const void*>(&rms_modulate_variant_kernel<kSchedLoadsFirst>); break;
+    case kSchedOnePlus: k = reinterpret_cast<const void*>(&rms_modulate_variant_kernel<kSchedOnePlus>); break;
+    case kSchedTwoRows: k = reinterpret_cast<const void*>(&rms_modulate_variant_kernel<kSchedTwoRows>); break;
+    case kSchedPrefetch: k = reinterpret_cast<const void*>(&rms_modulate_variant_kernel<kSchedPrefetch>); break;
+    default: return hipErrorInvalidValue;
+    }
+    float d_float = (float)kSchedD;
+    int vpr = (int)(kSchedD / 8);
+    void* args[] = {&x, &scale, &shift, &eps, &d_float, &out, &L, &vpr};
+    const int64_t row_bytes = kSchedD * 2;
+    return hipLaunchKernel(
+        k, dim3((uint32_t)ceil_div(L, kRowWaves * sched_rows_per_wave(sched)), (uint32_t)B),
+        dim3(kBlock * kRowWaves), args,
+        (size_t)row_wg_lds(row_bytes, staged_words_per_pack(sched) * row_bytes, kModRowBudget, 0),
+        stream);
 }
 
 hipError_t launch_ln_modulate(const void* x, const void* scale,

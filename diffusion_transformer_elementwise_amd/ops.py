@@ -5,7 +5,8 @@ from __future__ import annotations
 import torch
 
 from ._lib import (DTYPE_BF16, DTYPE_F16, DTYPE_F32, GATE_BCAST, GATE_FULL, MOD_ROW,
-                   MOD_TOKEN, RGA_OK, STORE_NT, RGAError, library, pointer_array)
+                   MOD_TOKEN, RGA_OK, SCHED_LIBRARY, STORE_NT, RGAError, library,
+                   pointer_array)
 
 
 # torch's raw accessor of the current stream (what its own compiled kernels
@@ -381,4 +382,43 @@ def fused_occupancy(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor, scale: to
                                        _DTYPES[dt], int(wg_per_cu), _stream_handle(dev))
     if st != RGA_OK:
         raise RGAError(st, "rga_fused_occupancy")
+    return x_out, y
+
+
+def modulate_variant(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                     eps: float = 1e-6, out: torch.Tensor | None = None,
+                     schedule: int = SCHED_LIBRARY) -> torch.Tensor:
+    """Measurement helper (rga_modulate_variant): the bf16 rms_modulate of
+    4096-element rows in a chosen schedule of the staged kernel (SCHED_*);
+    same result bit for bit."""
+    B, L, D = _x_shape(x, torch.bfloat16)
+    dev = x.device
+    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16, dev)
+    out = _output(out, "out", x, dev)
+    st = library().rga_modulate_variant(x.data_ptr(), scale.data_ptr(), shift.data_ptr(),
+                                        float(eps), out.data_ptr(), B, L, D, int(schedule),
+                                        _stream_handle(dev))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_modulate_variant")
+    return out
+
+
+def fused_variant(x: torch.Tensor, u: torch.Tensor, g: torch.Tensor, scale: torch.Tensor,
+                  shift: torch.Tensor, eps: float = 1e-6, x_out: torch.Tensor | None = None,
+                  y: torch.Tensor | None = None, schedule: int = SCHED_LIBRARY):
+    """Measurement helper (rga_fused_variant): the bf16 broadcast-gate
+    rga_gate_add_rms_modulate of 4096-element rows in a chosen schedule of
+    the staged kernel (SCHED_*); same results bit for bit."""
+    B, L, D = _x_shape(x, torch.bfloat16)
+    dev = x.device
+    _gate(x, u, g, GATE_BCAST, torch.bfloat16, dev)
+    _modulation(x, scale, shift, MOD_ROW, torch.bfloat16, dev)
+    x_out = _output(x_out, "x_out", x, dev)
+    y = _output(y, "y", x, dev)
+    st = library().rga_fused_variant(x.data_ptr(), u.data_ptr(), g.data_ptr(),
+                                     scale.data_ptr(), shift.data_ptr(), float(eps),
+                                     x_out.data_ptr(), y.data_ptr(), B, L, D, int(schedule),
+                                     _stream_handle(dev))
+    if st != RGA_OK:
+        raise RGAError(st, "rga_fused_variant")
     return x_out, y

@@ -133,6 +133,46 @@ int rga_check_fused_occupancy(const void* x, const void* u, const void* g, const
                               int64_t B, int64_t L, int64_t D, int gate_mode, int dtype,
                               int wg_per_cu);
 
+/* Schedules of rga_modulate_variant and rga_fused_variant. */
+enum {
+    RGA_SCHED_LIBRARY = 0,     /* the library's own schedule */
+    RGA_SCHED_LOADS_FIRST = 1, /* each row's loads issued before the workgroup
+                                  stages its scale and shift rows (the
+                                  modulation also reduces the row before the
+                                  workgroup's barrier) */
+    RGA_SCHED_ONE_PLUS = 2,    /* 1 + scale staged in LDS widened to binary32,
+                                  two words per pack, beside the shift row */
+    RGA_SCHED_TWO_ROWS = 3,    /* two rows per wave, one after the other */
+    RGA_SCHED_PREFETCH = 4,    /* two rows per wave, the second row's loads
+                                  issued before the first row is worked on */
+};
+
+/*
+ * rms_modulate (bf16, row modulation) and rga_gate_add_rms_modulate (bf16,
+ * RGA_GATE_BCAST) on rows of exactly 4096 elements, the workload's hidden
+ * size, in a chosen schedule of the kernels that stage the batch's rows in
+ * LDS (two rows, two waves, per workgroup; the library's occupancy rule),
+ * to measure the schedules the library does not use. Every schedule
+ * computes the same arithmetic in the same order: results equal the
+ * library's bit for bit. Arguments, layout, aliasing and errors as
+ * rms_modulate and rga_gate_add_rms_modulate (D % 8 == 0, 16-byte aligned
+ * pointers), plus: D other than 4096 (and not 0) is RGA_ERR_UNSUPPORTED, a
+ * schedule outside RGA_SCHED_* is RGA_ERR_INVALID_ARG.
+ */
+int rga_modulate_variant(const void* x, const void* scale, const void* shift, float eps,
+                         void* out, int64_t B, int64_t L, int64_t D, int schedule,
+                         hipStream_t stream);
+int rga_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                      const void* shift, float eps, void* x_out, void* y, int64_t B, int64_t L,
+                      int64_t D, int schedule, hipStream_t stream);
+
+/* Their validation alone, on the host. */
+int rga_check_modulate_variant(const void* x, const void* scale, const void* shift, float eps,
+                               const void* out, int64_t B, int64_t L, int64_t D, int schedule);
+int rga_check_fused_variant(const void* x, const void* u, const void* g, const void* scale,
+                            const void* shift, float eps, const void* x_out, const void* y,
+                            int64_t B, int64_t L, int64_t D, int schedule);
+
 #ifdef __cplusplus
 }
 #endif

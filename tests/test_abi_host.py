@@ -497,6 +497,28 @@ def test_measurement_validation_rules(dte):
     assert gv(0, 0, 0, 0, 0, 33, 4096, 1, 0) == ok
 
 
+def test_schedule_variants_take_the_workload_rows_only(dte):
+    ok, bad, uns = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED
+    x, s, t, o, u, g, y = (A + i * 512 * MB for i in range(7))
+    mv, fv = dte.check_modulate_variant, dte.check_fused_variant
+    for sched in range(5):
+        assert mv(x, s, t, 1e-6, o, 2, 32640, 4096, sched) == ok
+        assert fv(x, u, g, s, t, 1e-6, x, y, 2, 32640, 4096, sched) == ok
+    for sched in (-1, 5):
+        assert mv(x, s, t, 1e-6, o, 2, 32640, 4096, sched) == bad
+        assert fv(x, u, g, s, t, 1e-6, x, y, 2, 32640, 4096, sched) == bad
+    # only 4096-element rows; layout rules of the strict calls; empty is a no-op
+    for D in (4104, 2048, 8192):
+        assert mv(x, s, t, 1e-6, o, 2, 31, D, 0) == uns
+        assert fv(x, u, g, s, t, 1e-6, x, y, 2, 31, D, 0) == uns
+    assert mv(x + 2, s, t, 1e-6, o, 2, 31, 4096, 0) == uns
+    assert fv(x, u, g + 8, s, t, 1e-6, x, y, 2, 31, 4096, 0) == uns
+    assert mv(x, s, t, 1e-6, o, 0, 31, 4100, 0) == ok
+    assert mv(x, s, t, -1.0, o, 2, 31, 4096, 0) == bad
+    assert fv(x, u, g, s, t, 1e-6, x, x, 2, 31, 4096, 0) == dte.RGA_ERR_ALIAS
+    assert mv(x, s, t, 1e-6, s, 2, 31, 4096, 0) == dte.RGA_ERR_ALIAS
+
+
 def test_occupancy_helpers_follow_the_ex_rules(dte):
     ok, bad, uns = dte.RGA_OK, dte.RGA_ERR_INVALID_ARG, dte.RGA_ERR_UNSUPPORTED
     x, s, t, o, u, g, y = (A + i * 512 * MB for i in range(7))

@@ -131,3 +131,36 @@ def test_occupancy_helpers_equal_the_library(dte, D, dt):
         xo, fy = dte.fused_occupancy(x, u, g, s, t, 1e-6, wg_per_cu=w)
         assert np.array_equal(to_host_typed(xo), want_xo)
         assert np.array_equal(to_host_typed(fy), want_fy)
+
+
+# odd L (a wave past the last row), L = 1, L = 2 (a two-row wave's second
+# row absent for half the workgroups), and a larger grid
+@pytest.mark.parametrize("B,L", [(2, 37), (1, 1), (2, 2), (1, 515)])
+def test_schedule_variants_equal_the_oracle(dte, B, L):
+    D = 4096
+    seed = 13 * B + L
+    x = random_bits(seed, (B, L, D), N02)
+    u = random_bits(seed + 1, (B, L, D))
+    g = random_bits(seed + 2, (B, 1, D), U11)
+    s = random_bits(seed + 3, (B, 1, D), N001)
+    t = random_bits(seed + 4, (B, 1, D), N001)
+    want_y = oracle.rms_modulate(x, s, t, 1e-6)
+    want_x, want_fy = oracle.gate_add_rms_modulate(x, u, g, s, t, 1e-6, GATE_BCAST)
+    dx, du, dg, ds, dt = (to_dev(a) for a in (x, u, g, s, t))
+    for sched in (dte.SCHED_LIBRARY, dte.SCHED_LOADS_FIRST, dte.SCHED_ONE_PLUS,
+                  dte.SCHED_TWO_ROWS, dte.SCHED_PREFETCH):
+        say(f"[schedule variant] B={B} L={L} schedule={sched}")
+        got = to_host(dte.modulate_variant(dx, ds, dt, 1e-6, schedule=sched))
+        d = ulp_diff(got, want_y)
+        assert d.max() == 0, f"modulation, schedule {sched}: max {d.max()} ULP"
+        xo, fy = dte.fused_variant(dx, du, dg, ds, dt, 1e-6, schedule=sched)
+        got_x, got_y = to_host(xo), to_host(fy)
+        assert same_bits(got_x, want_x), first_mismatch(got_x, want_x)
+        d = ulp_diff(got_y, want_fy)
+        assert d.max() == 0, f"fused call, schedule {sched}: max {d.max()} ULP"
+        # in place, as the bench runs it
+        xi = dx.clone()
+        y = torch.empty_like(xi)
+        dte.fused_variant(xi, du, dg, ds, dt, 1e-6, x_out=xi, y=y, schedule=sched)
+        assert same_bits(to_host(xi), want_x)
+        assert ulp_diff(to_host(y), want_fy).max() == 0
