@@ -719,17 +719,22 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
         return;
     const int64_t row = (b * L + r) * D;
     const int lane = threadIdx.x & (kBlock - 1);
+    const void* px = elem_ptr<DT>(x, row);
+    // every stream of the row at the phase of x's 128-byte lines (each
+    // access instruction covering whole lines where the streams share x's
+    // line position), as far as the slots have room for it
+    const int room = 64 * K - planes;
+    const int phase = line_lead(px) < room ? line_lead(px) : room;
 
     u32x4 xv[K];
     {
         // every input's loads issued before any is realigned
         u32x4 uv[K], gv[FULL ? K : 1], xe, ue, ge;
-        const void* px = elem_ptr<DT>(x, row);
         const void* pu = elem_ptr<DT>(u, row);
-        load_run<K, true>(px, n, xv, xe);
-        load_run<K, true>(pu, n, uv, ue);
+        load_run<K, true>(px, n, xv, xe, phase);
+        load_run<K, true>(pu, n, uv, ue, phase);
         if constexpr (FULL)
-            load_run<K, true>(elem_ptr<DT>(g, row), n, gv, ge);
+            load_run<K, true>(elem_ptr<DT>(g, row), n, gv, ge, phase);
         realign_in<K>(xv, xe, start_offset(px));
         realign_in<K>(uv, ue, start_offset(pu));
         if constexpr (FULL)
@@ -739,15 +744,15 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
             Pack<DT> a, c, e;
             a.v = xv[k];
             c.v = uv[k];
-            e.v = FULL ? gv[FULL ? k : 0] : g_st[regs::staged_index<K>(k, lane, planes)];
+            e.v = FULL ? gv[FULL ? k : 0] : g_st[regs::staged_index<K>(k, lane, planes, phase)];
             xv[k] = gate_add8<DT>(a, c, e).v;
         }
     }
-    store_run<K, true>(elem_ptr<DT>(x_out, row), n, xv);
+    store_run<K, true>(elem_ptr<DT>(x_out, row), n, xv, phase);
     float mu, rr;
-    regs::row_factors<K, DT, regs::kRms>(xv, n, d_float, eps, &mu, &rr);
+    regs::row_factors<K, DT, regs::kRms>(xv, n, d_float, eps, &mu, &rr, phase);
     regs::apply_store_staged<K, DT, regs::kRms>(xv, staged, staged + planes, h_st, n, mu, rr,
-                                                elem_ptr<DT>(y, row));
+                                                elem_ptr<DT>(y, row), phase);
 }
 
 template <int K, bool FULL, int DT, int MOD>

@@ -161,24 +161,42 @@ __device__ __forceinline__ u32x4* aligned_down(void* p)
     return reinterpret_cast<u32x4*>(static_cast<char*>(p) - start_offset(p));
 }
 
-// Words of a run of n >= 1 2-byte elements at p into w[0..K) and extra.
+// The position of p's aligned window word 0 within its 128-byte line
+// (0..7 words). Access instructions that start at window word 64j - lead
+// cover whole lines: an instruction that straddles nine lines instead of
+// eight costs the memory system one more request per instruction, and a
+// line two workgroups (often on different XCDs, with their own L2s) each
+// touch part of is fetched twice.
+__device__ __forceinline__ int line_lead(const void* p)
+{
+    return (int)((reinterpret_cast<uintptr_t>(p) >> 4) & 7u);
+}
+
+// Words of a run of n >= 1 2-byte elements at p into w[0..K) and extra, at
+// a wave-uniform phase s (0..7): lane t, slot k holds window word
+// 64k + t - s, and extra (every lane) word 64K - s. With s the window's
+// line_lead each slot's access instruction covers whole 128-byte lines;
+// realign_in then leaves group 64k + t - s in lane t, slot k.
 template <int K, bool STREAM>
-__device__ __forceinline__ void load_run(const void* p, int n, u32x4 (&w)[K], u32x4& extra)
+__device__ __forceinline__ void load_run(const void* p, int n, u32x4 (&w)[K], u32x4& extra,
+                                         int phase = 0)
 {
     const int lane = threadIdx.x & 63;
     const int m = start_offset(p);
     const u32x4* w0 = aligned_down(p);
     const int count = (m + 2 * n + 15) >> 4;  // n >= 1
-    // lanes past the window re-read its last word (an index clamp rather
-    // than a branch, which would wait for each load before the next): those
-    // values only reach elements past the run, never summed nor stored
+    // indexes outside the window re-read its first or last word (a clamp
+    // rather than a branch, which would wait for each load before the
+    // next): those values only reach elements outside the run, never summed
+    // nor stored
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int i = lane + 64 * k;
-        const int ic = i < count ? i : count - 1;
+        const int i = lane + 64 * k - phase;
+        const int ic = i < 0 ? 0 : (i < count ? i : count - 1);
         w[k] = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
     }
-    extra = load16(w0 + (count > 64 * K ? 64 * K : count - 1));
+    const int ie = 64 * K - phase;
+    extra = load16(w0 + (ie < count ? ie : count - 1));
 }
 
 // Slots of a run from which realign_in uses the run-time cut (register use;
@@ -234,11 +252,13 @@ __device__ __forceinline__ void realign_in(u32x4 (&w)[K], const u32x4& extra, in
     });
 }
 
+// Groups of a run at phase s (load_run): lane t, slot k holds group
+// 64k + t - s.
 template <int K, bool STREAM>
-__device__ __forceinline__ void load_groups(const void* p, int n, u32x4 (&g)[K])
+__device__ __forceinline__ void load_groups(const void* p, int n, u32x4 (&g)[K], int phase = 0)
 {
     u32x4 extra;
-    load_run<K, STREAM>(p, n, g, extra);
+    load_run<K, STREAM>(p, n, g, extra, phase);
     realign_in<K>(g, extra, start_offset(p));
 }
 
@@ -277,12 +297,15 @@ __device__ __forceinline__ void put_word(u32x4* w0, int64_t i, const u32x4& v, i
     put_partial(w0, i, v, mo, end);
 }
 
-// Groups -> the n elements of a run at p: output word w joins groups w - 1
-// and w (cut at 16 - mo). Whole words are stored in the slot loop; the
-// run's first word (when mo > 0) and last word (when the run does not end
-// on a word boundary) are the only partial ones and are written after it.
+// Groups at phase s (lane t, slot k: group 64k + t - s) -> the n elements
+// of a run at p: output word w joins groups w - 1 and w (cut at 16 - mo), so
+// lane t, slot k forms word 64k + t - s (whole 128-byte lines per slot when
+// s is the output window's line_lead). Whole words are stored in the slot
+// loop; the run's first word (when mo > 0) and last word (when the run does
+// not end on a word boundary) are the only partial ones and are written
+// after it.
 template <int K, bool STREAM>
-__device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K])
+__device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K], int phase = 0)
 {
     if (n <= 0)
         return;
@@ -303,28 +326,29 @@ __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K])
             if constexpr (O != 0)
                 v = window_o<C>(lane_from_prev(g[k], fill), g[k], 16 - mo);
             fill = read_lane(g[k], 63);
-            const int w = lane + 64 * k;
+            const int w = lane + 64 * k - phase;
             if (16 * w >= mo && 16 * w + 16 <= end) {
                 if (STREAM)
                     store16_stream(w0 + w, v);
                 else
                     w0[w] = v;
             }
-            if (k == 0)
+            if (w == 0)
                 first = v;
             if (w == words - 1)
                 last = v;
         }
-        // word 64K (only reached when mo > 0): the tail of group 64K - 1
+        // word 64K - s (only reached when mo > 0): the tail of the last
+        // slot's lane 63 group
         if constexpr (O != 0)
-            if (words - 1 == 64 * K)
+            if (words - 1 == 64 * K - phase)
                 last = window_o<C>(fill, u32x4{0, 0, 0, 0}, 16 - mo);
     });
     const int wl = words - 1;
     const bool last_partial = (end & 15) != 0;
-    if (lane == 0 && mo != 0)
+    if (lane == phase && mo != 0)
         put_partial(w0, 0, first, mo, end);
-    if (last_partial && lane == (wl & 63) && !(wl == 0 && mo != 0))
+    if (last_partial && lane == ((wl + phase) & 63) && !(wl == 0 && mo != 0))
         put_partial(w0, wl, last, mo, end);
 }
 
@@ -351,15 +375,6 @@ __device__ __forceinline__ int64_t window_words(const void* p, int64_t nbytes)
     return nbytes > 0 ? (start_offset(p) + nbytes + 15) >> 4 : 0;
 }
 
-// Words of p's aligned window that precede the first 128-byte line boundary
-// at or after its start (0..7). Chunks start at window word 64j - lead, so
-// every chunk covers whole 128-byte lines of the output: chunks that split
-// lines had neighbouring workgroups (often on different XCDs, with their
-// own L2s) fetch the shared lines twice.
-__device__ __forceinline__ int line_lead(const void* p)
-{
-    return (int)((reinterpret_cast<uintptr_t>(p) >> 4) & 7u);
-}
 
 // The words an input supplies to lane t of chunk j, fetched (every load
 // issued, none waited on) so that a caller can fetch all its inputs before

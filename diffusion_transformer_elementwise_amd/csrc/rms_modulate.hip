@@ -767,12 +767,17 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kerne
     if (r >= L)
         return;
     const int64_t row = (b * L + r) * D;
+    const void* px = elem_ptr<DT>(x, row);
+    // the row at the phase of its 128-byte lines (each access instruction
+    // covering whole lines), as far as the slots have room for it
+    const int room = 64 * K - planes;
+    const int phase = line_lead(px) < room ? line_lead(px) : room;
     u32x4 xv[K];
-    load_groups<K, true>(elem_ptr<DT>(x, row), n, xv);
+    load_groups<K, true>(px, n, xv, phase);
     float mu, rr;
-    regs::row_factors<K, DT, kNorm>(xv, n, d_float, eps, &mu, &rr);
+    regs::row_factors<K, DT, kNorm>(xv, n, d_float, eps, &mu, &rr, phase);
     regs::apply_store_staged<K, DT, kNorm>(xv, staged, staged + planes, staged + 2 * planes, n,
-                                           mu, rr, elem_ptr<DT>(out, row));
+                                           mu, rr, elem_ptr<DT>(out, row), phase);
 }
 
 template <int K, int DT, int MOD, int NORM>

@@ -47,12 +47,19 @@ __device__ __forceinline__ float wave_sum(float acc)
     return acc;
 }
 
-// sum over the row of x (WHAT 0), x^2 (1) or (x - mu)^2 (2). Slots below
-// whole_slots<K>() are summed without masks: known whole at compile time,
-// where a run-time test left a compare and a select on every element (the
-// compiler turned the branch into selects).
+// sum over the row of x (WHAT 0), x^2 (1) or (x - mu)^2 (2), the row held at
+// phase s (lane t, slot k: group g = 64k + t - s; load_groups). Lane t
+// accumulates its slots in increasing k, which are groups j, j + 64, ... of
+// partial j = (t - s) mod 64 in increasing order (lanes t < s start at slot
+// 1); one rotation of the 64 partials by s lanes puts partial j in lane j
+// before the xor-distance exchanges, so the sum is that of the fixed order
+// bit for bit at any phase. Elements outside the row (groups below 0 or
+// past n) are skipped; slots 1 .. whole_slots<K>() - 1 are whole at any phase
+// (a row run with K slots has more than 512 times the ladder's previous
+// entry elements) and are summed without masks, known at compile time: a
+// run-time test left a compare and a select on every element.
 template <int K, int DT, int WHAT>
-__device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu)
+__device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu, int phase = 0)
 {
     constexpr int kWhole = whole_slots<K>();
     const int lane = threadIdx.x & 63;
@@ -61,11 +68,13 @@ __device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu)
     for (int k = 0; k < K; ++k) {
         Pack<DT> p;
         p.v = xv[k];
-        const int e0 = 8 * (lane + 64 * k);
-        const bool whole = k < kWhole || 512 * (k + 1) <= n;
+        const int g = lane + 64 * k - phase;
+        const int e0 = 8 * g;
+        const bool whole = (k >= 1 && k < kWhole) ||
+                           (64 * k >= phase && 512 * (k + 1) - 8 * phase <= n);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if (whole || e0 + e < n) {
+            if (whole || (g >= 0 && e0 + e < n)) {
                 float a = p.get(e);
                 if constexpr (WHAT == 0) {
                     acc = acc + a;
@@ -78,18 +87,21 @@ __device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu)
             }
         }
     }
+    // partial j from lane (j + s) mod 64 (ds_bpermute; the identity at s = 0)
+    acc = __int_as_float(
+        __builtin_amdgcn_ds_bpermute(((lane + phase) & 63) << 2, __float_as_int(acc)));
     return wave_sum(acc);
 }
 
 // mean (LayerNorm; 0 for RMSNorm) and 1 / sqrt(mean square + eps)
 template <int K, int DT, int NORM>
 __device__ __forceinline__ void row_factors(const u32x4 (&xv)[K], int n, float d_float, float eps,
-                                            float* mu, float* rr)
+                                            float* mu, float* rr, int phase = 0)
 {
     float m = 0.0f;
     if constexpr (NORM == kLn)
-        m = row_sum<K, DT, 0>(xv, n, 0.0f) / d_float;
-    const float ss = row_sum<K, DT, NORM == kLn ? 2 : 1>(xv, n, m);
+        m = row_sum<K, DT, 0>(xv, n, 0.0f, phase) / d_float;
+    const float ss = row_sum<K, DT, NORM == kLn ? 2 : 1>(xv, n, m, phase);
     const float ms = ss / d_float;
     const float t = ms + eps;
     const float q = sqrtf(t);
@@ -151,10 +163,12 @@ __device__ __forceinline__ void apply_store(u32x4 (&xv)[K], const void* scale, c
 // indexes are clamped into the plane (the groups they stand for are
 // neither summed nor stored).
 template <int K>
-__device__ __forceinline__ int staged_index(int k, int lane, int planes)
+__device__ __forceinline__ int staged_index(int k, int lane, int planes, int phase = 0)
 {
-    const int i = 64 * k + lane;
-    return (k < whole_slots<K>() || i < planes) ? i : planes - 1;
+    const int i = 64 * k + lane - phase;
+    if (k >= 1 && k < whole_slots<K>())
+        return i;
+    return i < 0 ? 0 : (i < planes ? i : planes - 1);
 }
 
 // The groups of the row of n elements at p into the plane at dst.
@@ -199,7 +213,7 @@ __device__ __forceinline__ void stage_one_plus(u32x4* a_lo, u32x4* a_hi, const v
 template <int K, int DT, int NORM>
 __device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* a_lo,
                                                    const u32x4* a_hi, const u32x4* h_lds, int n,
-                                                   float mu, float rr, void* out)
+                                                   float mu, float rr, void* out, int phase = 0)
 {
     const int lane = threadIdx.x & 63;
     const int planes = (n + 7) >> 3;
@@ -213,13 +227,13 @@ __device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* 
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int i = staged_index<K>(k, lane, planes);
+        const int i = staged_index<K>(k, lane, planes, phase);
         Pack<DT> xp, hp;
         xp.v = xv[k];
         hp.v = h_lds[i];
         xv[k] = modulate_group<DT, NORM == kLn>(xp, mu, rr, a_lo[i], a_hi[i], hp).v;
     }
-    store_run<K, true>(out, n, xv);
+    store_run<K, true>(out, n, xv, phase);
 }
 
 }  // namespace regs
