@@ -205,35 +205,58 @@ __device__ __forceinline__ void fused_staged_rows(
     const int lane = threadIdx.x & (kBlock - 1);
     const int64_t b = blockIdx.y;
     const int64_t r0 = (int64_t)blockIdx.x * kRowWaves * R + (threadIdx.x / kBlock);
-    using GP = Grouped<DT>;
     u32x4* s_st = staged;
     u32x4* h_st = staged + (kOnePlus ? 2 : 1) * vpr;
     u32x4* g_st = staged + (kOnePlus ? 3 : 2) * vpr;
 
+    // Rows other than WHOLE ones are held at the phase s of x's 128-byte
+    // lines (lane t, pack i: pack 64i + t - s; as far as the packs have room
+    // for it), so that each access instruction covers whole lines: the sum's
+    // 64 partials are rotated back to lane order before the exchanges (bit
+    // for bit the fixed order), and packs outside the row hold zeros and are
+    // not stored.
+    auto phase_of = [&](int64_t row) {
+        if constexpr (WHOLE) {
+            return 0;
+        } else {
+            const int lead = (int)((reinterpret_cast<uintptr_t>(static_cast<const u32x4*>(x) + row) >> 4) & 7u);
+            const int room = 64 * G - vpr;
+            return lead < room ? lead : room;
+        }
+    };
+    auto load_pack = [&](const void* base, int64_t row, int i, int phase) {
+        if constexpr (WHOLE) {
+            return Pack<DT>::load_stream(base, row + 64 * i + lane);
+        } else {
+            const int p = 64 * i + lane - phase;
+            const int pc = p < 0 ? 0 : (p < vpr ? p : vpr - 1);
+            Pack<DT> v = Pack<DT>::load_stream(base, row + pc);
+            const bool in = p >= 0 && p < vpr;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                v.v[d] = in ? v.v[d] : 0u;
+            return v;
+        }
+    };
     auto load_row = [&](Pack<DT> (&xv)[G], Pack<DT> (&uv)[G], Pack<DT> (&gv)[FULL ? G : 1],
-                        int64_t row) {
+                        int64_t row, int phase) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int h = vpr - 64 * i;
-            if constexpr (WHOLE) {
-                xv[i] = Pack<DT>::load_stream(x, row + 64 * i + lane);
-                uv[i] = Pack<DT>::load_stream(u, row + 64 * i + lane);
-                if constexpr (FULL)
-                    gv[i] = Pack<DT>::load_stream(g, row + 64 * i + lane);
-            } else {
-                xv[i] = GP::template load_clamped<true>(x, row + 64 * i, lane, h);
-                uv[i] = GP::template load_clamped<true>(u, row + 64 * i, lane, h);
-                if constexpr (FULL)
-                    gv[i] = GP::template load_clamped<true>(g, row + 64 * i, lane, h);
-            }
+            xv[i] = load_pack(x, row, i, phase);
+            uv[i] = load_pack(u, row, i, phase);
+            if constexpr (FULL)
+                gv[i] = load_pack(g, row, i, phase);
         }
     };
 
     Pack<DT> xv[G], uv[G], gv[FULL ? G : 1];
+    int phase = 0;
     if constexpr (SCHED == kSchedLoadsFirst) {
         // a wave past the last row (odd L) loads the last row and stores
         // nothing
-        load_row(xv, uv, gv, (b * L + (r0 < L ? r0 : L - 1)) * vpr);
+        const int64_t row = (b * L + (r0 < L ? r0 : L - 1)) * vpr;
+        phase = phase_of(row);
+        load_row(xv, uv, gv, row, phase);
     }
     // the batch's rows, vpr <= 64 G words each: every load issued before any
     // LDS write (one round trip to the L2, not one per word a thread
@@ -275,8 +298,10 @@ __device__ __forceinline__ void fused_staged_rows(
     __syncthreads();
     if (r0 >= L)
         return;
-    if constexpr (SCHED != kSchedLoadsFirst)
-        load_row(xv, uv, gv, (b * L + r0) * vpr);
+    if constexpr (SCHED != kSchedLoadsFirst) {
+        phase = phase_of((b * L + r0) * vpr);
+        load_row(xv, uv, gv, (b * L + r0) * vpr, phase);
+    }
 
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -285,26 +310,33 @@ __device__ __forceinline__ void fused_staged_rows(
         const bool more = j + 1 < R && r + kRowWaves < L;
         constexpr int kQ = SCHED == kSchedPrefetch ? G : 1;
         Pack<DT> xq[kQ], uq[kQ], gq[FULL ? kQ : 1];
+        int phase_q = 0;
         if constexpr (SCHED == kSchedPrefetch)
-            if (more)
-                load_row(xq, uq, gq, row + (int64_t)kRowWaves * vpr);
+            if (more) {
+                phase_q = phase_of(row + (int64_t)kRowWaves * vpr);
+                load_row(xq, uq, gq, row + (int64_t)kRowWaves * vpr, phase_q);
+            }
 
         Pack<DT> xn[G];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int h = vpr - 64 * i;
+            const int p = 64 * i + lane - phase;  // the pack this lane holds
+            const bool in = WHOLE || (p >= 0 && p < vpr);
             Pack<DT> gi;
-            if constexpr (FULL)
+            if constexpr (FULL) {
                 gi = gv[FULL ? i : 0];
-            else if constexpr (WHOLE)
-                gi.v = g_st[64 * i + lane];
-            else
-                gi = GP::lds_raw(g_st, 64 * i, lane, h);
+            } else if constexpr (WHOLE) {
+                gi.v = g_st[p];
+            } else {
+                // zeros outside the row: x' = +0 there
+                gi.v = g_st[p < 0 ? 0 : (p < vpr ? p : vpr - 1)];
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    gi.v[d] = in ? gi.v[d] : 0u;
+            }
             const Pack<DT> xr = gate_add8<DT>(xv[i], uv[i], gi);
-            if constexpr (WHOLE)
-                xr.store_stream(x_out, row + 64 * i + lane);
-            else
-                GP::store_stream_raw(xr, x_out, row + 64 * i, lane, h);
+            if (in)
+                xr.store_stream(x_out, row + p);
             xn[i] = xr;
         }
         float acc = 0.0f;
@@ -317,30 +349,28 @@ __device__ __forceinline__ void fused_staged_rows(
                 acc = acc + sa;
             }
         }
+        if constexpr (!WHOLE)
+            acc = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane + phase) & 63) << 2,
+                                                              __float_as_int(acc)));
         const float ms = wave_sum_dpp(acc) / d_float;
         const float t = ms + eps;
         const float q = sqrtf(t);
         const float rr = 1.0f / q;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int h = vpr - 64 * i;
+            const int p = 64 * i + lane - phase;
+            // scale and shift at the pack's index, clamped into the row for
+            // packs outside it (not stored)
+            const int pc = WHOLE ? p : (p < 0 ? 0 : (p < vpr ? p : vpr - 1));
             Pack<DT> o;
             if constexpr (kOnePlus) {
-                // past the row end the index is clamped into it: not stored
-                const int p = WHOLE ? 64 * i + lane
-                                    : (64 * i + lane < vpr ? 64 * i + lane : vpr - 1);
                 Pack<DT> h_;
-                h_.v = h_st[p];
-                o = modulate_group<DT, false>(xn[i], 0.0f, rr, s_st[p], s_st[vpr + p], h_);
+                h_.v = h_st[pc];
+                o = modulate_group<DT, false>(xn[i], 0.0f, rr, s_st[pc], s_st[vpr + pc], h_);
             } else {
                 Pack<DT> s_, h_;
-                if constexpr (WHOLE) {
-                    s_.v = s_st[64 * i + lane];
-                    h_.v = h_st[64 * i + lane];
-                } else {
-                    s_ = GP::lds_raw(s_st, 64 * i, lane, h);
-                    h_ = GP::lds_raw(h_st, 64 * i, lane, h);
-                }
+                s_.v = s_st[pc];
+                h_.v = h_st[pc];
                 float of[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -351,10 +381,8 @@ __device__ __forceinline__ void fused_staged_rows(
                 }
                 o = Pack<DT>::make(of);
             }
-            if constexpr (WHOLE)
-                o.store_stream(y, row + 64 * i + lane);
-            else
-                GP::store_stream_raw(o, y, row + 64 * i, lane, h);
+            if (WHOLE || (p >= 0 && p < vpr))
+                o.store_stream(y, row + p);
         }
 
         if (j + 1 < R) {
@@ -368,8 +396,10 @@ __device__ __forceinline__ void fused_staged_rows(
                     if constexpr (FULL)
                         gv[FULL ? i : 0] = gq[FULL ? i : 0];
                 }
+                phase = phase_q;
             } else {
-                load_row(xv, uv, gv, row + (int64_t)kRowWaves * vpr);
+                phase = phase_of(row + (int64_t)kRowWaves * vpr);
+                load_row(xv, uv, gv, row + (int64_t)kRowWaves * vpr, phase);
             }
         }
     }
@@ -848,7 +878,8 @@ typedef void (*fused_kernel_t)(const void*, const void*, const void*,
                                const void*, const void*, float, float, void*,
                                void*, int64_t, int);
 
-constexpr int kLadder[] = {1, 2, 4, 6, 8, 12, 16};
+constexpr int kLadder[] = {1, 2, 4, 6, 8, 9, 12, 16};
+constexpr int kLadderSize = sizeof(kLadder) / sizeof(kLadder[0]);
 static_assert(RGA_RMS_MAX_D / 512 == 16, "ladder tops out at RGA_RMS_MAX_D");
 
 template <bool FULL, int DT, int MOD>
@@ -859,9 +890,11 @@ fused_kernel_t pick(int groups)
                           &gate_add_rms_modulate_kernel<4, FULL, DT, MOD>,
                           &gate_add_rms_modulate_kernel<6, FULL, DT, MOD>,
                           &gate_add_rms_modulate_kernel<8, FULL, DT, MOD>,
+                          &gate_add_rms_modulate_kernel<9, FULL, DT, MOD>,
                           &gate_add_rms_modulate_kernel<12, FULL, DT, MOD>,
                           &gate_add_rms_modulate_kernel<16, FULL, DT, MOD>};
-    for (int i = 0; i < 7; ++i)
+    static_assert(sizeof(t) / sizeof(t[0]) == kLadderSize, "one kernel per ladder entry");
+    for (int i = 0; i < kLadderSize; ++i)
         if (groups <= kLadder[i])
             return t[i];
     return nullptr;
@@ -881,13 +914,14 @@ const void* pick_staged(int groups, bool whole)
 {
     const void* t[] = {staged_kernel<1, FULL, DT>(false), staged_kernel<2, FULL, DT>(false),
                        staged_kernel<4, FULL, DT>(false), staged_kernel<6, FULL, DT>(false),
-                       staged_kernel<8, FULL, DT>(false), staged_kernel<12, FULL, DT>(false),
-                       staged_kernel<16, FULL, DT>(false)};
+                       staged_kernel<8, FULL, DT>(false), staged_kernel<9, FULL, DT>(false),
+                       staged_kernel<12, FULL, DT>(false), staged_kernel<16, FULL, DT>(false)};
     const void* w[] = {staged_kernel<1, FULL, DT>(true), staged_kernel<2, FULL, DT>(true),
                        staged_kernel<4, FULL, DT>(true), staged_kernel<6, FULL, DT>(true),
-                       staged_kernel<8, FULL, DT>(true), staged_kernel<12, FULL, DT>(true),
-                       staged_kernel<16, FULL, DT>(true)};
-    for (int i = 0; i < 7; ++i)
+                       staged_kernel<8, FULL, DT>(true), staged_kernel<9, FULL, DT>(true),
+                       staged_kernel<12, FULL, DT>(true), staged_kernel<16, FULL, DT>(true)};
+    static_assert(sizeof(t) / sizeof(t[0]) == kLadderSize, "one kernel per ladder entry");
+    for (int i = 0; i < kLadderSize; ++i)
         if (groups <= kLadder[i])
             return (whole && groups == kLadder[i]) ? w[i] : t[i];
     return nullptr;

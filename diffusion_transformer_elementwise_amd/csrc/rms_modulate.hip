@@ -109,13 +109,26 @@ __device__ __forceinline__ float inv_std(float ss, float d_float, float eps)
     return 1.0f / q;
 }
 
-// The normalisation factor of one row held as G packs per lane (lane t,
-// pack i holds group t + 64i; lanes past the row end hold zeros, which add
-// +0 to a partial that is never -0 and are left out of the LayerNorm's sum of
-// squared deviations). Returns r; *mu is the LayerNorm mean (0 for RMS).
-template <int G, int DT, int NORM, bool DPP>
+// Partial j of lane (j + s) mod 64 into lane j (ds_bpermute), for rows held
+// at phase s: see row_factor.
+__device__ __forceinline__ float partials_in_order(float acc, int lane, int phase)
+{
+    return __int_as_float(
+        __builtin_amdgcn_ds_bpermute(((lane + phase) & 63) << 2, __float_as_int(acc)));
+}
+
+// The normalisation factor of one row held as G packs per lane at phase s
+// (lane t, pack i holds group 64i + t - s; packs outside the row hold zeros,
+// which add +0 to a partial that is never -0 and are left out of the
+// LayerNorm's sum of squared deviations). Lane t's packs in increasing i are
+// the groups of partial j = (t - s) mod 64 in increasing order; with s > 0
+// (PHASED) the 64 partials are rotated back to lane order before the
+// exchanges, so every sum is the fixed order's bit for bit. Returns r; *mu
+// is the LayerNorm mean (0 for RMS).
+template <int G, int DT, int NORM, bool DPP, bool PHASED = false>
 __device__ __forceinline__ float row_factor(const Pack<DT> (&xv)[G], int lane, int vpr,
-                                            float eps, float d_float, float* mu_out)
+                                            float eps, float d_float, float* mu_out,
+                                            int phase = 0)
 {
     float mu = 0.0f;
     if constexpr (NORM == kNormLn) {
@@ -126,12 +139,14 @@ __device__ __forceinline__ float row_factor(const Pack<DT> (&xv)[G], int lane, i
             for (int e = 0; e < 8; ++e)
                 acc = acc + xv[i].get(e);
         }
+        if constexpr (PHASED)
+            acc = partials_in_order(acc, lane, phase);
         mu = (DPP ? wave_sum_dpp(acc) : wave_sum(acc)) / d_float;
     }
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        if (NORM == kNormLn && lane + 64 * i >= vpr)
+        if (NORM == kNormLn && (lane + 64 * i - phase >= vpr || lane + 64 * i < phase))
             continue;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -142,6 +157,8 @@ __device__ __forceinline__ float row_factor(const Pack<DT> (&xv)[G], int lane, i
             acc = acc + sa;
         }
     }
+    if constexpr (PHASED)
+        acc = partials_in_order(acc, lane, phase);
     *mu_out = mu;
     return inv_std(DPP ? wave_sum_dpp(acc) : wave_sum(acc), d_float, eps);
 }
@@ -224,67 +241,94 @@ __device__ __forceinline__ void modulate_staged_row(
     // all. Otherwise no branch around a load: the index is clamped into the
     // row and zeros are selected past its end (a branch per load made the
     // compiler wait for each load before issuing the next).
-    auto load_row = [&](Pack<DT> (&xv)[G], int64_t row) {
+    // Other rows are held at the phase of their 128-byte lines (pack
+    // 64i + t - s in lane t, pack i; row_factor), as far as the packs have
+    // room for it, so that each access instruction covers whole lines.
+    auto phase_of = [&](int64_t row) {
+        if constexpr (WHOLE) {
+            return 0;
+        } else {
+            const int lead = (int)((reinterpret_cast<uintptr_t>(static_cast<const u32x4*>(x) + row) >> 4) & 7u);
+            const int room = 64 * G - vpr;
+            return lead < room ? lead : room;
+        }
+    };
+    auto load_row = [&](Pack<DT> (&xv)[G], int64_t row, int phase) {
 #pragma unroll
-        for (int i = 0; i < G; ++i)
-            xv[i] = WHOLE ? Pack<DT>::load_stream(x, row + 64 * i + lane)
-                          : Grouped<DT>::template load_clamped<true>(x, row + 64 * i, lane,
-                                                                     vpr - 64 * i);
+        for (int i = 0; i < G; ++i) {
+            if constexpr (WHOLE) {
+                xv[i] = Pack<DT>::load_stream(x, row + 64 * i + lane);
+            } else {
+                const int p = 64 * i + lane - phase;
+                const int pc = p < 0 ? 0 : (p < vpr ? p : vpr - 1);
+                xv[i] = Pack<DT>::load_stream(x, row + pc);
+                const bool in = p >= 0 && p < vpr;
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    xv[i].v[d] = in ? xv[i].v[d] : 0u;
+            }
+        }
     };
     Pack<DT> xv[G];
     float mu = 0.0f, rr = 0.0f;
+    int phase = 0;
     if constexpr (VAR == kSchedLoadsFirst) {
         // a wave past the last row (odd L) loads the last row and stores
         // nothing
-        load_row(xv, (b * L + (r0 < L ? r0 : L - 1)) * vpr);
+        const int64_t row = (b * L + (r0 < L ? r0 : L - 1)) * vpr;
+        phase = phase_of(row);
+        load_row(xv, row, phase);
     }
     stage_scale_shift<G, DT, kOnePlus>(staged, static_cast<const u32x4*>(scale) + b * vpr,
                                        static_cast<const u32x4*>(shift) + b * vpr, vpr);
     if constexpr (VAR == kSchedLoadsFirst)
-        rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
+        rr = row_factor<G, DT, NORM, true, !WHOLE>(xv, lane, vpr, eps, d_float, &mu, phase);
     __syncthreads();
     if (r0 >= L)
         return;
-    if constexpr (VAR != kSchedLoadsFirst)
-        load_row(xv, (b * L + r0) * vpr);
+    if constexpr (VAR != kSchedLoadsFirst) {
+        phase = phase_of((b * L + r0) * vpr);
+        load_row(xv, (b * L + r0) * vpr, phase);
+    }
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t r = r0 + (int64_t)kRowWaves * j;
         const int64_t row = (b * L + r) * vpr;
         const bool more = j + 1 < R && r + kRowWaves < L;
         Pack<DT> xq[VAR == kSchedPrefetch ? G : 1];
+        int phase_q = 0;
         if constexpr (VAR == kSchedPrefetch)
-            if (more)
-                load_row(xq, row + (int64_t)kRowWaves * vpr);
+            if (more) {
+                phase_q = phase_of(row + (int64_t)kRowWaves * vpr);
+                load_row(xq, row + (int64_t)kRowWaves * vpr, phase_q);
+            }
         if constexpr (VAR != kSchedLoadsFirst)
-            rr = row_factor<G, DT, NORM, true>(xv, lane, vpr, eps, d_float, &mu);
-        // element-wise; packs past the row end are not stored
+            rr = row_factor<G, DT, NORM, true, !WHOLE>(xv, lane, vpr, eps, d_float, &mu, phase);
+        // element-wise; packs outside the row are not stored
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int h = vpr - 64 * i;
+            const int p = 64 * i + lane - phase;  // the pack this lane holds
+            // its scale and shift words (the index clamped into the row: packs
+            // outside it are not stored)
+            const int pc = WHOLE ? p : (p < 0 ? 0 : (p < vpr ? p : vpr - 1));
             Pack<DT> o;
             if constexpr (kOnePlus) {
-                const int p = WHOLE ? 64 * i + lane
-                                    : (64 * i + lane < vpr ? 64 * i + lane : vpr - 1);
                 Pack<DT> h_;
-                h_.v = staged[2 * vpr + p];
-                o = modulate_group<DT, NORM == kNormLn>(xv[i], mu, rr, staged[p],
-                                                        staged[vpr + p], h_);
+                h_.v = staged[2 * vpr + pc];
+                o = modulate_group<DT, NORM == kNormLn>(xv[i], mu, rr, staged[pc],
+                                                        staged[vpr + pc], h_);
             } else {
                 Pack<DT> s_, h_;
-                if constexpr (WHOLE) {
-                    s_.v = staged[64 * i + lane];
-                    h_.v = staged[vpr + 64 * i + lane];
-                } else {
-                    s_ = Grouped<DT>::lds_raw(staged, 64 * i, lane, h);
-                    h_ = Grouped<DT>::lds_raw(staged + vpr, 64 * i, lane, h);
-                }
+                s_.v = staged[pc];
+                h_.v = staged[vpr + pc];
                 o = modulate_pack<DT, NORM>(xv[i], mu, rr, s_, h_);
             }
-            if constexpr (WHOLE)
-                o.store_stream(out, row + 64 * i + lane);
-            else
-                Grouped<DT>::store_stream_raw(o, out, row + 64 * i, lane, h);
+            if constexpr (WHOLE) {
+                o.store_stream(out, row + p);
+            } else {
+                if (p >= 0 && p < vpr)
+                    o.store_stream(out, row + p);
+            }
         }
         if (j + 1 < R) {
             if (!more)
@@ -293,8 +337,10 @@ __device__ __forceinline__ void modulate_staged_row(
 #pragma unroll
                 for (int i = 0; i < G; ++i)
                     xv[i] = xq[i];
+                phase = phase_q;
             } else {
-                load_row(xv, row + (int64_t)kRowWaves * vpr);
+                phase = phase_of(row + (int64_t)kRowWaves * vpr);
+                load_row(xv, row + (int64_t)kRowWaves * vpr, phase);
             }
         }
     }
@@ -804,7 +850,7 @@ typedef void (*rms_kernel_t)(const void*, const void*, const void*, float,
                              float, void*, int64_t, int);
 
 // Packs per lane are taken from a ladder (the smallest entry >= ceil(D/512)).
-constexpr int kLadder[] = {1, 2, 4, 6, 8, 12, 16};
+constexpr int kLadder[] = {1, 2, 4, 6, 8, 9, 12, 16};
 static_assert(RGA_RMS_MAX_D / 512 == 16, "ladder tops out at RGA_RMS_MAX_D");
 
 template <int NORM, int G, int DT, int MOD, bool WHOLE>
@@ -822,13 +868,14 @@ rms_kernel_t pick(int groups, bool whole)
     constexpr bool kW = staged_rows<DT, MOD>();  // only the staged rows have a WHOLE form
     rms_kernel_t t[] = {fast_kernel<NORM, 1, DT, MOD, false>(), fast_kernel<NORM, 2, DT, MOD, false>(),
                         fast_kernel<NORM, 4, DT, MOD, false>(), fast_kernel<NORM, 6, DT, MOD, false>(),
-                        fast_kernel<NORM, 8, DT, MOD, false>(), fast_kernel<NORM, 12, DT, MOD, false>(),
-                        fast_kernel<NORM, 16, DT, MOD, false>()};
+                        fast_kernel<NORM, 8, DT, MOD, false>(), fast_kernel<NORM, 9, DT, MOD, false>(),
+                        fast_kernel<NORM, 12, DT, MOD, false>(), fast_kernel<NORM, 16, DT, MOD, false>()};
     rms_kernel_t w[] = {fast_kernel<NORM, 1, DT, MOD, kW>(), fast_kernel<NORM, 2, DT, MOD, kW>(),
                         fast_kernel<NORM, 4, DT, MOD, kW>(), fast_kernel<NORM, 6, DT, MOD, kW>(),
-                        fast_kernel<NORM, 8, DT, MOD, kW>(), fast_kernel<NORM, 12, DT, MOD, kW>(),
-                        fast_kernel<NORM, 16, DT, MOD, kW>()};
-    for (int i = 0; i < 7; ++i)
+                        fast_kernel<NORM, 8, DT, MOD, kW>(), fast_kernel<NORM, 9, DT, MOD, kW>(),
+                        fast_kernel<NORM, 12, DT, MOD, kW>(), fast_kernel<NORM, 16, DT, MOD, kW>()};
+    static_assert(sizeof(kLadder) / sizeof(kLadder[0]) == 8, "one kernel per ladder entry");
+    for (int i = 0; i < 8; ++i)
         if (groups <= kLadder[i])
             return (whole && groups == kLadder[i]) ? w[i] : t[i];
     return nullptr;

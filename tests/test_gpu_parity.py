@@ -105,7 +105,10 @@ def test_gate_add_ragged_shapes(dte, B, L, D, mode):
     assert same_bits(got, want), first_mismatch(got, want)
 
 
-@pytest.mark.parametrize("B,L,D", RAGGED + [(1, 17, 6144), (2, 3, 7680)])
+# 4608: nine packs per lane, whole rows; 4104: nine packs per lane, rows at
+# every line phase
+@pytest.mark.parametrize("B,L,D", RAGGED + [(1, 17, 6144), (2, 3, 7680), (1, 19, 4608),
+                                            (2, 9, 4104)])
 def test_rms_ragged_shapes(dte, B, L, D):
     say(f"[rms ragged] B={B} L={L} D={D}")
     seed = 5 * B + 3 * L + D
@@ -310,7 +313,7 @@ def test_fused_residual_then_modulation_at_video_scale(dte, mode):
     _fused_case(dte, 2, 32640, 4096, mode, 1200 + mode)
 
 
-@pytest.mark.parametrize("B,L,D", RAGGED + [(1, 17, 6144)])
+@pytest.mark.parametrize("B,L,D", RAGGED + [(1, 17, 6144), (1, 19, 4608), (2, 9, 4104)])
 @pytest.mark.parametrize("mode", [GATE_FULL, GATE_BCAST])
 def test_fused_ragged_shapes(dte, B, L, D, mode):
     say(f"[fused ragged] B={B} L={L} D={D} mode={mode}")
