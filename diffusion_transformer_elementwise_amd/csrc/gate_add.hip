@@ -79,7 +79,12 @@ __global__ __launch_bounds__(kBlock) void gate_add_full_kernel(
 // y = batch b, where a chunk is up to 64 packs of a row. The lanes of a
 // chunk take its packs as in the full kernel; the matching gate packs come
 // from row b of g, which stays in the caches while the streams of x, u and
-// out pass through.
+// out pass through. With 2-byte storage, chunk c of a row covers its packs
+// 64c - s .. 64c - s + 63, s the position of the output row's first pack in
+// its 128-byte line (0 for rows of a multiple of 64 packs in a line-aligned
+// tensor), so that each access instruction covers whole lines: on MI355X a
+// 16-byte-aligned stream whose instructions straddle lines runs 15-20 %
+// slower. The launch gives each row enough chunks for that shift.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t L,
@@ -87,18 +92,43 @@ __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
 {
     const uint32_t l = blockIdx.x / chunks;
     const uint32_t chunk = blockIdx.x - l * chunks;
-    const uint32_t col0 = chunk * kBlock;
     const int t = threadIdx.x;
-    const int h = (vpr - col0 < (uint32_t)kBlock) ? (int)(vpr - col0) : kBlock;
-    if (t >= h)
-        return;
     const int64_t b = blockIdx.y;
-    const int64_t c0 = (b * L + l) * vpr + col0;
-    using I = Interleaved<DT>;
-    const Pack<DT> xv = I::load_stream(x, c0, t, h);
-    const Pack<DT> uv = I::load_stream(u, c0, t, h);
-    const Pack<DT> gv = I::load(g, b * vpr + col0, t, h);
-    I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
+    const int64_t row = (b * L + l) * vpr;
+    if constexpr (DT != kF32) {
+        const int lead =
+            (int)((reinterpret_cast<uintptr_t>(static_cast<const u32x4*>(out) + row) >> 4) & 7u);
+        const int p = (int)(chunk * kBlock) + t - lead;
+        if (p < 0 || p >= (int)vpr)
+            return;
+        const Pack<DT> xv = Pack<DT>::load_stream(x, row + p);
+        const Pack<DT> uv = Pack<DT>::load_stream(u, row + p);
+        const Pack<DT> gv = Pack<DT>::load(g, b * vpr + p);
+        gate_add8<DT>(xv, uv, gv).store_stream(out, row + p);
+    } else {
+        const uint32_t col0 = chunk * kBlock;
+        const int h = (vpr - col0 < (uint32_t)kBlock) ? (int)(vpr - col0) : kBlock;
+        if (t >= h)
+            return;
+        const int64_t c0 = row + col0;
+        using I = Interleaved<DT>;
+        const Pack<DT> xv = I::load_stream(x, c0, t, h);
+        const Pack<DT> uv = I::load_stream(u, c0, t, h);
+        const Pack<DT> gv = I::load(g, b * vpr + col0, t, h);
+        I::store_stream(gate_add8<DT>(xv, uv, gv), out, c0, t, h);
+    }
+}
+
+// Chunks per row of gate_add_bcast_kernel: every row's packs at its line
+// shift (up to 7 packs, 0 for rows that all start on a line).
+uint32_t bcast_chunks(const void* out, int64_t D, int es)
+{
+    const int64_t vpr = D / 8;
+    if (es == 4)
+        return (uint32_t)((vpr + kBlock - 1) / kBlock);
+    const bool rows_on_lines = (D * es) % 128 == 0;
+    const int64_t lead = rows_on_lines ? (int64_t)((reinterpret_cast<uintptr_t>(out) >> 4) & 7u) : 7;
+    return (uint32_t)((vpr + lead + kBlock - 1) / kBlock);
 }
 
 // Measurement variants of the bf16 broadcast-gate add (rga_gate_add_variant
@@ -269,7 +299,7 @@ hipError_t launch_typed(const void* x, const void* u, const void* g,
             stream);
     }
     uint32_t vpr = (uint32_t)(D / 8);
-    uint32_t chunks = (uint32_t)ceil_div(vpr, kBlock);
+    uint32_t chunks = bcast_chunks(out, D, es);
     void* args[] = {&x, &u, &g, &out, &L, &vpr, &chunks};
     return hipLaunchKernel(
         reinterpret_cast<const void*>(&gate_add_bcast_kernel<DT>),
@@ -290,7 +320,8 @@ bool gate_add_grid_fits(int64_t B, int64_t L, int64_t D, int gate_mode, int es,
                     : element_chunks(B * L * D * es) <= max_wg;
     if (B > 65535)  // grid y
         return false;
-    return fast ? L * ceil_div(D / 8, kBlock) <= max_wg
+    // the pack kernel's chunks per row, at most one more for the line shift
+    return fast ? L * (ceil_div(D / 8, kBlock) + 1) <= max_wg
                 : L * element_chunks(D * es) <= max_wg;
 }
 
