@@ -375,6 +375,9 @@ def main():
         ablations["schedules"] = run_schedules(dte, torch, dev, d4, cold_times, hev, stream,
                                                args.cold_reps, log)
         torch.cuda.empty_cache()
+        ablations["line_offsets"] = run_line_offsets(dte, torch, dev, cold_times,
+                                                     args.cold_reps, log)
+        torch.cuda.empty_cache()
 
     fused = {}
     if args.fused_reps > 0:
@@ -583,6 +586,42 @@ def run_occupancy(dte, torch, dev, d4, cold_times, hev, stream, reps, log):
                             "after_c4_us": round(pair, 2)}
                 log(f"occupancy {key}: cold {med:.2f} us, after c4 {pair:.2f} us")
         del x, u, g, s, t, y, xo
+    return out
+
+
+# bytes of the line-offset copies: not the flush size, so that their
+# dispatches (another grid) stay apart from the calibration copy's
+LINE_COPY_BYTES = FLUSH_BYTES - 4096
+
+
+def run_line_offsets(dte, torch, dev, cold_times, reps, log):
+    """A nontemporal copy of LINE_COPY_BYTES (rga_copy) with source and
+    destination at the same byte offset from a 128-byte line: 0 (every wave
+    instruction covers whole lines) and 16, 64, 112 (every instruction
+    straddles one line more). Cold calls in rounds over the offsets; the
+    median per offset."""
+    n = LINE_COPY_BYTES
+    src = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    assert src.data_ptr() % 128 == 0 and dst.data_ptr() % 128 == 0
+    dte.fill_(src.view(torch.int32), 0x3F803F80)
+    offs = (0, 16, 64, 112)
+    fns = {o: (lambda o=o: dte.copy_(dst[o:o + n], src[o:o + n])) for o in offs}
+    times = {o: [] for o in offs}
+    for o in offs:
+        fns[o]()
+    for _ in range(reps):
+        for o in offs:
+            times[o] += cold_times(fns[o], 1)
+    out = {}
+    for o in offs:
+        med = statistics.median(times[o])
+        gbps = 2 * n / (med * 1e-6) / 1e9
+        out[f"copy at byte offset {o}"] = {"bytes": 2 * n, "cold_us_median": round(med, 2),
+                                           "GBps": round(gbps, 1),
+                                           "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        log(f"line offset {o}: {med:.2f} us, {gbps:.0f} GB/s")
+    del src, dst
     return out
 
 
@@ -868,6 +907,12 @@ def run_variants(dte, torch, dev, cold_and_warm, log, full=False):
     rms("bf16_rms_modulate_token_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.MOD_TOKEN)
     fused("bf16_fused_token_[2,32640,4096]", 2, 32640, 4096, "bf16", dte.GATE_BCAST, dte.MOD_TOKEN)
     fused("f16_fused_[2,32640,4096]", 2, 32640, 4096, "f16", dte.GATE_BCAST, dte.MOD_ROW)
+    # rows of a multiple of 8 elements that do not start on 128-byte lines
+    # (4104: every row at another line position) and nine packs per lane (4608)
+    gate("bf16_bcast_gate_add_[1,32640,4104]", 1, 32640, 4104, "bf16", dte.GATE_BCAST)
+    rms("bf16_rms_modulate_[2,32640,4104]", 2, 32640, 4104, "bf16", dte.MOD_ROW)
+    fused("bf16_fused_[2,32640,4104]", 2, 32640, 4104, "bf16", dte.GATE_BCAST, dte.MOD_ROW)
+    rms("bf16_rms_modulate_[2,32640,4608]", 2, 32640, 4608, "bf16", dte.MOD_ROW)
     # element-wise paths: ragged D, an element offset, rows past the register limit
     gate("bf16_bcast_gate_add_ragged_[1,32640,4100]", 1, 32640, 4100, "bf16", dte.GATE_BCAST)
     gate("bf16_bcast_gate_add_offset1_[1,32640,4096]", 1, 32640, 4096, "bf16", dte.GATE_BCAST,
@@ -1124,6 +1169,8 @@ def known_launches():
             ("mix R [2,32640,4096], 1 word/lane", "stream_kernel<1, false, 1>", 2 * e4 // 16, 2 * e4),
             ("mix R [2,32640,4096], 2 words/lane", "stream_kernel<1, false, 2>", e4 // 16, 2 * e4),
             ("copy 1 GiB", "copy_kernel", FLUSH_BYTES // 16, 2 * FLUSH_BYTES),
+            ("copy 1 GiB - 4 KiB at line offsets 0/16/64/112", "copy_kernel",
+             LINE_COPY_BYTES // 16, 2 * LINE_COPY_BYTES),
             ("flush read 1 GiB", "read_kernel", 256 * 1024, FLUSH_BYTES)):
         out.append((label, k, n16 if k != "read_kernel" else n16, 1, nbytes, 0))
     for k, name in enumerate(SCHEDULES):
