@@ -596,24 +596,30 @@ def run_occupancy(dte, torch, dev, d4, cold_times, hev, stream, reps, log):
     return out
 
 
-# bytes of the line-offset copies: not the flush size, so that their
-# dispatches (another grid) stay apart from the calibration copy's
-LINE_COPY_BYTES = FLUSH_BYTES - 4096
+# bytes of the line-offset copies, one size per offset: not the flush size,
+# so that each offset's dispatches (its own grid) stay apart from the
+# calibration copy's and from the other offsets'
+LINE_OFFSETS = (0, 16, 64, 112)
+
+
+def line_copy_bytes(offset):
+    return FLUSH_BYTES - 4096 - 1024 * LINE_OFFSETS.index(offset)
 
 
 def run_line_offsets(dte, torch, dev, cold_times, reps, log):
-    """A nontemporal copy of LINE_COPY_BYTES (rga_copy) with source and
-    destination at the same byte offset from a 128-byte line: 0 (every wave
-    instruction covers whole lines) and 16, 64, 112 (every instruction
-    straddles one line more). Cold calls in rounds over the offsets; the
-    median per offset."""
-    n = LINE_COPY_BYTES
-    src = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    """A nontemporal copy of about 1 GiB (rga_copy, line_copy_bytes) with
+    source and destination at the same byte offset from a 128-byte line: 0
+    (every wave instruction covers whole lines) and 16, 64, 112 (every
+    instruction straddles one line more). Cold calls in rounds over the
+    offsets; the median per offset."""
+    n0 = FLUSH_BYTES
+    src = torch.empty(n0 + 256, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     assert src.data_ptr() % 128 == 0 and dst.data_ptr() % 128 == 0
     dte.fill_(src.view(torch.int32), 0x3F803F80)
-    offs = (0, 16, 64, 112)
-    fns = {o: (lambda o=o: dte.copy_(dst[o:o + n], src[o:o + n])) for o in offs}
+    offs = LINE_OFFSETS
+    fns = {o: (lambda o=o: dte.copy_(dst[o:o + line_copy_bytes(o)], src[o:o + line_copy_bytes(o)]))
+           for o in offs}
     times = {o: [] for o in offs}
     for o in offs:
         fns[o]()
@@ -622,6 +628,7 @@ def run_line_offsets(dte, torch, dev, cold_times, reps, log):
             times[o] += cold_times(fns[o], 1)
     out = {}
     for o in offs:
+        n = line_copy_bytes(o)
         med = statistics.median(times[o])
         gbps = 2 * n / (med * 1e-6) / 1e9
         out[f"copy at byte offset {o}"] = {"bytes": 2 * n, "cold_us_median": round(med, 2),
@@ -1180,8 +1187,14 @@ def known_launches():
             ("mix R [2,32640,4096], 1 word/lane", "stream_kernel<1, false, 1>", 2 * e4 // 16, 2 * e4),
             ("mix R [2,32640,4096], 2 words/lane", "stream_kernel<1, false, 2>", e4 // 16, 2 * e4),
             ("copy 1 GiB", "copy_kernel", FLUSH_BYTES // 16, 2 * FLUSH_BYTES),
-            ("copy 1 GiB - 4 KiB at line offsets 0/16/64/112", "copy_kernel",
-             LINE_COPY_BYTES // 16, 2 * LINE_COPY_BYTES),
+            ("copy 1 GiB at line offset 0", "copy_kernel", line_copy_bytes(0) // 16,
+             2 * line_copy_bytes(0)),
+            ("copy 1 GiB at line offset 16", "copy_kernel", line_copy_bytes(16) // 16,
+             2 * line_copy_bytes(16)),
+            ("copy 1 GiB at line offset 64", "copy_kernel", line_copy_bytes(64) // 16,
+             2 * line_copy_bytes(64)),
+            ("copy 1 GiB at line offset 112", "copy_kernel", line_copy_bytes(112) // 16,
+             2 * line_copy_bytes(112)),
             ("flush read 1 GiB", "read_kernel", 256 * 1024, FLUSH_BYTES)):
         out.append((label, k, n16 if k != "read_kernel" else n16, 1, nbytes, 0))
     for k, name in enumerate(SCHEDULES):
