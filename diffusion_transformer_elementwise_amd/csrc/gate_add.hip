@@ -83,8 +83,9 @@ __global__ __launch_bounds__(kBlock) void gate_add_full_kernel(
 // 64c - s .. 64c - s + 63, s the position of the output row's first pack in
 // its 128-byte line (0 for rows of a multiple of 64 packs in a line-aligned
 // tensor), so that each access instruction covers whole lines: on MI355X a
-// 16-byte-aligned stream whose instructions straddle lines runs 15-20 %
-// slower. The launch gives each row enough chunks for that shift.
+// 16-byte-aligned copy whose instructions each straddle one line more
+// fetched 12.5 % more from HBM and ran 10-26 % slower. The launch gives
+// each row enough chunks for that shift.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void gate_add_bcast_kernel(
     const void* x, const void* u, const void* g, void* out, int64_t L,
