@@ -265,17 +265,37 @@ __device__ __forceinline__ void load_groups(const void* p, int n, u32x4 (&g)[K],
 // The bytes of output word i inside the run [mo, end) of the window at
 // w0, as 2-byte stores (every element size here is a multiple of 2 and
 // every run boundary a multiple of the element size).
+// The widest aligned stores cover the bytes: a 2-byte store up to a 4-byte
+// boundary, a 4-byte one up to an 8-byte boundary, 8-byte ones, then what
+// is left (at most four store instructions where element by element took up
+// to seven).
 __device__ __forceinline__ void put_partial(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
                                             int64_t end)
 {
     const int64_t lo = 16 * i;
-    unsigned char* gb = reinterpret_cast<unsigned char*>(w0);
-    const int b0 = (int)((lo > mo ? lo : mo) - lo);
+    unsigned char* gb = reinterpret_cast<unsigned char*>(w0) + lo;
+    int b = (int)((lo > mo ? lo : mo) - lo);
     const int b1 = (int)((lo + 16 < end ? lo + 16 : end) - lo);
-    for (int j = b0; j < b1; j += 2) {
-        const uint32_t dw = j < 8 ? (j < 4 ? v[0] : v[1]) : (j < 12 ? v[2] : v[3]);
-        *reinterpret_cast<uint16_t*>(gb + lo + j) = (uint16_t)(dw >> (8 * (j & 2)));
+    // the dword holding byte j of the word
+    auto dw = [&](int j) { return j < 8 ? (j < 4 ? v[0] : v[1]) : (j < 12 ? v[2] : v[3]); };
+    if ((b & 2) != 0 && b < b1) {
+        *reinterpret_cast<uint16_t*>(gb + b) = (uint16_t)(dw(b) >> 16);
+        b += 2;
     }
+    if ((b & 4) != 0 && b + 4 <= b1) {
+        *reinterpret_cast<uint32_t*>(gb + b) = dw(b);
+        b += 4;
+    }
+    if (b + 8 <= b1) {
+        *reinterpret_cast<uint2*>(gb + b) = make_uint2(dw(b), dw(b + 4));
+        b += 8;
+    }
+    if (b + 4 <= b1) {
+        *reinterpret_cast<uint32_t*>(gb + b) = dw(b);
+        b += 4;
+    }
+    if (b < b1)
+        *reinterpret_cast<uint16_t*>(gb + b) = (uint16_t)dw(b);
 }
 
 // Output word i of the run [mo, end): one 16-byte store when it lies wholly
