@@ -35,6 +35,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// The calling wave's index in its workgroup, held by the whole wave in a
+// scalar register: the compiler takes threadIdx.x / 64 for a per-lane
+// value, and with it every row index, address, offset and branch derived
+// from it (vector arithmetic for each, lane masks for each branch).
+__device__ __forceinline__ int wave_in_group()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Plain 128-bit global load / store (global_load_dwordx4 / store).
 __device__ __forceinline__ u32x4 load16(const u32x4* p)
 {

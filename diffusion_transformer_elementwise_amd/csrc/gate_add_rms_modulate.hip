@@ -204,6 +204,9 @@ __device__ __forceinline__ void fused_staged_rows(
     extern __shared__ u32x4 staged[];
     const int lane = threadIdx.x & (kBlock - 1);
     const int64_t b = blockIdx.y;
+    // the wave index as a per-lane value (wave_in_group() would make it
+    // scalar): the compiler then orders this loop's loads as the library's
+    // timings were taken with
     const int64_t r0 = (int64_t)blockIdx.x * kRowWaves * R + (threadIdx.x / kBlock);
     u32x4* s_st = staged;
     u32x4* h_st = staged + (kOnePlus ? 2 : 1) * vpr;
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
     __shared__ float factor;
     constexpr int es = DT == kF32 ? 4 : 2;
     constexpr bool kTok = MOD == kModToken;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_in_group();
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
@@ -729,7 +732,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
     int64_t L, int64_t D)
 {
     extern __shared__ u32x4 staged[];
-    const int wave = threadIdx.x / kBlock;
+    const int wave = wave_in_group();
     const int64_t b = blockIdx.y;
     const int64_t r = (int64_t)blockIdx.x * kRowWaves + wave;
     const int n = (int)D;

@@ -323,7 +323,9 @@ __device__ __forceinline__ void put_word(u32x4* w0, int64_t i, const u32x4& v, i
 // s is the output window's line_lead). Whole words are stored in the slot
 // loop; the run's first word (when mo > 0) and last word (when the run does
 // not end on a word boundary) are the only partial ones and are written
-// after it.
+// after it. The phase is below 64, so word 0 is in slot 0; the last word's
+// slot is known to the whole wave, so neither is picked out lane by lane
+// in every slot.
 template <int K, bool STREAM>
 __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K], int phase = 0)
 {
@@ -334,6 +336,8 @@ __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K], i
     u32x4* w0 = aligned_down(p);
     const int end = mo + 2 * n;
     const int words = (end + 15) >> 4;
+    const int wl = words - 1;
+    const int kl = (wl + phase) >> 6;  // the slot of word wl (K: the tail below)
     u32x4 first = u32x4{0, 0, 0, 0}, last = u32x4{0, 0, 0, 0};
     dispatch_offset(mo, [&](auto off) {
         constexpr int O = decltype(off)::value;
@@ -353,18 +357,17 @@ __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K], i
                 else
                     w0[w] = v;
             }
-            if (w == 0)
+            if (k == 0)
                 first = v;
-            if (w == words - 1)
+            if (k == kl)
                 last = v;
         }
         // word 64K - s (only reached when mo > 0): the tail of the last
         // slot's lane 63 group
         if constexpr (O != 0)
-            if (words - 1 == 64 * K - phase)
+            if (kl == K)
                 last = window_o<C>(fill, u32x4{0, 0, 0, 0}, 16 - mo);
     });
-    const int wl = words - 1;
     const bool last_partial = (end & 15) != 0;
     if (lane == phase && mo != 0)
         put_partial(w0, 0, first, mo, end);

@@ -236,6 +236,8 @@ __device__ __forceinline__ void modulate_staged_row(
     extern __shared__ u32x4 staged[];
     const int lane = threadIdx.x & (kBlock - 1);
     const int64_t b = blockIdx.y;
+    // the wave index as a per-lane value, as in the fused residual update's
+    // staged kernel
     const int64_t r0 = (int64_t)blockIdx.x * kRowWaves * R + (threadIdx.x / kBlock);
     // WHOLE (D = 512 G): every lane's G packs lie in the row, no bounds at
     // all. Otherwise no branch around a load: the index is clamped into the
@@ -698,7 +700,7 @@ __global__ __launch_bounds__(kBlock * NW) void modulate_lds_kernel(
     constexpr int es = DT == kF32 ? 4 : 2;
     constexpr bool kTok = MOD == kModToken;
     constexpr int kStride = kRowStage * NW;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_in_group();
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;
@@ -798,7 +800,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kerne
     void* out, int64_t L, int64_t D)
 {
     extern __shared__ u32x4 staged[];
-    const int wave = threadIdx.x / kBlock;
+    const int wave = wave_in_group();
     const int64_t b = blockIdx.y;
     const int64_t r = (int64_t)blockIdx.x * kRowWaves + wave;
     const int n = (int)D;
