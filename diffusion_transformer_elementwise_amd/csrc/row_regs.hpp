@@ -54,36 +54,45 @@ __device__ __forceinline__ float wave_sum(float acc)
 // 1); one rotation of the 64 partials by s lanes puts partial j in lane j
 // before the xor-distance exchanges, so the sum is that of the fixed order
 // bit for bit at any phase. Elements outside the row (groups below 0 or
-// past n) are skipped; slots 1 .. whole_slots<K>() - 1 are whole at any phase
-// (a row run with K slots has more than 512 times the ladder's previous
-// entry elements) and are summed without masks, known at compile time: a
-// run-time test left a compare and a select on every element.
+// past n) add +0 instead of their term, which leaves the partial as it
+// was (a partial that starts at +0 never becomes -0), and the selection
+// is branch-free (a branch per element cost more than the terms). Slots
+// 1 .. whole_slots<K>() - 1 are whole at any phase (a row run with K slots
+// has more than 512 times the ladder's previous entry elements) and take
+// no selection, known at compile time; the others test wholeness once for
+// the wave.
 template <int K, int DT, int WHAT>
 __device__ __forceinline__ float row_sum(const u32x4 (&xv)[K], int n, float mu, int phase = 0)
 {
     constexpr int kWhole = whole_slots<K>();
     const int lane = threadIdx.x & 63;
+    auto term = [&](const Pack<DT>& p, int e) {
+        float a = p.get(e);
+        if constexpr (WHAT == 0)
+            return a;
+        if constexpr (WHAT == 2)
+            a = a - mu;
+        return a * a;
+    };
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         Pack<DT> p;
         p.v = xv[k];
         const int g = lane + 64 * k - phase;
-        const int e0 = 8 * g;
         const bool whole = (k >= 1 && k < kWhole) ||
                            (64 * k >= phase && 512 * (k + 1) - 8 * phase <= n);
+        if (whole) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (whole || (g >= 0 && e0 + e < n)) {
-                float a = p.get(e);
-                if constexpr (WHAT == 0) {
-                    acc = acc + a;
-                } else {
-                    if constexpr (WHAT == 2)
-                        a = a - mu;
-                    const float sa = a * a;
-                    acc = acc + sa;
-                }
+            for (int e = 0; e < 8; ++e)
+                acc = acc + term(p, e);
+        } else {
+            // elements of this group inside the row (none below group 0)
+            const int rem = g >= 0 ? n - 8 * g : 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = term(p, e);
+                acc = acc + (e < rem ? t : 0.0f);
             }
         }
     }
