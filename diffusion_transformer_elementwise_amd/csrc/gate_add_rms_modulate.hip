@@ -722,9 +722,11 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
 // Row modulation of 2-byte rows held in registers: kRowWaves waves per
 // workgroup, one row each. Before any row is loaded the workgroup stages
 // its batch's rows in the dynamic LDS once, as groups in planes of
-// P = ceil(D / 8) words (row_regs.hpp): wave 0 1 + scale in binary32
-// (elements 0-3 at [0, P), 4-7 at [P, 2P)) and a broadcast gate row (at
-// [3P, 4P)), wave 1 the shift row (at [2P, 3P)).
+// P = ceil(D / 8) words (row_regs.hpp): wave 0 the scale row as stored (at
+// [0, P); 1 + scale is formed per group) and a broadcast gate row (at
+// [2P, 3P)), wave 1 the shift row (at [P, 2P)). Staging the scale at its
+// 2-byte size rather than widened leaves room for 6 workgroups per CU,
+// where the widened staging allowed 4.
 template <int K, bool FULL, int DT>
 __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs_staged_kernel(
     const void* x, const void* u, const void* g, const void* scale,
@@ -738,10 +740,10 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
     const int n = (int)D;
     static_assert(kRowWaves == 2, "staged rows split over two waves");
     const int planes = (n + 7) >> 3;
-    u32x4* h_st = staged + 2 * planes;
-    u32x4* g_st = staged + 3 * planes;
+    u32x4* h_st = staged + planes;
+    u32x4* g_st = staged + 2 * planes;
     if (wave == 0) {
-        regs::stage_one_plus<K, DT>(staged, staged + planes, elem_ptr<DT>(scale, b * D), n);
+        regs::stage_row<K>(staged, elem_ptr<DT>(scale, b * D), n);
         if constexpr (!FULL)
             regs::stage_row<K>(g_st, elem_ptr<DT>(g, b * D), n);
     } else {
@@ -784,7 +786,7 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void gate_add_rms_modulate_regs
     store_run<K, true>(elem_ptr<DT>(x_out, row), n, xv, phase);
     float mu, rr;
     regs::row_factors<K, DT, regs::kRms>(xv, n, d_float, eps, &mu, &rr, phase);
-    regs::apply_store_staged<K, DT, regs::kRms>(xv, staged, staged + planes, h_st, n, mu, rr,
+    regs::apply_store_staged<K, DT, regs::kRms, false>(xv, staged, nullptr, h_st, n, mu, rr,
                                                 elem_ptr<DT>(y, row), phase);
 }
 
@@ -955,14 +957,15 @@ hipError_t launch_element(const void* x, const void* u, const void* g,
     if constexpr (DT != kF32 && MOD == kModRow) {
         const int K = pick_regs_slots(ceil_div(ceil_div(D, 8), 64));
         if (K > 0) {
-            // two rows per workgroup with 1 + scale, the shift (and a
+            // two rows per workgroup with the scale, the shift (and a
             // broadcast gate) row staged once (planes of ceil(D / 8)
             // words), occupancy capped
-            const int64_t stage = (FULL ? 3 : 4) * 16 * ceil_div(D, 8);
+            const int64_t stage = (FULL ? 2 : 3) * 16 * ceil_div(D, 8);
             return hipLaunchKernel(pick_regs_staged<FULL, DT>(K),
                                    dim3((uint32_t)ceil_div(L, kRowWaves), (uint32_t)B),
                                    dim3(kBlock * kRowWaves), args,
-                                   (size_t)row_wg_lds(2 * D, stage, kFusedRowBudget, wg_per_cu),
+                                   (size_t)row_wg_lds(2 * D, stage, kFusedElemRowBudget,
+                                                      wg_per_cu),
                                    stream);
         }
     }

@@ -60,11 +60,13 @@ inline int lds_row_waves(int64_t row_bytes)
 // that holds a row per wave streams best with few rows in flight per CU; the
 // sweeps over workgroups per CU on MI355X (the bench's occupancy ablation)
 // put the fast path's 8 KB modulation rows best at 5, the element path's
-// realigned rows at 6-8, and the fused call at 4.
+// realigned rows at 6-8, the fused call's fast path at 4 and its element
+// path at 5-6.
 constexpr int kRowWaves = 2;
-constexpr int64_t kModRowBudget = 40 * 1024;      // rms/LayerNorm modulation, fast path
-constexpr int64_t kModElemRowBudget = 48 * 1024;  // the same, element path
-constexpr int64_t kFusedRowBudget = 32 * 1024;    // residual update + modulation
+constexpr int64_t kModRowBudget = 40 * 1024;        // rms/LayerNorm modulation, fast path
+constexpr int64_t kModElemRowBudget = 48 * 1024;    // the same, element path
+constexpr int64_t kFusedRowBudget = 32 * 1024;      // residual update + modulation
+constexpr int64_t kFusedElemRowBudget = 48 * 1024;  // the same, element path
 // wg_per_cu overrides the rule for measurement (rga_measure.h): > 0 asks
 // for that many workgroups per CU, -1 for no cap (the staging alone).
 inline int64_t row_wg_lds(int64_t row_bytes, int64_t stage_bytes, int64_t row_budget,

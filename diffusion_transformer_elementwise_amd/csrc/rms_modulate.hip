@@ -807,10 +807,11 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kerne
     const int planes = (n + 7) >> 3;
     constexpr int kNorm = NORM == kNormLn ? regs::kLn : regs::kRms;
     static_assert(kRowWaves == 2, "one staged row per wave");
+    u32x4* h_st = staged + 2 * planes;
     if (wave == 0)
         regs::stage_one_plus<K, DT>(staged, staged + planes, elem_ptr<DT>(scale, b * D), n);
     else
-        regs::stage_row<K>(staged + 2 * planes, elem_ptr<DT>(shift, b * D), n);
+        regs::stage_row<K>(h_st, elem_ptr<DT>(shift, b * D), n);
     __syncthreads();
     if (r >= L)
         return;
@@ -824,8 +825,8 @@ __global__ __launch_bounds__(kBlock * kRowWaves) void modulate_regs_staged_kerne
     load_groups<K, true>(px, n, xv, phase);
     float mu, rr;
     regs::row_factors<K, DT, kNorm>(xv, n, d_float, eps, &mu, &rr, phase);
-    regs::apply_store_staged<K, DT, kNorm>(xv, staged, staged + planes, staged + 2 * planes, n,
-                                           mu, rr, elem_ptr<DT>(out, row), phase);
+    regs::apply_store_staged<K, DT, kNorm, true>(xv, staged, staged + planes, h_st, n, mu, rr,
+                                                 elem_ptr<DT>(out, row), phase);
 }
 
 template <int K, int DT, int MOD, int NORM>

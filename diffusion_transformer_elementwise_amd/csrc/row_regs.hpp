@@ -217,9 +217,11 @@ __device__ __forceinline__ void stage_one_plus(u32x4* a_lo, u32x4* a_hi, const v
     }
 }
 
-// apply_store with 1 + scale and the shift row staged in LDS
-// (stage_one_plus, stage_row): no per-row loads or realignment of them.
-template <int K, int DT, int NORM>
+// apply_store with the scale and shift rows staged in LDS: no per-row
+// loads or realignment of them. ONE_PLUS: 1 + scale staged in binary32
+// (stage_one_plus: a_lo, a_hi); otherwise the scale row as it is stored
+// (stage_row at a_lo), 1 + scale formed per group with the same rounding.
+template <int K, int DT, int NORM, bool ONE_PLUS>
 __device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* a_lo,
                                                    const u32x4* a_hi, const u32x4* h_lds, int n,
                                                    float mu, float rr, void* out, int phase = 0)
@@ -240,7 +242,13 @@ __device__ __forceinline__ void apply_store_staged(u32x4 (&xv)[K], const u32x4* 
         Pack<DT> xp, hp;
         xp.v = xv[k];
         hp.v = h_lds[i];
-        xv[k] = modulate_group<DT, NORM == kLn>(xp, mu, rr, a_lo[i], a_hi[i], hp).v;
+        if constexpr (ONE_PLUS) {
+            xv[k] = modulate_group<DT, NORM == kLn>(xp, mu, rr, a_lo[i], a_hi[i], hp).v;
+        } else {
+            u32x4 lo, hi;
+            one_plus<DT>(a_lo[i], lo, hi);
+            xv[k] = modulate_group<DT, NORM == kLn>(xp, mu, rr, lo, hi, hp).v;
+        }
     }
     store_run<K, true>(out, n, xv, phase);
 }
