@@ -1059,7 +1059,12 @@ bool rms_modulate_grid_fits(int64_t B, int64_t L, int64_t D, int es, bool fast)
     const bool regs = es == 2 && ceil_div(ceil_div(D, 8), 64) <= kRegsLadder[7];
     const bool lds = !fast && !regs && row_lds_bytes(D, es) <= kMaxRowLds;
     const int64_t wg = lds ? kBlock * lds_row_waves(D * es) : kBlock;
-    return L <= (((int64_t)1 << 32) - 1) / wg;
+    const int64_t limit = ((int64_t)1 << 32) - 1;  // work-items of one launch
+    // the staged row kernels: ceil(L / 2) workgroups of two waves (an odd
+    // L at the one-wave bound would ask for 2^32 work-items)
+    if (!lds && ceil_div(L, kRowWaves) > limit / (kBlock * kRowWaves))
+        return false;
+    return L <= limit / wg;
 }
 
 hipError_t launch_rms_modulate(const void* x, const void* scale,

@@ -445,6 +445,18 @@ def test_grid_limit_of_the_lds_staged_rows(dte):
     ts = [A + k * 64 * GB for k in range(8)]
     assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L, 100,
                                      dte.MOD_ROW, dte.DTYPE_BF16) == ok
+    # row modulation of 2-byte rows runs two rows per 128-lane workgroup:
+    # ceil(L / 2) * 128 work-items, so the largest L is 2 * floor((2^32 - 1)
+    # / 128), one below the 64-lane bound (2^32 work-items at that odd L)
+    L_pair = 2 * (((1 << 32) - 1) // 128)
+    assert L_pair + 1 == ((1 << 32) - 1) // 64
+    for D in (100, 8):  # the element path's and the fast path's staged rows
+        for L, want in ((L_pair, ok), (L_pair + 1, uns)):
+            assert dte.check_rms_modulate_ex(ts[0], ts[1], ts[2], 1e-6, ts[3], 1, L, D,
+                                             dte.MOD_ROW, dte.DTYPE_BF16) == want, (D, L)
+            assert dte.check_gate_add_rms_modulate_ex(ts[0], ts[1], ts[2], ts[3], ts[4], 1e-6,
+                                                      ts[5], ts[6], 1, L, D, dte.GATE_BCAST,
+                                                      dte.MOD_ROW, dte.DTYPE_BF16) == want, (D, L)
 
 
 def test_package_fails_loudly_without_the_library(tmp_path):
