@@ -172,6 +172,16 @@ __device__ __forceinline__ int line_lead(const void* p)
     return (int)((reinterpret_cast<uintptr_t>(p) >> 4) & 7u);
 }
 
+// Word i at w0, which every lane of the wave reads (a run's extra word),
+// through the vector memory path: at a wave-uniform index the compiler
+// would issue a scalar load instead, which reads the line through the
+// scalar cache apart from the run's vector loads of it.
+__device__ __forceinline__ u32x4 load16_uniform(const u32x4* w0, int i)
+{
+    __asm__ volatile("" : "+v"(i));
+    return load16(w0 + i);
+}
+
 // Words of a run of n >= 1 2-byte elements at p into w[0..K) and extra, at
 // a wave-uniform phase s (0..7): lane t, slot k holds window word
 // 64k + t - s, and extra (every lane) word 64K - s. With s the window's
@@ -196,7 +206,7 @@ __device__ __forceinline__ void load_run(const void* p, int n, u32x4 (&w)[K], u3
         w[k] = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
     }
     const int ie = 64 * K - phase;
-    extra = load16(w0 + (ie < count ? ie : count - 1));
+    extra = load16_uniform(w0, ie < count ? ie : count - 1);
 }
 
 // Slots of a run from which realign_in uses the run-time cut (register use;
@@ -221,7 +231,7 @@ __device__ __forceinline__ void load_run_at(const void* p, int n, int k0, u32x4 
         w[j] = STREAM ? load16_stream(w0 + ic) : load16(w0 + ic);
     }
     const int ie = 64 * (k0 + KB);
-    extra = load16(w0 + (ie < count ? ie : count - 1));
+    extra = load16_uniform(w0, ie < count ? ie : count - 1);
 }
 
 // Words -> groups, in place (m = the run's start offset).
