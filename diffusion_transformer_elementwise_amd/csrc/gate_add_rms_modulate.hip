@@ -579,7 +579,10 @@ __global__ __launch_bounds__(kBlock * NW) void gate_add_rms_modulate_lds_kernel(
     __shared__ float factor;
     constexpr int es = DT == kF32 ? 4 : 2;
     constexpr bool kTok = MOD == kModToken;
-    const int wave = wave_in_group();
+    // the wave index as a per-lane value (wave_in_group() would make it
+    // scalar): the compiler then schedules this kernel as its timings
+    // were taken with
+    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
     const int64_t row = (b * L + blockIdx.x) * D;

@@ -274,13 +274,29 @@ __device__ __forceinline__ void load_groups(const void* p, int n, u32x4 (&g)[K],
 
 // The bytes of output word i inside the run [mo, end) of the window at
 // w0, as 2-byte stores (every element size here is a multiple of 2 and
-// every run boundary a multiple of the element size).
-// The widest aligned stores cover the bytes: a 2-byte store up to a 4-byte
-// boundary, a 4-byte one up to an 8-byte boundary, 8-byte ones, then what
-// is left (at most four store instructions where element by element took up
-// to seven).
+// every run boundary a multiple of the element size): the chunked kernels'
+// edge words (few, and compact code where it is inlined at many sites).
 __device__ __forceinline__ void put_partial(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
                                             int64_t end)
+{
+    const int64_t lo = 16 * i;
+    unsigned char* gb = reinterpret_cast<unsigned char*>(w0);
+    const int b0 = (int)((lo > mo ? lo : mo) - lo);
+    const int b1 = (int)((lo + 16 < end ? lo + 16 : end) - lo);
+    for (int j = b0; j < b1; j += 2) {
+        const uint32_t dw = j < 8 ? (j < 4 ? v[0] : v[1]) : (j < 12 ? v[2] : v[3]);
+        *reinterpret_cast<uint16_t*>(gb + lo + j) = (uint16_t)(dw >> (8 * (j & 2)));
+    }
+}
+
+// The same bytes with the widest aligned stores that fit them: a 2-byte
+// store up to a 4-byte boundary, a 4-byte one up to an 8-byte boundary,
+// 8-byte ones, then what is left (at most four store instructions where two
+// bytes at a time took up to seven): the register rows' first and last
+// words, one lane each per row. (Inlined into the chunked kernels' many
+// store sites instead, it grew the 8-wave LDS row kernel by a third.)
+__device__ __forceinline__ void put_partial_wide(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
+                                                 int64_t end)
 {
     const int64_t lo = 16 * i;
     unsigned char* gb = reinterpret_cast<unsigned char*>(w0) + lo;
@@ -380,9 +396,9 @@ __device__ __forceinline__ void store_run(void* p, int n, const u32x4 (&g)[K], i
     });
     const bool last_partial = (end & 15) != 0;
     if (lane == phase && mo != 0)
-        put_partial(w0, 0, first, mo, end);
+        put_partial_wide(w0, 0, first, mo, end);
     if (last_partial && lane == ((wl + phase) & 63) && !(wl == 0 && mo != 0))
-        put_partial(w0, wl, last, mo, end);
+        put_partial_wide(w0, wl, last, mo, end);
 }
 
 // ---- Output-aligned chunks -----------------------------------------------
