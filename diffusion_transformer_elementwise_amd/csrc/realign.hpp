@@ -290,9 +290,10 @@ __device__ __forceinline__ void put_partial(u32x4* w0, int64_t i, const u32x4& v
 }
 
 // The same bytes with the widest aligned stores that fit them: a 2-byte
-// store up to a 4-byte boundary, a 4-byte one up to an 8-byte boundary,
-// 8-byte ones, then what is left (at most four store instructions where two
-// bytes at a time took up to seven): the register rows' first and last
+// store up to a 4-byte boundary, a 4-byte one up to an 8-byte boundary, an
+// 8-byte one, then what is left (at most four store instructions where two
+// bytes at a time took up to seven; they cover any run of up to 14 bytes,
+// and a partial word holds at most 14): the register rows' first and last
 // words, one lane each per row. (Inlined into the chunked kernels' many
 // store sites instead, it grew the 8-wave LDS row kernel by a third.)
 __device__ __forceinline__ void put_partial_wide(u32x4* w0, int64_t i, const u32x4& v, int64_t mo,
