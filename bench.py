@@ -45,7 +45,8 @@ Reported (one JSON line on stdout):
                inside a chain of kernels on rotating buffers
   fused        the residual update + next modulation fused into one pass
                (rga_gate_add_rms_modulate) at the [2,32640,4096] shapes,
-               against the step's own separate launches of the two kernels
+               back to back against the step's own separate launches of the
+               two kernels, and cold (each call after the 1 GiB read)
   roofline     the kernel with the largest share of the step's time, against
                the 8 TB/s HBM peak
   cpu_baseline the CPU oracle on the same workload on this host's cores
@@ -416,6 +417,16 @@ def main():
                  "separate_pair_us": round(pair, 2),
                  "separate_pair_from": "per_launch c5_bcast_gate_add_inplace + c5_rms_modulate",
                  "speedup_vs_separate": round(pair / fus, 3)}
+        if args.cold_reps > 0:
+            # the cold protocol of the step's launches (each call after the
+            # 1 GiB read), beside the back-to-back mean above
+            tc = cold_times(fn, args.cold_reps)
+            cm = statistics.median(tc)
+            fused.update({"cold_us_median": round(cm, 2),
+                          "cold_us_p10": round(float(np.percentile(tc, 10)), 2),
+                          "cold_us_p90": round(float(np.percentile(tc, 90)), 2),
+                          "cold_frac_of_hbm_peak": round(
+                              fused_bytes / (cm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
 
     # roofline of the kernel with the largest share of the step, from the
     # step's own launches (the other shapes above do not enter it)
