@@ -380,6 +380,36 @@ def test_in_place_ex(dte, dtype, D):
     _zero_ulp(to_host_typed(du), wy, dtype, "fused y over u")
 
 
+@pytest.mark.parametrize("mode", [GATE_BCAST, GATE_FULL])
+@pytest.mark.parametrize("dtype,B,L,D", [(BF16, 2, 33, 4100), (F16, 1, 17, 1003),
+                                         (BF16, 2, 9, 8191), (BF16, 1, 21, 4096)],
+                         ids=["k9", "k2-f16", "k16", "k8-offset"])
+def test_in_place_row_modulation_element_path(dte, dtype, B, L, D, mode):
+    # the element path's staged rows (row modulation: scale, shift and a
+    # broadcast gate staged per workgroup) in place: out == x for the
+    # modulation, x_out == x and y == u for the fused call. Rows of ragged D
+    # share a 16-byte word with their neighbours, each writing only its own
+    # bytes of it; "k8-offset" runs D = 4096 one element off a 16-byte
+    # boundary (the element path at every row)
+    off = 1 if D == 4096 else 0
+    say(f"[in place rows] {NAMES[dtype]} B={B} L={L} D={D} mode={mode} offset={off}")
+    x, u, g = _gate_inputs(8100 + D, B, L, D, mode, dtype)
+    s, t = _mod_inputs(8103 + D, B, L, D, MOD_ROW, dtype)
+    dx = to_dev_typed(x, dtype, offset=off)
+    dte.rga_rms_modulate_ex(dx, to_dev_typed(s, dtype, offset=off),
+                            to_dev_typed(t, dtype, offset=off), 1e-6, out=dx)
+    _zero_ulp(to_host_typed(dx), oracle.rms_modulate_ex(x, s, t, 1e-6, MOD_ROW, dtype),
+              dtype, "rms rows in place")
+    dx, du = to_dev_typed(x, dtype, offset=off), to_dev_typed(u, dtype, offset=off)
+    dte.rga_gate_add_rms_modulate_ex(dx, du, to_dev_typed(g, dtype, offset=off),
+                                     to_dev_typed(s, dtype, offset=off),
+                                     to_dev_typed(t, dtype, offset=off), 1e-6, x_out=dx, y=du,
+                                     gate_mode=mode)
+    wx, wy = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, mode, MOD_ROW, dtype)
+    _bit_exact(to_host_typed(dx), wx, dtype, "fused rows x_out in place")
+    _zero_ulp(to_host_typed(du), wy, dtype, "fused rows y over u")
+
+
 def test_ex_rejections(dte):
     x = torch.zeros(1, 2, 8, dtype=torch.float64, device="cuda")
     with pytest.raises(TypeError):
