@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from synth_inputs import CASES, GATE_BCAST, GATE_FULL, N001, N01, N02, U11, make_inputs, random_bits
+from synth_inputs import (BF16, CASES, GATE_BCAST, GATE_FULL, N001, N01, N02, U11, make_inputs,
+                          random_bits)
 from tests.exact_round import f32_to_bf16_bits
 from tests.gpu_util import first_mismatch, same_bits, say, to_dev, to_host, ulp_diff
 
@@ -119,6 +120,34 @@ def test_rms_ragged_shapes(dte, B, L, D):
     got = to_host(dte.rms_modulate(to_dev(x), to_dev(s), to_dev(t), 1e-6))
     d = _rms_check(got, want, f"{B}x{L}x{D}")
     assert d.max() == 0
+
+
+# Element-path rows that (nearly) fill their slots: the line phase is cut
+# to the room the slots leave (64 K - ceil(D / 8) groups: 0 or 1 here), so
+# rows whose line position asks for more run at a smaller phase.
+@pytest.mark.parametrize("D", [1009, 1023, 3057, 3071, 4600, 4607])
+def test_element_rows_near_slot_capacity(dte, D):
+    B, L = 2, 19
+    say(f"[element rows near capacity] B={B} L={L} D={D}")
+    seed = 9000 + D
+    x = random_bits(seed, (B, L, D), N02)
+    s = random_bits(seed + 1, (B, 1, D), N001)
+    t = random_bits(seed + 2, (B, 1, D), N001)
+    got = to_host(dte.rga_rms_modulate_ex(to_dev(x), to_dev(s), to_dev(t), 1e-6))
+    want = oracle.rms_modulate_ex(x, s, t, 1e-6, oracle.MOD_ROW, BF16)
+    d = _rms_check(got, want, f"rms {B}x{L}x{D}")
+    assert d.max() == 0
+    u = random_bits(seed + 3, (B, L, D), N01)
+    for mode in (GATE_BCAST, GATE_FULL):
+        g = random_bits(seed + 4 + mode, (B, L, D) if mode == GATE_FULL else (B, 1, D), N001)
+        want_x, want_y = oracle.gate_add_rms_modulate_ex(x, u, g, s, t, 1e-6, mode,
+                                                         oracle.MOD_ROW, BF16)
+        got_x, got_y = dte.rga_gate_add_rms_modulate_ex(to_dev(x), to_dev(u), to_dev(g),
+                                                        to_dev(s), to_dev(t), 1e-6,
+                                                        gate_mode=mode)
+        hx, hy = to_host(got_x), to_host(got_y)
+        assert same_bits(hx, want_x), first_mismatch(hx, want_x)
+        assert _rms_check(hy, want_y, f"fused {B}x{L}x{D} mode {mode}").max() == 0
 
 
 def test_gate_add_every_x_pattern_and_special_products(dte):
