@@ -39,7 +39,8 @@ def _identical(got, want, dtype, label):
 
 SHAPES = [(1, 1, 8), (2, 5, 24), (3, 7, 520), (1, 126, 2048), (2, 33, 4096), (1, 9, 8192),
           (1, 3, 1), (2, 5, 7), (3, 7, 13), (2, 9, 1001), (1, 17, 4100), (2, 3, 8200),
-          (1, 2, 16384), (1, 19, 4608), (2, 9, 4104)]
+          (1, 2, 16384), (1, 19, 4608), (2, 9, 4104), (2, 19, 1009), (1, 7, 3071),
+          (2, 5, 4607)]
 
 
 @pytest.mark.parametrize("dtype", [BF16, F16, F32], ids=NAMES.get)
